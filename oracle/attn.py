@@ -1,0 +1,68 @@
+"""Block-sparse attention (oracle; test infrastructure only).
+
+DFSAttn, Significance (block-wise execution over reordered tokens) and
+DynamicRad, section 2.2 (block-wise aggregation over a shared candidate set):
+each query block attends only to the real tokens of the key blocks in its
+list; everything else is skipped. Non-causal softmax attention with scale
+1/sqrt(D) (reading: the pages state no scale or causality); the log-sum-exp
+uses the natural logarithm.
+
+Computed in float64 as the plain two-pass formula: logits, subtract the row
+maximum, exponentiate, normalise, weight the values.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def attn_blocks(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray, perm: np.ndarray, B: int,
+                kv_idx: np.ndarray, kv_cnt: np.ndarray, scale: float | None = None,
+                rows: list | None = None):
+    """qp, kp, vp [heads, N_pad, D] float64; kv_idx [G, nb, max_kv] with G = heads or 1.
+
+    rows: optional per-head arrays of slot indices to evaluate (others are left 0).
+    Returns (op [heads, N_pad, D], lse [heads, N_pad]); pad query rows stay 0.
+    """
+    nh, n_pad, D = qp.shape
+    nb = n_pad // B
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    real = perm >= 0
+    op = np.zeros_like(qp)
+    lse = np.zeros((nh, n_pad), dtype=np.float64)
+    for h in range(nh):
+        g = h if kv_idx.shape[0] > 1 else 0
+        if rows is None:
+            want = np.nonzero(real)[0]
+        else:
+            want = np.asarray(rows[h], dtype=np.int64)
+            want = want[real[want]]
+        blocks = want // B
+        for I in np.unique(blocks):
+            qi = want[blocks == I]
+            sel = kv_idx[g, I, :kv_cnt[g, I]].astype(np.int64)
+            if sel.size == 0:
+                continue
+            keys = (sel[:, None] * B + np.arange(B)[None, :]).ravel()
+            keys = keys[real[keys]]
+            logits = (qp[h, qi] @ kp[h, keys].T) * scale
+            m = logits.max(axis=1, keepdims=True)
+            e = np.exp(logits - m)
+            l = e.sum(axis=1, keepdims=True)
+            op[h, qi] = (e @ vp[h, keys]) / l
+            lse[h, qi] = (m + np.log(l))[:, 0]
+    return op, lse
+
+
+def attn_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float | None = None):
+    """Dense softmax attention on token-major [1, N, heads, D] float64 arrays."""
+    _, N, nh, D = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.zeros_like(q)
+    for h in range(nh):
+        logits = (q[0, :, h] @ k[0, :, h].T) * scale
+        m = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - m)
+        out[0, :, h] = (e @ v[0, :, h]) / e.sum(axis=1, keepdims=True)
+    return out

@@ -1,0 +1,68 @@
+"""Token order plan (oracle; test infrastructure only).
+
+A plan maps slots of the reordered, padded sequence to original tokens:
+``perm[i]`` is the row-major token index n = (t*H + y)*W + x held by slot i,
+or -1 for a pad slot. Blocks are runs of B consecutive slots
+(DFSAttn, Methodology, designs 1-2: blocks are contiguous runs of the
+reordered 1D sequence); ``blk_len[I]`` counts the real tokens of block I.
+
+Orders:
+* "row": row-major flattening, the baseline the pages compare against
+  (DFSAttn, Experimental results, ablations).
+* "hilbert": in-grid cells sorted by their index on the enclosing
+  (2**b)**3 Hilbert cube; out-of-grid cells are skipped. Pads go at the tail.
+* "frame": frame-major; each frame's H*W tokens in row-major order, padded up
+  to whole tiles of B so no tile straddles two frames (LVSA, section 2: the
+  attention unit is the frame).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .hilbert import hilbert_index, hilbert_order_bits
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def plan(T: int, H: int, W: int, order: str, B: int):
+    """Return (perm int64[N_pad], blk_len int64[nb])."""
+    T, H, W, B = int(T), int(H), int(W), int(B)
+    if min(T, H, W, B) < 1:
+        raise ValueError("empty grid or block")
+    N = T * H * W
+    if order == "row":
+        n_pad = _ceil_div(N, B) * B
+        perm = np.full(n_pad, -1, dtype=np.int64)
+        perm[:N] = np.arange(N)
+    elif order == "hilbert":
+        b = hilbert_order_bits(T, H, W)
+        t, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+        h = hilbert_index(t.ravel(), y.ravel(), x.ravel(), b)
+        # cells were enumerated in row-major order, so the argsort is the
+        # list of row-major token indices in curve order (h is unique).
+        cells = np.argsort(h, kind="stable")
+        n_pad = _ceil_div(N, B) * B
+        perm = np.full(n_pad, -1, dtype=np.int64)
+        perm[:N] = cells
+    elif order == "frame":
+        P = H * W
+        tiles = _ceil_div(P, B)
+        per = tiles * B
+        perm = np.full(T * per, -1, dtype=np.int64)
+        for f in range(T):
+            perm[f * per: f * per + P] = np.arange(f * P, (f + 1) * P)
+    else:
+        raise ValueError(f"unknown order {order!r}")
+    nb = perm.size // B
+    blk_len = (perm.reshape(nb, B) >= 0).sum(axis=1).astype(np.int64)
+    return perm, blk_len
+
+
+def inverse_perm(perm: np.ndarray, N: int) -> np.ndarray:
+    """slot of each original token (inverse of the plan on real tokens)."""
+    inv = np.full(int(N), -1, dtype=np.int64)
+    idx = np.nonzero(perm >= 0)[0]
+    inv[perm[idx]] = idx
+    return inv

@@ -1,0 +1,112 @@
+"""Pins for the oracle's block-sparse attention (CPU only).
+
+Pinned against: torch's float64 scaled_dot_product_attention when every
+block is kept (a special case that must reduce to dense attention),
+logsumexp, masking invariants (keys outside the list and pad slots cannot
+matter), constant values, and row-subset consistency.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+
+def _all_blocks(nh, nb):
+    kv_idx = np.broadcast_to(np.arange(nb, dtype=np.int32), (nh, nb, nb)).copy()
+    return kv_idx, np.full((nh, nb), nb, dtype=np.int32)
+
+
+@pytest.mark.parametrize("idx", [1, 2])
+def test_full_keep_equals_dense_sdpa(idx):
+    w = wl.get(idx)
+    q, k, v = wl.make_qkv(w, 0)
+    perm, _ = oracle.plan(w.T, w.H, w.W, w.order, w.B)
+    nb = perm.size // w.B
+    qp, kp, vp = (oracle.gather(x, perm) for x in (q, k, v))
+    op, lse = oracle.attn_blocks(qp, kp, vp, perm, w.B, *_all_blocks(w.heads, nb))
+    o = oracle.scatter(op, perm, w.N)
+    qt, kt, vt = (x.double().permute(0, 2, 1, 3) for x in (q, k, v))    # [1, heads, N, D]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).permute(0, 2, 1, 3).numpy()
+    np.testing.assert_allclose(o, ref, rtol=1e-10, atol=1e-12)
+    logits = torch.einsum("bhnd,bhmd->bhnm", qt, kt) / np.sqrt(w.D)
+    ref_lse = torch.logsumexp(logits, dim=-1)[0].numpy()        # [heads, N]
+    inv = oracle.inverse_perm(perm, w.N)
+    np.testing.assert_allclose(lse[:, inv], ref_lse, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(o, oracle.attn_dense(*(x.double().numpy() for x in (q, k, v))),
+                               rtol=1e-10, atol=1e-12)
+
+
+def _random_case(seed=9, N=100, B=16, D=8, nh=2):
+    rng = np.random.default_rng(seed)
+    perm, _ = oracle.plan(1, 1, N, "row", B)
+    xs = [oracle.gather(rng.standard_normal((1, N, nh, D)), perm) for _ in range(3)]
+    nb = perm.size // B
+    sel = np.stack([np.stack([np.sort(rng.choice(nb, 3, replace=False)) for _ in range(nb)])
+                    for _ in range(nh)]).astype(np.int32)
+    cnt = np.full((nh, nb), 3, dtype=np.int32)
+    return perm, xs, sel, cnt, B
+
+
+def test_keys_outside_the_list_do_not_matter():
+    perm, (qp, kp, vp), sel, cnt, B = _random_case()
+    op, lse = oracle.attn_blocks(qp, kp, vp, perm, B, sel, cnt)
+    nb = sel.shape[1]
+    rng = np.random.default_rng(10)
+    kp2, vp2 = kp.copy(), vp.copy()
+    for h in range(sel.shape[0]):
+        I = 2
+        out = [J for J in range(nb) if J not in sel[h, I]]
+        for J in out:
+            kp2[h, J * B:(J + 1) * B] += rng.standard_normal((B, kp.shape[2])) * 5
+            vp2[h, J * B:(J + 1) * B] += rng.standard_normal((B, kp.shape[2])) * 5
+        op2, _ = oracle.attn_blocks(qp, kp2, vp2, perm, B, sel, cnt)
+        np.testing.assert_array_equal(op2[h, I * B:(I + 1) * B], op[h, I * B:(I + 1) * B])
+
+
+def test_pad_slots_are_ignored():
+    perm, (qp, kp, vp), sel, cnt, B = _random_case()
+    op, lse = oracle.attn_blocks(qp, kp, vp, perm, B, sel, cnt)
+    kp2, vp2 = kp.copy(), vp.copy()
+    kp2[:, perm < 0] = 100.0
+    vp2[:, perm < 0] = -7.0
+    op2, lse2 = oracle.attn_blocks(qp, kp2, vp2, perm, B, sel, cnt)
+    np.testing.assert_array_equal(op2, op)
+    np.testing.assert_array_equal(lse2, lse)
+    assert np.all(op[:, perm < 0] == 0)
+
+
+def test_constant_values_pass_through():
+    perm, (qp, kp, vp), sel, cnt, B = _random_case()
+    vconst = np.zeros_like(vp)
+    vconst[:, perm >= 0] = np.arange(vp.shape[2])[None, None, :] - 3.0
+    op, _ = oracle.attn_blocks(qp, kp, vconst, perm, B, sel, cnt)
+    np.testing.assert_allclose(op[:, perm >= 0], vconst[:, perm >= 0], rtol=1e-14, atol=1e-14)
+
+
+def test_row_subset_matches_full_evaluation():
+    perm, (qp, kp, vp), sel, cnt, B = _random_case()
+    op, lse = oracle.attn_blocks(qp, kp, vp, perm, B, sel, cnt)
+    rows = [np.array([0, 5, 17, 99]), np.array([3, 50])]
+    op2, lse2 = oracle.attn_blocks(qp, kp, vp, perm, B, sel, cnt, rows=rows)
+    for h, r in enumerate(rows):
+        # same formula; only the BLAS blocking of the products differs
+        np.testing.assert_allclose(op2[h, r], op[h, r], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(lse2[h, r], lse[h, r], rtol=1e-13, atol=1e-15)
+
+
+def test_cached_mask_step_uses_step0_lists():
+    """DFSAttn, Methodology, design 3: a cached mask is reused while attention
+    is recomputed on the new step's inputs."""
+    w = wl.get(2)
+    q0, k0, v0 = wl.make_qkv(w, 0)
+    q1, k1, v1 = wl.make_qkv(w, 1)
+    r0 = oracle.run_layer(w.T, w.H, w.W, w.order, w.B, q0, k0, v0, select="topk", s=w.s, k_top=8)
+    r1 = oracle.run_layer(w.T, w.H, w.W, w.order, w.B, q1, k1, v1, select="topk", s=w.s, k_top=8,
+                          mask=(r0["kv_idx"], r0["kv_cnt"]))
+    perm = r0["perm"]
+    qp, kp, vp = (oracle.gather(x, perm) for x in (q1, k1, v1))
+    op, _ = oracle.attn_blocks(qp, kp, vp, perm, w.B, r0["kv_idx"], r0["kv_cnt"])
+    np.testing.assert_array_equal(r1["op"], op)
+    assert r1["S"] is None

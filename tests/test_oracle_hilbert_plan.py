@@ -1,0 +1,178 @@
+"""Pins for the oracle's Hilbert index, plans and gather/scatter (CPU only).
+
+The pins come from the mathematics of Hilbert curves and from the plan's
+definition, not from the oracle itself: Gray-code base case, unit steps,
+octant recursion, endpoints, bijection, and brute-force filtering.
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+
+def _cube_order(b):
+    S = 1 << b
+    cells = np.array(list(itertools.product(range(S), repeat=3)), dtype=np.int64)
+    h = oracle.hilbert_index(cells[:, 0], cells[:, 1], cells[:, 2], b)
+    return cells, h
+
+
+def test_order1_is_gray_code(golden_dir):
+    rows = []
+    with open(os.path.join(golden_dir, "hilbert_order1.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                p = line.split()
+                rows.append((int(p[0]), tuple(int(c) for c in p[2:5])))
+    cells, h = _cube_order(1)
+    for i, cell in rows:
+        got = tuple(cells[np.nonzero(h == i)[0][0]])
+        assert got == cell
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5])
+def test_cube_bijection_and_unit_steps(b):
+    cells, h = _cube_order(b)
+    assert sorted(h.tolist()) == list(range(8 ** b))
+    path = cells[np.argsort(h)]
+    step = np.abs(np.diff(path, axis=0)).sum(axis=1)
+    assert np.all(step == 1), "every step of a Hilbert curve moves to a face neighbour"
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_octant_recursion(b):
+    """Every aligned run of 8**k consecutive indices fills one aligned cube of
+    side 2**k (the self-similarity that separates a Hilbert curve from other
+    unit-step orders such as a boustrophedon scan)."""
+    cells, h = _cube_order(b)
+    path = cells[np.argsort(h)]
+    for k in range(1, b):
+        run = 8 ** k
+        side = 1 << k
+        for r in range(0, 8 ** b, run):
+            chunk = path[r:r + run]
+            lo = chunk.min(axis=0)
+            assert np.all(lo % side == 0)
+            assert np.all(chunk.max(axis=0) - lo == side - 1)
+            assert len({tuple(c) for c in chunk}) == run
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5])
+def test_endpoints(b):
+    cells, h = _cube_order(b)
+    path = cells[np.argsort(h)]
+    assert tuple(path[0]) == (0, 0, 0)
+    # the curve ends on the corner adjacent to the start along axis 0
+    assert tuple(path[-1]) == ((1 << b) - 1, 0, 0)
+
+
+def test_order_bits():
+    assert oracle.hilbert_order_bits(1, 1, 1) == 1
+    assert oracle.hilbert_order_bits(8, 16, 16) == 4
+    assert oracle.hilbert_order_bits(21, 30, 52) == 6
+    assert oracle.hilbert_order_bits(33, 45, 80) == 7
+
+
+def _brute_filtered_order(T, H, W):
+    b = oracle.hilbert_order_bits(T, H, W)
+    cells, h = _cube_order(b)
+    out = []
+    for c in cells[np.argsort(h)]:
+        t, y, x = (int(v) for v in c)
+        if t < T and y < H and x < W:
+            out.append((t * H + y) * W + x)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("shape", [(3, 5, 7), (2, 3, 4), (5, 1, 6), (1, 1, 1), (4, 8, 8)])
+def test_hilbert_plan_skips_out_of_grid_cells(shape):
+    T, H, W = shape
+    B = 4
+    perm, blk_len = oracle.plan(T, H, W, "hilbert", B)
+    N = T * H * W
+    assert np.array_equal(perm[:N], _brute_filtered_order(T, H, W))
+    assert np.all(perm[N:] == -1)
+    assert perm.size % B == 0 and perm.size - N < B
+    assert blk_len.sum() == N
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_plan_is_bijection(idx):
+    w = wl.get(idx)
+    perm, blk_len = oracle.plan(w.T, w.H, w.W, w.order, w.B)
+    real = perm[perm >= 0]
+    assert np.array_equal(np.sort(real), np.arange(w.N))
+    assert blk_len.sum() == w.N
+    assert np.all(blk_len >= 1) and np.all(blk_len <= w.B)
+    nb = perm.size // w.B
+    assert np.array_equal(blk_len, (perm.reshape(nb, w.B) >= 0).sum(1))
+
+
+def test_workload_block_counts():
+    expect = {1: (4, 64), 2: (32, 64), 3: (256, 120), 4: (793, 24), 5: (929, 16)}
+    for idx, (nb, last) in expect.items():
+        w = wl.get(idx)
+        perm, blk_len = oracle.plan(w.T, w.H, w.W, w.order, w.B)
+        assert perm.size // w.B == nb
+        assert blk_len[-1] == last
+
+
+def test_row_and_frame_plans():
+    perm, blk = oracle.plan(3, 5, 7, "row", 16)
+    assert np.array_equal(perm[:105], np.arange(105)) and np.all(perm[105:] == -1)
+    perm, blk = oracle.plan(3, 5, 7, "frame", 16)   # 35 tokens -> 3 tiles per frame
+    assert perm.size == 3 * 48
+    for f in range(3):
+        tile = perm[f * 48:(f + 1) * 48]
+        assert np.array_equal(tile[:35], np.arange(f * 35, f * 35 + 35))
+        assert np.all(tile[35:] == -1)
+    assert blk.tolist() == [16, 16, 3] * 3
+
+
+def test_cfg2_grid_is_first_half_of_cube_curve():
+    """The order-4 curve spends its first half in the half cube t < 8 (its
+    first four octants share X0 = 0), so the 8x16x16 grid is a single
+    unbroken stretch of the curve with unit steps throughout."""
+    w = wl.get(2)
+    perm, _ = oracle.plan(w.T, w.H, w.W, "hilbert", w.B)
+    t, r = np.divmod(perm, w.H * w.W)
+    y, x = np.divmod(r, w.W)
+    step = np.abs(np.diff(t)) + np.abs(np.diff(y)) + np.abs(np.diff(x))
+    assert np.all(step == 1)
+
+
+def test_hilbert_blocks_are_more_compact_than_raster():
+    """DFSAttn, Methodology, design 1: the reorder keeps spatiotemporal
+    neighbourhoods together inside a block; measured as the mean volume of
+    each block's bounding box on the Wan 480p latent grid."""
+    w = wl.get(3)
+
+    def mean_box(order):
+        perm, _ = oracle.plan(w.T, w.H, w.W, order, w.B)
+        vols = []
+        for I in range(perm.size // w.B):
+            p = perm[I * w.B:(I + 1) * w.B]
+            p = p[p >= 0]
+            t, r = np.divmod(p, w.H * w.W)
+            y, x = np.divmod(r, w.W)
+            vols.append((np.ptp(t) + 1) * (np.ptp(y) + 1) * (np.ptp(x) + 1))
+        return float(np.mean(vols))
+
+    assert mean_box("hilbert") * 2 < mean_box("row")
+
+
+@pytest.mark.parametrize("idx", [1, 2])
+def test_gather_scatter_roundtrip(idx):
+    w = wl.get(idx)
+    q, _, _ = wl.make_qkv(w, 0)
+    perm, _ = oracle.plan(w.T, w.H, w.W, w.order, w.B)
+    xp = oracle.gather(q, perm)
+    assert np.all(xp[:, perm < 0, :] == 0)
+    back = oracle.scatter(xp, perm, w.N)
+    assert np.array_equal(back, q.double().numpy())
+    inv = oracle.inverse_perm(perm, w.N)
+    assert np.array_equal(perm[inv], np.arange(w.N))
