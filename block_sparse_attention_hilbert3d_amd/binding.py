@@ -1,0 +1,215 @@
+"""ctypes binding of libhsa.so: argument marshalling only.
+
+Each function has the name of the C entry point it wraps, takes torch device
+tensors, allocates outputs and workspaces with torch (device memory and the
+current stream are all torch provides here), and calls the library on the
+current HIP stream. Every step of the computation runs in the HIP kernels;
+there is no CPU path. A missing library or a failing call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhsa.so")
+
+HSA_F32, HSA_BF16 = 0, 1
+ORDERS = {"row": 0, "hilbert": 1, "frame": 2}
+AGGS = {"mass": 0, "max": 1}
+MODES = {"topk": 0, "thresh_global": 1, "lvsa": 2}
+
+_c_i32, _c_i64, _c_f32, _c_sz, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+
+class SelectParams(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("k", ctypes.c_int32), ("tau", ctypes.c_double),
+                ("budget_ratio", ctypes.c_double), ("frames", ctypes.c_int32),
+                ("tiles_per_frame", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("T_per", ctypes.c_int32), ("step", ctypes.c_int32)]
+
+
+_SIGS = {
+    "hsa_abi_version": (ctypes.c_int, []),
+    "hsa_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "hsa_last_error": (ctypes.c_char_p, []),
+    "hsa_plan_size": (ctypes.c_int, [_c_i32] * 5 + [ctypes.POINTER(_c_i32)] * 2),
+    "hsa_plan_ws_size": (_c_sz, [_c_i32] * 4),
+    "hsa_plan": (ctypes.c_int, [_c_i32] * 5 + [_p, _p, _p, _c_sz, _p]),
+    "hsa_perm": (ctypes.c_int, [_c_i32, _p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _p]),
+    "hsa_score_ws_size": (_c_sz, [_c_i32] * 4),
+    "hsa_score": (ctypes.c_int, [_p, _p, _p] + [_c_i32] * 7 + [_c_f32, _p, _p, _c_sz, _p]),
+    "hsa_select_ws_size": (_c_sz, [_c_i32, _c_i32, ctypes.POINTER(SelectParams)]),
+    "hsa_select": (ctypes.c_int, [_p, _c_i32, _c_i32, ctypes.POINTER(SelectParams), _p, _p, _c_i32, _p, _c_sz, _p]),
+    "hsa_attn": (ctypes.c_int, [_p] * 8 + [_c_i32] * 7 + [_c_f32, _p]),
+    "hsa_unperm": (ctypes.c_int, [_p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _p]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libhsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_attention_hilbert3d_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+class HsaError(RuntimeError):
+    pass
+
+
+def _check(status: int, name: str):
+    if status != 0:
+        L = lib()
+        raise HsaError(f"{name}: {L.hsa_status_str(status).decode()} "
+                       f"({L.hsa_last_error().decode()})")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HSA_BF16
+    if t.dtype == torch.float32:
+        return HSA_F32
+    raise HsaError(f"unsupported dtype {t.dtype}")
+
+
+def _need_device(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise HsaError("tensors must be contiguous device tensors")
+
+
+def hsa_plan_size(T: int, H: int, W: int, order: str, B: int):
+    n_pad, nb = _c_i32(), _c_i32()
+    _check(lib().hsa_plan_size(T, H, W, ORDERS[order], B, ctypes.byref(n_pad), ctypes.byref(nb)),
+           "hsa_plan_size")
+    return n_pad.value, nb.value
+
+
+def hsa_plan(T: int, H: int, W: int, order: str, B: int, device="cuda"):
+    """-> (perm int32[n_pad], blk_len int32[nb]) on the device."""
+    n_pad, nb = hsa_plan_size(T, H, W, order, B)
+    perm = torch.empty(n_pad, dtype=torch.int32, device=device)
+    blk_len = torch.empty(nb, dtype=torch.int32, device=device)
+    ws_n = lib().hsa_plan_ws_size(T, H, W, ORDERS[order])
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=device)
+    _check(lib().hsa_plan(T, H, W, ORDERS[order], B, _ptr(perm), _ptr(blk_len), _ptr(ws), ws_n,
+                          _stream()), "hsa_plan")
+    return perm, blk_len
+
+
+def hsa_perm(xs, perm: torch.Tensor, n_pad: int, outs=None):
+    """xs: list of [1, N, nh, D] (token stride may exceed nh*D) -> list of [nh, n_pad, D]."""
+    xs = list(xs)
+    x0 = xs[0]
+    _, N, nh, D = x0.shape
+    for x in xs:
+        if x.shape != x0.shape or x.dtype != x0.dtype or not x.is_cuda:
+            raise HsaError("hsa_perm: tensors must share shape, dtype and device")
+        if x.stride(3) != 1 or x.stride(2) != D:
+            raise HsaError("hsa_perm: heads and head dim must be contiguous")
+        if x.stride(1) != x0.stride(1):
+            raise HsaError("hsa_perm: tensors must share the token stride")
+    _need_device(perm)
+    if outs is None:
+        outs = [torch.empty((nh, n_pad, D), dtype=x0.dtype, device=x0.device) for _ in xs]
+    src = (ctypes.c_void_p * len(xs))(*[x.data_ptr() for x in xs])
+    dst = (ctypes.c_void_p * len(xs))(*[y.data_ptr() for y in outs])
+    _check(lib().hsa_perm(len(xs), src, dst, _ptr(perm), N, n_pad, nh, D, x0.stride(1),
+                          _dtype_code(x0), _stream()), "hsa_perm")
+    return outs
+
+
+def hsa_score(qp, kp, blk_len, B: int, s: int, agg: str = "mass", scale: float | None = None,
+              out=None, ws=None):
+    """qp, kp [nh, n_pad, D] -> S float32 [nh, nb, nb]."""
+    _need_device(qp, kp, blk_len)
+    nh, n_pad, D = qp.shape
+    nb = n_pad // B
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty((nh, nb, nb), dtype=torch.float32, device=qp.device)
+    ws_n = lib().hsa_score_ws_size(nh, n_pad, s, D)
+    if ws is None:
+        ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=qp.device)
+    _check(lib().hsa_score(_ptr(qp), _ptr(kp), _ptr(blk_len), nh, nb, B, s, D, _dtype_code(qp),
+                           AGGS[agg], scale, _ptr(out), _ptr(ws), ws.numel(), _stream()),
+           "hsa_score")
+    return out
+
+
+def make_params(mode: str, k=0, tau=0.0, budget_ratio=0.0, frames=0, tiles_per_frame=0, C=0,
+                T_per=1, step=0) -> SelectParams:
+    return SelectParams(MODES[mode], int(k), float(tau), float(budget_ratio), int(frames),
+                        int(tiles_per_frame), int(C), int(T_per), int(step))
+
+
+def hsa_select(S, nh: int, nb: int, params: SelectParams, max_kv: int, device="cuda",
+               outs=None, ws=None):
+    """-> (kv_idx int32 [G, nb, max_kv], kv_cnt int32 [G, nb]); G = 1 for LVSA."""
+    if S is not None:
+        _need_device(S)
+        device = S.device
+    G = 1 if params.mode == MODES["lvsa"] else nh
+    if outs is None:
+        outs = (torch.empty((G, nb, max_kv), dtype=torch.int32, device=device),
+                torch.empty((G, nb), dtype=torch.int32, device=device))
+    kv_idx, kv_cnt = outs
+    ws_n = lib().hsa_select_ws_size(nh, nb, ctypes.byref(params))
+    if ws is None:
+        ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=device)
+    _check(lib().hsa_select(_ptr(S), nh, nb, ctypes.byref(params), _ptr(kv_idx), _ptr(kv_cnt),
+                            max_kv, _ptr(ws), ws.numel(), _stream()), "hsa_select")
+    return kv_idx, kv_cnt
+
+
+def hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B: int, scale: float | None = None,
+             want_lse: bool = True, out=None, lse=None):
+    """-> (op [nh, n_pad, D] in the input dtype, lse float32 [nh, n_pad] or None)."""
+    _need_device(qp, kp, vp, blk_len, kv_idx, kv_cnt)
+    nh, n_pad, D = qp.shape
+    nb = n_pad // B
+    shared = 1 if kv_idx.shape[0] == 1 and nh > 1 else 0
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(qp)
+    if want_lse and lse is None:
+        lse = torch.empty((nh, n_pad), dtype=torch.float32, device=qp.device)
+    _check(lib().hsa_attn(_ptr(qp), _ptr(kp), _ptr(vp), _ptr(out), _ptr(lse if want_lse else None),
+                          _ptr(blk_len), _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], shared,
+                          nh, nb, B, D, _dtype_code(qp), scale, _stream()), "hsa_attn")
+    return out, (lse if want_lse else None)
+
+
+def hsa_unperm(op, perm, N: int, out=None):
+    """op [nh, n_pad, D] -> o [1, N, nh, D]."""
+    _need_device(op, perm)
+    nh, n_pad, D = op.shape
+    if out is None:
+        out = torch.empty((1, N, nh, D), dtype=op.dtype, device=op.device)
+    if out.stride(3) != 1 or out.stride(2) != D:
+        raise HsaError("hsa_unperm: heads and head dim of the output must be contiguous")
+    _check(lib().hsa_unperm(_ptr(op), _ptr(out), _ptr(perm), N, n_pad, nh, D, out.stride(1),
+                            _dtype_code(op), _stream()), "hsa_unperm")
+    return out

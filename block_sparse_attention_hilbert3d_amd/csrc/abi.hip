@@ -1,0 +1,266 @@
+// C ABI: argument validation (before any launch) and dispatch to the kernels.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "common.h"
+
+namespace hsa_host {
+
+static thread_local std::string g_last_error;
+
+hsa_status_t fail(hsa_status_t code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+hsa_status_t check_launch(const char *what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(HSA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return HSA_OK;
+}
+
+// Defined next to their kernels.
+size_t plan_hilbert_groups(int T, int H, int W, int &bits, uint32_t &cube);
+hsa_status_t launch_plan(int T, int H, int W, int order, int B, int n_pad, int nb, int32_t *perm,
+                         int32_t *blk_len, void *ws, hipStream_t stream);
+hsa_status_t launch_perm(int n, const void *const *xs, void *const *xps, const int32_t *perm,
+                         int n_pad, int nh, int D, int64_t tok_stride, int esize,
+                         hipStream_t stream);
+hsa_status_t launch_unperm(const void *op, void *o, const int32_t *perm, int n_pad, int nh, int D,
+                           int64_t tok_stride, int esize, hipStream_t stream);
+size_t score_ws_bytes(int nh, int n_pad, int s, int D);
+hsa_status_t launch_score(const void *qp, const void *kp, const int32_t *blk_len, int nh, int nb,
+                          int B, int s, int D, int dtype, int agg, float scale, float *S, void *ws,
+                          hipStream_t stream);
+size_t select_ws_bytes(int nh, int nb, int mode);
+hsa_status_t launch_select(const float *S, int nh, int nb, const hsa_select_params_t *p,
+                           int32_t *kv_idx, int32_t *kv_cnt, int max_kv, void *ws,
+                           hipStream_t stream);
+hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *op, float *lse,
+                         const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
+                         int max_kv, int kv_shared, int nh, int nb, int B, int D, int dtype,
+                         float scale, hipStream_t stream);
+
+static int esize_of(int dtype) { return dtype == HSA_BF16 ? 2 : 4; }
+
+static hsa_status_t check_dtype(int dtype) {
+  if (dtype != HSA_F32 && dtype != HSA_BF16) return fail(HSA_ERR_BAD_DTYPE, "dtype %d is not HSA_F32 or HSA_BF16", dtype);
+  return HSA_OK;
+}
+
+static hsa_status_t check_D(int D) {
+  if (D != 64 && D != 128) return fail(HSA_ERR_UNSUPPORTED, "head dim %d not in {64, 128}", D);
+  return HSA_OK;
+}
+
+static hsa_status_t check_B(int B) {
+  if (B != 64 && B != 128) return fail(HSA_ERR_UNSUPPORTED, "block size %d not in {64, 128}", B);
+  return HSA_OK;
+}
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static hsa_status_t plan_size(int T, int H, int W, int order, int B, int32_t *n_pad, int32_t *nb) {
+  if (T < 1 || H < 1 || W < 1 || T > 1024 || H > 1024 || W > 1024)
+    return fail(HSA_ERR_BAD_SHAPE, "grid %dx%dx%d: each side must be in 1..1024", T, H, W);
+  if (B < 1 || B > 4096) return fail(HSA_ERR_BAD_SHAPE, "block size %d out of range", B);
+  const int64_t N = static_cast<int64_t>(T) * H * W;
+  int64_t np;
+  if (order == HSA_ORDER_ROW || order == HSA_ORDER_HILBERT3D) {
+    np = (N + B - 1) / B * B;
+  } else if (order == HSA_ORDER_FRAME) {
+    np = static_cast<int64_t>(T) * ((static_cast<int64_t>(H) * W + B - 1) / B) * B;
+  } else {
+    return fail(HSA_ERR_BAD_ARG, "unknown order %d", order);
+  }
+  if (np >= (1ll << 31) - 1) return fail(HSA_ERR_BAD_SHAPE, "padded length %lld too large", static_cast<long long>(np));
+  *n_pad = static_cast<int32_t>(np);
+  *nb = static_cast<int32_t>(np / B);
+  return HSA_OK;
+}
+
+}  // namespace hsa_host
+
+using namespace hsa_host;
+
+extern "C" {
+
+int hsa_abi_version(void) { return HSA_ABI_VERSION; }
+
+const char *hsa_status_str(hsa_status_t s) {
+  switch (s) {
+    case HSA_OK: return "ok";
+    case HSA_ERR_NULL_PTR: return "null pointer";
+    case HSA_ERR_BAD_SHAPE: return "bad shape";
+    case HSA_ERR_BAD_DTYPE: return "bad dtype";
+    case HSA_ERR_UNSUPPORTED: return "unsupported";
+    case HSA_ERR_WORKSPACE: return "workspace too small";
+    case HSA_ERR_BAD_ARG: return "bad argument";
+    case HSA_ERR_HIP: return "hip error";
+  }
+  return "unknown status";
+}
+
+const char *hsa_last_error(void) { return g_last_error.c_str(); }
+
+hsa_status_t hsa_plan_size(int32_t T, int32_t H, int32_t W, int32_t order, int32_t B,
+                           int32_t *n_pad, int32_t *nb) {
+  if (!n_pad || !nb) return fail(HSA_ERR_NULL_PTR, "hsa_plan_size: null output");
+  g_last_error.clear();
+  return plan_size(T, H, W, order, B, n_pad, nb);
+}
+
+size_t hsa_plan_ws_size(int32_t T, int32_t H, int32_t W, int32_t order) {
+  if (order != HSA_ORDER_HILBERT3D || T < 1 || H < 1 || W < 1 || T > 1024 || H > 1024 || W > 1024) return 0;
+  int bits;
+  uint32_t cube;
+  return plan_hilbert_groups(T, H, W, bits, cube) * sizeof(int32_t);
+}
+
+hsa_status_t hsa_plan(int32_t T, int32_t H, int32_t W, int32_t order, int32_t B, int32_t *perm,
+                      int32_t *blk_len, void *ws, size_t ws_bytes, hsa_stream_t stream) {
+  g_last_error.clear();
+  if (!perm || !blk_len) return fail(HSA_ERR_NULL_PTR, "hsa_plan: perm and blk_len are required");
+  int32_t n_pad, nb;
+  hsa_status_t st = plan_size(T, H, W, order, B, &n_pad, &nb);
+  if (st != HSA_OK) return st;
+  const size_t need = hsa_plan_ws_size(T, H, W, order);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(HSA_ERR_WORKSPACE, "hsa_plan: workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+  return launch_plan(T, H, W, order, B, n_pad, nb, perm, blk_len, ws, static_cast<hipStream_t>(stream));
+}
+
+hsa_status_t hsa_perm(int32_t n_tensors, const void *const *xs, void *const *xps,
+                      const int32_t *perm, int32_t N, int32_t n_pad, int32_t nh, int32_t D,
+                      int64_t tok_stride, int32_t dtype, hsa_stream_t stream) {
+  g_last_error.clear();
+  if (n_tensors < 1 || n_tensors > 3) return fail(HSA_ERR_BAD_ARG, "hsa_perm: n_tensors %d not in 1..3", n_tensors);
+  if (!xs || !xps || !perm) return fail(HSA_ERR_NULL_PTR, "hsa_perm: null pointer array or perm");
+  for (int i = 0; i < n_tensors; ++i)
+    if (!xs[i] || !xps[i]) return fail(HSA_ERR_NULL_PTR, "hsa_perm: tensor %d is null", i);
+  hsa_status_t st;
+  if ((st = check_dtype(dtype)) != HSA_OK || (st = check_D(D)) != HSA_OK) return st;
+  if (N < 1 || n_pad < N || nh < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_perm: N=%d n_pad=%d nh=%d", N, n_pad, nh);
+  if (tok_stride < static_cast<int64_t>(nh) * D) return fail(HSA_ERR_BAD_SHAPE, "hsa_perm: tok_stride %lld < nh*D", static_cast<long long>(tok_stride));
+  const int es = esize_of(dtype);
+  if ((tok_stride * es) % 16 != 0) return fail(HSA_ERR_BAD_ARG, "hsa_perm: token stride must be a multiple of 16 bytes");
+  if (static_cast<int64_t>(nh) * n_pad * D >= (1ll << 40)) return fail(HSA_ERR_BAD_SHAPE, "hsa_perm: tensor too large");
+  for (int i = 0; i < n_tensors; ++i)
+    if (!aligned16(xs[i]) || !aligned16(xps[i])) return fail(HSA_ERR_BAD_ARG, "hsa_perm: tensor %d not 16-byte aligned", i);
+  return launch_perm(n_tensors, xs, xps, perm, n_pad, nh, D, tok_stride, es, static_cast<hipStream_t>(stream));
+}
+
+size_t hsa_score_ws_size(int32_t nh, int32_t n_pad, int32_t s, int32_t D) {
+  if (nh < 1 || n_pad < 1 || s < 1 || D < 1 || n_pad % s) return 0;
+  return score_ws_bytes(nh, n_pad, s, D);
+}
+
+hsa_status_t hsa_score(const void *qp, const void *kp, const int32_t *blk_len, int32_t nh,
+                       int32_t nb, int32_t B, int32_t s, int32_t D, int32_t dtype, int32_t agg,
+                       float scale, float *S, void *ws, size_t ws_bytes, hsa_stream_t stream) {
+  g_last_error.clear();
+  if (!qp || !kp || !blk_len || !S) return fail(HSA_ERR_NULL_PTR, "hsa_score: null input or output");
+  hsa_status_t st;
+  if ((st = check_dtype(dtype)) != HSA_OK || (st = check_D(D)) != HSA_OK || (st = check_B(B)) != HSA_OK) return st;
+  if (s != 16 && s != 32 && s != 64 && s != 128) return fail(HSA_ERR_UNSUPPORTED, "hsa_score: sub-block %d not in {16,32,64,128}", s);
+  if (B % s) return fail(HSA_ERR_BAD_SHAPE, "hsa_score: sub-block %d does not divide block %d", s, B);
+  if (nh < 1 || nb < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_score: nh=%d nb=%d", nh, nb);
+  if (static_cast<int64_t>(nb) * (B / s) > 2048) return fail(HSA_ERR_UNSUPPORTED, "hsa_score: %lld sub-blocks > 2048", static_cast<long long>(nb) * (B / s));
+  if (agg != HSA_AGG_MASS && agg != HSA_AGG_MAX) return fail(HSA_ERR_BAD_ARG, "hsa_score: unknown aggregation %d", agg);
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(HSA_ERR_BAD_ARG, "hsa_score: scale must be finite and positive");
+  if (!aligned16(qp) || !aligned16(kp) || !aligned16(S)) return fail(HSA_ERR_BAD_ARG, "hsa_score: buffers must be 16-byte aligned");
+  const size_t need = score_ws_bytes(nh, nb * B, s, D);
+  if (!ws || ws_bytes < need) return fail(HSA_ERR_WORKSPACE, "hsa_score: workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (!aligned16(ws)) return fail(HSA_ERR_BAD_ARG, "hsa_score: workspace must be 16-byte aligned");
+  return launch_score(qp, kp, blk_len, nh, nb, B, s, D, dtype, agg, scale, S, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t hsa_select_ws_size(int32_t nh, int32_t nb, const hsa_select_params_t *p) {
+  if (!p || nh < 1 || nb < 1) return 0;
+  return select_ws_bytes(nh, nb, p->mode);
+}
+
+hsa_status_t hsa_select(const float *S, int32_t nh, int32_t nb, const hsa_select_params_t *p,
+                        int32_t *kv_idx, int32_t *kv_cnt, int32_t max_kv, void *ws,
+                        size_t ws_bytes, hsa_stream_t stream) {
+  g_last_error.clear();
+  if (!p || !kv_idx || !kv_cnt) return fail(HSA_ERR_NULL_PTR, "hsa_select: params and lists are required");
+  if (nh < 1 || nb < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: nh=%d nb=%d", nh, nb);
+  if (max_kv < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: max_kv=%d", max_kv);
+  switch (p->mode) {
+    case HSA_SELECT_TOPK:
+      if (!S) return fail(HSA_ERR_NULL_PTR, "hsa_select: scores required");
+      if (nb > 1024) return fail(HSA_ERR_UNSUPPORTED, "hsa_select: nb %d > 1024", nb);
+      if (p->k < 1 || p->k > nb) return fail(HSA_ERR_BAD_ARG, "hsa_select: k=%d not in 1..%d", p->k, nb);
+      if (max_kv < p->k) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: max_kv %d < k %d", max_kv, p->k);
+      break;
+    case HSA_SELECT_THRESH_GLOBAL: {
+      if (!S) return fail(HSA_ERR_NULL_PTR, "hsa_select: scores required");
+      if (nb > 1024) return fail(HSA_ERR_UNSUPPORTED, "hsa_select: nb %d > 1024", nb);
+      if (!(p->tau >= 0.0) || !(p->tau <= 4.0)) return fail(HSA_ERR_BAD_ARG, "hsa_select: tau %g not in [0, 4]", p->tau);
+      if (!(p->budget_ratio >= 0.0) || !(p->budget_ratio <= 1.0)) return fail(HSA_ERR_BAD_ARG, "hsa_select: budget_ratio %g not in [0, 1]", p->budget_ratio);
+      if (max_kv != nb) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: THRESH_GLOBAL needs max_kv == nb");
+      const size_t need = select_ws_bytes(nh, nb, p->mode);
+      if (!ws || ws_bytes < need) return fail(HSA_ERR_WORKSPACE, "hsa_select: workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+      if (!aligned16(ws)) return fail(HSA_ERR_BAD_ARG, "hsa_select: workspace must be 16-byte aligned");
+      break;
+    }
+    case HSA_SELECT_LVSA: {
+      if (p->frames < 1 || p->frames > 1024 || p->tiles_per_frame < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: frames=%d tiles_per_frame=%d", p->frames, p->tiles_per_frame);
+      if (static_cast<int64_t>(p->frames) * p->tiles_per_frame != nb) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: frames*tiles_per_frame != nb");
+      if (p->C < 1 || p->T_per < 1 || p->step < 0) return fail(HSA_ERR_BAD_ARG, "hsa_select: C=%d T_per=%d step=%d", p->C, p->T_per, p->step);
+      // largest |A(t)|: all anchors plus max(C - anchors, 1) window frames
+      const int rot = p->step % p->T_per;
+      const int anchors = rot < p->frames ? (p->frames - 1 - rot) / p->T_per + 1 : 0;
+      const int others = p->frames - anchors;
+      const int nw = others < (p->C - anchors > 1 ? p->C - anchors : 1) ? others : (p->C - anchors > 1 ? p->C - anchors : 1);
+      const int64_t need = static_cast<int64_t>(anchors + nw) * p->tiles_per_frame;
+      if (max_kv < need) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: max_kv %d < %lld tiles per list", max_kv, static_cast<long long>(need));
+      break;
+    }
+    default:
+      return fail(HSA_ERR_BAD_ARG, "hsa_select: unknown mode %d", p->mode);
+  }
+  return launch_select(S, nh, nb, p, kv_idx, kv_cnt, max_kv, ws, static_cast<hipStream_t>(stream));
+}
+
+hsa_status_t hsa_attn(const void *qp, const void *kp, const void *vp, void *op, float *lse,
+                      const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
+                      int32_t max_kv, int32_t kv_shared, int32_t nh, int32_t nb, int32_t B,
+                      int32_t D, int32_t dtype, float scale, hsa_stream_t stream) {
+  g_last_error.clear();
+  if (!qp || !kp || !vp || !op || !blk_len || !kv_idx || !kv_cnt) return fail(HSA_ERR_NULL_PTR, "hsa_attn: null input or output");
+  hsa_status_t st;
+  if ((st = check_dtype(dtype)) != HSA_OK || (st = check_D(D)) != HSA_OK || (st = check_B(B)) != HSA_OK) return st;
+  if (nh < 1 || nb < 1 || max_kv < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn: nh=%d nb=%d max_kv=%d", nh, nb, max_kv);
+  if (static_cast<int64_t>(nh) * nb >= (1ll << 31)) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn: too many blocks");
+  if (kv_shared != 0 && kv_shared != 1) return fail(HSA_ERR_BAD_ARG, "hsa_attn: kv_shared must be 0 or 1");
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(HSA_ERR_BAD_ARG, "hsa_attn: scale must be finite and positive");
+  if (!aligned16(qp) || !aligned16(kp) || !aligned16(vp) || !aligned16(op)) return fail(HSA_ERR_BAD_ARG, "hsa_attn: tensors must be 16-byte aligned");
+  return launch_attn(qp, kp, vp, op, lse, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, B, D, dtype, scale, static_cast<hipStream_t>(stream));
+}
+
+hsa_status_t hsa_unperm(const void *op, void *o, const int32_t *perm, int32_t N, int32_t n_pad,
+                        int32_t nh, int32_t D, int64_t tok_stride, int32_t dtype,
+                        hsa_stream_t stream) {
+  g_last_error.clear();
+  if (!op || !o || !perm) return fail(HSA_ERR_NULL_PTR, "hsa_unperm: null input or output");
+  hsa_status_t st;
+  if ((st = check_dtype(dtype)) != HSA_OK || (st = check_D(D)) != HSA_OK) return st;
+  if (N < 1 || n_pad < N || nh < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_unperm: N=%d n_pad=%d nh=%d", N, n_pad, nh);
+  if (tok_stride < static_cast<int64_t>(nh) * D) return fail(HSA_ERR_BAD_SHAPE, "hsa_unperm: tok_stride < nh*D");
+  const int es = esize_of(dtype);
+  if ((tok_stride * es) % 16 != 0) return fail(HSA_ERR_BAD_ARG, "hsa_unperm: token stride must be a multiple of 16 bytes");
+  if (!aligned16(op) || !aligned16(o)) return fail(HSA_ERR_BAD_ARG, "hsa_unperm: tensors must be 16-byte aligned");
+  return launch_unperm(op, o, perm, n_pad, nh, D, tok_stride, es, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

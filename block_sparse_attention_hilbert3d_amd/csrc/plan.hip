@@ -1,0 +1,197 @@
+// Token-order plan kernels.
+//
+// DFSAttn (Methodology, design 1): reorder every token along one global 3D
+// Hilbert curve before attention. This file walks the enclosing 2^b cube in
+// curve order by DECODING each curve index to its cell (Skilling's transpose
+// method, "Programming the Hilbert curve", 2004: Gray-decode the transposed
+// index, then undo the curve's excess work level by level), keeps in-grid
+// cells, and compacts them with a two-kernel scan. Pads go at the tail.
+#include "common.h"
+
+namespace hsa {
+
+constexpr int kPlanThreads = 256;
+constexpr int kPlanItems = 8;  // consecutive curve indices per thread
+constexpr int kPlanCells = kPlanThreads * kPlanItems;
+
+// Cell (x0, x1, x2) = (t, y, x) visited at curve index h on the 2^b cube.
+__device__ __forceinline__ void hilbert_decode3(uint32_t h, int b, uint32_t &x0, uint32_t &x1,
+                                                uint32_t &x2) {
+  uint32_t a0 = 0, a1 = 0, a2 = 0;
+  // Transposed form: bit (3j + 2 - i) of h is bit j of axis word i.
+  for (int j = 0; j < b; ++j) {
+    a0 |= ((h >> (3 * j + 2)) & 1u) << j;
+    a1 |= ((h >> (3 * j + 1)) & 1u) << j;
+    a2 |= ((h >> (3 * j)) & 1u) << j;
+  }
+  // Gray decode across the three words.
+  const uint32_t g = a2 >> 1;
+  a2 ^= a1;
+  a1 ^= a0;
+  a0 ^= g;
+  // Undo excess work from the lowest level up; words are visited last to
+  // first at each level (a bit of word i inverts word 0's lower bits,
+  // otherwise word 0 and word i exchange their lower bits).
+  const uint32_t end = 2u << (b - 1);
+  for (uint32_t q = 2; q != end; q <<= 1) {
+    const uint32_t low = q - 1;
+    uint32_t sw;
+    if (a2 & q) {
+      a0 ^= low;
+    } else {
+      sw = (a0 ^ a2) & low;
+      a0 ^= sw;
+      a2 ^= sw;
+    }
+    if (a1 & q) {
+      a0 ^= low;
+    } else {
+      sw = (a0 ^ a1) & low;
+      a0 ^= sw;
+      a1 ^= sw;
+    }
+    if (a0 & q) a0 ^= low;
+  }
+  x0 = a0;
+  x1 = a1;
+  x2 = a2;
+}
+
+__device__ __forceinline__ bool in_grid(uint32_t h, int b, int T, int H, int W, int32_t &tok) {
+  uint32_t t, y, x;
+  hilbert_decode3(h, b, t, y, x);
+  tok = static_cast<int32_t>((t * static_cast<uint32_t>(H) + y) * static_cast<uint32_t>(W) + x);
+  return t < static_cast<uint32_t>(T) && y < static_cast<uint32_t>(H) &&
+         x < static_cast<uint32_t>(W);
+}
+
+// Block-wide exclusive scan of one int per thread; returns the total.
+__device__ int block_exclusive_scan(int v, int &excl, int *sh /* kPlanThreads/64 + 1 */) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) sh[wid] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    if (w < wid) base += sh[w];
+    total += sh[w];
+  }
+  excl = base + incl - v;
+  __syncthreads();
+  return total;
+}
+
+__global__ void __launch_bounds__(kPlanThreads)
+hilbert_count_kernel(int b, uint32_t cube, int T, int H, int W, int32_t *counts) {
+  __shared__ int sh[kPlanThreads / 64 + 1];
+  const uint32_t base = blockIdx.x * kPlanCells + threadIdx.x * kPlanItems;
+  int c = 0;
+  for (int j = 0; j < kPlanItems; ++j) {
+    const uint32_t h = base + j;
+    int32_t tok;
+    if (h < cube && in_grid(h, b, T, H, W, tok)) ++c;
+  }
+  int excl;
+  const int total = block_exclusive_scan(c, excl, sh);
+  if (threadIdx.x == 0) counts[blockIdx.x] = total;
+}
+
+__global__ void __launch_bounds__(kPlanThreads)
+hilbert_write_kernel(int b, uint32_t cube, int T, int H, int W, const int32_t *counts,
+                     int32_t *perm) {
+  __shared__ int sh[kPlanThreads / 64 + 1];
+  __shared__ int sh_off;
+  // Offset of this workgroup: sum of the counts of all earlier workgroups.
+  int part = 0;
+  for (int i = threadIdx.x; i < static_cast<int>(blockIdx.x); i += kPlanThreads) part += counts[i];
+  int excl0;
+  const int before = block_exclusive_scan(part, excl0, sh);
+  if (threadIdx.x == 0) sh_off = before;
+  __syncthreads();
+  const int offset = sh_off;
+
+  const uint32_t base = blockIdx.x * kPlanCells + threadIdx.x * kPlanItems;
+  int c = 0;
+  for (int j = 0; j < kPlanItems; ++j) {
+    const uint32_t h = base + j;
+    int32_t tok;
+    if (h < cube && in_grid(h, b, T, H, W, tok)) ++c;
+  }
+  int excl;
+  block_exclusive_scan(c, excl, sh);
+  // Decode again rather than holding the cells in a dynamically indexed array.
+  int k = offset + excl;
+  for (int j = 0; j < kPlanItems; ++j) {
+    const uint32_t h = base + j;
+    int32_t tok;
+    if (h < cube && in_grid(h, b, T, H, W, tok)) perm[k++] = tok;
+  }
+}
+
+// ROW / FRAME plans are closed-form; HILBERT only needs tail pads here.
+// Also fills blk_len for every order.
+__global__ void plan_fill_kernel(int order, int T, int H, int W, int B, int n_pad, int nb,
+                                 int32_t *perm, int32_t *blk_len) {
+  const int N = T * H * W;
+  const int P = H * W;
+  const int tiles = (P + B - 1) / B;
+  const int per = tiles * B;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_pad; i += gridDim.x * blockDim.x) {
+    if (order == HSA_ORDER_FRAME) {
+      const int f = i / per, r = i - f * per;
+      perm[i] = (r < P) ? f * P + r : -1;
+    } else if (order == HSA_ORDER_ROW) {
+      perm[i] = (i < N) ? i : -1;
+    } else if (i >= N) {
+      perm[i] = -1;
+    }
+    if (i < nb) {
+      int len;
+      if (order == HSA_ORDER_FRAME) {
+        const int j = i % tiles;
+        len = min(B, P - j * B);
+      } else {
+        len = min(B, N - i * B);
+      }
+      blk_len[i] = max(len, 0);
+    }
+  }
+}
+
+}  // namespace hsa
+
+namespace hsa_host {
+
+size_t plan_hilbert_groups(int T, int H, int W, int &bits, uint32_t &cube) {
+  const int m = max(T, max(H, W));
+  int b = 1;
+  while ((1 << b) < m) ++b;
+  bits = b;
+  cube = 1u << (3 * b);
+  return (cube + hsa::kPlanCells - 1) / hsa::kPlanCells;
+}
+
+hsa_status_t launch_plan(int T, int H, int W, int order, int B, int n_pad, int nb, int32_t *perm,
+                         int32_t *blk_len, void *ws, hipStream_t stream) {
+  if (order == HSA_ORDER_HILBERT3D) {
+    int b;
+    uint32_t cube;
+    const size_t groups = plan_hilbert_groups(T, H, W, b, cube);
+    int32_t *counts = static_cast<int32_t *>(ws);
+    hipLaunchKernelGGL(hsa::hilbert_count_kernel, dim3(groups), dim3(hsa::kPlanThreads), 0,
+                       stream, b, cube, T, H, W, counts);
+    hipLaunchKernelGGL(hsa::hilbert_write_kernel, dim3(groups), dim3(hsa::kPlanThreads), 0,
+                       stream, b, cube, T, H, W, counts, perm);
+  }
+  const int blocks = min((n_pad + 255) / 256, 4096);
+  hipLaunchKernelGGL(hsa::plan_fill_kernel, dim3(blocks), dim3(256), 0, stream, order, T, H, W,
+                     B, n_pad, nb, perm, blk_len);
+  return check_launch("hsa_plan");
+}
+
+}  // namespace hsa_host

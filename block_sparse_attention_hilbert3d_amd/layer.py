@@ -1,0 +1,110 @@
+"""One block-sparse attention layer: the five C entry points in sequence.
+
+reorder (hsa_perm) -> score (hsa_score) -> select (hsa_select) -> attend
+(hsa_attn) -> restore order (hsa_unperm), with the plan computed once per
+grid shape (hsa_plan). Buffers and workspaces are allocated once per layer
+so a step enqueues kernels only.
+
+Mask caching (DFSAttn, Methodology, design 3): ``step(..., reuse_mask=True)``
+skips scoring and selection and attends with the lists kept from the last
+refresh, on the new step's Q/K/V.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import binding as B_
+
+
+class SparseAttentionLayer:
+    def __init__(self, T: int, H: int, W: int, heads: int, D: int, *, order: str, B: int,
+                 select: str, s: int = 0, agg: str = "mass", k: int = 0, tau: float = 0.0,
+                 C: int = 0, T_per: int = 1, dtype=torch.bfloat16, device="cuda",
+                 want_lse: bool = True):
+        self.T, self.H, self.W, self.heads, self.D = T, H, W, heads, D
+        self.N = T * H * W
+        self.order, self.B, self.select, self.s, self.agg = order, B, select, s, agg
+        self.k, self.tau, self.C, self.T_per = k, tau, C, T_per
+        self.dtype, self.device = dtype, device
+        self.scale = 1.0 / math.sqrt(D)
+        self.perm, self.blk_len = B_.hsa_plan(T, H, W, order, B, device=device)
+        self.n_pad = self.perm.numel()
+        self.nb = self.n_pad // B
+        self.tiles_per_frame = self.nb // T if order == "frame" else 0
+        shape = (heads, self.n_pad, D)
+        self.xp = [torch.empty(shape, dtype=dtype, device=device) for _ in range(3)]
+        self.op = torch.empty(shape, dtype=dtype, device=device)
+        self.lse = torch.empty((heads, self.n_pad), dtype=torch.float32, device=device) if want_lse else None
+        self.want_lse = want_lse
+        self.o = torch.empty((1, self.N, heads, D), dtype=dtype, device=device)
+        if select == "lvsa":
+            self.max_kv = self._lvsa_width()
+            G = 1
+            self.S = None
+            self.score_ws = None
+        else:
+            self.max_kv = k if select == "topk" else self.nb
+            G = heads
+            self.S = torch.empty((heads, self.nb, self.nb), dtype=torch.float32, device=device)
+            n = B_.lib().hsa_score_ws_size(heads, self.n_pad, s, D)
+            self.score_ws = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+        self.kv_idx = torch.empty((G, self.nb, self.max_kv), dtype=torch.int32, device=device)
+        self.kv_cnt = torch.empty((G, self.nb), dtype=torch.int32, device=device)
+        p = self.params(0, 0.0)
+        n = B_.lib().hsa_select_ws_size(heads, self.nb, p)
+        self.select_ws = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+    def _lvsa_width(self) -> int:
+        worst = 0
+        for step in range(self.T_per):
+            rot = step % self.T_per
+            anchors = (self.T - 1 - rot) // self.T_per + 1 if rot < self.T else 0
+            nw = min(max(self.C - anchors, 1), self.T - anchors)
+            worst = max(worst, anchors + nw)
+        return worst * self.tiles_per_frame
+
+    def params(self, step: int, budget_ratio: float) -> B_.SelectParams:
+        return B_.make_params(self.select, k=self.k, tau=self.tau, budget_ratio=budget_ratio,
+                              frames=self.T, tiles_per_frame=self.tiles_per_frame, C=self.C,
+                              T_per=self.T_per, step=step)
+
+    def reorder(self, q, k, v):
+        B_.hsa_perm([q, k, v], self.perm, self.n_pad, outs=self.xp)
+
+    def make_mask(self, step: int = 0, budget_ratio: float = 0.0):
+        qp, kp, _ = self.xp
+        if self.select != "lvsa":
+            B_.hsa_score(qp, kp, self.blk_len, self.B, self.s, self.agg, self.scale, out=self.S,
+                         ws=self.score_ws)
+        B_.hsa_select(self.S, self.heads, self.nb, self.params(step, budget_ratio), self.max_kv,
+                      device=self.device, outs=(self.kv_idx, self.kv_cnt), ws=self.select_ws)
+
+    def attend(self):
+        qp, kp, vp = self.xp
+        B_.hsa_attn(qp, kp, vp, self.blk_len, self.kv_idx, self.kv_cnt, self.B, self.scale,
+                    want_lse=self.want_lse, out=self.op, lse=self.lse)
+
+    def restore(self):
+        return B_.hsa_unperm(self.op, self.perm, self.N, out=self.o)
+
+    def step(self, q, k, v, step: int = 0, budget_ratio: float = 0.0, reuse_mask: bool = False):
+        """One layer: returns the output [1, N, heads, D] (a buffer owned by the layer)."""
+        self.reorder(q, k, v)
+        if not reuse_mask:
+            self.make_mask(step, budget_ratio)
+        self.attend()
+        return self.restore()
+
+
+def layer_for_workload(w, device="cuda", want_lse=True) -> SparseAttentionLayer:
+    """Layer configured for one of the synthetic workloads (workloads.Workload)."""
+    dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    nb = B_.hsa_plan_size(w.T, w.H, w.W, w.order, w.B)[1]
+    k = 0
+    if w.select == "topk":
+        k = w.k if w.k > 0 else max(1, int(math.floor(w.keep_ratio * nb + 0.5)))
+    return SparseAttentionLayer(w.T, w.H, w.W, w.heads, w.D, order=w.order, B=w.B,
+                                select=w.select, s=w.s, k=k, tau=w.tau, C=w.C, T_per=w.T_per,
+                                dtype=dtype, device=device, want_lse=want_lse)

@@ -1,0 +1,209 @@
+/*
+ * hsa.h -- dynamic block-sparse self-attention over spatiotemporal video
+ * tokens, MI355X (gfx950) HIP library, plain C ABI.
+ *
+ * The path has five steps, each one entry point (plus a once-per-shape plan):
+ *   hsa_plan    token order for a latent grid (Hilbert / row-major / frame)
+ *   hsa_perm    gather Q, K, V into the reordered, padded, head-major layout
+ *   hsa_score   sub-block pooled block-to-block importance scores
+ *   hsa_select  per-query-block lists of key blocks (top-k, threshold +
+ *               global budget, or the LVSA frame mask)
+ *   hsa_attn    block-sparse flash attention over the listed key blocks
+ *   hsa_unperm  scatter the output back to the original token order
+ *
+ * Conventions shared by every entry point
+ *  - The caller owns every buffer. Device buffers are device pointers (for
+ *    example from torch), 16-byte aligned. The library never allocates or
+ *    frees memory, never synchronises, and keeps no pointer after it returns.
+ *    Host structs are read only during the call.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = null stream) and
+ *    runs asynchronously; outputs are valid once the stream reaches the work.
+ *  - Arguments are validated before any launch. On failure nothing is
+ *    enqueued, no output is touched, a nonzero hsa_status_t is returned and
+ *    hsa_last_error() (per thread) describes the problem.
+ *  - Element types: HSA_F32 (float) or HSA_BF16 (bfloat16 bits). Head dim
+ *    D in {64, 128}; block size B in {64, 128}; sub-block s in {16,32,64,128}
+ *    dividing B.
+ *  - Layouts (batch 1; a batch is a loop in the caller):
+ *      token-major   x [N tokens][nh heads][D], consecutive tokens
+ *                    `tok_stride` elements apart (>= nh*D, so fused QKV
+ *                    buffers can be read in place);
+ *      reordered     xp [nh][n_pad][D], slot i of head h at (h*n_pad+i)*D;
+ *      perm          int32 [n_pad]: token held by slot i, -1 for a pad slot;
+ *      blk_len       int32 [nb]: real tokens in block I (they are the first
+ *                    blk_len[I] slots of the block; pads follow);
+ *      scores        float [nh][nb][nb];
+ *      lists         kv_idx int32 [G][nb][max_kv] ascending, -1 after
+ *                    kv_cnt int32 [G][nb] entries; G = nh, or 1 when shared.
+ *  - Token n is grid cell (t, y, x) with n = (t*H + y)*W + x.
+ */
+#ifndef HSA_H
+#define HSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HSA_ABI_VERSION 1
+
+typedef enum hsa_status {
+  HSA_OK = 0,
+  HSA_ERR_NULL_PTR = 1,     /* a required pointer is NULL */
+  HSA_ERR_BAD_SHAPE = 2,    /* sizes inconsistent or out of range */
+  HSA_ERR_BAD_DTYPE = 3,    /* element type not HSA_F32 / HSA_BF16 */
+  HSA_ERR_UNSUPPORTED = 4,  /* valid but not implemented (e.g. D = 96) */
+  HSA_ERR_WORKSPACE = 5,    /* workspace missing or too small */
+  HSA_ERR_BAD_ARG = 6,      /* other invalid argument (mode, alignment, ...) */
+  HSA_ERR_HIP = 7           /* the HIP runtime rejected a launch */
+} hsa_status_t;
+
+typedef enum { HSA_F32 = 0, HSA_BF16 = 1 } hsa_dtype_t;
+typedef enum { HSA_ORDER_ROW = 0, HSA_ORDER_HILBERT3D = 1, HSA_ORDER_FRAME = 2 } hsa_order_t;
+typedef enum { HSA_AGG_MASS = 0, HSA_AGG_MAX = 1 } hsa_agg_t;
+typedef enum {
+  HSA_SELECT_TOPK = 0,
+  HSA_SELECT_THRESH_GLOBAL = 1,
+  HSA_SELECT_LVSA = 2
+} hsa_select_mode_t;
+
+typedef void *hsa_stream_t; /* a hipStream_t */
+
+/* Selection parameters; which fields are read depends on `mode`. */
+typedef struct hsa_select_params {
+  int32_t mode;            /* hsa_select_mode_t */
+  int32_t k;               /* TOPK: key blocks kept per query block, 1..nb */
+  double tau;              /* THRESH_GLOBAL: cumulative score per query block, >= 0 */
+  double budget_ratio;     /* THRESH_GLOBAL: head budget floor(ratio*nb*nb + 0.5) pairs */
+  int32_t frames;          /* LVSA: number of frames T (nb = frames*tiles_per_frame) */
+  int32_t tiles_per_frame; /* LVSA: tiles (blocks) per frame */
+  int32_t C;               /* LVSA: frame budget per query frame, >= 1 */
+  int32_t T_per;           /* LVSA: anchor period in frames, >= 1 */
+  int32_t step;            /* LVSA: denoising step index, >= 0 */
+} hsa_select_params_t;
+
+/* Library version (HSA_ABI_VERSION) and status strings. */
+int hsa_abi_version(void);
+const char *hsa_status_str(hsa_status_t status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *hsa_last_error(void);
+
+/*
+ * hsa_plan_size -- host-only: padded length and block count of a plan.
+ * ROW / HILBERT3D: n_pad = ceil(N/B)*B. FRAME: n_pad = T*ceil(H*W/B)*B.
+ * Grid sides 1..1024, N < 2^31.
+ */
+hsa_status_t hsa_plan_size(int32_t T, int32_t H, int32_t W, int32_t order, int32_t B,
+                           int32_t *n_pad, int32_t *nb);
+
+/* Workspace bytes hsa_plan needs (0 for ROW and FRAME). */
+size_t hsa_plan_ws_size(int32_t T, int32_t H, int32_t W, int32_t order);
+
+/*
+ * hsa_plan -- token order for a T x H x W latent grid.
+ * DFSAttn (Methodology, design 1): tokens are reordered along one global 3D
+ * Hilbert curve so consecutive runs (blocks) are compact spatiotemporal
+ * neighbourhoods. HILBERT3D walks the enclosing 2^b cube (b = ceil(log2 of
+ * the longest side)) in curve order (Skilling's transpose construction, axes
+ * (t, y, x), t most significant), keeps in-grid cells and pads the tail.
+ * ROW is row-major with tail pads; FRAME is frame-major with each frame's
+ * tokens padded to whole blocks (LVSA section 2 attends frame by frame).
+ * Outputs: perm int32[n_pad] and blk_len int32[nb] (device).
+ * ws: device workspace of hsa_plan_ws_size bytes (may be NULL if 0).
+ */
+hsa_status_t hsa_plan(int32_t T, int32_t H, int32_t W, int32_t order, int32_t B,
+                      int32_t *perm, int32_t *blk_len, void *ws, size_t ws_bytes,
+                      hsa_stream_t stream);
+
+/*
+ * hsa_perm -- gather into the reordered layout: xp[h][i][:] = x[perm[i]][h][:]
+ * and zero rows for pad slots (DFSAttn, Methodology, design 1: reorder
+ * before attention). Copies 1..3 tensors (Q, K, V) in one launch.
+ * xs[j]: token-major input j; xps[j]: reordered output j (nh*n_pad*D
+ * elements). xs and xps are host arrays of n_tensors device pointers.
+ * tok_stride: elements between consecutive tokens of x; (tok_stride *
+ * element size) must be a multiple of 16 bytes.
+ */
+hsa_status_t hsa_perm(int32_t n_tensors, const void *const *xs, void *const *xps,
+                      const int32_t *perm, int32_t N, int32_t n_pad, int32_t nh, int32_t D,
+                      int64_t tok_stride, int32_t dtype, hsa_stream_t stream);
+
+/* Workspace bytes for hsa_score: pooled Q and K sub-block means (float) and
+ * per-sub-block token counts. */
+size_t hsa_score_ws_size(int32_t nh, int32_t n_pad, int32_t s, int32_t D);
+
+/*
+ * hsa_score -- block importance from sub-block summaries.
+ * DFSAttn (Methodology, design 2: hierarchical block scoring): blocks are
+ * split into sub-blocks of s slots; sub-block means qbar_u, kbar_v (float,
+ * over real tokens only) give logits z[u][v] = scale * qbar_u . kbar_v.
+ * agg = MASS: p[u][v] = c_v exp(z[u][v] - max) / sum_v' c_v' exp(...) with
+ *   c the real-token count of a sub-block; S[I][J] = sum_{u in I} c_u
+ *   sum_{v in J} p[u][v] / sum_{u in I} c_u  (rows sum to 1).
+ * agg = MAX: S[I][J] = max over u in I, v in J of z[u][v].
+ * qp, kp: reordered [nh][nb*B][D]; blk_len: [nb]; S out: float [nh][nb][nb].
+ * Limits: nb*B/s <= 2048 sub-blocks. Computed in float32 (matrix cores).
+ */
+hsa_status_t hsa_score(const void *qp, const void *kp, const int32_t *blk_len, int32_t nh,
+                       int32_t nb, int32_t B, int32_t s, int32_t D, int32_t dtype, int32_t agg,
+                       float scale, float *S, void *ws, size_t ws_bytes, hsa_stream_t stream);
+
+/* Workspace bytes for hsa_select (0 for TOPK and LVSA). */
+size_t hsa_select_ws_size(int32_t nh, int32_t nb, const hsa_select_params_t *p);
+
+/*
+ * hsa_select -- per-query-block ascending lists of key blocks.
+ * Ranking is by score, ties to the lower index (lower I*nb + J globally).
+ * TOPK (DFSAttn, Methodology, design 3: a sparsity budget): the k highest
+ *   scores of each row. Lists [nh][nb][max_kv], max_kv >= k.
+ * THRESH_GLOBAL (VMoBA abstract: threshold selection by cumulative similarity
+ *   and global selection over the head; DFSAttn design 3: a budget that
+ *   shrinks over steps): per row, the shortest score-ranked prefix whose sum
+ *   reaches tau (sums exact in 2^-62 fixed point; at least one block); then
+ *   per head the best-ranked remaining pairs are added until the head holds
+ *   floor(budget_ratio*nb*nb + 0.5) pairs. Scores must be finite and >= 0
+ *   (MASS). Lists [nh][nb][max_kv]; max_kv must be nb.
+ * LVSA (LVSA section 2, A(t) = G_s u W(t)): frame t attends to the anchor
+ *   frames f = step (mod T_per) and to the C - |G_s| nearest non-anchor
+ *   frames (ties to the earlier frame; at least one); every tile of frame t
+ *   lists every tile of those frames. S is not read (may be NULL). One list
+ *   set shared by all heads: kv_idx [nb][max_kv], kv_cnt [nb].
+ * ws: device workspace of hsa_select_ws_size bytes.
+ */
+hsa_status_t hsa_select(const float *S, int32_t nh, int32_t nb, const hsa_select_params_t *p,
+                        int32_t *kv_idx, int32_t *kv_cnt, int32_t max_kv, void *ws,
+                        size_t ws_bytes, hsa_stream_t stream);
+
+/*
+ * hsa_attn -- block-sparse attention: for every query slot i of block I,
+ *   o_i = sum_j softmax_j(scale * q_i . k_j) v_j over the real key slots j of
+ *   the blocks listed for I (DFSAttn Significance: block-wise execution over
+ *   reordered tokens; DynamicRad section 2.2: a shared candidate set
+ *   aggregated block-wise). Non-causal. Unlisted blocks are never read.
+ * qp, kp, vp, op: reordered [nh][nb*B][D]; op rows of pad slots are zero.
+ * lse: optional float [nh][nb*B] natural-log log-sum-exp (NULL to skip).
+ * kv_shared: 1 if the lists are [nb][max_kv] shared by all heads.
+ * BF16 runs on bf16 matrix cores with float accumulation and softmax; the
+ * probabilities are rounded to bf16 for the value product and the output is
+ * rounded to bf16 (nearest even). F32 computes in float throughout.
+ */
+hsa_status_t hsa_attn(const void *qp, const void *kp, const void *vp, void *op, float *lse,
+                      const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
+                      int32_t max_kv, int32_t kv_shared, int32_t nh, int32_t nb, int32_t B,
+                      int32_t D, int32_t dtype, float scale, hsa_stream_t stream);
+
+/*
+ * hsa_unperm -- scatter back to token order: o[perm[i]][h][:] = op[h][i][:]
+ * for every real slot i (pad slots are dropped). Layouts as hsa_perm.
+ */
+hsa_status_t hsa_unperm(const void *op, void *o, const int32_t *perm, int32_t N, int32_t n_pad,
+                        int32_t nh, int32_t D, int64_t tok_stride, int32_t dtype,
+                        hsa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSA_H */

@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments before launching anything
+(every call below fails validation, so no kernel is ever enqueued)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hsa.h")
+LIB = os.path.join(ROOT, "block_sparse_attention_hilbert3d_amd", "libhsa.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libhsa.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_steps():
+    names = _declared()
+    for n in ["hsa_plan", "hsa_perm", "hsa_score", "hsa_select", "hsa_attn", "hsa_unperm"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (hsa_[a-z_0-9]+)$", out, flags=re.M))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    L = ctypes.CDLL(LIB)
+    for n in _declared():
+        assert getattr(L, n) is not None
+
+
+@pytest.fixture(scope="module")
+def B():
+    from block_sparse_attention_hilbert3d_amd import binding
+    return binding
+
+
+def _err(B, status):
+    return status, B.lib().hsa_last_error().decode()
+
+
+def test_version_and_strings(B):
+    L = B.lib()
+    assert L.hsa_abi_version() == 1
+    assert L.hsa_status_str(0) == b"ok"
+    assert L.hsa_status_str(5) == b"workspace too small"
+
+
+def test_plan_size_closed_forms(B):
+    assert B.hsa_plan_size(21, 30, 52, "hilbert", 128) == (32768, 256)
+    assert B.hsa_plan_size(61, 30, 52, "frame", 128) == (101504, 793)
+    assert B.hsa_plan_size(33, 45, 80, "hilbert", 128) == (118912, 929)
+    assert B.hsa_plan_size(4, 8, 8, "row", 64) == (256, 4)
+    with pytest.raises(B.HsaError):
+        B.hsa_plan_size(0, 8, 8, "row", 64)
+    with pytest.raises(B.HsaError):
+        B.hsa_plan_size(2000, 8, 8, "row", 64)
+
+
+def test_plan_workspace_sizes(B):
+    L = B.lib()
+    assert L.hsa_plan_ws_size(21, 30, 52, 0) == 0
+    assert L.hsa_plan_ws_size(21, 30, 52, 1) == (64 ** 3 // 2048) * 4
+    assert L.hsa_plan_ws_size(33, 45, 80, 1) == (128 ** 3 // 2048) * 4
+
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+NULL = ctypes.c_void_p(0)
+
+
+def test_perm_validation(B):
+    L = B.lib()
+    arr = (ctypes.c_void_p * 3)(FAKE.value, FAKE.value, FAKE.value)
+    assert L.hsa_perm(4, arr, arr, FAKE, 10, 16, 2, 64, 128, 1, NULL) == 6          # n_tensors
+    assert L.hsa_perm(1, arr, arr, NULL, 10, 16, 2, 64, 128, 1, NULL) == 1          # perm
+    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 96, 192, 1, NULL) == 4          # D
+    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 64, 128, 7, NULL) == 3          # dtype
+    assert L.hsa_perm(1, arr, arr, FAKE, 20, 16, 2, 64, 128, 1, NULL) == 2          # n_pad < N
+    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 64, 100, 1, NULL) == 2          # stride < nh*D
+    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 64, 132, 1, NULL) == 6          # stride alignment
+    bad = (ctypes.c_void_p * 1)(0x10004)
+    assert L.hsa_perm(1, bad, arr, FAKE, 10, 16, 2, 64, 128, 1, NULL) == 6          # pointer alignment
+    assert b"aligned" in L.hsa_last_error()
+
+
+def test_score_validation(B):
+    L = B.lib()
+    ok = (FAKE, FAKE, FAKE)
+    ws_n = L.hsa_score_ws_size(2, 256, 16, 64)
+    assert ws_n > 0
+    args = lambda **kw: dict(dict(nh=2, nb=4, Bs=64, s=16, D=64, dt=1, agg=0, scale=0.125,
+                                  ws=FAKE, wsn=ws_n), **kw)
+
+    def call(a):
+        return L.hsa_score(*ok, a["nh"], a["nb"], a["Bs"], a["s"], a["D"], a["dt"], a["agg"],
+                           a["scale"], FAKE, a["ws"], a["wsn"], NULL)
+    assert call(args(s=24)) == 4
+    assert call(args(Bs=64, s=128)) == 2
+    assert call(args(agg=5)) == 6
+    assert call(args(scale=-1.0)) == 6
+    assert call(args(wsn=ws_n - 1)) == 5
+    assert call(args(ws=NULL)) == 5
+    assert call(args(nb=300, Bs=128, s=16)) == 4        # 2400 sub-blocks > 2048
+    assert L.hsa_score(NULL, FAKE, FAKE, 2, 4, 64, 16, 64, 1, 0, 0.125, FAKE, FAKE, ws_n, NULL) == 1
+
+
+def test_select_validation(B):
+    L = B.lib()
+    p = B.make_params("topk", k=5)
+    assert L.hsa_select(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 8, NULL, 0, NULL) == 6     # k > nb
+    p = B.make_params("topk", k=3)
+    assert L.hsa_select(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 2, NULL, 0, NULL) == 2     # max_kv < k
+    assert L.hsa_select(NULL, 2, 4, ctypes.byref(p), FAKE, FAKE, 4, NULL, 0, NULL) == 1
+    p = B.make_params("thresh_global", tau=0.25, budget_ratio=0.3)
+    n = L.hsa_select_ws_size(2, 4, ctypes.byref(p))
+    assert n > 0
+    assert L.hsa_select(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 3, FAKE, n, NULL) == 2     # max_kv != nb
+    assert L.hsa_select(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 4, FAKE, n - 1, NULL) == 5
+    p = B.make_params("thresh_global", tau=0.25, budget_ratio=1.5)
+    assert L.hsa_select(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 4, FAKE, n, NULL) == 6
+    p = B.make_params("lvsa", frames=61, tiles_per_frame=13, C=21, T_per=8, step=0)
+    assert L.hsa_select(NULL, 12, 793, ctypes.byref(p), FAKE, FAKE, 21 * 13 - 1, NULL, 0, NULL) == 2
+    p = B.make_params("lvsa", frames=61, tiles_per_frame=13, C=21, T_per=8, step=0)
+    assert L.hsa_select(NULL, 12, 792, ctypes.byref(p), FAKE, FAKE, 21 * 13, NULL, 0, NULL) == 2
+    p = B.make_params("lvsa", frames=61, tiles_per_frame=13, C=0, T_per=8, step=0)
+    assert L.hsa_select(NULL, 12, 793, ctypes.byref(p), FAKE, FAKE, 21 * 13, NULL, 0, NULL) == 6
+    p = B.SelectParams(9, 1, 0.0, 0.0, 0, 0, 0, 1, 0)
+    assert L.hsa_select(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 4, NULL, 0, NULL) == 6
+
+
+def test_attn_and_unperm_validation(B):
+    L = B.lib()
+    a = [FAKE] * 8
+    assert L.hsa_attn(NULL, *a[1:4], NULL, *a[5:8], 4, 0, 2, 4, 64, 64, 1, 0.125, NULL) == 1
+    assert L.hsa_attn(*a[:4], NULL, *a[5:8], 4, 0, 2, 4, 96, 64, 1, 0.125, NULL) == 4      # B
+    assert L.hsa_attn(*a[:4], NULL, *a[5:8], 4, 2, 2, 4, 64, 64, 1, 0.125, NULL) == 6      # kv_shared
+    assert L.hsa_attn(*a[:4], NULL, *a[5:8], 4, 0, 2, 4, 64, 64, 1, float("nan"), NULL) == 6
+    assert L.hsa_unperm(FAKE, FAKE, FAKE, 10, 8, 2, 64, 128, 1, NULL) == 2
+    assert L.hsa_unperm(FAKE, NULL, FAKE, 10, 16, 2, 64, 128, 1, NULL) == 1

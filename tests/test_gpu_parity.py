@@ -1,0 +1,325 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: plans, permutations and selected block lists bit-exact; scores within
+1e-5 (MASS) / 1e-4 (MAX) max-abs of the float64 oracle; attention within
+1e-4 (float32) / 2e-2 (bfloat16) max-abs, on every row for the small
+workloads and on 4096 seeded rows per head (plus the first and the ragged
+last block) for the large ones, in the same launch configuration the
+benchmark uses.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from _gpu_common import (SCORE_TOL, TOL, attn_rows, dev, lists_equal, max_err_rows,
+                         oracle_select, to_np, topk_k)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hsa():
+    import block_sparse_attention_hilbert3d_amd as m
+    m.lib()
+    return m
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ---------------------------------------------------------------- plan / perm
+
+@pytest.mark.parametrize("shape,order,B", [
+    ((3, 5, 7), "hilbert", 64), ((1, 1, 1), "hilbert", 64), ((2, 3, 4), "hilbert", 64),
+    ((5, 1, 6), "hilbert", 128), ((16, 16, 16), "hilbert", 64), ((8, 16, 16), "hilbert", 64),
+    ((21, 30, 52), "hilbert", 128), ((33, 45, 80), "hilbert", 128), ((2, 3, 600), "hilbert", 128),
+    ((4, 8, 8), "row", 64), ((3, 5, 7), "row", 128), ((61, 30, 52), "frame", 128),
+    ((3, 5, 7), "frame", 64), ((2, 9, 9), "frame", 128),
+])
+def test_plan_bit_exact(hsa, shape, order, B):
+    T, H, W = shape
+    _say(f"plan {shape} {order} B={B}")
+    perm, blk_len = hsa.hsa_plan(T, H, W, order, B, device=dev())
+    torch.cuda.synchronize()
+    ref_perm, ref_len = oracle.plan(T, H, W, order, B)
+    assert np.array_equal(perm.cpu().numpy().astype(np.int64), ref_perm)
+    assert np.array_equal(blk_len.cpu().numpy().astype(np.int64), ref_len)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_perm_unperm_bit_exact(hsa, idx):
+    w = wl.get(idx)
+    _say(f"perm/unperm workload {idx}")
+    q, k, v = (x.to(dev()) for x in wl.make_qkv(w, 0))
+    perm, _ = hsa.hsa_plan(w.T, w.H, w.W, w.order, w.B, device=dev())
+    n_pad = perm.numel()
+    qp, kp, vp = hsa.hsa_perm([q, k, v], perm, n_pad)
+    o = hsa.hsa_unperm(vp, perm, w.N)
+    torch.cuda.synchronize()
+    ref_perm = perm.cpu().numpy().astype(np.int64)
+    for x, xp in ((q, qp), (k, kp), (v, vp)):
+        assert np.array_equal(to_np(xp), oracle.gather(x.cpu(), ref_perm))
+    assert torch.equal(o, v)
+
+
+def test_perm_fused_qkv_stride(hsa):
+    """Q, K, V read in place from one fused [N, 3, heads, D] projection buffer."""
+    w = wl.get(2)
+    _say("perm fused stride")
+    g = torch.Generator().manual_seed(11)
+    fused = torch.randn((1, w.N, 3, w.heads, w.D), generator=g).to(torch.bfloat16).to(dev())
+    q, k, v = fused[:, :, 0], fused[:, :, 1], fused[:, :, 2]
+    perm, _ = hsa.hsa_plan(w.T, w.H, w.W, w.order, w.B, device=dev())
+    xps = hsa.hsa_perm([q, k, v], perm, perm.numel())
+    out = torch.zeros_like(fused)
+    for j, xp in enumerate(xps):
+        hsa.hsa_unperm(xp, perm, w.N, out=out[:, :, j])
+    torch.cuda.synchronize()
+    assert torch.equal(out, fused)
+    ref_perm = perm.cpu().numpy().astype(np.int64)
+    assert np.array_equal(to_np(xps[1]), oracle.gather(k.cpu(), ref_perm))
+
+
+# ---------------------------------------------------------------- score / select
+
+def _gpu_scores(hsa, w, step, agg="mass"):
+    q, k, v = (x.to(dev()) for x in wl.make_qkv(w, step))
+    perm, blk_len = hsa.hsa_plan(w.T, w.H, w.W, w.order, w.B, device=dev())
+    qp, kp, vp = hsa.hsa_perm([q, k, v], perm, perm.numel())
+    S = hsa.hsa_score(qp, kp, blk_len, w.B, w.s, agg)
+    torch.cuda.synchronize()
+    return q, k, v, perm, blk_len, qp, kp, vp, S
+
+
+@pytest.mark.parametrize("idx,agg", [(1, "mass"), (2, "mass"), (3, "mass"), (5, "mass"),
+                                     (1, "max"), (2, "max"), (3, "max")])
+def test_score_matches_oracle(hsa, idx, agg):
+    w = wl.get(idx)
+    _say(f"score workload {idx} {agg}")
+    q, k, v, perm, blk_len, qp, kp, vp, S = _gpu_scores(hsa, w, 0, agg)
+    ref_perm = perm.cpu().numpy().astype(np.int64)
+    ref = oracle.score(oracle.gather(q.cpu(), ref_perm), oracle.gather(k.cpu(), ref_perm),
+                       ref_perm, w.B, w.s, agg)
+    err = np.abs(to_np(S) - ref).max()
+    _say(f"  max |S_gpu - S_oracle| = {err:.3e}")
+    assert err <= SCORE_TOL[agg]
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 5])
+def test_select_bit_exact_on_gpu_scores(hsa, idx):
+    w = wl.get(idx)
+    _say(f"select workload {idx}")
+    step = 0
+    q, k, v, perm, blk_len, qp, kp, vp, S = _gpu_scores(hsa, w, step)
+    nb = perm.numel() // w.B
+    Sn = S.cpu().numpy()                         # float32 scores, exact in float64
+    if w.select == "topk":
+        p = hsa.make_params("topk", k=topk_k(w, nb))
+        max_kv = topk_k(w, nb)
+    else:
+        p = hsa.make_params("thresh_global", tau=w.tau, budget_ratio=wl.budget_ratio(w, step))
+        max_kv = nb
+    kv_idx, kv_cnt = hsa.hsa_select(S, w.heads, nb, p, max_kv)
+    torch.cuda.synchronize()
+    ref_idx, ref_cnt = oracle_select(w, Sn.astype(np.float64), nb, step)
+    assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), ref_idx, ref_cnt)
+    if w.select == "topk":
+        # against the float64 oracle scores: any difference must be a near-tie
+        ref_perm = perm.cpu().numpy().astype(np.int64)
+        S64 = oracle.score(oracle.gather(q.cpu(), ref_perm), oracle.gather(k.cpu(), ref_perm),
+                           ref_perm, w.B, w.s)
+        o_idx, _ = oracle.select_topk(S64, topk_k(w, nb))
+        g_idx = kv_idx.cpu().numpy()
+        flips = 0
+        for h in range(w.heads):
+            for i in range(nb):
+                a, b = set(o_idx[h, i]), set(g_idx[h, i])
+                if a != b:
+                    kth = np.sort(S64[h, i])[::-1][topk_k(w, nb) - 1]
+                    for j in a ^ b:
+                        flips += 1
+                        assert abs(S64[h, i, j] - kth) <= 2 * SCORE_TOL["mass"]
+        _say(f"  near-tie flips vs float64 scores: {flips}")
+
+
+@pytest.mark.parametrize("step", [0, 1, 5, 7, 8, 13])
+def test_lvsa_lists_bit_exact(hsa, step):
+    w = wl.get(4)
+    _say(f"lvsa lists step {step}")
+    nb = hsa.hsa_plan_size(w.T, w.H, w.W, "frame", w.B)[1]
+    tiles = nb // w.T
+    p = hsa.make_params("lvsa", frames=w.T, tiles_per_frame=tiles, C=w.C, T_per=w.T_per, step=step)
+    kv_idx, kv_cnt = hsa.hsa_select(None, w.heads, nb, p, w.C * tiles, device=dev())
+    torch.cuda.synchronize()
+    ref_idx, ref_cnt = oracle.select_lvsa(w.T, tiles, w.C, w.T_per, step, w.C * tiles)
+    assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), ref_idx, ref_cnt)
+
+
+@pytest.mark.parametrize("T,C,P,step", [(10, 5, 4, 1), (12, 3, 1, 2), (12, 30, 4, 3), (7, 2, 3, 0)])
+def test_lvsa_small_cases(hsa, T, C, P, step):
+    _say(f"lvsa small T={T} C={C} P={P} s={step}")
+    tiles = 3
+    sets = oracle.lvsa_frame_sets(T, C, P, step)
+    width = max(len(a) for a in sets) * tiles
+    p = hsa.make_params("lvsa", frames=T, tiles_per_frame=tiles, C=C, T_per=P, step=step)
+    kv_idx, kv_cnt = hsa.hsa_select(None, 1, T * tiles, p, width + 5, device=dev())
+    torch.cuda.synchronize()
+    ref_idx, ref_cnt = oracle.select_lvsa(T, tiles, C, P, step, width + 5)
+    assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), ref_idx, ref_cnt)
+
+
+def test_select_ties_and_edges(hsa):
+    """Exact ties resolve to the lowest index; k = nb keeps everything; the
+    threshold rule on tied rows and a zero budget."""
+    _say("select ties")
+    nh, nb = 3, 70
+    g = np.random.default_rng(12)
+    S = g.random((nh, nb, nb)).astype(np.float32)
+    S[0, 5, :] = 0.25
+    S[1, 3, ::4] = S[1, 3, 2]
+    S /= S.sum(axis=2, keepdims=True)
+    St = torch.from_numpy(S).to(dev())
+    for k in (1, 7, nb):
+        kv_idx, kv_cnt = hsa.hsa_select(St, nh, nb, hsa.make_params("topk", k=k), k)
+        ref = oracle.select_topk(S.astype(np.float64), k)
+        assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), *ref)
+    for tau, ratio in ((0.25, 0.0), (0.5, 0.3), (1e-12, 0.05), (0.0, 0.1), (0.999, 0.9), (2.0, 0.0)):
+        p = hsa.make_params("thresh_global", tau=tau, budget_ratio=ratio)
+        kv_idx, kv_cnt = hsa.hsa_select(St, nh, nb, p, nb)
+        ref = oracle.select_thresh_global(S.astype(np.float64), tau, ratio)
+        assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), *ref), (tau, ratio)
+
+
+# ---------------------------------------------------------------- attention / layer
+
+def _layer(hsa, w, step, mask=None):
+    q, k, v = (x.to(dev()) for x in wl.make_qkv(w, step))
+    L = hsa.layer_for_workload(w, device=dev())
+    if mask is not None:
+        L.reorder(q, k, v)
+        L.kv_idx.copy_(mask[0])
+        L.kv_cnt.copy_(mask[1])
+        L.attend()
+        o = L.restore()
+    else:
+        o = L.step(q, k, v, step=step, budget_ratio=wl.budget_ratio(w, step))
+    torch.cuda.synchronize()
+    return q, k, v, L, o
+
+
+def _check_layer(hsa, w, step, q, k, v, L, o, check_select=True):
+    perm = L.perm.cpu().numpy().astype(np.int64)
+    nb = perm.size // w.B
+    assert np.array_equal(perm, oracle.plan(w.T, w.H, w.W, w.order, w.B)[0])
+    kv_idx, kv_cnt = L.kv_idx.cpu().numpy(), L.kv_cnt.cpu().numpy()
+    if check_select:
+        S = None if w.select == "lvsa" else L.S.cpu().numpy().astype(np.float64)
+        ref = oracle_select(w, S, nb, step, max_kv=kv_idx.shape[2])
+        assert lists_equal(kv_idx, kv_cnt, *ref)
+    qp, kp, vp = (oracle.gather(x.cpu(), perm) for x in (q, k, v))
+    rows = attn_rows(w, step, perm)
+    ref_op, ref_lse = oracle.attn_blocks(qp, kp, vp, perm, w.B, kv_idx, kv_cnt, rows=rows)
+    op = to_np(L.op)
+    err = max_err_rows(op, ref_op, rows)
+    lse_err = max_err_rows(to_np(L.lse)[:, :, None], ref_lse[:, :, None], rows)
+    omax = max(float(np.abs(ref_op[h, r]).max()) for h, r in enumerate(rows))
+    _say(f"  workload {w.idx} step {step}: max|o err| = {err:.3e} (max|o| = {omax:.2f}), "
+         f"lse err = {lse_err:.3e}, rows/head = {len(rows[0])}")
+    assert err <= TOL[w.dtype]
+    assert lse_err <= (1e-4 if w.dtype == "f32" else 1e-3)
+    assert np.all(op[:, perm < 0] == 0), "pad query rows must be zero"
+    # the restored output is exactly the reordered output scattered back
+    assert np.array_equal(to_np(o), oracle.scatter(op, perm, w.N))
+
+
+@pytest.mark.parametrize("idx", [1, 2])
+def test_layer_all_rows(hsa, idx):
+    w = wl.get(idx)
+    _say(f"layer workload {idx} (all rows)")
+    _check_layer(hsa, w, 0, *_layer(hsa, w, 0))
+
+
+@pytest.mark.parametrize("idx,step", [(3, 0), (4, 0), (4, 5), (5, 0), (5, 9)])
+def test_layer_sampled_rows(hsa, idx, step):
+    w = wl.get(idx)
+    _say(f"layer workload {idx} step {step} (sampled rows)")
+    _check_layer(hsa, w, step, *_layer(hsa, w, step))
+
+
+def test_cached_mask_step(hsa):
+    """DFSAttn design 3: steps 1..4 of the Wan workload reuse the step-0 mask
+    and recompute attention on fresh Q/K/V."""
+    w = wl.get(3)
+    _say("cached mask step (workload 3, step 0 -> 2)")
+    q0, k0, v0 = (x.to(dev()) for x in wl.make_qkv(w, 0))
+    L = hsa.layer_for_workload(w, device=dev())
+    L.step(q0, k0, v0, step=0)
+    mask0 = (L.kv_idx.clone(), L.kv_cnt.clone())
+    q2, k2, v2 = (x.to(dev()) for x in wl.make_qkv(w, 2))
+    o = L.step(q2, k2, v2, step=2, reuse_mask=True)
+    torch.cuda.synchronize()
+    assert torch.equal(L.kv_idx, mask0[0])
+    _check_layer(hsa, w, 2, q2, k2, v2, L, o, check_select=False)
+
+
+@pytest.mark.parametrize("B,D,dtype", [(64, 64, "bf16"), (128, 128, "bf16"), (64, 128, "bf16"),
+                                       (128, 64, "bf16"), (64, 64, "f32"), (128, 128, "f32")])
+def test_full_keep_is_dense_attention(hsa, B, D, dtype):
+    """Keeping every block must give dense softmax attention (ragged grid)."""
+    _say(f"full keep B={B} D={D} {dtype}")
+    T, H, W, nh = 3, 9, 11, 2                       # 297 tokens: ragged last block
+    g = torch.Generator().manual_seed(B + D)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q, k, v = (torch.randn((1, T * H * W, nh, D), generator=g).to(tdt) for _ in range(3))
+    perm, blk_len = hsa.hsa_plan(T, H, W, "hilbert", B, device=dev())
+    nb = perm.numel() // B
+    qp, kp, vp = hsa.hsa_perm([x.to(dev()) for x in (q, k, v)], perm, perm.numel())
+    kv_idx = torch.arange(nb, dtype=torch.int32, device=dev()).repeat(nh, nb, 1).contiguous()
+    kv_cnt = torch.full((nh, nb), nb, dtype=torch.int32, device=dev())
+    op, lse = hsa.hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B)
+    o = hsa.hsa_unperm(op, perm, T * H * W)
+    torch.cuda.synchronize()
+    ref = oracle.attn_dense(*(x.double().numpy() for x in (q, k, v)))
+    err = np.abs(to_np(o) - ref).max()
+    _say(f"  max err vs dense = {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+def test_lists_with_single_and_repeated_blocks(hsa):
+    """Uneven list lengths (1 .. nb) across heads and query blocks."""
+    _say("uneven lists")
+    T, H, W, nh, B, D = 4, 16, 16, 3, 64, 64
+    g = torch.Generator().manual_seed(3)
+    q, k, v = (torch.randn((1, T * H * W, nh, D), generator=g).to(torch.bfloat16) for _ in range(3))
+    perm, blk_len = hsa.hsa_plan(T, H, W, "hilbert", B, device=dev())
+    nb = perm.numel() // B
+    rng = np.random.default_rng(4)
+    cnt = rng.integers(1, nb + 1, size=(nh, nb)).astype(np.int32)
+    idx = np.full((nh, nb, nb), -1, dtype=np.int32)
+    for h in range(nh):
+        for i in range(nb):
+            idx[h, i, :cnt[h, i]] = np.sort(rng.choice(nb, cnt[h, i], replace=False))
+    qp, kp, vp = hsa.hsa_perm([x.to(dev()) for x in (q, k, v)], perm, perm.numel())
+    op, _ = hsa.hsa_attn(qp, kp, vp, blk_len, torch.from_numpy(idx).to(dev()),
+                         torch.from_numpy(cnt).to(dev()), B)
+    torch.cuda.synchronize()
+    p = perm.cpu().numpy().astype(np.int64)
+    ref, _ = oracle.attn_blocks(*(oracle.gather(x, p) for x in (q, k, v)), p, B, idx, cnt)
+    assert np.abs(to_np(op) - ref).max() <= TOL["bf16"]
+
+
+def test_deterministic(hsa):
+    w = wl.get(2)
+    _say("determinism")
+    outs = []
+    for _ in range(2):
+        q, k, v, L, o = _layer(hsa, w, 0)
+        outs.append((o.clone(), L.S.clone(), L.kv_idx.clone(), L.lse.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
