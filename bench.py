@@ -53,10 +53,11 @@ def _traffic(w_idx):
     return c.get("hbm_bytes_per_launch")
 
 
-def _cpu_baseline(w, q, k, v, rows_per_head=512):
+def _cpu_baseline(w, q, k, v, blocks_per_head=32):
     """Time the CPU oracle on a bounded sample of the same layer: plan,
-    gather, scoring and selection on the whole problem, attention on
-    `rows_per_head` seeded query rows per head, extrapolated to every row."""
+    gather, scoring and selection on the whole problem, attention on every
+    row of `blocks_per_head` seeded query blocks per head, extrapolated
+    linearly to all query blocks."""
     import numpy as np
     import oracle
     import workloads as wl
@@ -70,21 +71,24 @@ def _cpu_baseline(w, q, k, v, rows_per_head=512):
     kk = w.k if w.k > 0 else max(1, int(math.floor(w.keep_ratio * nb + 0.5)))
     kv_idx, kv_cnt = oracle.select_topk(S, kk)
     t2 = time.perf_counter()
-    inv = oracle.inverse_perm(perm, w.N)
-    rows = [inv[wl.sample_rows(w, 0, h, rows_per_head)] for h in range(w.heads)]
+    nblk = min(blocks_per_head, nb)
+    rows = []
+    for h in range(w.heads):
+        blocks = wl.sample_blocks(w, 0, h, nb, nblk)
+        rows.append((blocks[:, None] * w.B + np.arange(w.B)[None, :]).ravel())
     oracle.attn_blocks(qp, kp, vp, perm, w.B, kv_idx, kv_cnt, rows=rows)
     t3 = time.perf_counter()
-    full_attn = (t3 - t2) * w.N / rows_per_head
+    full_attn = (t3 - t2) * nb / nblk
     layer_s = (t1 - t0) + (t2 - t1) + full_attn
     try:
         from threadpoolctl import threadpool_info
         blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         blas = 1
-    cores = len(os.sched_getaffinity(0))
     return dict(layer_s=layer_s, plan_gather_s=t1 - t0, score_select_s=t2 - t1,
                 attn_sample_s=t3 - t2, attn_extrapolated_s=full_attn, wall_s=t3 - t0,
-                cores=min(cores, blas) if blas > 1 else 1, rows_per_head=rows_per_head)
+                cores=max(1, min(len(os.sched_getaffinity(0)), blas)), blocks_per_head=nblk,
+                nb=nb)
 
 
 def main():
@@ -232,8 +236,9 @@ def main():
             "cores": cb["cores"], "kind": "oracle",
             "sample": (f"float64 numpy oracle on this host: plan+gather {cb['plan_gather_s']:.2f}s and "
                        f"score+select {cb['score_select_s']:.2f}s on the whole layer, attention on "
-                       f"{cb['rows_per_head']} seeded rows/head ({cb['attn_sample_s']:.2f}s) "
-                       f"extrapolated linearly to all {N} rows; layer {cb['layer_s']:.1f}s"),
+                       f"{cb['blocks_per_head']} seeded query blocks/head ({cb['attn_sample_s']:.2f}s) "
+                       f"extrapolated linearly to all {cb['nb']} blocks; layer {cb['layer_s']:.1f}s; "
+                       f"cores = BLAS threads"),
             "ms_per_layer": cb["layer_s"] * 1e3,
         }
     print(json.dumps(out), flush=True)

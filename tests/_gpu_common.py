@@ -41,17 +41,17 @@ def lists_equal(a_idx, a_cnt, b_idx, b_cnt):
 
 def attn_rows(w, step, perm):
     """Per-head slot indices the oracle evaluates: every real slot for small
-    workloads; otherwise the seeded token sample plus the first and last
-    blocks (so the ragged tail is always covered)."""
+    workloads; otherwise all rows of sample_rows/B seeded query blocks per
+    head (4096 rows at B = 128) plus the first and the ragged last block."""
     real = np.nonzero(perm >= 0)[0]
     if w.sample_rows == 0:
         return [real] * w.heads
-    inv = oracle.inverse_perm(perm, w.N)
     n_pad = perm.size
-    edge = np.concatenate([np.arange(0, w.B), np.arange(n_pad - w.B, n_pad)])
+    nb = n_pad // w.B
     rows = []
     for h in range(w.heads):
-        r = np.union1d(inv[wl.sample_rows(w, step, h)], edge)
+        blocks = np.union1d(wl.sample_blocks(w, step, h, nb), [0, nb - 1])
+        r = (blocks[:, None] * w.B + np.arange(w.B)[None, :]).ravel()
         rows.append(r[perm[r] >= 0])
     return rows
 

@@ -199,6 +199,7 @@ def test_select_ties_and_edges(hsa):
 # ---------------------------------------------------------------- attention / layer
 
 def _layer(hsa, w, step, mask=None):
+    _say(f"  generating inputs for workload {w.idx} step {step}")
     q, k, v = (x.to(dev()) for x in wl.make_qkv(w, step))
     L = hsa.layer_for_workload(w, device=dev())
     if mask is not None:
@@ -214,6 +215,7 @@ def _layer(hsa, w, step, mask=None):
 
 
 def _check_layer(hsa, w, step, q, k, v, L, o, check_select=True):
+    _say("  GPU layer done; checking plan and lists")
     perm = L.perm.cpu().numpy().astype(np.int64)
     nb = perm.size // w.B
     assert np.array_equal(perm, oracle.plan(w.T, w.H, w.W, w.order, w.B)[0])
@@ -222,6 +224,7 @@ def _check_layer(hsa, w, step, q, k, v, L, o, check_select=True):
         S = None if w.select == "lvsa" else L.S.cpu().numpy().astype(np.float64)
         ref = oracle_select(w, S, nb, step, max_kv=kv_idx.shape[2])
         assert lists_equal(kv_idx, kv_cnt, *ref)
+    _say("  lists ok; oracle attention on the sampled rows")
     qp, kp, vp = (oracle.gather(x.cpu(), perm) for x in (q, k, v))
     rows = attn_rows(w, step, perm)
     ref_op, ref_lse = oracle.attn_blocks(qp, kp, vp, perm, w.B, kv_idx, kv_cnt, rows=rows)

@@ -18,7 +18,8 @@ Input recipe (one generator per (workload, step, stream, head)):
 
 * seed = idx * 10**6 + step * 10**4 + stream * 10**3 + head, fed to
   ``numpy.random.default_rng``; streams: 0 = smoothed field, 1 = Q noise,
-  2 = K noise, 3 = i.i.d. Q, 4 = i.i.d. K, 5 = V, 9 = sampled query rows.
+  2 = K noise, 3 = i.i.d. Q, 4 = i.i.d. K, 5 = V, 8 = sampled query blocks,
+  9 = sampled query rows.
 * "iid": Q, K ~ N(0, 1) drawn in float64 as [N, D] per head.
 * "smooth": one field F per (head, channel) on the T x H x W latent grid,
   white noise smoothed by a Gaussian of sigma 2 cells (scipy.ndimage,
@@ -41,7 +42,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "get", "seed_of", "make_qkv", "sample_rows",
+__all__ = ["Workload", "WORKLOADS", "get", "seed_of", "make_qkv", "sample_rows", "sample_blocks",
            "budget_ratio", "n_tokens"]
 
 
@@ -184,6 +185,20 @@ def sample_rows(w: Workload | int, step: int, head: int, count: int | None = Non
         return np.arange(w.N, dtype=np.int64)
     rng = np.random.default_rng(seed_of(w.idx, step, 9, head))
     return np.sort(rng.choice(w.N, size=count, replace=False)).astype(np.int64)
+
+
+def sample_blocks(w: Workload | int, step: int, head: int, nb: int, count: int | None = None) -> np.ndarray:
+    """Seeded sorted draw without replacement of query blocks whose rows are
+    checked (count defaults to sample_rows / B, i.e. the same number of rows
+    as sample_rows, grouped by block so the key sets are gathered once)."""
+    if not isinstance(w, Workload):
+        w = get(w)
+    if count is None:
+        count = max(1, -(-w.sample_rows // w.B)) if w.sample_rows > 0 else nb
+    if count >= nb:
+        return np.arange(nb, dtype=np.int64)
+    rng = np.random.default_rng(seed_of(w.idx, step, 8, head))
+    return np.sort(rng.choice(nb, size=count, replace=False)).astype(np.int64)
 
 
 def topk_of(w: Workload, nb: int) -> int:
