@@ -129,7 +129,7 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         qp, kp, _ = L.xp
-        hsa.hsa_score(qp, kp, L.blk_len, B, w.s, "mass", L.scale, out=L.S, ws=L.score_ws)
+        hsa.hsa_score(qp, kp, L.blk_len, B, w.s, "mass", L.scale, out=L.S, pooled=L.pooled)
         if ev is not None:
             ev[2].record(stream)
         hsa.hsa_select(L.S, nh, nb, L.params(0, 0.0), L.max_kv, outs=(L.kv_idx, L.kv_cnt),
@@ -182,12 +182,16 @@ def main():
     t_attn = stage_ms["attn"] * 1e-3
     achieved = flop_tiles / t_attn / 1e12
     row = N * nh * D * esz
+    U = L.n_pad // w.s
+    pooled_bytes = 2 * nh * U * D * 4
     stage_bytes = {
-        "perm": 3 * 2 * row,
-        "score": 2 * row + nh * nb * nb * 4,
+        # Q, K, V read and written once, plus the Q/K sub-block means
+        "perm": 3 * 2 * row + pooled_bytes,
+        "score": pooled_bytes + nh * nb * nb * 4,
         "select": nh * nb * nb * 4 + nh * nb * (L.max_kv + 1) * 4,
         "unperm": 2 * row,
     }
+    score_flop = 2.0 * U * U * D * nh
     stages = {}
     for n in names:
         t = stage_ms[n] * 1e-3
@@ -195,6 +199,13 @@ def main():
             stages[n] = {"ms": stage_ms[n], "tflops_computed_tiles": achieved,
                          "tflops_useful": flop_useful / t / 1e12,
                          "frac_mfma_peak": achieved / BF16_PEAK_TFLOPS}
+        elif n == "score":
+            # pooling happens inside perm; what remains is the fp32 contraction
+            stages[n] = {"ms": stage_ms[n], "bytes": stage_bytes[n], "flop": score_flop,
+                         "tflops": score_flop / t / 1e12,
+                         "frac_fp32_mfma_peak": score_flop / t / 1e12 / FP32_PEAK_TFLOPS,
+                         "GB/s": stage_bytes[n] / t / 1e9,
+                         "frac_hbm_peak": stage_bytes[n] / t / 1e9 / HBM_PEAK_GBS}
         else:
             gbs = stage_bytes[n] / t / 1e9
             stages[n] = {"ms": stage_ms[n], "bytes": stage_bytes[n], "GB/s": gbs,

@@ -39,9 +39,10 @@ _SIGS = {
     "hsa_plan_size": (ctypes.c_int, [_c_i32] * 5 + [ctypes.POINTER(_c_i32)] * 2),
     "hsa_plan_ws_size": (_c_sz, [_c_i32] * 4),
     "hsa_plan": (ctypes.c_int, [_c_i32] * 5 + [_p, _p, _p, _c_sz, _p]),
-    "hsa_perm": (ctypes.c_int, [_c_i32, _p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _p]),
+    "hsa_perm": (ctypes.c_int, [_c_i32, _p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
+                                _c_i32, _p, _p]),
     "hsa_score_ws_size": (_c_sz, [_c_i32] * 4),
-    "hsa_score": (ctypes.c_int, [_p, _p, _p] + [_c_i32] * 7 + [_c_f32, _p, _p, _c_sz, _p]),
+    "hsa_score": (ctypes.c_int, [_p, _p, _p, _p] + [_c_i32] * 7 + [_c_f32, _p, _p, _c_sz, _p]),
     "hsa_select_ws_size": (_c_sz, [_c_i32, _c_i32, ctypes.POINTER(SelectParams)]),
     "hsa_select": (ctypes.c_int, [_p, _c_i32, _c_i32, ctypes.POINTER(SelectParams), _p, _p, _c_i32, _p, _c_sz, _p]),
     "hsa_attn": (ctypes.c_int, [_p] * 8 + [_c_i32] * 7 + [_c_f32, _p]),
@@ -119,8 +120,10 @@ def hsa_plan(T: int, H: int, W: int, order: str, B: int, device="cuda"):
     return perm, blk_len
 
 
-def hsa_perm(xs, perm: torch.Tensor, n_pad: int, outs=None):
-    """xs: list of [1, N, nh, D] (token stride may exceed nh*D) -> list of [nh, n_pad, D]."""
+def hsa_perm(xs, perm: torch.Tensor, n_pad: int, outs=None, pool_s: int = 0, pooled=None):
+    """xs: list of [1, N, nh, D] (token stride may exceed nh*D) -> list of [nh, n_pad, D].
+    With pool_s > 0 also fills `pooled` (float32 [2, nh, n_pad // pool_s, D], allocated if
+    None) with the sub-block means of xs[0] and xs[1]; returns (outs, pooled) then."""
     xs = list(xs)
     x0 = xs[0]
     _, N, nh, D = x0.shape
@@ -134,27 +137,35 @@ def hsa_perm(xs, perm: torch.Tensor, n_pad: int, outs=None):
     _need_device(perm)
     if outs is None:
         outs = [torch.empty((nh, n_pad, D), dtype=x0.dtype, device=x0.device) for _ in xs]
+    if pool_s and pooled is None:
+        pooled = torch.empty((2, nh, n_pad // pool_s, D), dtype=torch.float32, device=x0.device)
     src = (ctypes.c_void_p * len(xs))(*[x.data_ptr() for x in xs])
     dst = (ctypes.c_void_p * len(xs))(*[y.data_ptr() for y in outs])
     _check(lib().hsa_perm(len(xs), src, dst, _ptr(perm), N, n_pad, nh, D, x0.stride(1),
-                          _dtype_code(x0), _stream()), "hsa_perm")
-    return outs
+                          _dtype_code(x0), int(pool_s), _ptr(pooled if pool_s else None),
+                          _stream()), "hsa_perm")
+    return (outs, pooled) if pool_s else outs
 
 
 def hsa_score(qp, kp, blk_len, B: int, s: int, agg: str = "mass", scale: float | None = None,
-              out=None, ws=None):
-    """qp, kp [nh, n_pad, D] -> S float32 [nh, nb, nb]."""
-    _need_device(qp, kp, blk_len)
+              out=None, ws=None, pooled=None):
+    """qp, kp [nh, n_pad, D] -> S float32 [nh, nb, nb]. With `pooled` (the means
+    hsa_perm wrote for the same s) the pooling pass is skipped."""
+    _need_device(qp, kp, blk_len, pooled)
     nh, n_pad, D = qp.shape
     nb = n_pad // B
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     if out is None:
         out = torch.empty((nh, nb, nb), dtype=torch.float32, device=qp.device)
-    ws_n = lib().hsa_score_ws_size(nh, n_pad, s, D)
-    if ws is None:
-        ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=qp.device)
-    _check(lib().hsa_score(_ptr(qp), _ptr(kp), _ptr(blk_len), nh, nb, B, s, D, _dtype_code(qp),
-                           AGGS[agg], scale, _ptr(out), _ptr(ws), ws.numel(), _stream()),
+    ws_n = 0
+    if pooled is None:
+        ws_n = lib().hsa_score_ws_size(nh, n_pad, s, D)
+        if ws is None:
+            ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=qp.device)
+    _check(lib().hsa_score(_ptr(qp), _ptr(kp), _ptr(pooled), _ptr(blk_len), nh, nb, B, s, D,
+                           _dtype_code(qp), AGGS[agg], scale, _ptr(out),
+                           _ptr(ws if pooled is None else None),
+                           ws.numel() if (pooled is None and ws is not None) else 0, _stream()),
            "hsa_score")
     return out
 

@@ -32,14 +32,14 @@ size_t plan_hilbert_groups(int T, int H, int W, int &bits, uint32_t &cube);
 hsa_status_t launch_plan(int T, int H, int W, int order, int B, int n_pad, int nb, int32_t *perm,
                          int32_t *blk_len, void *ws, hipStream_t stream);
 hsa_status_t launch_perm(int n, const void *const *xs, void *const *xps, const int32_t *perm,
-                         int n_pad, int nh, int D, int64_t tok_stride, int esize,
-                         hipStream_t stream);
+                         int n_pad, int nh, int D, int64_t tok_stride, int esize, int pool_s,
+                         float *pooled, hipStream_t stream);
 hsa_status_t launch_unperm(const void *op, void *o, const int32_t *perm, int n_pad, int nh, int D,
                            int64_t tok_stride, int esize, hipStream_t stream);
 size_t score_ws_bytes(int nh, int n_pad, int s, int D);
-hsa_status_t launch_score(const void *qp, const void *kp, const int32_t *blk_len, int nh, int nb,
-                          int B, int s, int D, int dtype, int agg, float scale, float *S, void *ws,
-                          hipStream_t stream);
+hsa_status_t launch_score(const void *qp, const void *kp, const float *pooled,
+                          const int32_t *blk_len, int nh, int nb, int B, int s, int D, int dtype,
+                          int agg, float scale, float *S, void *ws, hipStream_t stream);
 size_t select_ws_bytes(int nh, int nb, int mode);
 hsa_status_t launch_select(const float *S, int nh, int nb, const hsa_select_params_t *p,
                            int32_t *kv_idx, int32_t *kv_cnt, int max_kv, void *ws,
@@ -140,7 +140,8 @@ hsa_status_t hsa_plan(int32_t T, int32_t H, int32_t W, int32_t order, int32_t B,
 
 hsa_status_t hsa_perm(int32_t n_tensors, const void *const *xs, void *const *xps,
                       const int32_t *perm, int32_t N, int32_t n_pad, int32_t nh, int32_t D,
-                      int64_t tok_stride, int32_t dtype, hsa_stream_t stream) {
+                      int64_t tok_stride, int32_t dtype, int32_t pool_s, float *pooled,
+                      hsa_stream_t stream) {
   g_last_error.clear();
   if (n_tensors < 1 || n_tensors > 3) return fail(HSA_ERR_BAD_ARG, "hsa_perm: n_tensors %d not in 1..3", n_tensors);
   if (!xs || !xps || !perm) return fail(HSA_ERR_NULL_PTR, "hsa_perm: null pointer array or perm");
@@ -153,9 +154,17 @@ hsa_status_t hsa_perm(int32_t n_tensors, const void *const *xs, void *const *xps
   const int es = esize_of(dtype);
   if ((tok_stride * es) % 16 != 0) return fail(HSA_ERR_BAD_ARG, "hsa_perm: token stride must be a multiple of 16 bytes");
   if (static_cast<int64_t>(nh) * n_pad * D >= (1ll << 40)) return fail(HSA_ERR_BAD_SHAPE, "hsa_perm: tensor too large");
+  if (static_cast<int64_t>(nh) * D * es / 16 > 1024) return fail(HSA_ERR_UNSUPPORTED, "hsa_perm: nh*D*elem_size must be <= 16 KB");
   for (int i = 0; i < n_tensors; ++i)
     if (!aligned16(xs[i]) || !aligned16(xps[i])) return fail(HSA_ERR_BAD_ARG, "hsa_perm: tensor %d not 16-byte aligned", i);
-  return launch_perm(n_tensors, xs, xps, perm, n_pad, nh, D, tok_stride, es, static_cast<hipStream_t>(stream));
+  if (pooled) {
+    if (pool_s != 16 && pool_s != 32 && pool_s != 64 && pool_s != 128) return fail(HSA_ERR_UNSUPPORTED, "hsa_perm: pool_s %d not in {16,32,64,128}", pool_s);
+    if (n_pad % pool_s) return fail(HSA_ERR_BAD_SHAPE, "hsa_perm: pool_s %d does not divide n_pad %d", pool_s, n_pad);
+    if (n_tensors < 2) return fail(HSA_ERR_BAD_ARG, "hsa_perm: pooling needs Q and K (n_tensors >= 2)");
+    if (!aligned16(pooled)) return fail(HSA_ERR_BAD_ARG, "hsa_perm: pooled must be 16-byte aligned");
+  }
+  return launch_perm(n_tensors, xs, xps, perm, n_pad, nh, D, tok_stride, es, pool_s, pooled,
+                     static_cast<hipStream_t>(stream));
 }
 
 size_t hsa_score_ws_size(int32_t nh, int32_t n_pad, int32_t s, int32_t D) {
@@ -163,11 +172,12 @@ size_t hsa_score_ws_size(int32_t nh, int32_t n_pad, int32_t s, int32_t D) {
   return score_ws_bytes(nh, n_pad, s, D);
 }
 
-hsa_status_t hsa_score(const void *qp, const void *kp, const int32_t *blk_len, int32_t nh,
-                       int32_t nb, int32_t B, int32_t s, int32_t D, int32_t dtype, int32_t agg,
-                       float scale, float *S, void *ws, size_t ws_bytes, hsa_stream_t stream) {
+hsa_status_t hsa_score(const void *qp, const void *kp, const float *pooled,
+                       const int32_t *blk_len, int32_t nh, int32_t nb, int32_t B, int32_t s,
+                       int32_t D, int32_t dtype, int32_t agg, float scale, float *S, void *ws,
+                       size_t ws_bytes, hsa_stream_t stream) {
   g_last_error.clear();
-  if (!qp || !kp || !blk_len || !S) return fail(HSA_ERR_NULL_PTR, "hsa_score: null input or output");
+  if ((!pooled && (!qp || !kp)) || !blk_len || !S) return fail(HSA_ERR_NULL_PTR, "hsa_score: null input or output");
   hsa_status_t st;
   if ((st = check_dtype(dtype)) != HSA_OK || (st = check_D(D)) != HSA_OK || (st = check_B(B)) != HSA_OK) return st;
   if (s != 16 && s != 32 && s != 64 && s != 128) return fail(HSA_ERR_UNSUPPORTED, "hsa_score: sub-block %d not in {16,32,64,128}", s);
@@ -176,11 +186,17 @@ hsa_status_t hsa_score(const void *qp, const void *kp, const int32_t *blk_len, i
   if (static_cast<int64_t>(nb) * (B / s) > 2048) return fail(HSA_ERR_UNSUPPORTED, "hsa_score: %lld sub-blocks > 2048", static_cast<long long>(nb) * (B / s));
   if (agg != HSA_AGG_MASS && agg != HSA_AGG_MAX) return fail(HSA_ERR_BAD_ARG, "hsa_score: unknown aggregation %d", agg);
   if (!(scale > 0.f) || !isfinite(scale)) return fail(HSA_ERR_BAD_ARG, "hsa_score: scale must be finite and positive");
-  if (!aligned16(qp) || !aligned16(kp) || !aligned16(S)) return fail(HSA_ERR_BAD_ARG, "hsa_score: buffers must be 16-byte aligned");
-  const size_t need = score_ws_bytes(nh, nb * B, s, D);
-  if (!ws || ws_bytes < need) return fail(HSA_ERR_WORKSPACE, "hsa_score: workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
-  if (!aligned16(ws)) return fail(HSA_ERR_BAD_ARG, "hsa_score: workspace must be 16-byte aligned");
-  return launch_score(qp, kp, blk_len, nh, nb, B, s, D, dtype, agg, scale, S, ws, static_cast<hipStream_t>(stream));
+  if (!aligned16(S)) return fail(HSA_ERR_BAD_ARG, "hsa_score: S must be 16-byte aligned");
+  if (pooled) {
+    if (!aligned16(pooled)) return fail(HSA_ERR_BAD_ARG, "hsa_score: pooled must be 16-byte aligned");
+  } else {
+    if (!aligned16(qp) || !aligned16(kp)) return fail(HSA_ERR_BAD_ARG, "hsa_score: buffers must be 16-byte aligned");
+    const size_t need = score_ws_bytes(nh, nb * B, s, D);
+    if (!ws || ws_bytes < need) return fail(HSA_ERR_WORKSPACE, "hsa_score: workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+    if (!aligned16(ws)) return fail(HSA_ERR_BAD_ARG, "hsa_score: workspace must be 16-byte aligned");
+  }
+  return launch_score(qp, kp, pooled, blk_len, nh, nb, B, s, D, dtype, agg, scale, S, ws,
+                      static_cast<hipStream_t>(stream));
 }
 
 size_t hsa_select_ws_size(int32_t nh, int32_t nb, const hsa_select_params_t *p) {
@@ -259,6 +275,7 @@ hsa_status_t hsa_unperm(const void *op, void *o, const int32_t *perm, int32_t N,
   if (tok_stride < static_cast<int64_t>(nh) * D) return fail(HSA_ERR_BAD_SHAPE, "hsa_unperm: tok_stride < nh*D");
   const int es = esize_of(dtype);
   if ((tok_stride * es) % 16 != 0) return fail(HSA_ERR_BAD_ARG, "hsa_unperm: token stride must be a multiple of 16 bytes");
+  if (static_cast<int64_t>(nh) * D * es / 16 > 1024) return fail(HSA_ERR_UNSUPPORTED, "hsa_unperm: nh*D*elem_size must be <= 16 KB");
   if (!aligned16(op) || !aligned16(o)) return fail(HSA_ERR_BAD_ARG, "hsa_unperm: tensors must be 16-byte aligned");
   return launch_unperm(op, o, perm, n_pad, nh, D, tok_stride, es, static_cast<hipStream_t>(stream));
 }

@@ -7,15 +7,19 @@
 //
 // bf16 kernel (gfx950 matrix cores, wave64):
 //  - one wave per 32 query rows; Q stays in registers as the B operand;
-//  - per listed key block: K tile staged row-major and V tile staged
-//    transposed in LDS (padded strides), then S^T = K Q^T on
-//    v_mfma_f32_32x32x16_bf16 so each lane holds 32-key runs of ONE query:
-//    the row max / row sum are in-lane plus one cross-half exchange;
-//  - online softmax in the log2 domain (scale folded with log2 e), keys
-//    beyond the block's real length masked to -inf;
+//  - per listed key block, K and V tiles go HBM/L2 -> LDS with direct
+//    (register-free) 16-byte loads into XOR-swizzled layouts; the next
+//    tile's K is requested as soon as S is computed and its V as soon as the
+//    value product is done, each waited for with its own vmcnt threshold;
+//  - S^T = K Q^T on v_mfma_f32_32x32x16_bf16 so each lane holds 32-key runs
+//    of ONE query: the row max / row sum are in-lane plus one cross-half
+//    exchange;
+//  - online softmax in the log2 domain (scale folded into one FMA), keys
+//    beyond a ragged block's real length masked to -inf, and a lazy rescale
+//    that only touches O when a row max grows by more than 2^8;
 //  - P is rounded to bf16 straight from the accumulator layout and used as
-//    the B operand of O^T += V^T P^T; the key order inside each 16-key slice
-//    follows the accumulator layout and the V^T reads use the same order;
+//    the B operand of O^T += V^T P^T; V^T comes from the row-major V tile via
+//    ds_read_b64_tr_b16 (no transpose pass) in the accumulator's key order;
 //  - epilogue divides by the row sum, rounds to bf16, zeroes pad rows and
 //    writes the natural-log log-sum-exp.
 // f32 kernel: a plain one-thread-per-query online-softmax loop with K/V tiles
@@ -24,37 +28,136 @@
 
 namespace hsa {
 
-template <int D, int BK>
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// One 16-byte-per-lane direct global->LDS load: lane l's 16 bytes come from
+// sbase + voff (sbase wave-uniform) and land at lds_base + 16*l. Issued from
+// asm so the compiler does not add blanket vmcnt(0) waits in front of
+// unrelated LDS reads; the caller waits with wait_vmcnt() and a barrier
+// before the data is read. No register is written.
+__device__ __forceinline__ void load_lds16(const void *sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding), leaving the other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// Generic pointer to a __shared__ object -> LDS pointer / LDS byte address.
+__device__ __forceinline__ lds_char_t *to_lds(const void *p) { return (lds_char_t *)(p); }
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>((uintptr_t)to_lds(p));
+}
+
+// Tile layouts in LDS: BK rows (keys) of CPR 16-byte chunks (D bf16 each).
+// K: chunk c of row r sits at slot c ^ (r mod CPR) so the 32 lanes reading a
+//    fragment (32 rows, one chunk) hit distinct banks.
+// V: chunk c of row r sits at slot c ^ ((4 (r mod 4)) mod CPR) so the
+//    transposed reads (4 rows x 4 chunks per half-wave) hit distinct banks.
+template <int CPR>
+__device__ __forceinline__ int k_slot(int r, int c) { return r * CPR + (c ^ (r & (CPR - 1))); }
+template <int CPR>
+__device__ __forceinline__ int v_slot(int r, int c) { return r * CPR + (c ^ (((r & 3) << 2) & (CPR - 1))); }
+
+// Per-lane byte offsets (within a 1 KB slice) of the direct tile loads.
+// A wave's i-th load fills LDS slots P = (w*NI + i)*64 + lane, i.e. rows
+// r = (w*NI + i)*(64/CPR) + lane/CPR, physical chunk lane%CPR; it reads the
+// logical chunk that the swizzle stores there. The swizzle key depends on
+// r mod CPR (K) or r mod 4 (V), which repeats every 4 loads (K) or never
+// changes (V), so 4 offsets cover every load.
+template <int D, bool IS_V>
+__device__ __forceinline__ uint32_t tile_lane_offset(int i, int lane) {
+  constexpr int CPR = D / 8;
+  const int r = i * (64 / CPR) + lane / CPR;   // row within the slice group, mod 16 exact
+  const int cs = lane & (CPR - 1);
+  const int c = IS_V ? (cs ^ (((r & 3) << 2) & (CPR - 1))) : (cs ^ (r & (CPR - 1)));
+  return static_cast<uint32_t>((lane / CPR) * D * 2 + c * 16);
+}
+
+// Issue the direct loads of one BKxD bf16 tile (row-major in HBM) into a
+// swizzled LDS tile; each wave moves NI consecutive 1 KB slices.
+template <int D, int BK, int NW>
+__device__ __forceinline__ void issue_tile(const uint16_t *gtile, uint32_t lds_tile, int w,
+                                           const uint32_t (&loff)[4]) {
+  constexpr int CPR = D / 8;
+  constexpr int NI = BK * CPR / (64 * NW);
+  static_assert(CPR == 8 || NI % 4 == 0, "the swizzle key must not depend on the wave");
+  const char *gbase = reinterpret_cast<const char *>(gtile) + w * NI * 1024;
+  const uint32_t lbase = lds_tile + w * NI * 1024;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    load_lds16(gbase + i * 1024, loff[i & 3], lbase + i * 1024);
+}
+
+template <int D, int BK, bool LSE>
 __global__ void __launch_bounds__(BK * 2, 2)
 attn_bf16_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
                  const uint16_t *__restrict__ vp, uint16_t *__restrict__ op,
                  float *__restrict__ lse, const int32_t *__restrict__ blk_len,
                  const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt,
                  int max_kv, int kv_shared, int nh, int nb, float scale_log2) {
-  constexpr int NW = BK / 32;  // waves per workgroup, 32 query rows each
-  constexpr int NT = NW * 64;
-  constexpr int KS = D + 8;    // LDS stride of a K row (elements)
-  constexpr int VS = BK + 4;   // LDS stride of a V^T row (elements)
-  constexpr int MT = BK / 32;  // 32-key slices of a tile
-  constexpr int DK = D / 16;   // 16-wide k-steps over the head dim
-  constexpr int DM = D / 32;   // 32-row slices of the head dim
-  constexpr int PK = BK / 16;  // 16-key k-steps of the value product
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BK * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VS];
+  constexpr int NW = BK / 32;   // waves per workgroup, 32 query rows each
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int NI = BK * CPR / (64 * NW);  // direct loads per wave per tile
+  constexpr int MT = BK / 32;   // 32-key slices of a tile
+  constexpr int DK = D / 16;    // 16-wide k-steps over the head dim
+  constexpr int DM = D / 32;    // 32-row slices of the head dim
+  constexpr int PK = BK / 16;   // 16-key k-steps of the value product
+  constexpr float kLazy = 8.f;  // rescale only when a row max grows by > 2^8
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[BK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[BK * D];
 
   const int total = nh * nb;
   const int bid = xcd_remap(blockIdx.x, total);
   const int h = bid / nb, I = bid - (bid / nb) * nb;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    koff[i] = tile_lane_offset<D, false>(i, lane);
+    voff[i] = tile_lane_offset<D, true>(i, lane);
+  }
   const int g = lane >> 5, ln = lane & 31;
   const int64_t head_off = static_cast<int64_t>(h) * nb * BK * D;
   const int qslot = I * BK + w * 32 + ln;
+  const uint32_t ldsK = lds_addr(sK), ldsV = lds_addr(sV);
+  lds_char_t *const vl = to_lds(sV);
 
+  const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
+  const int cnt = kv_cnt[lrow];
+  const int32_t *list = kv_idx + lrow * max_kv;
+  const uint16_t *kbase = kp + head_off;
+  const uint16_t *vbase = vp + head_off;
+
+  // Q first, and retired before any direct load is in flight: the empty asm
+  // reads every Q register, so the compiler places its waits for the Q loads
+  // here rather than inside the loop, where they would also stall on the
+  // asynchronous K/V traffic it cannot see.
   bf16x8 qf[DK];
   {
     const uint16_t *qrow = qp + head_off + static_cast<int64_t>(qslot) * D + g * 8;
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qrow + ks * 16);
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) asm volatile("" ::"v"(qf[ks]));
+  }
+
+  int J = cnt > 0 ? list[0] : 0;
+  if (cnt > 0) {
+    issue_tile<D, BK, NW>(kbase + static_cast<int64_t>(J) * BK * D, ldsK, w, koff);
+    issue_tile<D, BK, NW>(vbase + static_cast<int64_t>(J) * BK * D, ldsV, w, voff);
   }
 
   f32x16 oacc[DM];
@@ -62,103 +165,128 @@ attn_bf16_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ k
   for (int md = 0; md < DM; ++md)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;
-  float m_run = -1e30f, l_run = 0.f;
+  float m_ref = -1e30f, l_run = 0.f, e_run = 0.f;
 
-  const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
-  const int cnt = kv_cnt[lrow];
-  const int32_t *list = kv_idx + lrow * max_kv;
+  // Per-lane LDS chunk offsets. K fragment (slice mt, k-step ks): row
+  // mt*32 + ln, chunk (2ks + g) ^ (ln mod CPR). V transposed read (head-dim
+  // slice md, key step ks2): within each 16-lane group the source lane jj
+  // addresses key row ks2*16 + g*4 + jj/4 (+8 for the upper half) and
+  // head-dim column md*32 + (group&1)*16 + 4(jj%4); the swizzle key of those
+  // rows is 4(jj/4), which only touches the chunk bits that md sets.
+  int kofs[DK];
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) kofs[ks] = ln * CPR + ((2 * ks + g) ^ (ln & (CPR - 1)));
+  const int q16 = lane >> 4, jj = lane & 15;
+  int vofs[DM];  // byte offsets
+#pragma unroll
+  for (int md = 0; md < DM; ++md) {
+    const int col = md * 32 + (q16 & 1) * 16 + 4 * (jj & 3);
+    const int chunk = (col >> 3) ^ ((jj & 12) & (CPR - 1));
+    vofs[md] = ((g * 4 + (jj >> 2)) * CPR + chunk) * 16 + ((col >> 2) & 1) * 8;
+  }
 
   for (int c = 0; c < cnt; ++c) {
-    const int J = list[c];
     const int kvalid = blk_len[J];
-    const uint16_t *kt = kp + head_off + static_cast<int64_t>(J) * BK * D;
-    const uint16_t *vt = vp + head_off + static_cast<int64_t>(J) * BK * D;
-    // K tile, row-major: 16-byte chunks, consecutive lanes along a row.
-#pragma unroll
-    for (int ch = tid; ch < BK * D / 8; ch += NT) {
-      const int row = ch / (D / 8), col = (ch - row * (D / 8)) * 8;
-      *reinterpret_cast<uint4 *>(&sK[row * KS + col]) =
-          *reinterpret_cast<const uint4 *>(kt + row * D + col);
-    }
-    // V tile, transposed: each lane takes two consecutive keys of one
-    // 8-wide column chunk and writes 8 key-pair words.
-#pragma unroll
-    for (int ch = tid; ch < (BK / 2) * (D / 8); ch += NT) {
-      const int kpair = ch % (BK / 2), dc = ch / (BK / 2);
-      const uint4 a = *reinterpret_cast<const uint4 *>(vt + (2 * kpair) * D + dc * 8);
-      const uint4 b = *reinterpret_cast<const uint4 *>(vt + (2 * kpair + 1) * D + dc * 8);
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-      const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t lo = (j & 1) ? (aw[j >> 1] >> 16) : (aw[j >> 1] & 0xFFFFu);
-        const uint32_t hi = (j & 1) ? (bw[j >> 1] & 0xFFFF0000u) : (bw[j >> 1] << 16);
-        *reinterpret_cast<uint32_t *>(&sV[(dc * 8 + j) * VS + 2 * kpair]) = lo | hi;
-      }
-    }
-    __syncthreads();
+    const bool more = c + 1 < cnt;
+    const int Jn = more ? list[c + 1] : J;
 
-    // S^T: rows = keys, columns = this wave's 32 queries.
+    // K(c) has landed once only V(c)'s NI loads may still be outstanding.
+    wait_vmcnt<NI>();
+    __syncthreads();
     f32x16 sacc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
+      // all k-step fragments of the slice first, so the reads overlap
+      bf16x8 kf[DK];
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks)
+        kf[ks] = *reinterpret_cast<const bf16x8 *>(&sK[(mt * 32 * CPR + kofs[ks]) * 8]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[mt][i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&sK[(mt * 32 + ln) * KS + ks * 16 + g * 8]);
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
-      }
+      for (int ks = 0; ks < DK; ++ks)
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[mt], 0, 0, 0);
     }
-    // Accumulator element i of slice mt is key mt*32 + (i/4)*8 + g*4 + i%4.
-    float mx = -1e30f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = mt * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        const float s = (key < kvalid) ? sacc[mt][i] * scale_log2 : -INFINITY;
-        sacc[mt][i] = s;
-        mx = fmaxf(mx, s);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    float rs = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(sacc[mt][i] - m_new);
-        sacc[mt][i] = p;
-        rs += p;
-      }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int md = 0; md < DM; ++md)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[md][i] *= alpha;
+    __syncthreads();  // every wave is done with K(c)
+    if (more) issue_tile<D, BK, NW>(kbase + static_cast<int64_t>(Jn) * BK * D, ldsK, w, koff);
 
-    // O^T += V^T P^T over 16-key steps. Step ks2 takes accumulator elements
-    // (ks2%2)*8 + j of slice ks2/2: keys ks2*16 + g*4 + {0..3} and
-    // ks2*16 + 8 + g*4 + {0..3}; the V^T operand reads the same keys.
+    // Accumulator element i of slice mt is key mt*32 + (i/4)*8 + g*4 + i%4.
+    if (kvalid < BK) {
+      // key = g*4 + (a compile-time offset): compare the offset against one
+      // per-lane limit instead of materialising 64 key indices
+      const int lim = kvalid - g * 4;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (mt * 32 + (i >> 2) * 8 + (i & 3) >= lim) sacc[mt][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    // Lazy rescale: keep the reference max unless some row grew past it by
+    // more than 2^8 (p stays <= 256, exact in float and bf16 range).
+    if (__any(mx > m_ref + kLazy)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_run *= alpha;
+      e_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < DM; ++md)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[md][i] *= alpha;
+      m_ref = m_new;
+    }
+    // V(c) has landed once only K(c+1)'s loads may still be outstanding.
+    if (more) wait_vmcnt<NI>(); else wait_vmcnt<0>();
+    __syncthreads();
+    // P (bf16) straight from the accumulator layout, then O^T += V^T P^T.
+    // Step ks2 uses accumulator elements (ks2%2)*8 + j of slice ks2/2: keys
+    // ks2*16 + g*4 + {0..3} and ks2*16 + 8 + g*4 + {0..3}; the two transposed
+    // V reads deliver the same keys for the lane's head-dim column.
+    float rs = 0.f, es = 0.f;  // sums of the rounded and of the exact weights
 #pragma unroll
     for (int ks2 = 0; ks2 < PK; ++ks2) {
-      bf16x8 pf;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pf[j] = static_cast<__bf16>(sacc[ks2 >> 1][(ks2 & 1) * 8 + j]);
+      bf16x8 va[DM];
 #pragma unroll
       for (int md = 0; md < DM; ++md) {
-        const uint16_t *vr = &sV[(md * 32 + ln) * VS + ks2 * 16 + g * 4];
-        const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 8);
-        const uint4 packed = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, packed);
-        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf, oacc[md], 0, 0, 0);
+        lds_i16x4_t *a0 = (lds_i16x4_t *)(vl + vofs[md] + ks2 * 16 * CPR * 16);
+        lds_i16x4_t *a1 = (lds_i16x4_t *)(vl + vofs[md] + (ks2 * 16 + 8) * CPR * 16);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1);
+        const i16x8_t both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        va[md] = __builtin_bit_cast(bf16x8, both);
       }
+      // v_exp_f32 directly: weights below 2^-126 of the row max flush to 0.
+      // The row sum adds the bf16-rounded weights the value product uses, so
+      // the output stays a convex combination of values (a single dominant
+      // key passes its value through without the weight's rounding error).
+      bf16x8 pf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[ks2 >> 1][(ks2 & 1) * 8 + j], scale_log2, -m_ref));
+        if constexpr (LSE) es += p;
+        pf[j] = static_cast<__bf16>(p);
+      }
+      // one v_dot2 against (1, 1) adds both rounded weights of a packed pair
+      const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+      const bf16x2 p01 = {pf[0], pf[1]}, p23 = {pf[2], pf[3]}, p45 = {pf[4], pf[5]}, p67 = {pf[6], pf[7]};
+      rs = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, rs, false);
+      rs = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, rs, false);
+      rs = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, rs, false);
+      rs = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, rs, false);
+#pragma unroll
+      for (int md = 0; md < DM; ++md)
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[md], pf, oacc[md], 0, 0, 0);
     }
-    __syncthreads();
+    l_run += rs;
+    e_run += es;
+    __syncthreads();  // every wave is done with V(c)
+    if (more) issue_tile<D, BK, NW>(vbase + static_cast<int64_t>(Jn) * BK * D, ldsV, w, voff);
+    J = Jn;
   }
 
   // Epilogue: lane holds query ln, head-dim rows md*32 + (i/4)*8 + g*4 + i%4.
@@ -177,9 +305,14 @@ attn_bf16_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ k
                           (static_cast<uint32_t>(f32_to_bf16(oacc[md][i4 * 4 + 3] * inv)) << 16);
       *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(w0, w1);
     }
-  if (lse != nullptr && g == 0) {
-    const float ln2 = 0.6931471805599453f;
-    lse[static_cast<int64_t>(h) * nb * BK + qslot] = real ? (m_run + log2f(l_tot)) * ln2 : 0.f;
+  if constexpr (LSE) {
+    // log-sum-exp of the exact (unrounded) weights
+    const float e_tot = e_run + __shfl_xor(e_run, 32, 64);
+    if (g == 0) {
+      const float ln2 = 0.6931471805599453f;
+      lse[static_cast<int64_t>(h) * nb * BK + qslot] =
+          (real && e_tot > 0.f) ? (m_ref + log2f(e_tot)) * ln2 : 0.f;
+    }
   }
 }
 
@@ -261,10 +394,15 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                    *v = static_cast<const uint16_t *>(vp);
     uint16_t *o = static_cast<uint16_t *>(op);
     const dim3 block(B * 2);
-    if (D == 128 && B == 128) launch_k(hsa::attn_bf16_kernel<128, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, scale_log2);
-    else if (D == 64 && B == 128) launch_k(hsa::attn_bf16_kernel<64, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, scale_log2);
-    else if (D == 128 && B == 64) launch_k(hsa::attn_bf16_kernel<128, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, scale_log2);
-    else launch_k(hsa::attn_bf16_kernel<64, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, scale_log2);
+#define HSA_ATTN_BF16(DD, BB, L)                                                              \
+  launch_k(hsa::attn_bf16_kernel<DD, BB, L>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, \
+           kv_cnt, max_kv, kv_shared, nh, nb, scale_log2)
+    const bool L = lse != nullptr;
+    if (D == 128 && B == 128) { if (L) HSA_ATTN_BF16(128, 128, true); else HSA_ATTN_BF16(128, 128, false); }
+    else if (D == 64 && B == 128) { if (L) HSA_ATTN_BF16(64, 128, true); else HSA_ATTN_BF16(64, 128, false); }
+    else if (D == 128 && B == 64) { if (L) HSA_ATTN_BF16(128, 64, true); else HSA_ATTN_BF16(128, 64, false); }
+    else { if (L) HSA_ATTN_BF16(64, 64, true); else HSA_ATTN_BF16(64, 64, false); }
+#undef HSA_ATTN_BF16
   } else {
     const float *q = static_cast<const float *>(qp), *k = static_cast<const float *>(kp),
                 *v = static_cast<const float *>(vp);

@@ -5,7 +5,8 @@
 // importance. Two kernels:
 //  1. pool: sub-block means of Qp and Kp over real tokens (float32). A pure
 //     HBM stream: one wave per sub-block, 16-byte loads, a butterfly
-//     reduction across the lanes that share a column group.
+//     reduction across the lanes that share a column group. Skipped when the
+//     caller passes the means hsa_perm computed while reordering.
 //  2. contract + aggregate: per head, a strip of 16 query sub-blocks against
 //     all key sub-blocks on float32 matrix cores (v_mfma_f32_16x16x4_f32),
 //     logits kept in registers; the MASS softmax (count-weighted, max
@@ -21,7 +22,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kPoolWaves * 64)
 pool_kernel(const T *__restrict__ qp, const T *__restrict__ kp, const int32_t *__restrict__ blk_len,
             int n_pad, int nsub, int s, int R, float *__restrict__ means /* [2][nh][nsub][D] */,
-            int32_t *__restrict__ counts, int nh) {
+            int nh) {
   constexpr int kCols = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int kGroups = D / kCols;     // lanes per row
   constexpr int kRows = 64 / kGroups;    // rows per load instruction
@@ -69,7 +70,6 @@ pool_kernel(const T *__restrict__ qp, const T *__restrict__ kp, const int32_t *_
           make_float4(acc[j] * inv, acc[j + 1] * inv, acc[j + 2] * inv, acc[j + 3] * inv);
     }
   }
-  if (which == 0 && h == 0 && lane == 0) counts[u] = c;
 }
 
 // Sum (or max) across the R lanes of a query block: lanes u0..u0+15 hold
@@ -82,13 +82,19 @@ __device__ __forceinline__ float reduce_block_lanes(float v, int R, bool take_ma
   return v;
 }
 
-template <int D, int MAXT, bool MAXAGG>
-__global__ void __launch_bounds__(256)
+// Real tokens of sub-block v (real tokens are the first blk_len slots of a block).
+__device__ __forceinline__ int sub_count(const int32_t *blk_len, int v, int R, int s) {
+  const int I = v / R;
+  return min(max(blk_len[I] - (v - I * R) * s, 0), s);
+}
+
+template <int D, int NWV, int MAXT, bool MAXAGG>
+__global__ void __launch_bounds__(NWV * 64)
 contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
-                const int32_t *__restrict__ counts, int U, int R, int nb, float scale,
+                const int32_t *__restrict__ blk_len, int s, int U, int R, int nb, float scale,
                 float *__restrict__ S) {
   constexpr int DQ = D / 4;  // k-slots per lane group
-  __shared__ float red[4][16];
+  __shared__ float red[NWV][16];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int ul = lane & 15;
@@ -97,7 +103,7 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
   const int u0 = blockIdx.x * 16;
   const int u = u0 + ul;
   const int tiles = (U + 15) / 16;
-  const int VT = (tiles + 3) / 4;  // tiles per wave (<= MAXT)
+  const int VT = (tiles + NWV - 1) / NWV;  // tiles per wave (<= MAXT)
   const float *qb = qbar + static_cast<int64_t>(h) * U * D;
   const float *kb = kbar + static_cast<int64_t>(h) * U * D;
 
@@ -112,7 +118,7 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
 #pragma unroll
     for (int j = 0; j < DQ; ++j) qreg[j] = 0.f;
   }
-  const int cu = (u < U) ? counts[u] : 0;
+  const int cu = (u < U) ? sub_count(blk_len, u, R, s) : 0;
 
   // Logits z[t][r]: query sub-block u, key sub-block v = v0 + 4g + r.
   float z[MAXT][4];  // -inf marks an empty key sub-block
@@ -120,30 +126,28 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
   for (int t = 0; t < MAXT; ++t) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) z[t][r] = -INFINITY;
-    if (t < VT) {
-      const int v0 = (w * VT + t) * 16;
-      if (v0 < U) {
-        const int vrow = v0 + ul;
-        float kreg[DQ];
-        if (vrow < U) {
+    const int v0 = (w * VT + t) * 16;
+    if (t < VT && v0 < U) {
+      const int vrow = v0 + ul;
+      float kreg[DQ];
+      if (vrow < U) {
 #pragma unroll
-          for (int j = 0; j < DQ; j += 4) {
-            const float4 tt = *reinterpret_cast<const float4 *>(kb + static_cast<int64_t>(vrow) * D + g * DQ + j);
-            kreg[j] = tt.x; kreg[j + 1] = tt.y; kreg[j + 2] = tt.z; kreg[j + 3] = tt.w;
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < DQ; ++j) kreg[j] = 0.f;
+        for (int j = 0; j < DQ; j += 4) {
+          const float4 tt = *reinterpret_cast<const float4 *>(kb + static_cast<int64_t>(vrow) * D + g * DQ + j);
+          kreg[j] = tt.x; kreg[j + 1] = tt.y; kreg[j + 2] = tt.z; kreg[j + 3] = tt.w;
         }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      } else {
 #pragma unroll
-        for (int j = 0; j < DQ; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kreg[j], qreg[j], acc, 0, 0, 0);
+        for (int j = 0; j < DQ; ++j) kreg[j] = 0.f;
+      }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int v = v0 + 4 * g + r;
-          const int c = (v < U) ? counts[v] : 0;
-          if (c > 0 && cu > 0) z[t][r] = acc[r] * scale;
-        }
+      for (int j = 0; j < DQ; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kreg[j], qreg[j], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = v0 + 4 * g + r;
+        const int c = (v < U) ? sub_count(blk_len, v, R, s) : 0;
+        if (c > 0 && cu > 0) z[t][r] = acc[r] * scale;
       }
     }
   }
@@ -159,7 +163,9 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
     m = fmaxf(m, __shfl_xor(m, 32, 64));
     if (g == 0) red[w][ul] = m;
     __syncthreads();
-    m = fmaxf(fmaxf(red[0][ul], red[1][ul]), fmaxf(red[2][ul], red[3][ul]));
+    m = red[0][ul];
+#pragma unroll
+    for (int i = 1; i < NWV; ++i) m = fmaxf(m, red[i][ul]);
     __syncthreads();
     // Count-weighted exponentials and their row sum.
     float den = 0.f;
@@ -169,7 +175,8 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float e = 0.f;
-        if (t < VT && z[t][r] != -INFINITY) e = static_cast<float>(counts[v0 + r]) * expf(z[t][r] - m);
+        if (t < VT && z[t][r] != -INFINITY)
+          e = static_cast<float>(sub_count(blk_len, v0 + r, R, s)) * expf(z[t][r] - m);
         z[t][r] = e;
         den += e;
       }
@@ -178,7 +185,9 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
     den += __shfl_xor(den, 32, 64);
     if (g == 0) red[w][ul] = den;
     __syncthreads();
-    den = (red[0][ul] + red[1][ul]) + (red[2][ul] + red[3][ul]);
+    den = 0.f;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) den += red[i][ul];
     const float wu = (den > 0.f) ? static_cast<float>(cu) / den : 0.f;
     const float cblk = reduce_block_lanes(static_cast<float>(cu), R, false);
     const float inv_c = cblk > 0.f ? 1.f / cblk : 0.f;
@@ -262,58 +271,59 @@ namespace hsa_host {
 
 size_t score_ws_bytes(int nh, int n_pad, int s, int D) {
   const size_t U = static_cast<size_t>(n_pad / s);
-  size_t means = 2ull * nh * U * D * sizeof(float);
-  means = (means + 255) & ~static_cast<size_t>(255);
-  return means + U * sizeof(int32_t);
+  return 2ull * nh * U * D * sizeof(float);
 }
 
 template <int D, bool MAXAGG>
-static void launch_contract(int U, dim3 grid, const float *qb, const float *kb, const int32_t *cnt,
-                            int R, int nb, float scale, float *S, hipStream_t stream) {
+static void launch_contract(int U, dim3 grid, const float *qb, const float *kb,
+                            const int32_t *blk_len, int s, int R, int nb, float scale, float *S,
+                            hipStream_t stream) {
+  // Many short waves per workgroup (each owns a few 16-wide key tiles) keep
+  // enough independent loads and MFMA chains in flight per SIMD.
   const int tiles = (U + 15) / 16;
-  const int VT = (tiles + 3) / 4;
-  if (VT <= 4)
-    hipLaunchKernelGGL((hsa::contract_kernel<D, 4, MAXAGG>), grid, dim3(256), 0, stream, qb, kb, cnt, U, R, nb, scale, S);
-  else if (VT <= 16)
-    hipLaunchKernelGGL((hsa::contract_kernel<D, 16, MAXAGG>), grid, dim3(256), 0, stream, qb, kb, cnt, U, R, nb, scale, S);
+  if (tiles <= 16)
+    hipLaunchKernelGGL((hsa::contract_kernel<D, 4, 4, MAXAGG>), grid, dim3(256), 0, stream, qb, kb, blk_len, s, U, R, nb, scale, S);
+  else if (tiles <= 64)
+    hipLaunchKernelGGL((hsa::contract_kernel<D, 16, 4, MAXAGG>), grid, dim3(1024), 0, stream, qb, kb, blk_len, s, U, R, nb, scale, S);
   else
-    hipLaunchKernelGGL((hsa::contract_kernel<D, 32, MAXAGG>), grid, dim3(256), 0, stream, qb, kb, cnt, U, R, nb, scale, S);
+    hipLaunchKernelGGL((hsa::contract_kernel<D, 16, 8, MAXAGG>), grid, dim3(1024), 0, stream, qb, kb, blk_len, s, U, R, nb, scale, S);
 }
 
-hsa_status_t launch_score(const void *qp, const void *kp, const int32_t *blk_len, int nh, int nb,
-                          int B, int s, int D, int dtype, int agg, float scale, float *S, void *ws,
-                          hipStream_t stream) {
+hsa_status_t launch_score(const void *qp, const void *kp, const float *pooled,
+                          const int32_t *blk_len, int nh, int nb, int B, int s, int D, int dtype,
+                          int agg, float scale, float *S, void *ws, hipStream_t stream) {
   const int n_pad = nb * B;
   const int U = n_pad / s;
   const int R = B / s;
-  float *means = static_cast<float *>(ws);
-  size_t off = 2ull * nh * U * D * sizeof(float);
-  off = (off + 255) & ~static_cast<size_t>(255);
-  int32_t *counts = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + off);
-  const dim3 pgrid((U + hsa::kPoolWaves - 1) / hsa::kPoolWaves, nh, 2);
-  const dim3 pblock(hsa::kPoolWaves * 64);
-  if (dtype == HSA_BF16) {
-    const uint16_t *q = static_cast<const uint16_t *>(qp), *k = static_cast<const uint16_t *>(kp);
-    if (D == 128)
-      hipLaunchKernelGGL((hsa::pool_kernel<uint16_t, 128>), pgrid, pblock, 0, stream, q, k, blk_len, n_pad, U, s, R, means, counts, nh);
-    else
-      hipLaunchKernelGGL((hsa::pool_kernel<uint16_t, 64>), pgrid, pblock, 0, stream, q, k, blk_len, n_pad, U, s, R, means, counts, nh);
-  } else {
-    const float *q = static_cast<const float *>(qp), *k = static_cast<const float *>(kp);
-    if (D == 128)
-      hipLaunchKernelGGL((hsa::pool_kernel<float, 128>), pgrid, pblock, 0, stream, q, k, blk_len, n_pad, U, s, R, means, counts, nh);
-    else
-      hipLaunchKernelGGL((hsa::pool_kernel<float, 64>), pgrid, pblock, 0, stream, q, k, blk_len, n_pad, U, s, R, means, counts, nh);
+  const float *means = pooled;
+  if (means == nullptr) {
+    float *m = static_cast<float *>(ws);
+    const dim3 pgrid((U + hsa::kPoolWaves - 1) / hsa::kPoolWaves, nh, 2);
+    const dim3 pblock(hsa::kPoolWaves * 64);
+    if (dtype == HSA_BF16) {
+      const uint16_t *q = static_cast<const uint16_t *>(qp), *k = static_cast<const uint16_t *>(kp);
+      if (D == 128)
+        hipLaunchKernelGGL((hsa::pool_kernel<uint16_t, 128>), pgrid, pblock, 0, stream, q, k, blk_len, n_pad, U, s, R, m, nh);
+      else
+        hipLaunchKernelGGL((hsa::pool_kernel<uint16_t, 64>), pgrid, pblock, 0, stream, q, k, blk_len, n_pad, U, s, R, m, nh);
+    } else {
+      const float *q = static_cast<const float *>(qp), *k = static_cast<const float *>(kp);
+      if (D == 128)
+        hipLaunchKernelGGL((hsa::pool_kernel<float, 128>), pgrid, pblock, 0, stream, q, k, blk_len, n_pad, U, s, R, m, nh);
+      else
+        hipLaunchKernelGGL((hsa::pool_kernel<float, 64>), pgrid, pblock, 0, stream, q, k, blk_len, n_pad, U, s, R, m, nh);
+    }
+    means = m;
   }
   const float *qb = means;
   const float *kb = means + static_cast<size_t>(nh) * U * D;
   const dim3 cgrid((U + 15) / 16, nh);
   if (D == 128) {
-    if (agg == HSA_AGG_MAX) launch_contract<128, true>(U, cgrid, qb, kb, counts, R, nb, scale, S, stream);
-    else launch_contract<128, false>(U, cgrid, qb, kb, counts, R, nb, scale, S, stream);
+    if (agg == HSA_AGG_MAX) launch_contract<128, true>(U, cgrid, qb, kb, blk_len, s, R, nb, scale, S, stream);
+    else launch_contract<128, false>(U, cgrid, qb, kb, blk_len, s, R, nb, scale, S, stream);
   } else {
-    if (agg == HSA_AGG_MAX) launch_contract<64, true>(U, cgrid, qb, kb, counts, R, nb, scale, S, stream);
-    else launch_contract<64, false>(U, cgrid, qb, kb, counts, R, nb, scale, S, stream);
+    if (agg == HSA_AGG_MAX) launch_contract<64, true>(U, cgrid, qb, kb, blk_len, s, R, nb, scale, S, stream);
+    else launch_contract<64, false>(U, cgrid, qb, kb, blk_len, s, R, nb, scale, S, stream);
   }
   return check_launch("hsa_score");
 }

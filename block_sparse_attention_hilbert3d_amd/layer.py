@@ -48,8 +48,10 @@ class SparseAttentionLayer:
             self.max_kv = k if select == "topk" else self.nb
             G = heads
             self.S = torch.empty((heads, self.nb, self.nb), dtype=torch.float32, device=device)
-            n = B_.lib().hsa_score_ws_size(heads, self.n_pad, s, D)
-            self.score_ws = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+            self.score_ws = None
+            # sub-block means written by the reorder pass (fused pooling)
+            self.pooled = torch.empty((2, heads, self.n_pad // s, D), dtype=torch.float32,
+                                      device=device)
         self.kv_idx = torch.empty((G, self.nb, self.max_kv), dtype=torch.int32, device=device)
         self.kv_cnt = torch.empty((G, self.nb), dtype=torch.int32, device=device)
         p = self.params(0, 0.0)
@@ -70,14 +72,19 @@ class SparseAttentionLayer:
                               frames=self.T, tiles_per_frame=self.tiles_per_frame, C=self.C,
                               T_per=self.T_per, step=step)
 
-    def reorder(self, q, k, v):
-        B_.hsa_perm([q, k, v], self.perm, self.n_pad, outs=self.xp)
+    def reorder(self, q, k, v, pool: bool = True):
+        """Gather Q/K/V; on steps that refresh the mask also pool Q/K sub-blocks."""
+        if pool and self.select != "lvsa":
+            B_.hsa_perm([q, k, v], self.perm, self.n_pad, outs=self.xp, pool_s=self.s,
+                        pooled=self.pooled)
+        else:
+            B_.hsa_perm([q, k, v], self.perm, self.n_pad, outs=self.xp)
 
     def make_mask(self, step: int = 0, budget_ratio: float = 0.0):
         qp, kp, _ = self.xp
         if self.select != "lvsa":
             B_.hsa_score(qp, kp, self.blk_len, self.B, self.s, self.agg, self.scale, out=self.S,
-                         ws=self.score_ws)
+                         pooled=self.pooled)
         B_.hsa_select(self.S, self.heads, self.nb, self.params(step, budget_ratio), self.max_kv,
                       device=self.device, outs=(self.kv_idx, self.kv_cnt), ws=self.select_ws)
 
@@ -91,7 +98,7 @@ class SparseAttentionLayer:
 
     def step(self, q, k, v, step: int = 0, budget_ratio: float = 0.0, reuse_mask: bool = False):
         """One layer: returns the output [1, N, heads, D] (a buffer owned by the layer)."""
-        self.reorder(q, k, v)
+        self.reorder(q, k, v, pool=not reuse_mask)
         if not reuse_mask:
             self.make_mask(step, budget_ratio)
         self.attend()

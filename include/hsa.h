@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define HSA_ABI_VERSION 1
+#define HSA_ABI_VERSION 2
 
 typedef enum hsa_status {
   HSA_OK = 0,
@@ -124,14 +124,21 @@ hsa_status_t hsa_plan(int32_t T, int32_t H, int32_t W, int32_t order, int32_t B,
  * xs[j]: token-major input j; xps[j]: reordered output j (nh*n_pad*D
  * elements). xs and xps are host arrays of n_tensors device pointers.
  * tok_stride: elements between consecutive tokens of x; (tok_stride *
- * element size) must be a multiple of 16 bytes.
+ * element size) must be a multiple of 16 bytes; nh*D*element size <= 16 KB.
+ * pooled (optional, NULL to skip): also writes the sub-block means that
+ * hierarchical scoring pools (DFSAttn, Methodology, design 2) for tensors 0
+ * and 1 while they stream through: pooled[(j*nh + h)*(n_pad/pool_s) + u][d]
+ * (float) = mean over the real slots of sub-block u (slots u*pool_s ..
+ * u*pool_s + pool_s - 1) of x_j[perm[slot]][h][d], 0 for an empty sub-block.
+ * pool_s in {16, 32, 64, 128} must divide n_pad; needs n_tensors >= 2.
  */
 hsa_status_t hsa_perm(int32_t n_tensors, const void *const *xs, void *const *xps,
                       const int32_t *perm, int32_t N, int32_t n_pad, int32_t nh, int32_t D,
-                      int64_t tok_stride, int32_t dtype, hsa_stream_t stream);
+                      int64_t tok_stride, int32_t dtype, int32_t pool_s, float *pooled,
+                      hsa_stream_t stream);
 
-/* Workspace bytes for hsa_score: pooled Q and K sub-block means (float) and
- * per-sub-block token counts. */
+/* Workspace bytes for hsa_score when it pools itself: pooled Q and K
+ * sub-block means (float). */
 size_t hsa_score_ws_size(int32_t nh, int32_t n_pad, int32_t s, int32_t D);
 
 /*
@@ -144,11 +151,15 @@ size_t hsa_score_ws_size(int32_t nh, int32_t n_pad, int32_t s, int32_t D);
  *   sum_{v in J} p[u][v] / sum_{u in I} c_u  (rows sum to 1).
  * agg = MAX: S[I][J] = max over u in I, v in J of z[u][v].
  * qp, kp: reordered [nh][nb*B][D]; blk_len: [nb]; S out: float [nh][nb][nb].
+ * pooled (optional): the means hsa_perm wrote with pool_s = s; when given,
+ * qp, kp and ws are not used (may be NULL) and no pooling pass runs.
+ * Otherwise ws must hold hsa_score_ws_size bytes.
  * Limits: nb*B/s <= 2048 sub-blocks. Computed in float32 (matrix cores).
  */
-hsa_status_t hsa_score(const void *qp, const void *kp, const int32_t *blk_len, int32_t nh,
-                       int32_t nb, int32_t B, int32_t s, int32_t D, int32_t dtype, int32_t agg,
-                       float scale, float *S, void *ws, size_t ws_bytes, hsa_stream_t stream);
+hsa_status_t hsa_score(const void *qp, const void *kp, const float *pooled,
+                       const int32_t *blk_len, int32_t nh, int32_t nb, int32_t B, int32_t s,
+                       int32_t D, int32_t dtype, int32_t agg, float scale, float *S, void *ws,
+                       size_t ws_bytes, hsa_stream_t stream);
 
 /* Workspace bytes for hsa_select (0 for TOPK and LVSA). */
 size_t hsa_select_ws_size(int32_t nh, int32_t nb, const hsa_select_params_t *p);

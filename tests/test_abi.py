@@ -50,7 +50,7 @@ def _err(B, status):
 
 def test_version_and_strings(B):
     L = B.lib()
-    assert L.hsa_abi_version() == 1
+    assert L.hsa_abi_version() == 2
     assert L.hsa_status_str(0) == b"ok"
     assert L.hsa_status_str(5) == b"workspace too small"
 
@@ -80,29 +80,33 @@ NULL = ctypes.c_void_p(0)
 def test_perm_validation(B):
     L = B.lib()
     arr = (ctypes.c_void_p * 3)(FAKE.value, FAKE.value, FAKE.value)
-    assert L.hsa_perm(4, arr, arr, FAKE, 10, 16, 2, 64, 128, 1, NULL) == 6          # n_tensors
-    assert L.hsa_perm(1, arr, arr, NULL, 10, 16, 2, 64, 128, 1, NULL) == 1          # perm
-    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 96, 192, 1, NULL) == 4          # D
-    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 64, 128, 7, NULL) == 3          # dtype
-    assert L.hsa_perm(1, arr, arr, FAKE, 20, 16, 2, 64, 128, 1, NULL) == 2          # n_pad < N
-    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 64, 100, 1, NULL) == 2          # stride < nh*D
-    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 64, 132, 1, NULL) == 6          # stride alignment
+    P = (0, NULL)                                                                  # no pooling
+    assert L.hsa_perm(4, arr, arr, FAKE, 10, 16, 2, 64, 128, 1, *P, NULL) == 6          # n_tensors
+    assert L.hsa_perm(1, arr, arr, NULL, 10, 16, 2, 64, 128, 1, *P, NULL) == 1          # perm
+    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 96, 192, 1, *P, NULL) == 4          # D
+    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 64, 128, 7, *P, NULL) == 3          # dtype
+    assert L.hsa_perm(1, arr, arr, FAKE, 20, 16, 2, 64, 128, 1, *P, NULL) == 2          # n_pad < N
+    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 64, 100, 1, *P, NULL) == 2          # stride < nh*D
+    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 64, 132, 1, *P, NULL) == 6          # stride alignment
+    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 200, 64, 12800, 1, *P, NULL) == 4      # row > 16 KB
     bad = (ctypes.c_void_p * 1)(0x10004)
-    assert L.hsa_perm(1, bad, arr, FAKE, 10, 16, 2, 64, 128, 1, NULL) == 6          # pointer alignment
+    assert L.hsa_perm(1, bad, arr, FAKE, 10, 16, 2, 64, 128, 1, *P, NULL) == 6          # pointer alignment
     assert b"aligned" in L.hsa_last_error()
+    assert L.hsa_perm(2, arr, arr, FAKE, 10, 16, 2, 64, 128, 1, 24, FAKE, NULL) == 4    # pool_s
+    assert L.hsa_perm(2, arr, arr, FAKE, 10, 24, 2, 64, 128, 1, 16, FAKE, NULL) == 2    # pool_s | n_pad
+    assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 64, 128, 1, 16, FAKE, NULL) == 6    # needs Q and K
 
 
 def test_score_validation(B):
     L = B.lib()
-    ok = (FAKE, FAKE, FAKE)
     ws_n = L.hsa_score_ws_size(2, 256, 16, 64)
     assert ws_n > 0
     args = lambda **kw: dict(dict(nh=2, nb=4, Bs=64, s=16, D=64, dt=1, agg=0, scale=0.125,
                                   ws=FAKE, wsn=ws_n), **kw)
 
     def call(a):
-        return L.hsa_score(*ok, a["nh"], a["nb"], a["Bs"], a["s"], a["D"], a["dt"], a["agg"],
-                           a["scale"], FAKE, a["ws"], a["wsn"], NULL)
+        return L.hsa_score(FAKE, FAKE, NULL, FAKE, a["nh"], a["nb"], a["Bs"], a["s"], a["D"],
+                           a["dt"], a["agg"], a["scale"], FAKE, a["ws"], a["wsn"], NULL)
     assert call(args(s=24)) == 4
     assert call(args(Bs=64, s=128)) == 2
     assert call(args(agg=5)) == 6
@@ -110,7 +114,10 @@ def test_score_validation(B):
     assert call(args(wsn=ws_n - 1)) == 5
     assert call(args(ws=NULL)) == 5
     assert call(args(nb=300, Bs=128, s=16)) == 4        # 2400 sub-blocks > 2048
-    assert L.hsa_score(NULL, FAKE, FAKE, 2, 4, 64, 16, 64, 1, 0, 0.125, FAKE, FAKE, ws_n, NULL) == 1
+    assert L.hsa_score(NULL, FAKE, NULL, FAKE, 2, 4, 64, 16, 64, 1, 0, 0.125, FAKE, FAKE, ws_n, NULL) == 1
+    # with pooled means the workspace is not needed, but S must still be valid
+    assert L.hsa_score(NULL, NULL, FAKE, FAKE, 2, 4, 64, 16, 64, 1, 0, 0.125, NULL, NULL, 0, NULL) == 1
+    assert L.hsa_score(NULL, NULL, ctypes.c_void_p(0x10008), FAKE, 2, 4, 64, 16, 64, 1, 0, 0.125, FAKE, NULL, 0, NULL) == 6
 
 
 def test_select_validation(B):

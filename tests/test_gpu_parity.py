@@ -86,6 +86,26 @@ def test_perm_fused_qkv_stride(hsa):
     assert np.array_equal(to_np(xps[1]), oracle.gather(k.cpu(), ref_perm))
 
 
+@pytest.mark.parametrize("idx", [1, 2, 3, 5])
+def test_fused_pooling_matches_oracle(hsa, idx):
+    """Sub-block means written by the reorder pass equal the oracle's pooling,
+    and scoring from them matches scoring with its own pooling pass."""
+    w = wl.get(idx)
+    _say(f"fused pooling workload {idx}")
+    q, k, v = (x.to(dev()) for x in wl.make_qkv(w, 0))
+    perm, blk_len = hsa.hsa_plan(w.T, w.H, w.W, w.order, w.B, device=dev())
+    (qp, kp, vp), pooled = hsa.hsa_perm([q, k, v], perm, perm.numel(), pool_s=w.s)
+    S_fused = hsa.hsa_score(qp, kp, blk_len, w.B, w.s, pooled=pooled)
+    S_self = hsa.hsa_score(qp, kp, blk_len, w.B, w.s)
+    torch.cuda.synchronize()
+    p = perm.cpu().numpy().astype(np.int64)
+    for j, x in enumerate((q, k)):
+        ref, _ = oracle.pool(oracle.gather(x.cpu(), p), p, w.s)
+        err = np.abs(to_np(pooled[j]) - ref).max()
+        assert err <= 1e-5 * max(1.0, np.abs(ref).max()), err
+    assert np.abs(to_np(S_fused) - to_np(S_self)).max() <= SCORE_TOL["mass"]
+
+
 # ---------------------------------------------------------------- score / select
 
 def _gpu_scores(hsa, w, step, agg="mass"):
