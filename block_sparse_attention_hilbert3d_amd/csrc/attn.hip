@@ -316,6 +316,224 @@ attn_bf16_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ k
   }
 }
 
+// Software-pipelined variant. Each listed key block is processed in stages
+// of ST keys (ST = 64 splits a 128-key block in two). K and V stages are
+// double-buffered in LDS so that S(c+1) = K(c+1) Q^T is computed in the same
+// scheduling region as the softmax and value product of stage c: the matrix
+// core works on one stage while the vector ALU exponentiates the other.
+// Loads for K(c+2) and V(c+1) are issued at the start of iteration c and
+// have a whole iteration to land. With 64-key stages the four buffers take
+// 64 KB, so two workgroups share a CU and each SIMD interleaves two waves.
+template <int D, int BK, int ST, bool LSE>
+__global__ void __launch_bounds__(BK * 2, 2)
+attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
+                      const uint16_t *__restrict__ vp, uint16_t *__restrict__ op,
+                      float *__restrict__ lse, const int32_t *__restrict__ blk_len,
+                      const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt,
+                      int max_kv, int kv_shared, int nh, int nb, float scale_log2) {
+  constexpr int NW = BK / 32;
+  constexpr int CPR = D / 8;
+  constexpr int NS = BK / ST;   // stages per key block
+  constexpr int MT = ST / 32;
+  constexpr int DK = D / 16;
+  constexpr int DM = D / 32;
+  constexpr int PK = ST / 16;
+  constexpr int TILE = ST * D;  // elements per stage buffer
+  static_assert(BK % ST == 0 && ST % 32 == 0, "stage size");
+  constexpr float kLazy = 8.f;
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[2 * TILE];
+
+  const int total = nh * nb;
+  const int bid = xcd_remap(blockIdx.x, total);
+  const int h = bid / nb, I = bid - (bid / nb) * nb;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, ln = lane & 31;
+  const int64_t head_off = static_cast<int64_t>(h) * nb * BK * D;
+  const int qslot = I * BK + w * 32 + ln;
+  const uint32_t ldsK = lds_addr(sK), ldsV = lds_addr(sV);
+  lds_char_t *const vl = to_lds(sV);
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    koff[i] = tile_lane_offset<D, false>(i, lane);
+    voff[i] = tile_lane_offset<D, true>(i, lane);
+  }
+  const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
+  const int cnt = kv_cnt[lrow];
+  const int32_t *list = kv_idx + lrow * max_kv;
+  const uint16_t *kbase = kp + head_off;
+  const uint16_t *vbase = vp + head_off;
+  // stage t covers keys (t % NS)*ST .. +ST of listed block t / NS
+  const int nst = cnt * NS;
+  auto stage_block = [&](int t) { return list[t / NS]; };
+  auto stage_ofs = [&](int t) {
+    return static_cast<int64_t>(stage_block(t)) * BK * D + static_cast<int64_t>(t % NS) * ST * D;
+  };
+  auto stage_valid = [&](int t) { return min(max(blk_len[stage_block(t)] - (t % NS) * ST, 0), ST); };
+
+  bf16x8 qf[DK];
+  {
+    const uint16_t *qrow = qp + head_off + static_cast<int64_t>(qslot) * D + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qrow + ks * 16);
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) asm volatile("" ::"v"(qf[ks]));
+  }
+  int kofs[DK];
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) kofs[ks] = ln * CPR + ((2 * ks + g) ^ (ln & (CPR - 1)));
+  const int q16 = lane >> 4, jj = lane & 15;
+  int vofs[DM];
+#pragma unroll
+  for (int md = 0; md < DM; ++md) {
+    const int col = md * 32 + (q16 & 1) * 16 + 4 * (jj & 3);
+    const int chunk = (col >> 3) ^ ((jj & 12) & (CPR - 1));
+    vofs[md] = ((g * 4 + (jj >> 2)) * CPR + chunk) * 16 + ((col >> 2) & 1) * 8;
+  }
+
+  f32x16 oacc[DM];
+#pragma unroll
+  for (int md = 0; md < DM; ++md)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;
+  float m_ref = -1e30f, l_run = 0.f, e_run = 0.f;
+
+  auto compute_s = [&](f32x16 (&sacc)[MT], int buf) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      bf16x8 kf[DK];
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks)
+        kf[ks] = *reinterpret_cast<const bf16x8 *>(&sK[buf * TILE + (mt * 32 * CPR + kofs[ks]) * 8]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[mt][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks)
+        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[mt], 0, 0, 0);
+    }
+  };
+  // Mask the ragged tail, then rescale O if this tile's max outgrows the
+  // reference by more than 2^8 (lazy rescale).
+  auto mask_and_rescale = [&](f32x16 (&sacc)[MT], int kvalid) {
+    if (kvalid < ST) {
+      const int lim = kvalid - g * 4;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (mt * 32 + (i >> 2) * 8 + (i & 3) >= lim) sacc[mt][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    if (__any(mx > m_ref + kLazy)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_run *= alpha;
+      e_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < DM; ++md)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[md][i] *= alpha;
+      m_ref = m_new;
+    }
+  };
+  auto exp_pv = [&](const f32x16 (&sacc)[MT], int buf) {
+    float rs = 0.f, es = 0.f;
+#pragma unroll
+    for (int ks2 = 0; ks2 < PK; ++ks2) {
+      bf16x8 va[DM];
+#pragma unroll
+      for (int md = 0; md < DM; ++md) {
+        lds_i16x4_t *a0 = (lds_i16x4_t *)(vl + buf * TILE * 2 + vofs[md] + ks2 * 16 * CPR * 16);
+        lds_i16x4_t *a1 = (lds_i16x4_t *)(vl + buf * TILE * 2 + vofs[md] + (ks2 * 16 + 8) * CPR * 16);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1);
+        const i16x8_t both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        va[md] = __builtin_bit_cast(bf16x8, both);
+      }
+      bf16x8 pf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[ks2 >> 1][(ks2 & 1) * 8 + j], scale_log2, -m_ref));
+        if constexpr (LSE) es += p;
+        pf[j] = static_cast<__bf16>(p);
+      }
+      const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+      const bf16x2 p01 = {pf[0], pf[1]}, p23 = {pf[2], pf[3]}, p45 = {pf[4], pf[5]}, p67 = {pf[6], pf[7]};
+      rs = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, rs, false);
+      rs = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, rs, false);
+      rs = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, rs, false);
+      rs = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, rs, false);
+#pragma unroll
+      for (int md = 0; md < DM; ++md)
+        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[md], pf, oacc[md], 0, 0, 0);
+    }
+    l_run += rs;
+    if constexpr (LSE) e_run += es;
+  };
+
+  // Prologue: K(0), V(0) and K(1) in flight, S(0) once all three landed.
+  f32x16 sA[MT], sB[MT];
+  if (nst > 0) {
+    issue_tile<D, ST, NW>(kbase + stage_ofs(0), ldsK, w, koff);
+    issue_tile<D, ST, NW>(vbase + stage_ofs(0), ldsV, w, voff);
+    if (nst > 1) issue_tile<D, ST, NW>(kbase + stage_ofs(1), ldsK + TILE * 2, w, koff);
+    // iteration 0 reads K(1) as well, so all three stages must have landed
+    wait_vmcnt<0>();
+    __syncthreads();
+    compute_s(sA, 0);
+    mask_and_rescale(sA, stage_valid(0));
+  }
+  // Iteration c: issue K(c+2) and V(c+1); S(c+1) alongside softmax + PV(c);
+  // then wait for this iteration's loads.
+  auto body = [&](int c, f32x16 (&cur)[MT], f32x16 (&nxt)[MT]) {
+    const bool has1 = c + 1 < nst, has2 = c + 2 < nst;
+    __syncthreads();  // K(c) and V(c-1) buffers are free, K(c+1) and V(c) visible
+    if (has2) issue_tile<D, ST, NW>(kbase + stage_ofs(c + 2), ldsK + (c & 1) * TILE * 2, w, koff);
+    if (has1) issue_tile<D, ST, NW>(vbase + stage_ofs(c + 1), ldsV + ((c + 1) & 1) * TILE * 2, w, voff);
+    // Unconditional so it shares a scheduling region with exp_pv; on the
+    // last stage it reads an idle buffer (no load in flight) and is unused.
+    compute_s(nxt, (c + 1) & 1);
+    exp_pv(cur, c & 1);
+    if (has1) mask_and_rescale(nxt, stage_valid(c + 1));
+    wait_vmcnt<0>();
+  };
+  for (int c = 0; c < nst; c += 2) {
+    body(c, sA, sB);
+    if (c + 1 < nst) body(c + 1, sB, sA);
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const bool real = (w * 32 + ln) < blk_len[I];
+  const float inv = (real && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  uint16_t *orow = op + head_off + static_cast<int64_t>(qslot) * D;
+#pragma unroll
+  for (int md = 0; md < DM; ++md)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = md * 32 + i4 * 8 + g * 4;
+      const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(oacc[md][i4 * 4 + 0] * inv)) |
+                          (static_cast<uint32_t>(f32_to_bf16(oacc[md][i4 * 4 + 1] * inv)) << 16);
+      const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(oacc[md][i4 * 4 + 2] * inv)) |
+                          (static_cast<uint32_t>(f32_to_bf16(oacc[md][i4 * 4 + 3] * inv)) << 16);
+      *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(w0, w1);
+    }
+  if constexpr (LSE) {
+    const float e_tot = e_run + __shfl_xor(e_run, 32, 64);
+    if (g == 0) {
+      const float ln2 = 0.6931471805599453f;
+      lse[static_cast<int64_t>(h) * nb * BK + qslot] =
+          (real && e_tot > 0.f) ? (m_ref + log2f(e_tot)) * ln2 : 0.f;
+    }
+  }
+}
+
 template <int D, int BK>
 __global__ void __launch_bounds__(BK)
 attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
@@ -395,8 +613,8 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
     uint16_t *o = static_cast<uint16_t *>(op);
     const dim3 block(B * 2);
 #define HSA_ATTN_BF16(DD, BB, L)                                                              \
-  launch_k(hsa::attn_bf16_kernel<DD, BB, L>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, \
-           kv_cnt, max_kv, kv_shared, nh, nb, scale_log2)
+  launch_k(hsa::attn_bf16_pipe_kernel<DD, BB, 64, L>, grid, block, stream, q, k, v, o, lse, blk_len, \
+           kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, scale_log2)
     const bool L = lse != nullptr;
     if (D == 128 && B == 128) { if (L) HSA_ATTN_BF16(128, 128, true); else HSA_ATTN_BF16(128, 128, false); }
     else if (D == 64 && B == 128) { if (L) HSA_ATTN_BF16(64, 128, true); else HSA_ATTN_BF16(64, 128, false); }
