@@ -250,7 +250,7 @@ def main():
         "flop": {"dense": flop_dense, "computed_tiles": flop_tiles, "useful": flop_useful},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": _traffic(w.idx),
-                     "kernel": "attn_bf16_kernel<128,128>" if w.dtype == "bf16" else "attn_f32_kernel"},
+                     "kernel": "attn_bf16_pipe_kernel" if w.dtype == "bf16" else "attn_f32_kernel"},
     }
     if not args.no_cpu:
         cb = _cpu_baseline(w, *sets_cpu[0])

@@ -6,22 +6,28 @@
 // key blocks not in its list are never loaded.
 //
 // bf16 kernel (gfx950 matrix cores, wave64):
-//  - one wave per 32 query rows; Q stays in registers as the B operand;
-//  - per listed key block, K and V tiles go HBM/L2 -> LDS with direct
-//    (register-free) 16-byte loads into XOR-swizzled layouts; the next
-//    tile's K is requested as soon as S is computed and its V as soon as the
-//    value product is done, each waited for with its own vmcnt threshold;
+//  - one wave per 32 query rows (or 64 with two query tiles per wave); Q
+//    stays in registers as the B operand;
+//  - each listed key block is consumed in stages of 64 keys; K and V stages
+//    go HBM/L2 -> LDS with direct (register-free) 16-byte loads into
+//    XOR-swizzled, double-buffered layouts, requested one iteration (V) or
+//    two (K) before they are read, so one barrier and one wait per stage;
 //  - S^T = K Q^T on v_mfma_f32_32x32x16_bf16 so each lane holds 32-key runs
-//    of ONE query: the row max / row sum are in-lane plus one cross-half
-//    exchange;
+//    of ONE query: the row max is in-lane plus one half-wave lane swap; the
+//    next stage's S is computed in the same scheduling region as the current
+//    stage's softmax and value product, so matrix and vector work overlap;
 //  - online softmax in the log2 domain (scale folded into one FMA), keys
 //    beyond a ragged block's real length masked to -inf, and a lazy rescale
 //    that only touches O when a row max grows by more than 2^8;
 //  - P is rounded to bf16 straight from the accumulator layout and used as
 //    the B operand of O^T += V^T P^T; V^T comes from the row-major V tile via
 //    ds_read_b64_tr_b16 (no transpose pass) in the accumulator's key order;
+//    the normalising row sum adds the rounded weights (v_dot2 with ones), so
+//    output rows are convex combinations of V rows even under rounding;
+//  - the list of key blocks and their real lengths is held in lanes and read
+//    with v_readlane, keeping scalar memory round trips out of the loop;
 //  - epilogue divides by the row sum, rounds to bf16, zeroes pad rows and
-//    writes the natural-log log-sum-exp.
+//    writes the natural-log log-sum-exp (from an unrounded fp32 sum).
 // f32 kernel: a plain one-thread-per-query online-softmax loop with K/V tiles
 // in LDS, for float inputs (small shapes).
 #include "common.h"
@@ -100,238 +106,26 @@ __device__ __forceinline__ void issue_tile(const uint16_t *gtile, uint32_t lds_t
     load_lds16(gbase + i * 1024, loff[i & 3], lbase + i * 1024);
 }
 
-template <int D, int BK, bool LSE>
-__global__ void __launch_bounds__(BK * 2, 2)
-attn_bf16_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
-                 const uint16_t *__restrict__ vp, uint16_t *__restrict__ op,
-                 float *__restrict__ lse, const int32_t *__restrict__ blk_len,
-                 const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt,
-                 int max_kv, int kv_shared, int nh, int nb, float scale_log2) {
-  constexpr int NW = BK / 32;   // waves per workgroup, 32 query rows each
-  constexpr int CPR = D / 8;    // 16-byte chunks per row
-  constexpr int NI = BK * CPR / (64 * NW);  // direct loads per wave per tile
-  constexpr int MT = BK / 32;   // 32-key slices of a tile
-  constexpr int DK = D / 16;    // 16-wide k-steps over the head dim
-  constexpr int DM = D / 32;    // 32-row slices of the head dim
-  constexpr int PK = BK / 16;   // 16-key k-steps of the value product
-  constexpr float kLazy = 8.f;  // rescale only when a row max grows by > 2^8
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[BK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[BK * D];
-
-  const int total = nh * nb;
-  const int bid = xcd_remap(blockIdx.x, total);
-  const int h = bid / nb, I = bid - (bid / nb) * nb;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
-  uint32_t koff[4], voff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    koff[i] = tile_lane_offset<D, false>(i, lane);
-    voff[i] = tile_lane_offset<D, true>(i, lane);
-  }
-  const int g = lane >> 5, ln = lane & 31;
-  const int64_t head_off = static_cast<int64_t>(h) * nb * BK * D;
-  const int qslot = I * BK + w * 32 + ln;
-  const uint32_t ldsK = lds_addr(sK), ldsV = lds_addr(sV);
-  lds_char_t *const vl = to_lds(sV);
-
-  const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
-  const int cnt = kv_cnt[lrow];
-  const int32_t *list = kv_idx + lrow * max_kv;
-  const uint16_t *kbase = kp + head_off;
-  const uint16_t *vbase = vp + head_off;
-
-  // Q first, and retired before any direct load is in flight: the empty asm
-  // reads every Q register, so the compiler places its waits for the Q loads
-  // here rather than inside the loop, where they would also stall on the
-  // asynchronous K/V traffic it cannot see.
-  bf16x8 qf[DK];
-  {
-    const uint16_t *qrow = qp + head_off + static_cast<int64_t>(qslot) * D + g * 8;
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qrow + ks * 16);
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) asm volatile("" ::"v"(qf[ks]));
-  }
-
-  int J = cnt > 0 ? list[0] : 0;
-  if (cnt > 0) {
-    issue_tile<D, BK, NW>(kbase + static_cast<int64_t>(J) * BK * D, ldsK, w, koff);
-    issue_tile<D, BK, NW>(vbase + static_cast<int64_t>(J) * BK * D, ldsV, w, voff);
-  }
-
-  f32x16 oacc[DM];
-#pragma unroll
-  for (int md = 0; md < DM; ++md)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;
-  float m_ref = -1e30f, l_run = 0.f, e_run = 0.f;
-
-  // Per-lane LDS chunk offsets. K fragment (slice mt, k-step ks): row
-  // mt*32 + ln, chunk (2ks + g) ^ (ln mod CPR). V transposed read (head-dim
-  // slice md, key step ks2): within each 16-lane group the source lane jj
-  // addresses key row ks2*16 + g*4 + jj/4 (+8 for the upper half) and
-  // head-dim column md*32 + (group&1)*16 + 4(jj%4); the swizzle key of those
-  // rows is 4(jj/4), which only touches the chunk bits that md sets.
-  int kofs[DK];
-#pragma unroll
-  for (int ks = 0; ks < DK; ++ks) kofs[ks] = ln * CPR + ((2 * ks + g) ^ (ln & (CPR - 1)));
-  const int q16 = lane >> 4, jj = lane & 15;
-  int vofs[DM];  // byte offsets
-#pragma unroll
-  for (int md = 0; md < DM; ++md) {
-    const int col = md * 32 + (q16 & 1) * 16 + 4 * (jj & 3);
-    const int chunk = (col >> 3) ^ ((jj & 12) & (CPR - 1));
-    vofs[md] = ((g * 4 + (jj >> 2)) * CPR + chunk) * 16 + ((col >> 2) & 1) * 8;
-  }
-
-  for (int c = 0; c < cnt; ++c) {
-    const int kvalid = blk_len[J];
-    const bool more = c + 1 < cnt;
-    const int Jn = more ? list[c + 1] : J;
-
-    // K(c) has landed once only V(c)'s NI loads may still be outstanding.
-    wait_vmcnt<NI>();
-    __syncthreads();
-    f32x16 sacc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      // all k-step fragments of the slice first, so the reads overlap
-      bf16x8 kf[DK];
-#pragma unroll
-      for (int ks = 0; ks < DK; ++ks)
-        kf[ks] = *reinterpret_cast<const bf16x8 *>(&sK[(mt * 32 * CPR + kofs[ks]) * 8]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[mt][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < DK; ++ks)
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[mt], 0, 0, 0);
-    }
-    __syncthreads();  // every wave is done with K(c)
-    if (more) issue_tile<D, BK, NW>(kbase + static_cast<int64_t>(Jn) * BK * D, ldsK, w, koff);
-
-    // Accumulator element i of slice mt is key mt*32 + (i/4)*8 + g*4 + i%4.
-    if (kvalid < BK) {
-      // key = g*4 + (a compile-time offset): compare the offset against one
-      // per-lane limit instead of materialising 64 key indices
-      const int lim = kvalid - g * 4;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (mt * 32 + (i >> 2) * 8 + (i & 3) >= lim) sacc[mt][i] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
-    // Lazy rescale: keep the reference max unless some row grew past it by
-    // more than 2^8 (p stays <= 256, exact in float and bf16 range).
-    if (__any(mx > m_ref + kLazy)) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_run *= alpha;
-      e_run *= alpha;
-#pragma unroll
-      for (int md = 0; md < DM; ++md)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[md][i] *= alpha;
-      m_ref = m_new;
-    }
-    // V(c) has landed once only K(c+1)'s loads may still be outstanding.
-    if (more) wait_vmcnt<NI>(); else wait_vmcnt<0>();
-    __syncthreads();
-    // P (bf16) straight from the accumulator layout, then O^T += V^T P^T.
-    // Step ks2 uses accumulator elements (ks2%2)*8 + j of slice ks2/2: keys
-    // ks2*16 + g*4 + {0..3} and ks2*16 + 8 + g*4 + {0..3}; the two transposed
-    // V reads deliver the same keys for the lane's head-dim column.
-    float rs = 0.f, es = 0.f;  // sums of the rounded and of the exact weights
-#pragma unroll
-    for (int ks2 = 0; ks2 < PK; ++ks2) {
-      bf16x8 va[DM];
-#pragma unroll
-      for (int md = 0; md < DM; ++md) {
-        lds_i16x4_t *a0 = (lds_i16x4_t *)(vl + vofs[md] + ks2 * 16 * CPR * 16);
-        lds_i16x4_t *a1 = (lds_i16x4_t *)(vl + vofs[md] + (ks2 * 16 + 8) * CPR * 16);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1);
-        const i16x8_t both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        va[md] = __builtin_bit_cast(bf16x8, both);
-      }
-      // v_exp_f32 directly: weights below 2^-126 of the row max flush to 0.
-      // The row sum adds the bf16-rounded weights the value product uses, so
-      // the output stays a convex combination of values (a single dominant
-      // key passes its value through without the weight's rounding error).
-      bf16x8 pf;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[ks2 >> 1][(ks2 & 1) * 8 + j], scale_log2, -m_ref));
-        if constexpr (LSE) es += p;
-        pf[j] = static_cast<__bf16>(p);
-      }
-      // one v_dot2 against (1, 1) adds both rounded weights of a packed pair
-      const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-      const bf16x2 p01 = {pf[0], pf[1]}, p23 = {pf[2], pf[3]}, p45 = {pf[4], pf[5]}, p67 = {pf[6], pf[7]};
-      rs = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, rs, false);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, rs, false);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, rs, false);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, rs, false);
-#pragma unroll
-      for (int md = 0; md < DM; ++md)
-        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[md], pf, oacc[md], 0, 0, 0);
-    }
-    l_run += rs;
-    e_run += es;
-    __syncthreads();  // every wave is done with V(c)
-    if (more) issue_tile<D, BK, NW>(vbase + static_cast<int64_t>(Jn) * BK * D, ldsV, w, voff);
-    J = Jn;
-  }
-
-  // Epilogue: lane holds query ln, head-dim rows md*32 + (i/4)*8 + g*4 + i%4.
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const bool real = (w * 32 + ln) < blk_len[I];
-  const float inv = (real && l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  uint16_t *orow = op + head_off + static_cast<int64_t>(qslot) * D;
-#pragma unroll
-  for (int md = 0; md < DM; ++md)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d0 = md * 32 + i4 * 8 + g * 4;
-      const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(oacc[md][i4 * 4 + 0] * inv)) |
-                          (static_cast<uint32_t>(f32_to_bf16(oacc[md][i4 * 4 + 1] * inv)) << 16);
-      const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(oacc[md][i4 * 4 + 2] * inv)) |
-                          (static_cast<uint32_t>(f32_to_bf16(oacc[md][i4 * 4 + 3] * inv)) << 16);
-      *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(w0, w1);
-    }
-  if constexpr (LSE) {
-    // log-sum-exp of the exact (unrounded) weights
-    const float e_tot = e_run + __shfl_xor(e_run, 32, 64);
-    if (g == 0) {
-      const float ln2 = 0.6931471805599453f;
-      lse[static_cast<int64_t>(h) * nb * BK + qslot] =
-          (real && e_tot > 0.f) ? (m_ref + log2f(e_tot)) * ln2 : 0.f;
-    }
-  }
-}
-
 // Software-pipelined variant. Each listed key block is processed in stages
 // of ST keys (ST = 64 splits a 128-key block in two). K and V stages are
 // double-buffered in LDS so that S(c+1) = K(c+1) Q^T is computed in the same
 // scheduling region as the softmax and value product of stage c: the matrix
 // core works on one stage while the vector ALU exponentiates the other.
 // Loads for K(c+2) and V(c+1) are issued at the start of iteration c and
-// have a whole iteration to land. With 64-key stages the four buffers take
-// 64 KB, so two workgroups share a CU and each SIMD interleaves two waves.
-template <int D, int BK, int ST, bool LSE>
-__global__ void __launch_bounds__(BK * 2, 2)
+// have a whole iteration to land.
+// A wave owns QT tiles of 32 queries. With QT = 2 every K or V fragment read
+// from LDS feeds two matrix instructions, halving LDS read traffic per flop;
+// the wave then needs about 400 registers, so each SIMD runs one wave and the
+// overlap of matrix and vector work comes from the pipelining alone. With
+// QT = 1 two workgroups of four waves share a CU, two waves per SIMD.
+template <int D, int BK, int ST, int QT, bool LSE>
+__global__ void __launch_bounds__(BK * 2 / QT, QT == 1 ? 2 : 1)
 attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
                       const uint16_t *__restrict__ vp, uint16_t *__restrict__ op,
                       float *__restrict__ lse, const int32_t *__restrict__ blk_len,
                       const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt,
                       int max_kv, int kv_shared, int nh, int nb, float scale_log2) {
-  constexpr int NW = BK / 32;
+  constexpr int NW = BK / (32 * QT);
   constexpr int CPR = D / 8;
   constexpr int NS = BK / ST;   // stages per key block
   constexpr int MT = ST / 32;
@@ -340,6 +134,7 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   constexpr int PK = ST / 16;
   constexpr int TILE = ST * D;  // elements per stage buffer
   static_assert(BK % ST == 0 && ST % 32 == 0, "stage size");
+  static_assert(NW >= 1 && BK % (32 * QT) == 0, "query tiles per wave");
   constexpr float kLazy = 8.f;
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2 * TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2 * TILE];
@@ -351,7 +146,7 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ln = lane & 31;
   const int64_t head_off = static_cast<int64_t>(h) * nb * BK * D;
-  const int qslot = I * BK + w * 32 + ln;
+  const int qrow0 = w * 32 * QT + ln;  // row of query tile 0 within the block
   const uint32_t ldsK = lds_addr(sK), ldsV = lds_addr(sV);
   lds_char_t *const vl = to_lds(sV);
   uint32_t koff[4], voff[4];
@@ -365,22 +160,61 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   const int32_t *list = kv_idx + lrow * max_kv;
   const uint16_t *kbase = kp + head_off;
   const uint16_t *vbase = vp + head_off;
-  // stage t covers keys (t % NS)*ST .. +ST of listed block t / NS
+  // Stage t covers keys (t % NS)*ST .. +ST of listed block t / NS. The
+  // listed blocks and their real lengths sit in lanes (lane i of the lo/hi
+  // pair holds entry mbase + i / mbase + 64 + i), so a stage's address and
+  // length cost two lane reads instead of dependent scalar loads. The window
+  // slides by 64 entries when the list is longer than 128.
   const int nst = cnt * NS;
-  auto stage_block = [&](int t) { return list[t / NS]; };
-  auto stage_ofs = [&](int t) {
-    return static_cast<int64_t>(stage_block(t)) * BK * D + static_cast<int64_t>(t % NS) * ST * D;
+  int mbase = 0, lo_J, lo_L, hi_J, hi_L;
+  auto fetch = [&](int b0, int &mJ, int &mL) {
+    const int i = b0 + lane;
+    mJ = i < cnt ? list[i] : 0;
+    mL = i < cnt ? blk_len[mJ] : 0;
   };
-  auto stage_valid = [&](int t) { return min(max(blk_len[stage_block(t)] - (t % NS) * ST, 0), ST); };
+  fetch(0, lo_J, lo_L);
+  fetch(64, hi_J, hi_L);
+  wait_vmcnt<0>();
+  auto entry = [&](int b, int &J, int &L) {  // b in [mbase, mbase + 128), wave-uniform
+    const int r = b - mbase;
+    const int rl = r & 63;
+    const int jl = __builtin_amdgcn_readlane(lo_J, rl), jh = __builtin_amdgcn_readlane(hi_J, rl);
+    const int ll = __builtin_amdgcn_readlane(lo_L, rl), lh = __builtin_amdgcn_readlane(hi_L, rl);
+    J = r < 64 ? jl : jh;
+    L = r < 64 ? ll : lh;
+  };
+  auto stage_ofs = [&](int t) {
+    int J, L;
+    entry(t / NS, J, L);
+    return static_cast<int64_t>(J) * BK * D + static_cast<int64_t>(t % NS) * ST * D;
+  };
+  auto stage_valid = [&](int t) {
+    int J, L;
+    entry(t / NS, J, L);
+    return min(max(L - (t % NS) * ST, 0), ST);
+  };
+  // keep entries (c + 1) / NS .. (c + 2) / NS inside the window
+  auto slide = [&](int c) {
+    if ((c + 1) / NS - mbase >= 64) {
+      mbase += 64;
+      lo_J = hi_J;
+      lo_L = hi_L;
+      fetch(mbase + 64, hi_J, hi_L);
+      wait_vmcnt<0>();  // settle the window here, not at its first lane read
+    }
+  };
 
-  bf16x8 qf[DK];
-  {
-    const uint16_t *qrow = qp + head_off + static_cast<int64_t>(qslot) * D + g * 8;
+  bf16x8 qf[QT][DK];
 #pragma unroll
-    for (int ks = 0; ks < DK; ++ks) qf[ks] = *reinterpret_cast<const bf16x8 *>(qrow + ks * 16);
+  for (int qt = 0; qt < QT; ++qt) {
+    const uint16_t *qrow = qp + head_off + static_cast<int64_t>(I * BK + qrow0 + qt * 32) * D + g * 8;
 #pragma unroll
-    for (int ks = 0; ks < DK; ++ks) asm volatile("" ::"v"(qf[ks]));
+    for (int ks = 0; ks < DK; ++ks) qf[qt][ks] = *reinterpret_cast<const bf16x8 *>(qrow + ks * 16);
   }
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) asm volatile("" ::"v"(qf[qt][ks]));
   int kofs[DK];
 #pragma unroll
   for (int ks = 0; ks < DK; ++ks) kofs[ks] = ln * CPR + ((2 * ks + g) ^ (ln & (CPR - 1)));
@@ -393,14 +227,22 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     vofs[md] = ((g * 4 + (jj >> 2)) * CPR + chunk) * 16 + ((col >> 2) & 1) * 8;
   }
 
-  f32x16 oacc[DM];
+  f32x16 oacc[QT][DM];
 #pragma unroll
-  for (int md = 0; md < DM; ++md)
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[md][i] = 0.f;
-  float m_ref = -1e30f, l_run = 0.f, e_run = 0.f;
+    for (int md = 0; md < DM; ++md)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[qt][md][i] = 0.f;
+  float m_ref[QT], l_run[QT], e_run[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    m_ref[qt] = -1e30f;
+    l_run[qt] = 0.f;
+    e_run[qt] = 0.f;
+  }
 
-  auto compute_s = [&](f32x16 (&sacc)[MT], int buf) {
+  auto compute_s = [&](f32x16 (&sacc)[MT][QT], int buf) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       bf16x8 kf[DK];
@@ -408,43 +250,59 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
       for (int ks = 0; ks < DK; ++ks)
         kf[ks] = *reinterpret_cast<const bf16x8 *>(&sK[buf * TILE + (mt * 32 * CPR + kofs[ks]) * 8]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[mt][i] = 0.f;
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[mt][qt][i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks)
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[mt], 0, 0, 0);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          sacc[mt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qt][ks], sacc[mt][qt], 0, 0, 0);
     }
   };
   // Mask the ragged tail, then rescale O if this tile's max outgrows the
   // reference by more than 2^8 (lazy rescale).
-  auto mask_and_rescale = [&](f32x16 (&sacc)[MT], int kvalid) {
+  auto mask_and_rescale = [&](f32x16 (&sacc)[MT][QT], int kvalid) {
     if (kvalid < ST) {
       const int lim = kvalid - g * 4;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (mt * 32 + (i >> 2) * 8 + (i & 3) >= lim) sacc[mt][i] = -INFINITY;
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (mt * 32 + (i >> 2) * 8 + (i & 3) >= lim) sacc[mt][qt][i] = -INFINITY;
     }
-    float mx = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int qt = 0; qt < QT; ++qt) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
-    if (__any(mx > m_ref + kLazy)) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_run *= alpha;
-      e_run *= alpha;
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int md = 0; md < DM; ++md)
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][qt][i]);
+      // other half-wave's max via a lane swap (no LDS round trip)
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+      if (__any(mx > m_ref[qt] + kLazy)) {
+        const float m_new = fmaxf(m_ref[qt], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
+        l_run[qt] *= alpha;
+        e_run[qt] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[md][i] *= alpha;
-      m_ref = m_new;
+        for (int md = 0; md < DM; ++md)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[qt][md][i] *= alpha;
+        m_ref[qt] = m_new;
+      }
     }
   };
-  auto exp_pv = [&](const f32x16 (&sacc)[MT], int buf) {
-    float rs = 0.f, es = 0.f;
+  auto exp_pv = [&](const f32x16 (&sacc)[MT][QT], int buf) {
+    float rs[QT], es[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      rs[qt] = 0.f;
+      es[qt] = 0.f;
+    }
 #pragma unroll
     for (int ks2 = 0; ks2 < PK; ++ks2) {
       bf16x8 va[DM];
@@ -457,29 +315,36 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
         const i16x8_t both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         va[md] = __builtin_bit_cast(bf16x8, both);
       }
-      bf16x8 pf;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[ks2 >> 1][(ks2 & 1) * 8 + j], scale_log2, -m_ref));
-        if constexpr (LSE) es += p;
-        pf[j] = static_cast<__bf16>(p);
+      for (int qt = 0; qt < QT; ++qt) {
+        bf16x8 pf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = __builtin_amdgcn_exp2f(
+              fmaf(sacc[ks2 >> 1][qt][(ks2 & 1) * 8 + j], scale_log2, -m_ref[qt]));
+          if constexpr (LSE) es[qt] += p;
+          pf[j] = static_cast<__bf16>(p);
+        }
+        const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+        const bf16x2 p01 = {pf[0], pf[1]}, p23 = {pf[2], pf[3]}, p45 = {pf[4], pf[5]}, p67 = {pf[6], pf[7]};
+        rs[qt] = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, rs[qt], false);
+        rs[qt] = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, rs[qt], false);
+        rs[qt] = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, rs[qt], false);
+        rs[qt] = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, rs[qt], false);
+#pragma unroll
+        for (int md = 0; md < DM; ++md)
+          oacc[qt][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[md], pf, oacc[qt][md], 0, 0, 0);
       }
-      const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-      const bf16x2 p01 = {pf[0], pf[1]}, p23 = {pf[2], pf[3]}, p45 = {pf[4], pf[5]}, p67 = {pf[6], pf[7]};
-      rs = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, rs, false);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, rs, false);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, rs, false);
-      rs = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, rs, false);
-#pragma unroll
-      for (int md = 0; md < DM; ++md)
-        oacc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[md], pf, oacc[md], 0, 0, 0);
     }
-    l_run += rs;
-    if constexpr (LSE) e_run += es;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      l_run[qt] += rs[qt];
+      if constexpr (LSE) e_run[qt] += es[qt];
+    }
   };
 
   // Prologue: K(0), V(0) and K(1) in flight, S(0) once all three landed.
-  f32x16 sA[MT], sB[MT];
+  f32x16 sA[MT][QT], sB[MT][QT];
   if (nst > 0) {
     issue_tile<D, ST, NW>(kbase + stage_ofs(0), ldsK, w, koff);
     issue_tile<D, ST, NW>(vbase + stage_ofs(0), ldsV, w, voff);
@@ -492,16 +357,18 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   }
   // Iteration c: issue K(c+2) and V(c+1); S(c+1) alongside softmax + PV(c);
   // then wait for this iteration's loads.
-  auto body = [&](int c, f32x16 (&cur)[MT], f32x16 (&nxt)[MT]) {
+  auto body = [&](int c, f32x16 (&cur)[MT][QT], f32x16 (&nxt)[MT][QT]) {
     const bool has1 = c + 1 < nst, has2 = c + 2 < nst;
     __syncthreads();  // K(c) and V(c-1) buffers are free, K(c+1) and V(c) visible
+    slide(c);
     if (has2) issue_tile<D, ST, NW>(kbase + stage_ofs(c + 2), ldsK + (c & 1) * TILE * 2, w, koff);
     if (has1) issue_tile<D, ST, NW>(vbase + stage_ofs(c + 1), ldsV + ((c + 1) & 1) * TILE * 2, w, voff);
     // Unconditional so it shares a scheduling region with exp_pv; on the
     // last stage it reads an idle buffer (no load in flight) and is unused.
     compute_s(nxt, (c + 1) & 1);
     exp_pv(cur, c & 1);
-    if (has1) mask_and_rescale(nxt, stage_valid(c + 1));
+    // an empty mask on the last stage leaves the running max untouched
+    mask_and_rescale(nxt, has1 ? stage_valid(c + 1) : 0);
     wait_vmcnt<0>();
   };
   for (int c = 0; c < nst; c += 2) {
@@ -509,27 +376,32 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     if (c + 1 < nst) body(c + 1, sB, sA);
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const bool real = (w * 32 + ln) < blk_len[I];
-  const float inv = (real && l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  uint16_t *orow = op + head_off + static_cast<int64_t>(qslot) * D;
 #pragma unroll
-  for (int md = 0; md < DM; ++md)
+  for (int qt = 0; qt < QT; ++qt) {
+    const int row = qrow0 + qt * 32;
+    const int qslot = I * BK + row;
+    const float l_tot = l_run[qt] + __shfl_xor(l_run[qt], 32, 64);
+    const bool real = row < blk_len[I];
+    const float inv = (real && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    uint16_t *orow = op + head_off + static_cast<int64_t>(qslot) * D;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d0 = md * 32 + i4 * 8 + g * 4;
-      const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(oacc[md][i4 * 4 + 0] * inv)) |
-                          (static_cast<uint32_t>(f32_to_bf16(oacc[md][i4 * 4 + 1] * inv)) << 16);
-      const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(oacc[md][i4 * 4 + 2] * inv)) |
-                          (static_cast<uint32_t>(f32_to_bf16(oacc[md][i4 * 4 + 3] * inv)) << 16);
-      *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(w0, w1);
-    }
-  if constexpr (LSE) {
-    const float e_tot = e_run + __shfl_xor(e_run, 32, 64);
-    if (g == 0) {
-      const float ln2 = 0.6931471805599453f;
-      lse[static_cast<int64_t>(h) * nb * BK + qslot] =
-          (real && e_tot > 0.f) ? (m_ref + log2f(e_tot)) * ln2 : 0.f;
+    for (int md = 0; md < DM; ++md)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = md * 32 + i4 * 8 + g * 4;
+        const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(oacc[qt][md][i4 * 4 + 0] * inv)) |
+                            (static_cast<uint32_t>(f32_to_bf16(oacc[qt][md][i4 * 4 + 1] * inv)) << 16);
+        const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(oacc[qt][md][i4 * 4 + 2] * inv)) |
+                            (static_cast<uint32_t>(f32_to_bf16(oacc[qt][md][i4 * 4 + 3] * inv)) << 16);
+        *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(w0, w1);
+      }
+    if constexpr (LSE) {
+      const float e_tot = e_run[qt] + __shfl_xor(e_run[qt], 32, 64);
+      if (g == 0) {
+        const float ln2 = 0.6931471805599453f;
+        lse[static_cast<int64_t>(h) * nb * BK + qslot] =
+            (real && e_tot > 0.f) ? (m_ref[qt] + log2f(e_tot)) * ln2 : 0.f;
+      }
     }
   }
 }
@@ -612,14 +484,14 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                    *v = static_cast<const uint16_t *>(vp);
     uint16_t *o = static_cast<uint16_t *>(op);
     const dim3 block(B * 2);
-#define HSA_ATTN_BF16(DD, BB, L)                                                              \
-  launch_k(hsa::attn_bf16_pipe_kernel<DD, BB, 64, L>, grid, block, stream, q, k, v, o, lse, blk_len, \
-           kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, scale_log2)
+#define HSA_ATTN_BF16(DD, BB, QQ, L)                                                          \
+  launch_k(hsa::attn_bf16_pipe_kernel<DD, BB, (QQ == 2 ? 32 : 64), QQ, L>, grid, dim3(BB * 2 / QQ), stream, q, k, v, o, \
+           lse, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, scale_log2)
     const bool L = lse != nullptr;
-    if (D == 128 && B == 128) { if (L) HSA_ATTN_BF16(128, 128, true); else HSA_ATTN_BF16(128, 128, false); }
-    else if (D == 64 && B == 128) { if (L) HSA_ATTN_BF16(64, 128, true); else HSA_ATTN_BF16(64, 128, false); }
-    else if (D == 128 && B == 64) { if (L) HSA_ATTN_BF16(128, 64, true); else HSA_ATTN_BF16(128, 64, false); }
-    else { if (L) HSA_ATTN_BF16(64, 64, true); else HSA_ATTN_BF16(64, 64, false); }
+    if (D == 128 && B == 128) { if (L) HSA_ATTN_BF16(128, 128, 1, true); else HSA_ATTN_BF16(128, 128, 1, false); }
+    else if (D == 64 && B == 128) { if (L) HSA_ATTN_BF16(64, 128, 1, true); else HSA_ATTN_BF16(64, 128, 1, false); }
+    else if (D == 128 && B == 64) { if (L) HSA_ATTN_BF16(128, 64, 1, true); else HSA_ATTN_BF16(128, 64, 1, false); }
+    else { if (L) HSA_ATTN_BF16(64, 64, 1, true); else HSA_ATTN_BF16(64, 64, 1, false); }
 #undef HSA_ATTN_BF16
   } else {
     const float *q = static_cast<const float *>(qp), *k = static_cast<const float *>(kp),
