@@ -40,32 +40,6 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// One 16-byte-per-lane direct global->LDS load: lane l's 16 bytes come from
-// sbase + voff (sbase wave-uniform) and land at lds_base + 16*l. Issued from
-// asm so the compiler does not add blanket vmcnt(0) waits in front of
-// unrelated LDS reads; the caller waits with wait_vmcnt() and a barrier
-// before the data is read. No register is written.
-__device__ __forceinline__ void load_lds16(const void *sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff),
-               "s"(sbase)
-               : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(n) (gfx9 encoding), leaving the other counters untouched.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-typedef __attribute__((address_space(3))) char lds_char_t;
-
-// Generic pointer to a __shared__ object -> LDS pointer / LDS byte address.
-__device__ __forceinline__ lds_char_t *to_lds(const void *p) { return (lds_char_t *)(p); }
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return static_cast<uint32_t>((uintptr_t)to_lds(p));
-}
-
 // Tile layouts in LDS: BK rows (keys) of CPR 16-byte chunks (D bf16 each).
 // K: chunk c of row r sits at slot c ^ (r mod CPR) so the 32 lanes reading a
 //    fragment (32 rows, one chunk) hit distinct banks.

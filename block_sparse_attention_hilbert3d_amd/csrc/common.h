@@ -51,6 +51,32 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return (b % 8) * per + b / 8;
 }
 
+// One 16-byte-per-lane direct global->LDS load: lane l's 16 bytes come from
+// sbase + voff (sbase wave-uniform) and land at lds_base + 16*l. Issued from
+// asm so the compiler does not add blanket vmcnt(0) waits in front of
+// unrelated LDS reads; the caller waits with wait_vmcnt() and a barrier
+// before the data is read. No register is written.
+__device__ __forceinline__ void load_lds16(const void *sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding), leaving the other counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// Generic pointer to a __shared__ object -> LDS pointer / LDS byte address.
+__device__ __forceinline__ lds_char_t *to_lds(const void *p) { return (lds_char_t *)(p); }
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return static_cast<uint32_t>((uintptr_t)to_lds(p));
+}
+
 }  // namespace hsa
 
 // Host-side error plumbing (abi.hip).

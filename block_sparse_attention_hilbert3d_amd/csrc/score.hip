@@ -88,15 +88,29 @@ __device__ __forceinline__ int sub_count(const int32_t *blk_len, int v, int R, i
   return min(max(blk_len[I] - (v - I * R) * s, 0), s);
 }
 
+constexpr int kMaxSub = 2048;  // sub-blocks per head (validated at the boundary)
+
+// Each lane group g of an MFMA chain owns columns 16m + 4g .. +3 (m = 0 ..
+// D/16 - 1) of its row, so a row's four lane groups read 64 contiguous bytes
+// per load and the k-slots of Q and K line up.
 template <int D, int NWV, int MAXT, bool MAXAGG>
 __global__ void __launch_bounds__(NWV * 64)
 contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
                 const int32_t *__restrict__ blk_len, int s, int U, int R, int nb, float scale,
                 float *__restrict__ S) {
-  constexpr int DQ = D / 4;  // k-slots per lane group
+  constexpr int DQ = D / 4;          // MFMA steps (k-slots per lane group)
+  constexpr int CPR = D / 4;         // 16-byte chunks per fp32 row
+  constexpr int NI = 16 * D * 4 / 1024;  // direct loads per 16-row tile
   __shared__ float red[NWV][16];
+  __shared__ float cnt_s[kMaxSub];   // real tokens of every key sub-block
+  // One key tile per wave, chunk c of row r at slot c ^ (r mod 16): the 16
+  // rows read by one MFMA operand load hit distinct banks.
+  __shared__ __attribute__((aligned(1024))) float kt[NWV][16 * D];
+  for (int v = threadIdx.x; v < U; v += NWV * 64) cnt_s[v] = static_cast<float>(sub_count(blk_len, v, R, s));
+  // MASS works in the log2 domain: logits carry scale * log2(e).
+  const float zscale = MAXAGG ? scale : scale * 1.4426950408889634f;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ul = lane & 15;
   const int g = lane >> 4;
   const int h = blockIdx.y;
@@ -104,21 +118,40 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
   const int u = u0 + ul;
   const int tiles = (U + 15) / 16;
   const int VT = (tiles + NWV - 1) / NWV;  // tiles per wave (<= MAXT)
+  const int nt = min(VT, max(tiles - w * VT, 0));  // tiles this wave owns
   const float *qb = qbar + static_cast<int64_t>(h) * U * D;
   const float *kb = kbar + static_cast<int64_t>(h) * U * D;
+  const uint32_t slot = __builtin_amdgcn_readfirstlane(lds_addr(&kt[w][0]));
+  const float *kslot = &kt[w][0];
+
+  // Direct loads of tile t into this wave's slot; rows past U repeat row
+  // U - 1 (their logits are discarded).
+  auto issue = [&](int t) {
+    const int v0 = (w * VT + t) * 16;
+    const float *base = kb + static_cast<int64_t>(v0) * D;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int P = i * 64 + lane;
+      const int row = P / CPR, c = (P % CPR) ^ (row & 15);
+      const int rowc = min(v0 + row, U - 1) - v0;
+      load_lds16(base, static_cast<uint32_t>(rowc * D * 4 + c * 16), slot + i * 1024);
+    }
+  };
+  if (nt > 0) issue(0);
 
   float qreg[DQ];
   if (u < U) {
 #pragma unroll
-    for (int j = 0; j < DQ; j += 4) {
-      const float4 t = *reinterpret_cast<const float4 *>(qb + static_cast<int64_t>(u) * D + g * DQ + j);
-      qreg[j] = t.x; qreg[j + 1] = t.y; qreg[j + 2] = t.z; qreg[j + 3] = t.w;
+    for (int m = 0; m < DQ / 4; ++m) {
+      const float4 t = *reinterpret_cast<const float4 *>(qb + static_cast<int64_t>(u) * D + 16 * m + 4 * g);
+      qreg[4 * m] = t.x; qreg[4 * m + 1] = t.y; qreg[4 * m + 2] = t.z; qreg[4 * m + 3] = t.w;
     }
   } else {
 #pragma unroll
     for (int j = 0; j < DQ; ++j) qreg[j] = 0.f;
   }
-  const int cu = (u < U) ? sub_count(blk_len, u, R, s) : 0;
+  __syncthreads();  // cnt_s
+  const int cu = (u < U) ? static_cast<int>(cnt_s[u]) : 0;
 
   // Logits z[t][r]: query sub-block u, key sub-block v = v0 + 4g + r.
   float z[MAXT][4];  // -inf marks an empty key sub-block
@@ -126,28 +159,26 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
   for (int t = 0; t < MAXT; ++t) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) z[t][r] = -INFINITY;
-    const int v0 = (w * VT + t) * 16;
-    if (t < VT && v0 < U) {
-      const int vrow = v0 + ul;
+    if (t < nt) {
+      wait_vmcnt<0>();  // tile t is in the slot (and the Q loads are in)
       float kreg[DQ];
-      if (vrow < U) {
 #pragma unroll
-        for (int j = 0; j < DQ; j += 4) {
-          const float4 tt = *reinterpret_cast<const float4 *>(kb + static_cast<int64_t>(vrow) * D + g * DQ + j);
-          kreg[j] = tt.x; kreg[j + 1] = tt.y; kreg[j + 2] = tt.z; kreg[j + 3] = tt.w;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < DQ; ++j) kreg[j] = 0.f;
+      for (int m = 0; m < DQ / 4; ++m) {
+        const float4 k4 = *reinterpret_cast<const float4 *>(kslot + ul * D + (((g + 4 * m) ^ ul) * 4));
+        kreg[4 * m] = k4.x; kreg[4 * m + 1] = k4.y; kreg[4 * m + 2] = k4.z; kreg[4 * m + 3] = k4.w;
       }
+      // the slot is reused by the next tile's loads: its reads must be done
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      if (t + 1 < nt) issue(t + 1);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < DQ; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kreg[j], qreg[j], acc, 0, 0, 0);
+      const int v0 = (w * VT + t) * 16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int v = v0 + 4 * g + r;
-        const int c = (v < U) ? sub_count(blk_len, v, R, s) : 0;
-        if (c > 0 && cu > 0) z[t][r] = acc[r] * scale;
+        const float c = (v < U) ? cnt_s[v] : 0.f;
+        if (c > 0.f && cu > 0) z[t][r] = acc[r] * zscale;
       }
     }
   }
@@ -175,8 +206,7 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float e = 0.f;
-        if (t < VT && z[t][r] != -INFINITY)
-          e = static_cast<float>(sub_count(blk_len, v0 + r, R, s)) * expf(z[t][r] - m);
+        if (t < VT && z[t][r] != -INFINITY) e = cnt_s[v0 + r] * __builtin_amdgcn_exp2f(z[t][r] - m);
         z[t][r] = e;
         den += e;
       }
