@@ -91,6 +91,17 @@ def _cpu_baseline(w, q, k, v, blocks_per_head=32):
                 nb=nb)
 
 
+def _keep_text(w, L, nb, tiles_steps, nh):
+    mean_per_row = float(sum(tiles_steps)) / len(tiles_steps) / (nh * nb)
+    if w.select == "topk":
+        return f"top-{L.k} of {nb} key blocks per query block"
+    if w.select == "lvsa":
+        return (f"LVSA C={w.C} frames, T_per={w.T_per}: {mean_per_row:.1f} of {nb} tiles per "
+                f"query tile (mean over {len(tiles_steps)} steps)")
+    return (f"cumulative threshold tau={w.tau} + global budget: {mean_per_row:.1f} of {nb} blocks per "
+            f"query block (mean over {len(tiles_steps)} steps)")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,8 +125,6 @@ def main():
     import workloads as wl
 
     w = wl.get(args.workload)
-    if w.select != "topk":
-        raise SystemExit("bench.py times the top-k workloads (1-3)")
     dev = torch.device("cuda:0")
     sets_cpu = [wl.make_qkv(w, s) for s in range(2)]
     sets = [tuple(x.to(dev) for x in s) for s in sets_cpu]
@@ -124,19 +133,27 @@ def main():
     esz = 2 if w.dtype == "bf16" else 4
     stream = torch.cuda.current_stream()
 
+    scored = w.select != "lvsa"
+    # the diffusion step a timed step stands for: its budget (threshold mode)
+    # or its anchor rotation (LVSA); top-k steps refresh the same way each time
+    def step_of(i):
+        return i % max(w.steps, 1)
+
     def one_step(i, ev=None):
         q, k, v = sets[i % 2]
+        st = step_of(i)
         if ev is not None:
             ev[0].record(stream)
-        L.reorder(q, k, v)
+        L.reorder(q, k, v, pool=scored)
         if ev is not None:
             ev[1].record(stream)
-        qp, kp, _ = L.xp
-        hsa.hsa_score(qp, kp, L.blk_len, B, w.s, "mass", L.scale, out=L.S, pooled=L.pooled)
+        if scored:
+            qp, kp, _ = L.xp
+            hsa.hsa_score(qp, kp, L.blk_len, B, w.s, "mass", L.scale, out=L.S, pooled=L.pooled)
         if ev is not None:
             ev[2].record(stream)
-        hsa.hsa_select(L.S, nh, nb, L.params(0, 0.0), L.max_kv, outs=(L.kv_idx, L.kv_cnt),
-                       ws=L.select_ws)
+        hsa.hsa_select(L.S, nh, nb, L.params(st, wl.budget_ratio(w, st)), L.max_kv,
+                       outs=(L.kv_idx, L.kv_cnt), ws=L.select_ws, device=dev)
         if ev is not None:
             ev[3].record(stream)
         L.attend()
@@ -171,6 +188,14 @@ def main():
     ms_step = start.elapsed_time(end) / K
     names = ["perm", "score", "select", "attn", "unperm"]
     stage_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    per_step = np.array([e[0].elapsed_time(e[5]) for e in evs])
+    # computed tile pairs of every timed step (lists change with the step in
+    # threshold and LVSA modes); attention time is the mean over those steps
+    tiles_steps = []
+    for i in range(K):
+        one_step(i)
+        tiles_steps.append(int(L.kv_cnt.sum().item()) * (nh if L.kv_idx.shape[0] == 1 else 1))
+    torch.cuda.synchronize()
 
     # cached-mask steps (mask reused: reorder, attention, restore)
     cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
@@ -182,31 +207,36 @@ def main():
     torch.cuda.synchronize()
     ms_cached = float(np.mean([a.elapsed_time(b) for a, b in cevs]))
 
+    flop_tiles = 4.0 * B * B * D * float(np.mean(tiles_steps))
+    # useful pairs of the last timed step's lists, scaled to the mean tile count
     kv_cnt = L.kv_cnt.cpu().numpy()
-    tiles = int(kv_cnt.sum())
-    flop_tiles = 4.0 * B * B * D * tiles
     blk_len = L.blk_len.cpu().numpy().astype(np.int64)
     kv_idx = L.kv_idx.cpu().numpy()
-    kept_keys = int(sum(blk_len[kv_idx[h, i, :kv_cnt[h, i]]].sum() * blk_len[i]
-                        for h in range(nh) for i in range(nb)))
-    flop_useful = 4.0 * D * kept_keys
+    G = kv_idx.shape[0]
+    kept_keys = sum(int((blk_len[kv_idx[h, i, :kv_cnt[h, i]]].sum()) * blk_len[i])
+                    for h in range(G) for i in range(nb)) * (nh // G)
+    flop_useful = 4.0 * D * kept_keys * float(np.mean(tiles_steps)) / max(tiles_steps[-1], 1)
     flop_dense = 4.0 * N * N * D * nh
     t_attn = stage_ms["attn"] * 1e-3
     achieved = flop_tiles / t_attn / 1e12
     row = N * nh * D * esz
-    U = L.n_pad // w.s
+    U = L.n_pad // w.s if scored else 0
     pooled_bytes = 2 * nh * U * D * 4
+    G = L.kv_idx.shape[0]
     stage_bytes = {
         # Q, K, V read and written once, plus the Q/K sub-block means
         "perm": 3 * 2 * row + pooled_bytes,
         "score": pooled_bytes + nh * nb * nb * 4,
-        "select": nh * nb * nb * 4 + nh * nb * (L.max_kv + 1) * 4,
+        # S read (scored modes) and the lists written
+        "select": (nh * nb * nb * 4 if scored else 0) + G * nb * (L.max_kv + 1) * 4,
         "unperm": 2 * row,
     }
     score_flop = 2.0 * U * U * D * nh
     stages = {}
     for n in names:
         t = stage_ms[n] * 1e-3
+        if n == "score" and not scored:
+            continue
         if n == "attn":
             stages[n] = {"ms": stage_ms[n], "tflops_computed_tiles": achieved,
                          "tflops_useful": flop_useful / t / 1e12,
@@ -241,8 +271,9 @@ def main():
         "config": {"workload": f"Wan-2.1-1.3B-like 480p 81-frame latent {w.T}x{w.H}x{w.W}"
                                if w.idx == 3 else w.name,
                    "tokens": N, "heads": nh, "head_dim": D, "block": B, "sub_block": w.s,
-                   "order": w.order, "keep": f"top-{L.k} of {nb} key blocks per query block",
+                   "order": w.order, "keep": _keep_text(w, L, nb, tiles_steps, nh),
                    "batch": 1},
+        "ms_per_step_p10_p50_p90": [float(np.percentile(per_step, p)) for p in (10, 50, 90)],
         "ms_per_layer_cached_mask": ms_cached,
         "ms_per_layer_refresh_cycle": cycle_ms,
         "refresh_interval": w.refresh,
@@ -252,7 +283,7 @@ def main():
                      "frac": achieved / peak, "traffic": _traffic(w.idx),
                      "kernel": "attn_bf16_pipe_kernel" if w.dtype == "bf16" else "attn_f32_kernel"},
     }
-    if not args.no_cpu:
+    if not args.no_cpu and w.select == "topk":
         cb = _cpu_baseline(w, *sets_cpu[0])
         out["cpu_baseline"] = {
             "value": flop_dense / cb["layer_s"] / 1e12, "unit": "TFLOP/s (dense-equivalent)",

@@ -308,13 +308,14 @@ template <int D, bool MAXAGG>
 static void launch_contract(int U, dim3 grid, const float *qb, const float *kb,
                             const int32_t *blk_len, int s, int R, int nb, float scale, float *S,
                             hipStream_t stream) {
-  // Many short waves per workgroup (each owns a few 16-wide key tiles) keep
-  // enough independent loads and MFMA chains in flight per SIMD.
+  // Each wave owns up to MAXT 16-wide key tiles of the strip. Up to 1024 key
+  // sub-blocks, eight waves of eight tiles let two workgroups share a CU, so
+  // one's softmax phase overlaps the other's matrix work.
   const int tiles = (U + 15) / 16;
   if (tiles <= 16)
     hipLaunchKernelGGL((hsa::contract_kernel<D, 4, 4, MAXAGG>), grid, dim3(256), 0, stream, qb, kb, blk_len, s, U, R, nb, scale, S);
   else if (tiles <= 64)
-    hipLaunchKernelGGL((hsa::contract_kernel<D, 16, 4, MAXAGG>), grid, dim3(1024), 0, stream, qb, kb, blk_len, s, U, R, nb, scale, S);
+    hipLaunchKernelGGL((hsa::contract_kernel<D, 8, 8, MAXAGG>), grid, dim3(512), 0, stream, qb, kb, blk_len, s, U, R, nb, scale, S);
   else
     hipLaunchKernelGGL((hsa::contract_kernel<D, 16, 8, MAXAGG>), grid, dim3(1024), 0, stream, qb, kb, blk_len, s, U, R, nb, scale, S);
 }
