@@ -154,6 +154,8 @@ def main():
             ev[2].record(stream)
         hsa.hsa_select(L.S, nh, nb, L.params(st, wl.budget_ratio(w, st)), L.max_kv,
                        outs=(L.kv_idx, L.kv_cnt), ws=L.select_ws, device=dev)
+        if L.order is not None:  # longest lists first (threshold mode)
+            hsa.hsa_attn_order(L.kv_cnt, L.max_kv, out=L.order)
         if ev is not None:
             ev[3].record(stream)
         L.attend()

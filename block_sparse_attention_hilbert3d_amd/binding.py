@@ -45,7 +45,8 @@ _SIGS = {
     "hsa_score": (ctypes.c_int, [_p, _p, _p, _p] + [_c_i32] * 7 + [_c_f32, _p, _p, _c_sz, _p]),
     "hsa_select_ws_size": (_c_sz, [_c_i32, _c_i32, ctypes.POINTER(SelectParams)]),
     "hsa_select": (ctypes.c_int, [_p, _c_i32, _c_i32, ctypes.POINTER(SelectParams), _p, _p, _c_i32, _p, _c_sz, _p]),
-    "hsa_attn": (ctypes.c_int, [_p] * 8 + [_c_i32] * 7 + [_c_f32, _p]),
+    "hsa_attn": (ctypes.c_int, [_p] * 9 + [_c_i32] * 7 + [_c_f32, _p]),
+    "hsa_attn_order": (ctypes.c_int, [_p, _c_i32, _c_i32, _c_i32, _p, _p]),
     "hsa_unperm": (ctypes.c_int, [_p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _p]),
 }
 
@@ -195,10 +196,21 @@ def hsa_select(S, nh: int, nb: int, params: SelectParams, max_kv: int, device="c
     return kv_idx, kv_cnt
 
 
+def hsa_attn_order(kv_cnt, max_kv: int, out=None):
+    """kv_cnt int32 [G, nb] -> int32 [G*nb] row order, longest lists first."""
+    _need_device(kv_cnt)
+    G, nb = kv_cnt.shape
+    if out is None:
+        out = torch.empty(G * nb, dtype=torch.int32, device=kv_cnt.device)
+    _check(lib().hsa_attn_order(_ptr(kv_cnt), G, nb, max_kv, _ptr(out), _stream()), "hsa_attn_order")
+    return out
+
+
 def hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B: int, scale: float | None = None,
-             want_lse: bool = True, out=None, lse=None):
-    """-> (op [nh, n_pad, D] in the input dtype, lse float32 [nh, n_pad] or None)."""
-    _need_device(qp, kp, vp, blk_len, kv_idx, kv_cnt)
+             want_lse: bool = True, out=None, lse=None, order=None):
+    """-> (op [nh, n_pad, D] in the input dtype, lse float32 [nh, n_pad] or None).
+    `order` (from hsa_attn_order) sets the processing order; results do not depend on it."""
+    _need_device(qp, kp, vp, blk_len, kv_idx, kv_cnt, order)
     nh, n_pad, D = qp.shape
     nb = n_pad // B
     shared = 1 if kv_idx.shape[0] == 1 and nh > 1 else 0
@@ -208,7 +220,7 @@ def hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B: int, scale: float | None = 
     if want_lse and lse is None:
         lse = torch.empty((nh, n_pad), dtype=torch.float32, device=qp.device)
     _check(lib().hsa_attn(_ptr(qp), _ptr(kp), _ptr(vp), _ptr(out), _ptr(lse if want_lse else None),
-                          _ptr(blk_len), _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], shared,
+                          _ptr(blk_len), _ptr(kv_idx), _ptr(kv_cnt), _ptr(order), kv_idx.shape[-1], shared,
                           nh, nb, B, D, _dtype_code(qp), scale, _stream()), "hsa_attn")
     return out, (lse if want_lse else None)
 

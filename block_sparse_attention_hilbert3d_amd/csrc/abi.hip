@@ -46,8 +46,10 @@ hsa_status_t launch_select(const float *S, int nh, int nb, const hsa_select_para
                            hipStream_t stream);
 hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *op, float *lse,
                          const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
-                         int max_kv, int kv_shared, int nh, int nb, int B, int D, int dtype,
-                         float scale, hipStream_t stream);
+                         const int32_t *order, int max_kv, int kv_shared, int nh, int nb, int B,
+                         int D, int dtype, float scale, hipStream_t stream);
+hsa_status_t launch_attn_order(const int32_t *kv_cnt, int G, int nb, int max_kv, int32_t *order,
+                               hipStream_t stream);
 
 static int esize_of(int dtype) { return dtype == HSA_BF16 ? 2 : 4; }
 
@@ -67,6 +69,7 @@ static hsa_status_t check_B(int B) {
 }
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 static hsa_status_t plan_size(int T, int H, int W, int order, int B, int32_t *n_pad, int32_t *nb) {
   if (T < 1 || H < 1 || W < 1 || T > 1024 || H > 1024 || W > 1024)
@@ -250,8 +253,9 @@ hsa_status_t hsa_select(const float *S, int32_t nh, int32_t nb, const hsa_select
 
 hsa_status_t hsa_attn(const void *qp, const void *kp, const void *vp, void *op, float *lse,
                       const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
-                      int32_t max_kv, int32_t kv_shared, int32_t nh, int32_t nb, int32_t B,
-                      int32_t D, int32_t dtype, float scale, hsa_stream_t stream) {
+                      const int32_t *order, int32_t max_kv, int32_t kv_shared, int32_t nh,
+                      int32_t nb, int32_t B, int32_t D, int32_t dtype, float scale,
+                      hsa_stream_t stream) {
   g_last_error.clear();
   if (!qp || !kp || !vp || !op || !blk_len || !kv_idx || !kv_cnt) return fail(HSA_ERR_NULL_PTR, "hsa_attn: null input or output");
   hsa_status_t st;
@@ -261,7 +265,19 @@ hsa_status_t hsa_attn(const void *qp, const void *kp, const void *vp, void *op, 
   if (kv_shared != 0 && kv_shared != 1) return fail(HSA_ERR_BAD_ARG, "hsa_attn: kv_shared must be 0 or 1");
   if (!(scale > 0.f) || !isfinite(scale)) return fail(HSA_ERR_BAD_ARG, "hsa_attn: scale must be finite and positive");
   if (!aligned16(qp) || !aligned16(kp) || !aligned16(vp) || !aligned16(op)) return fail(HSA_ERR_BAD_ARG, "hsa_attn: tensors must be 16-byte aligned");
-  return launch_attn(qp, kp, vp, op, lse, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, B, D, dtype, scale, static_cast<hipStream_t>(stream));
+  if (order && !aligned4(order)) return fail(HSA_ERR_BAD_ARG, "hsa_attn: order must be 4-byte aligned");
+  return launch_attn(qp, kp, vp, op, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, B, D, dtype, scale, static_cast<hipStream_t>(stream));
+}
+
+hsa_status_t hsa_attn_order(const int32_t *kv_cnt, int32_t G, int32_t nb, int32_t max_kv,
+                            int32_t *order, hsa_stream_t stream) {
+  g_last_error.clear();
+  if (!kv_cnt || !order) return fail(HSA_ERR_NULL_PTR, "hsa_attn_order: null input or output");
+  if (G < 1 || nb < 1 || max_kv < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn_order: G=%d nb=%d max_kv=%d", G, nb, max_kv);
+  if (static_cast<int64_t>(G) * nb >= (1ll << 31)) return fail(HSA_ERR_UNSUPPORTED, "hsa_attn_order: G*nb >= 2^31");
+  if (max_kv > 4095) return fail(HSA_ERR_UNSUPPORTED, "hsa_attn_order: max_kv > 4095");
+  if (!aligned4(kv_cnt) || !aligned4(order)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_order: arrays must be 4-byte aligned");
+  return launch_attn_order(kv_cnt, G, nb, max_kv, order, static_cast<hipStream_t>(stream));
 }
 
 hsa_status_t hsa_unperm(const void *op, void *o, const int32_t *perm, int32_t N, int32_t n_pad,

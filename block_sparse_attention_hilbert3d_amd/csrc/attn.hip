@@ -80,6 +80,26 @@ __device__ __forceinline__ void issue_tile(const uint16_t *gtile, uint32_t lds_t
     load_lds16(gbase + i * 1024, loff[i & 3], lbase + i * 1024);
 }
 
+// (head, query block) of workgroup b. Without an order, neighbouring blocks
+// of one head go to one XCD (shared L2). With one, the b-th workgroup takes
+// list row order[b] (longest lists first); shared lists order blocks, and
+// the nh heads of a block are consecutive workgroups.
+__device__ __forceinline__ void block_of(int b, const int32_t *order, int kv_shared, int nh, int nb,
+                                         int &h, int &I) {
+  if (order == nullptr) {
+    const int bid = xcd_remap(b, nh * nb);
+    h = bid / nb;
+    I = bid - h * nb;
+  } else if (kv_shared) {
+    h = b % nh;
+    I = min(max(order[b / nh], 0), nb - 1);
+  } else {
+    const int e = min(max(order[b], 0), nh * nb - 1);
+    h = e / nb;
+    I = e - h * nb;
+  }
+}
+
 // Software-pipelined variant. Each listed key block is processed in stages
 // of ST keys (ST = 64 splits a 128-key block in two). K and V stages are
 // double-buffered in LDS so that S(c+1) = K(c+1) Q^T is computed in the same
@@ -98,7 +118,8 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
                       const uint16_t *__restrict__ vp, uint16_t *__restrict__ op,
                       float *__restrict__ lse, const int32_t *__restrict__ blk_len,
                       const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt,
-                      int max_kv, int kv_shared, int nh, int nb, float scale_log2) {
+                      const int32_t *__restrict__ order, int max_kv, int kv_shared, int nh,
+                      int nb, float scale_log2) {
   constexpr int NW = BK / (32 * QT);
   constexpr int CPR = D / 8;
   constexpr int NS = BK / ST;   // stages per key block
@@ -113,9 +134,8 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2 * TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2 * TILE];
 
-  const int total = nh * nb;
-  const int bid = xcd_remap(blockIdx.x, total);
-  const int h = bid / nb, I = bid - (bid / nb) * nb;
+  int h, I;
+  block_of(blockIdx.x, order, kv_shared, nh, nb, h, I);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ln = lane & 31;
@@ -385,11 +405,12 @@ __global__ void __launch_bounds__(BK)
 attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
                 const float *__restrict__ vp, float *__restrict__ op, float *__restrict__ lse,
                 const int32_t *__restrict__ blk_len, const int32_t *__restrict__ kv_idx,
-                const int32_t *__restrict__ kv_cnt, int max_kv, int kv_shared, int nh, int nb,
-                float scale_log2) {
+                const int32_t *__restrict__ kv_cnt, const int32_t *__restrict__ order, int max_kv,
+                int kv_shared, int nh, int nb, float scale_log2) {
   __shared__ __attribute__((aligned(16))) float sK[BK * D];
   __shared__ __attribute__((aligned(16))) float sV[BK * D];
-  const int h = blockIdx.x / nb, I = blockIdx.x % nb;
+  int h, I;
+  block_of(blockIdx.x, order, kv_shared, nh, nb, h, I);
   const int tid = threadIdx.x;
   const int64_t head_off = static_cast<int64_t>(h) * nb * BK * D;
   const int qslot = I * BK + tid;
@@ -438,9 +459,65 @@ attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
   if (lse != nullptr) lse[static_cast<int64_t>(h) * nb * BK + qslot] = real ? (m + log2f(l)) * 0.6931471805599453f : 0.f;
 }
 
+// Counting sort of each head's list rows by length, longest first (one
+// workgroup per head; heads stay in order so a head's key/value blocks are
+// read by workgroups that run together): a histogram of lengths, a scan from
+// the longest length down, then every row takes the next free position of
+// its length.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderBins = 4096;
+
+__global__ void __launch_bounds__(kOrderThreads)
+attn_order_kernel(const int32_t *__restrict__ kv_cnt, int nb, int max_kv, int32_t *__restrict__ order) {
+  __shared__ int next[kOrderBins];
+  __shared__ int part[kOrderThreads];
+  const int tid = threadIdx.x;
+  const int base_row = blockIdx.x * nb;
+  const int32_t *cnt = kv_cnt + base_row;
+  for (int c = tid; c < kOrderBins; c += kOrderThreads) next[c] = 0;
+  __syncthreads();
+  for (int e = tid; e < nb; e += kOrderThreads) atomicAdd(&next[min(max(cnt[e], 0), max_kv)], 1);
+  __syncthreads();
+  // exclusive scan over lengths max, max-1, ..., 0: each thread owns a run
+  // of bins, sums it, the run totals are scanned, then each run is expanded
+  constexpr int kPer = kOrderBins / kOrderThreads;
+  int run[kPer], tot = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    run[j] = next[kOrderBins - 1 - (tid * kPer + j)];
+    tot += run[j];
+  }
+  part[tid] = tot;
+  __syncthreads();
+  for (int off = 1; off < kOrderThreads; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int pos = part[tid] - tot;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    next[kOrderBins - 1 - (tid * kPer + j)] = pos;
+    pos += run[j];
+  }
+  __syncthreads();
+  for (int e = tid; e < nb; e += kOrderThreads) {
+    const int p = atomicAdd(&next[min(max(cnt[e], 0), max_kv)], 1);
+    order[base_row + p] = base_row + e;
+  }
+}
+
 }  // namespace hsa
 
 namespace hsa_host {
+
+hsa_status_t launch_attn_order(const int32_t *kv_cnt, int G, int nb, int max_kv, int32_t *order,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(hsa::attn_order_kernel, dim3(G), dim3(hsa::kOrderThreads), 0, stream, kv_cnt, nb,
+                     max_kv, order);
+  return check_launch("hsa_attn_order");
+}
 
 template <typename K, typename... A>
 static void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t stream, A... args) {
@@ -449,8 +526,8 @@ static void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t stream, A... a
 
 hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *op, float *lse,
                          const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
-                         int max_kv, int kv_shared, int nh, int nb, int B, int D, int dtype,
-                         float scale, hipStream_t stream) {
+                         const int32_t *order, int max_kv, int kv_shared, int nh, int nb, int B,
+                         int D, int dtype, float scale, hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid(nh * nb);
   if (dtype == HSA_BF16) {
@@ -460,7 +537,7 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
     const dim3 block(B * 2);
 #define HSA_ATTN_BF16(DD, BB, QQ, L)                                                          \
   launch_k(hsa::attn_bf16_pipe_kernel<DD, BB, (QQ == 2 ? 32 : 64), QQ, L>, grid, dim3(BB * 2 / QQ), stream, q, k, v, o, \
-           lse, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, scale_log2)
+           lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2)
     const bool L = lse != nullptr;
     if (D == 128 && B == 128) { if (L) HSA_ATTN_BF16(128, 128, 1, true); else HSA_ATTN_BF16(128, 128, 1, false); }
     else if (D == 64 && B == 128) { if (L) HSA_ATTN_BF16(64, 128, 1, true); else HSA_ATTN_BF16(64, 128, 1, false); }
@@ -472,10 +549,10 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                 *v = static_cast<const float *>(vp);
     float *o = static_cast<float *>(op);
     const dim3 block(B);
-    if (D == 128 && B == 128) launch_k(hsa::attn_f32_kernel<128, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, scale_log2);
-    else if (D == 64 && B == 128) launch_k(hsa::attn_f32_kernel<64, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, scale_log2);
-    else if (D == 128 && B == 64) launch_k(hsa::attn_f32_kernel<128, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, scale_log2);
-    else launch_k(hsa::attn_f32_kernel<64, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, scale_log2);
+    if (D == 128 && B == 128) launch_k(hsa::attn_f32_kernel<128, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2);
+    else if (D == 64 && B == 128) launch_k(hsa::attn_f32_kernel<64, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2);
+    else if (D == 128 && B == 64) launch_k(hsa::attn_f32_kernel<128, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2);
+    else launch_k(hsa::attn_f32_kernel<64, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2);
   }
   return check_launch("hsa_attn");
 }

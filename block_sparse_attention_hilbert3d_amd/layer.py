@@ -54,6 +54,9 @@ class SparseAttentionLayer:
                                       device=device)
         self.kv_idx = torch.empty((G, self.nb, self.max_kv), dtype=torch.int32, device=device)
         self.kv_cnt = torch.empty((G, self.nb), dtype=torch.int32, device=device)
+        # threshold lists differ in length from row to row: attend longest first
+        self.order = (torch.arange(G * self.nb, dtype=torch.int32, device=device)
+                      if select == "thresh_global" else None)
         p = self.params(0, 0.0)
         n = B_.lib().hsa_select_ws_size(heads, self.nb, p)
         self.select_ws = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
@@ -87,11 +90,13 @@ class SparseAttentionLayer:
                          pooled=self.pooled)
         B_.hsa_select(self.S, self.heads, self.nb, self.params(step, budget_ratio), self.max_kv,
                       device=self.device, outs=(self.kv_idx, self.kv_cnt), ws=self.select_ws)
+        if self.order is not None:
+            B_.hsa_attn_order(self.kv_cnt, self.max_kv, out=self.order)
 
     def attend(self):
         qp, kp, vp = self.xp
         B_.hsa_attn(qp, kp, vp, self.blk_len, self.kv_idx, self.kv_cnt, self.B, self.scale,
-                    want_lse=self.want_lse, out=self.op, lse=self.lse)
+                    want_lse=self.want_lse, out=self.op, lse=self.lse, order=self.order)
 
     def restore(self):
         return B_.hsa_unperm(self.op, self.perm, self.N, out=self.o)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define HSA_ABI_VERSION 2
+#define HSA_ABI_VERSION 3
 
 typedef enum hsa_status {
   HSA_OK = 0,
@@ -196,14 +196,37 @@ hsa_status_t hsa_select(const float *S, int32_t nh, int32_t nb, const hsa_select
  * qp, kp, vp, op: reordered [nh][nb*B][D]; op rows of pad slots are zero.
  * lse: optional float [nh][nb*B] natural-log log-sum-exp (NULL to skip).
  * kv_shared: 1 if the lists are [nb][max_kv] shared by all heads.
+ * order: optional int32 [G*nb] processing order from hsa_attn_order (G = nh,
+ *   or 1 when shared): the b-th workgroup launched handles list row order[b]
+ *   (when shared, the b-th group of nh workgroups handles block order[b] for
+ *   every head). NULL: natural order, neighbouring blocks on one XCD. Entries
+ *   are clamped to the valid range; a non-permutation computes some rows
+ *   twice and leaves others unwritten.
  * BF16 runs on bf16 matrix cores with float accumulation and softmax; the
  * probabilities are rounded to bf16 for the value product and the output is
  * rounded to bf16 (nearest even). F32 computes in float throughout.
  */
 hsa_status_t hsa_attn(const void *qp, const void *kp, const void *vp, void *op, float *lse,
                       const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
-                      int32_t max_kv, int32_t kv_shared, int32_t nh, int32_t nb, int32_t B,
-                      int32_t D, int32_t dtype, float scale, hsa_stream_t stream);
+                      const int32_t *order, int32_t max_kv, int32_t kv_shared, int32_t nh,
+                      int32_t nb, int32_t B, int32_t D, int32_t dtype, float scale,
+                      hsa_stream_t stream);
+
+/*
+ * hsa_attn_order -- a processing order for hsa_attn that dispatches each
+ *   head's longest lists first, so that rows with many key blocks (the
+ *   cumulative threshold with a global budget gives rows very different list
+ *   lengths, VMoBA abstract) do not trail at the end of the launch, while a
+ *   head's rows stay together (they share key/value blocks in cache).
+ * kv_cnt: int32 [G][nb] list lengths (G = nh, or 1 for shared lists), each in
+ *   [0, max_kv] (values outside are clamped for sorting); max_kv <= 4095.
+ * order: int32 [G*nb] output, a permutation of the list rows g*nb + I: head
+ *   g's rows occupy positions g*nb .. g*nb + nb - 1 with non-increasing
+ *   kv_cnt. Rows of equal length may appear in any order; hsa_attn's results
+ *   do not depend on the order. One workgroup per head.
+ */
+hsa_status_t hsa_attn_order(const int32_t *kv_cnt, int32_t G, int32_t nb, int32_t max_kv,
+                            int32_t *order, hsa_stream_t stream);
 
 /*
  * hsa_unperm -- scatter back to token order: o[perm[i]][h][:] = op[h][i][:]

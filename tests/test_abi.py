@@ -50,7 +50,7 @@ def _err(B, status):
 
 def test_version_and_strings(B):
     L = B.lib()
-    assert L.hsa_abi_version() == 2
+    assert L.hsa_abi_version() == 3
     assert L.hsa_status_str(0) == b"ok"
     assert L.hsa_status_str(5) == b"workspace too small"
 
@@ -147,9 +147,15 @@ def test_select_validation(B):
 def test_attn_and_unperm_validation(B):
     L = B.lib()
     a = [FAKE] * 8
-    assert L.hsa_attn(NULL, *a[1:4], NULL, *a[5:8], 4, 0, 2, 4, 64, 64, 1, 0.125, NULL) == 1
-    assert L.hsa_attn(*a[:4], NULL, *a[5:8], 4, 0, 2, 4, 96, 64, 1, 0.125, NULL) == 4      # B
-    assert L.hsa_attn(*a[:4], NULL, *a[5:8], 4, 2, 2, 4, 64, 64, 1, 0.125, NULL) == 6      # kv_shared
-    assert L.hsa_attn(*a[:4], NULL, *a[5:8], 4, 0, 2, 4, 64, 64, 1, float("nan"), NULL) == 6
+    assert L.hsa_attn(NULL, *a[1:4], NULL, *a[5:8], NULL, 4, 0, 2, 4, 64, 64, 1, 0.125, NULL) == 1
+    assert L.hsa_attn(*a[:4], NULL, *a[5:8], NULL, 4, 0, 2, 4, 96, 64, 1, 0.125, NULL) == 4      # B
+    assert L.hsa_attn(*a[:4], NULL, *a[5:8], NULL, 4, 2, 2, 4, 64, 64, 1, 0.125, NULL) == 6      # kv_shared
+    assert L.hsa_attn(*a[:4], NULL, *a[5:8], NULL, 4, 0, 2, 4, 64, 64, 1, float("nan"), NULL) == 6
+    assert L.hsa_attn(*a[:4], NULL, *a[5:8], ctypes.c_void_p(0x10002), 4, 0, 2, 4, 64, 64, 1, 0.125,
+                      NULL) == 6                                                                 # order alignment
+    assert L.hsa_attn_order(NULL, 2, 4, 4, FAKE, NULL) == 1
+    assert L.hsa_attn_order(FAKE, 0, 4, 4, FAKE, NULL) == 2
+    assert L.hsa_attn_order(FAKE, 2, 4, 4096, FAKE, NULL) == 4                                   # max_kv
+    assert L.hsa_attn_order(FAKE, 1 << 16, 1 << 16, 4, FAKE, NULL) == 4                          # G*nb
     assert L.hsa_unperm(FAKE, FAKE, FAKE, 10, 8, 2, 64, 128, 1, NULL) == 2
     assert L.hsa_unperm(FAKE, NULL, FAKE, 10, 16, 2, 64, 128, 1, NULL) == 1

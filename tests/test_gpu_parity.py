@@ -337,6 +337,47 @@ def test_lists_with_single_and_repeated_blocks(hsa):
     assert np.abs(to_np(op) - ref).max() <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("G,nb,max_kv", [(3, 64, 64), (24, 929, 929), (1, 793, 273), (5, 7, 4095)])
+def test_attn_order_longest_first(hsa, G, nb, max_kv):
+    """The processing order is a permutation of the list rows that keeps each
+    head's rows in that head's range, with non-increasing lengths inside it
+    (equal lengths in any order)."""
+    _say(f"attn order G={G} nb={nb}")
+    rng = np.random.default_rng(G * 1000 + nb)
+    cnt = rng.integers(0, max_kv + 1, size=(G, nb)).astype(np.int32)
+    cnt[0, 0] = max_kv
+    order = hsa.hsa_attn_order(torch.from_numpy(cnt).to(dev()), max_kv)
+    o = order.cpu().numpy().astype(np.int64).reshape(G, nb)
+    for g in range(G):
+        assert np.array_equal(np.sort(o[g]), np.arange(g * nb, (g + 1) * nb))
+        assert np.all(np.diff(cnt.ravel()[o[g]]) <= 0)
+
+
+def test_attn_order_does_not_change_results(hsa):
+    """Uneven lists attended in longest-first order give the same bits as the
+    natural order, for per-head and for shared lists."""
+    _say("attn order vs natural order")
+    T, H, W, nh, B, D = 4, 16, 16, 3, 64, 64
+    g = torch.Generator().manual_seed(5)
+    q, k, v = (torch.randn((1, T * H * W, nh, D), generator=g).to(torch.bfloat16) for _ in range(3))
+    perm, blk_len = hsa.hsa_plan(T, H, W, "hilbert", B, device=dev())
+    nb = perm.numel() // B
+    qp, kp, vp = hsa.hsa_perm([x.to(dev()) for x in (q, k, v)], perm, perm.numel())
+    rng = np.random.default_rng(6)
+    for G in (nh, 1):
+        cnt = rng.integers(1, nb + 1, size=(G, nb)).astype(np.int32)
+        idx = np.full((G, nb, nb), -1, dtype=np.int32)
+        for h in range(G):
+            for i in range(nb):
+                idx[h, i, :cnt[h, i]] = np.sort(rng.choice(nb, cnt[h, i], replace=False))
+        kv_idx, kv_cnt = torch.from_numpy(idx).to(dev()), torch.from_numpy(cnt).to(dev())
+        order = hsa.hsa_attn_order(kv_cnt, nb)
+        a, la = hsa.hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B)
+        b, lb = hsa.hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B, order=order)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b) and torch.equal(la, lb)
+
+
 def test_deterministic(hsa):
     w = wl.get(2)
     _say("determinism")
