@@ -165,6 +165,23 @@ def main():
         if ev is not None:
             ev[5].record(stream)
 
+    # measured device-to-device copy bandwidth (context for the HBM fractions:
+    # the practical ceiling of plain streaming on this part)
+    ca = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    cb = torch.empty_like(ca)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    copy_us = []
+    for r in range(4):
+        flush.fill_(r)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cb.copy_(ca)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_us.append(e0.elapsed_time(e1) * 1e3)
+    copy_gbs = 2 * ca.numel() * 4 / min(copy_us[1:]) / 1e3
+    del ca, cb, flush
+
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -280,6 +297,7 @@ def main():
         "ms_per_layer_refresh_cycle": cycle_ms,
         "refresh_interval": w.refresh,
         "stages": stages,
+        "measured_copy_GB/s": copy_gbs,
         "flop": {"dense": flop_dense, "computed_tiles": flop_tiles, "useful": flop_useful},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": _traffic(w.idx),

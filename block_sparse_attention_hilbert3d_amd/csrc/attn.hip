@@ -361,6 +361,9 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     // last stage it reads an idle buffer (no load in flight) and is unused.
     compute_s(nxt, (c + 1) & 1);
     exp_pv(cur, c & 1);
+    // LLVM's interleave strategy for matrix and exponential instructions
+    // (measured ~2 % faster than the default schedule here)
+    __builtin_amdgcn_iglp_opt(3);
     // an empty mask on the last stage leaves the running max untouched
     mask_and_rescale(nxt, has1 ? stage_valid(c + 1) : 0);
     wait_vmcnt<0>();
