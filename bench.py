@@ -108,6 +108,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--order", choices=["row", "hilbert", "frame", "tile2d", "cube3d"], default=None,
+                    help="token order instead of the workload's own (e.g. the VMoBA 2D/3D partitions)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one device-to-device copy of this many MiB (a kernel of known "
@@ -125,6 +127,9 @@ def main():
     import workloads as wl
 
     w = wl.get(args.workload)
+    if args.order is not None:
+        from dataclasses import replace
+        w = replace(w, order=args.order)
     dev = torch.device("cuda:0")
     sets_cpu = [wl.make_qkv(w, s) for s in range(2)]
     sets = [tuple(x.to(dev) for x in s) for s in sets_cpu]

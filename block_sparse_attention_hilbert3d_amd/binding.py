@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhsa.so")
 
 HSA_F32, HSA_BF16 = 0, 1
-ORDERS = {"row": 0, "hilbert": 1, "frame": 2}
+ORDERS = {"row": 0, "hilbert": 1, "frame": 2, "tile2d": 3, "cube3d": 4}
 AGGS = {"mass": 0, "max": 1}
 MODES = {"topk": 0, "thresh_global": 1, "lvsa": 2}
 

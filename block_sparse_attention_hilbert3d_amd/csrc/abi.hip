@@ -79,6 +79,12 @@ static hsa_status_t plan_size(int T, int H, int W, int order, int B, int32_t *n_
   int64_t np;
   if (order == HSA_ORDER_ROW || order == HSA_ORDER_HILBERT3D) {
     np = (N + B - 1) / B * B;
+  } else if (order == HSA_ORDER_TILE2D || order == HSA_ORDER_CUBE3D) {
+    const bool two = order == HSA_ORDER_TILE2D;
+    const int unit = two ? 8 : 64;
+    if (B % unit != 0) return fail(HSA_ERR_UNSUPPORTED, "%s needs B a multiple of %d (B=%d)", two ? "TILE2D" : "CUBE3D", unit, B);
+    const int tT = two ? 1 : B / 64, tH = 8, tW = two ? B / 8 : 8;
+    np = static_cast<int64_t>((T + tT - 1) / tT) * ((H + tH - 1) / tH) * ((W + tW - 1) / tW) * B;
   } else if (order == HSA_ORDER_FRAME) {
     np = static_cast<int64_t>(T) * ((static_cast<int64_t>(H) * W + B - 1) / B) * B;
   } else {

@@ -133,8 +133,39 @@ hilbert_write_kernel(int b, uint32_t cube, int T, int H, int W, const int32_t *c
   }
 }
 
-// ROW / FRAME plans are closed-form; HILBERT only needs tail pads here.
-// Also fills blk_len for every order.
+// Tiled partitions: block k is tile k (row-major over tile coordinates,
+// tiles tT x tH x tW clipped to the grid); slot r of the block holds the
+// r-th cell of the tile in row-major order, or a pad past its volume.
+struct Tiling {
+  int tT, tH, tW, nT, nH, nW;
+};
+__device__ __forceinline__ Tiling tiling_of(int order, int T, int H, int W, int B) {
+  Tiling g;
+  const bool two = order == HSA_ORDER_TILE2D;
+  g.tT = two ? 1 : B / 64;
+  g.tH = 8;
+  g.tW = two ? B / 8 : 8;
+  g.nT = (T + g.tT - 1) / g.tT;
+  g.nH = (H + g.tH - 1) / g.tH;
+  g.nW = (W + g.tW - 1) / g.tW;
+  return g;
+}
+// volume of tile k; its origin and clipped extents through the references
+__device__ __forceinline__ int tile_box(const Tiling &g, int k, int T, int H, int W, int &t0, int &y0,
+                                        int &x0, int &eH, int &eW) {
+  const int a = k / (g.nH * g.nW), rem = k - a * g.nH * g.nW;
+  const int b = rem / g.nW, c = rem - b * g.nW;
+  t0 = a * g.tT;
+  y0 = b * g.tH;
+  x0 = c * g.tW;
+  const int eT = min(g.tT, T - t0);
+  eH = min(g.tH, H - y0);
+  eW = min(g.tW, W - x0);
+  return eT * eH * eW;
+}
+
+// ROW / FRAME / TILE2D / CUBE3D plans are closed-form; HILBERT only needs
+// tail pads here. Also fills blk_len for every order.
 __global__ void plan_fill_kernel(int order, int T, int H, int W, int B, int n_pad, int nb,
                                  int32_t *perm, int32_t *blk_len) {
   const int N = T * H * W;
@@ -147,6 +178,17 @@ __global__ void plan_fill_kernel(int order, int T, int H, int W, int B, int n_pa
       perm[i] = (r < P) ? f * P + r : -1;
     } else if (order == HSA_ORDER_ROW) {
       perm[i] = (i < N) ? i : -1;
+    } else if (order == HSA_ORDER_TILE2D || order == HSA_ORDER_CUBE3D) {
+      const Tiling g = tiling_of(order, T, H, W, B);
+      const int k = i / B, r = i - k * B;
+      int t0, y0, x0, eH, eW;
+      const int vol = tile_box(g, k, T, H, W, t0, y0, x0, eH, eW);
+      if (r < vol) {
+        const int dt = r / (eH * eW), rr = r - dt * eH * eW, dy = rr / eW, dx = rr - dy * eW;
+        perm[i] = ((t0 + dt) * H + (y0 + dy)) * W + (x0 + dx);
+      } else {
+        perm[i] = -1;
+      }
     } else if (i >= N) {
       perm[i] = -1;
     }
@@ -155,6 +197,9 @@ __global__ void plan_fill_kernel(int order, int T, int H, int W, int B, int n_pa
       if (order == HSA_ORDER_FRAME) {
         const int j = i % tiles;
         len = min(B, P - j * B);
+      } else if (order == HSA_ORDER_TILE2D || order == HSA_ORDER_CUBE3D) {
+        int t0, y0, x0, eH, eW;
+        len = tile_box(tiling_of(order, T, H, W, B), i, T, H, W, t0, y0, x0, eH, eW);
       } else {
         len = min(B, N - i * B);
       }

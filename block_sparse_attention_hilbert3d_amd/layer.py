@@ -110,6 +110,16 @@ class SparseAttentionLayer:
         return self.restore()
 
 
+VMOBA_CYCLE = ("row", "tile2d", "cube3d")
+
+
+def vmoba_order(layer_index: int) -> str:
+    """Token order of transformer layer `layer_index` under VMoBA's layer-wise
+    recurrent 1D-2D-3D block partitions (VMoBA abstract): 1D chunks of the
+    row-major sequence, then per-frame 2D tiles, then 3D cubes, repeating."""
+    return VMOBA_CYCLE[layer_index % 3]
+
+
 def layer_for_workload(w, device="cuda", want_lse=True) -> SparseAttentionLayer:
     """Layer configured for one of the synthetic workloads (workloads.Workload)."""
     dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16

@@ -61,7 +61,13 @@ typedef enum hsa_status {
 } hsa_status_t;
 
 typedef enum { HSA_F32 = 0, HSA_BF16 = 1 } hsa_dtype_t;
-typedef enum { HSA_ORDER_ROW = 0, HSA_ORDER_HILBERT3D = 1, HSA_ORDER_FRAME = 2 } hsa_order_t;
+typedef enum {
+  HSA_ORDER_ROW = 0,
+  HSA_ORDER_HILBERT3D = 1,
+  HSA_ORDER_FRAME = 2,
+  HSA_ORDER_TILE2D = 3, /* per-frame spatial tiles of 8 x (B/8) tokens */
+  HSA_ORDER_CUBE3D = 4  /* spatiotemporal cubes of (B/64) x 8 x 8 tokens */
+} hsa_order_t;
 typedef enum { HSA_AGG_MASS = 0, HSA_AGG_MAX = 1 } hsa_agg_t;
 typedef enum {
   HSA_SELECT_TOPK = 0,
@@ -93,12 +99,14 @@ const char *hsa_last_error(void);
 /*
  * hsa_plan_size -- host-only: padded length and block count of a plan.
  * ROW / HILBERT3D: n_pad = ceil(N/B)*B. FRAME: n_pad = T*ceil(H*W/B)*B.
- * Grid sides 1..1024, N < 2^31.
+ * TILE2D / CUBE3D with tiles tT x tH x tW: one block per tile,
+ * nb = ceil(T/tT)*ceil(H/tH)*ceil(W/tW). Grid sides 1..1024, n_pad < 2^31.
+ * TILE2D needs B a multiple of 8, CUBE3D a multiple of 64.
  */
 hsa_status_t hsa_plan_size(int32_t T, int32_t H, int32_t W, int32_t order, int32_t B,
                            int32_t *n_pad, int32_t *nb);
 
-/* Workspace bytes hsa_plan needs (0 for ROW and FRAME). */
+/* Workspace bytes hsa_plan needs (0 for every order but HILBERT3D). */
 size_t hsa_plan_ws_size(int32_t T, int32_t H, int32_t W, int32_t order);
 
 /*
@@ -110,6 +118,12 @@ size_t hsa_plan_ws_size(int32_t T, int32_t H, int32_t W, int32_t order);
  * (t, y, x), t most significant), keeps in-grid cells and pads the tail.
  * ROW is row-major with tail pads; FRAME is frame-major with each frame's
  * tokens padded to whole blocks (LVSA section 2 attends frame by frame).
+ * TILE2D and CUBE3D are the 2D and 3D block partitions that VMoBA (abstract:
+ * layer-wise recurrent 1D-2D-3D partitions; ROW is the 1D one) cycles
+ * through: the grid is cut into tiles of 1 x 8 x B/8 (TILE2D) or
+ * B/64 x 8 x 8 (CUBE3D) cells (t, y, x), edge tiles clipped to the grid;
+ * each tile is one block (its cells in row-major order, then pads), blocks
+ * in row-major order of their (t, y, x) tile coordinates.
  * Outputs: perm int32[n_pad] and blk_len int32[nb] (device).
  * ws: device workspace of hsa_plan_ws_size bytes (may be NULL if 0).
  */

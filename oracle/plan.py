@@ -14,6 +14,13 @@ Orders:
 * "frame": frame-major; each frame's H*W tokens in row-major order, padded up
   to whole tiles of B so no tile straddles two frames (LVSA, section 2: the
   attention unit is the frame).
+* "tile2d" / "cube3d": the 2D and 3D block partitions of VMoBA (abstract:
+  layer-wise recurrent 1D-2D-3D partitions, "row" being the 1D one). The grid
+  is cut into tiles of 1 x 8 x B/8 (2D) or B/64 x 8 x 8 (3D) cells, tiles at
+  the far edges clipped to the grid; every tile is one block: its cells in
+  row-major order, then pads up to B. Tiles (blocks) are taken in row-major
+  order of their tile coordinates. (Reading: the pages name the partitions
+  only; the tile shapes are the ones whose volume is the block size B.)
 """
 from __future__ import annotations
 
@@ -53,6 +60,25 @@ def plan(T: int, H: int, W: int, order: str, B: int):
         perm = np.full(T * per, -1, dtype=np.int64)
         for f in range(T):
             perm[f * per: f * per + P] = np.arange(f * P, (f + 1) * P)
+    elif order in ("tile2d", "cube3d"):
+        if order == "tile2d":
+            if B % 8:
+                raise ValueError("tile2d needs B a multiple of 8")
+            tT, tH, tW = 1, 8, B // 8
+        else:
+            if B % 64:
+                raise ValueError("cube3d needs B a multiple of 64")
+            tT, tH, tW = B // 64, 8, 8
+        slots = []
+        for a in range(0, T, tT):
+            for b in range(0, H, tH):
+                for c in range(0, W, tW):
+                    tile = [(t * H + y) * W + x
+                            for t in range(a, min(a + tT, T))
+                            for y in range(b, min(b + tH, H))
+                            for x in range(c, min(c + tW, W))]
+                    slots.extend(tile + [-1] * (B - len(tile)))
+        perm = np.asarray(slots, dtype=np.int64)
     else:
         raise ValueError(f"unknown order {order!r}")
     nb = perm.size // B

@@ -41,6 +41,9 @@ def _say(msg):
     ((21, 30, 52), "hilbert", 128), ((33, 45, 80), "hilbert", 128), ((2, 3, 600), "hilbert", 128),
     ((4, 8, 8), "row", 64), ((3, 5, 7), "row", 128), ((61, 30, 52), "frame", 128),
     ((3, 5, 7), "frame", 64), ((2, 9, 9), "frame", 128),
+    ((3, 5, 7), "tile2d", 64), ((21, 30, 52), "tile2d", 128), ((2, 17, 40), "tile2d", 128),
+    ((4, 16, 32), "tile2d", 128), ((3, 5, 7), "cube3d", 64), ((21, 30, 52), "cube3d", 128),
+    ((5, 9, 17), "cube3d", 128), ((33, 45, 80), "cube3d", 128), ((1, 1, 1), "cube3d", 128),
 ])
 def test_plan_bit_exact(hsa, shape, order, B):
     T, H, W = shape
@@ -272,6 +275,18 @@ def test_layer_all_rows(hsa, idx):
 def test_layer_sampled_rows(hsa, idx, step):
     w = wl.get(idx)
     _say(f"layer workload {idx} step {step} (sampled rows)")
+    _check_layer(hsa, w, step, *_layer(hsa, w, step))
+
+
+@pytest.mark.parametrize("idx,order,step", [(2, "tile2d", 0), (2, "cube3d", 0), (3, "tile2d", 0),
+                                            (3, "cube3d", 0), (5, "cube3d", 0), (5, "tile2d", 9)])
+def test_layer_vmoba_partitions(hsa, idx, order, step):
+    """The VMoBA 2D and 3D block partitions as the token order of a whole
+    layer (scores, selection and attention on tile blocks): every row for the
+    small workload, sampled rows for the large ones."""
+    from dataclasses import replace
+    w = replace(wl.get(idx), order=order)
+    _say(f"layer workload {idx} with {order} blocks, step {step}")
     _check_layer(hsa, w, step, *_layer(hsa, w, step))
 
 

@@ -176,3 +176,86 @@ def test_gather_scatter_roundtrip(idx):
     assert np.array_equal(back, q.double().numpy())
     inv = oracle.inverse_perm(perm, w.N)
     assert np.array_equal(perm[inv], np.arange(w.N))
+
+
+# ---------------------------------------------------------------- VMoBA tiled partitions
+
+def _tile_shape(order, B):
+    return (1, 8, B // 8) if order == "tile2d" else (B // 64, 8, 8)
+
+
+def _coords(perm, H, W):
+    t, r = np.divmod(perm, H * W)
+    y, x = np.divmod(r, W)
+    return t, y, x
+
+
+@pytest.mark.parametrize("order,shape,B", [
+    ("tile2d", (3, 5, 7), 64), ("tile2d", (21, 30, 52), 128), ("tile2d", (2, 17, 40), 128),
+    ("cube3d", (3, 5, 7), 64), ("cube3d", (21, 30, 52), 128), ("cube3d", (5, 9, 17), 128),
+])
+def test_tiled_plan_blocks_are_clipped_tiles(order, shape, B):
+    """Every real token appears once; block k holds exactly the cells of the
+    k-th tile (row-major over tile coordinates, clipped to the grid) in
+    row-major order, followed by pads; blk_len is the clipped volume."""
+    T, H, W = shape
+    N = T * H * W
+    perm, blk_len = oracle.plan(T, H, W, order, B)
+    tT, tH, tW = _tile_shape(order, B)
+    nT, nH, nW = -(-T // tT), -(-H // tH), -(-W // tW)
+    assert perm.size == nT * nH * nW * B
+    real = perm[perm >= 0]
+    assert np.array_equal(np.sort(real), np.arange(N))
+    k = 0
+    for a in range(nT):
+        for b in range(nH):
+            for c in range(nW):
+                blk = perm[k * B:(k + 1) * B]
+                n = int(blk_len[k])
+                assert np.all(blk[:n] >= 0) and np.all(blk[n:] == -1)
+                t, y, x = _coords(blk[:n], H, W)
+                box = (min(tT, T - a * tT), min(tH, H - b * tH), min(tW, W - c * tW))
+                assert n == box[0] * box[1] * box[2]
+                assert t.min() == a * tT and y.min() == b * tH and x.min() == c * tW
+                assert (np.ptp(t) + 1, np.ptp(y) + 1, np.ptp(x) + 1) == box
+                assert np.all(np.diff(blk[:n]) > 0)
+                k += 1
+
+
+@pytest.mark.parametrize("order,shape,B", [("tile2d", (4, 16, 32), 128), ("tile2d", (2, 8, 24), 64),
+                                           ("cube3d", (4, 16, 24), 128), ("cube3d", (3, 8, 16), 64)])
+def test_tiled_blocks_are_tiles_on_divisible_grids(order, shape, B):
+    """When every side is a multiple of the tile, block I is one aligned tile."""
+    T, H, W = shape
+    perm, blk_len = oracle.plan(T, H, W, order, B)
+    assert np.all(blk_len == B)
+    tT, tH, tW = _tile_shape(order, B)
+    for I in range(perm.size // B):
+        t, y, x = _coords(perm[I * B:(I + 1) * B], H, W)
+        assert t.min() % tT == 0 and y.min() % tH == 0 and x.min() % tW == 0
+        assert (t.max() - t.min(), y.max() - y.min(), x.max() - x.min()) == (tT - 1, tH - 1, tW - 1)
+
+
+def test_tiled_plans_reduce_to_row_major():
+    """One tile per frame (2D) or per grid (3D) gives the row-major order."""
+    row, _ = oracle.plan(3, 8, 16, "row", 128)
+    assert np.array_equal(oracle.plan(3, 8, 16, "tile2d", 128)[0], row)
+    row, _ = oracle.plan(1, 8, 8, "row", 64)
+    assert np.array_equal(oracle.plan(1, 8, 8, "cube3d", 64)[0], row)
+    assert np.array_equal(oracle.plan(1, 8, 8, "tile2d", 64)[0], row)
+
+
+def test_tiled_blocks_are_more_compact_than_raster():
+    """The 2D and 3D partitions keep blocks as compact boxes on the Wan grid."""
+    w = wl.get(3)
+
+    def mean_box(order):
+        perm, _ = oracle.plan(w.T, w.H, w.W, order, w.B)
+        vols = []
+        for I in range(perm.size // w.B):
+            t, y, x = _coords(perm[I * w.B:(I + 1) * w.B][perm[I * w.B:(I + 1) * w.B] >= 0], w.H, w.W)
+            vols.append((np.ptp(t) + 1) * (np.ptp(y) + 1) * (np.ptp(x) + 1))
+        return float(np.mean(vols))
+
+    row = mean_box("row")
+    assert mean_box("tile2d") * 2 < row and mean_box("cube3d") * 2 < row
