@@ -20,8 +20,10 @@ values. Each function cites the page and section it follows:
   complexity paragraph.
 * VMoBA (Mixture of Block Attention for video diffusion), abstract: global
   block selection per head and threshold selection by cumulative similarity.
-* DynamicRad (Content-Adaptive Sparse Attention), section 2.2: a shared
-  candidate set aggregated block-wise for a block attention kernel.
+* DynamicRad (Content-Adaptive Sparse Attention), section 2: a shared
+  candidate set aggregated block-wise for a block attention kernel; the
+  static-ratio and dynamic-threshold modes over a logarithmic radial window
+  with a long-range factor.
 
 Readings of points the pages leave open are listed in the repository's
 design notes and repeated at each function. Parity-unpinned items: the MASS
@@ -34,7 +36,8 @@ from .plan import plan, inverse_perm
 from .gather import gather, scatter
 from .score import pool, score_mass, score_max, score
 from .select import (select_topk, select_thresh_global, lvsa_frame_sets,
-                     select_lvsa, thresh_fixed_point, budget_pairs)
+                     select_lvsa, thresh_fixed_point, budget_pairs, radial_width,
+                     radial_window, select_radial, select_radial_dynamic)
 from .attn import attn_blocks, attn_dense
 from .layer import run_layer
 
@@ -42,5 +45,6 @@ __all__ = [
     "hilbert_index", "hilbert_order_bits", "plan", "inverse_perm", "gather", "scatter",
     "pool", "score_mass", "score_max", "score", "select_topk", "select_thresh_global",
     "lvsa_frame_sets", "select_lvsa", "thresh_fixed_point", "budget_pairs",
+    "radial_width", "radial_window", "select_radial", "select_radial_dynamic",
     "attn_blocks", "attn_dense", "run_layer",
 ]

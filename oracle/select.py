@@ -147,3 +147,72 @@ def select_lvsa(T: int, tiles_per_frame: int, C: int, T_per: int, step: int,
     width = max(len(r) for r in rows)
     max_kv = width if max_kv is None else int(max_kv)
     return _pack([rows], T * n, max_kv)
+
+
+def radial_width(d: int, tiles_per_frame: int, lam: float) -> int:
+    """DynamicRad, section 2 item 2: a logarithmic radial window whose size
+    decays exponentially with temporal distance, with a long-range factor.
+
+    Reading: at temporal distance d the window keeps ceil(P / 2**k) of the
+    P tiles of the key frame, k = floor(log2(d + 1)) (the window halves each
+    time the distance doubles: d = 0 keeps the whole frame, d = 1..2 half,
+    d = 3..6 a quarter, ...); the long-range factor lam in [0, 1] is a floor,
+    at least ceil(lam * P) tiles of every frame, so distant (for example
+    periodic) frames keep a share; at least one tile, at most P."""
+    P = int(tiles_per_frame)
+    k = int(d + 1).bit_length() - 1
+    w = max(-(-P // (1 << k)), int(math.ceil(float(lam) * P)), 1)
+    return min(w, P)
+
+
+def radial_window(j: int, d: int, tiles_per_frame: int, lam: float):
+    """Tile indices (within a key frame) kept for query tile j at distance d:
+    the radial_width nearest tiles to position j, nearest first with ties to
+    the lower index (a tile's row-major position in its frame stands for its
+    spatial place)."""
+    P = int(tiles_per_frame)
+    w = radial_width(d, P, lam)
+    return np.array(sorted(sorted(range(P), key=lambda x: (abs(x - j), x))[:w]), dtype=np.int64)
+
+
+def select_radial(T: int, tiles_per_frame: int, lam: float, max_kv: int | None = None):
+    """DynamicRad static-ratio mode (section 2 item 1): every query tile keeps,
+    in every frame, the radial window around its own position for that
+    frame's temporal distance. Geometry only, so one list set for all heads
+    (the shared candidate set of section 2 item 2). Blocks are frame tiles:
+    block t*P + j is tile j of frame t."""
+    T, P = int(T), int(tiles_per_frame)
+    rows = []
+    for t in range(T):
+        for j in range(P):
+            rows.append(np.concatenate([f * P + radial_window(j, abs(t - f), P, lam) for f in range(T)]))
+    width = max(len(r) for r in rows)
+    max_kv = width if max_kv is None else int(max_kv)
+    return _pack([rows], T * P, max_kv)
+
+
+def select_radial_dynamic(S32: np.ndarray, T: int, tiles_per_frame: int, lam: float, delta: float,
+                          max_kv: int | None = None):
+    """DynamicRad dynamic-threshold mode (section 2 item 1): pre-softmax logits
+    serve as importance and a pair outside the radial window is kept when its
+    logit clears a threshold.
+
+    Reading: S32 holds float32 block logits (MAX aggregation of sub-block
+    logits, [nh][nb][nb]); the threshold of row I is its best logit minus
+    delta (weights within a factor e**-delta of the row's strongest block),
+    formed and compared in float32; each head keeps the union of the radial
+    window and the blocks at or above the threshold."""
+    T, P = int(T), int(tiles_per_frame)
+    nb = T * P
+    S32 = np.asarray(S32, dtype=np.float32)
+    base, _ = select_radial(T, P, lam)
+    lists = []
+    for h in range(S32.shape[0]):
+        rows = []
+        for i in range(nb):
+            thr = np.float32(S32[h, i].max()) - np.float32(delta)
+            strong = np.nonzero(S32[h, i] >= thr)[0]
+            rows.append(np.union1d(base[0, i][base[0, i] >= 0], strong))
+        lists.append(rows)
+    max_kv = nb if max_kv is None else int(max_kv)
+    return _pack(lists, nb, max_kv)

@@ -179,3 +179,88 @@ def test_lvsa_tile_lists_and_cost():
     Pf, D, nh = 1560, 128, 12
     useful = sum(4 * D * nh * Pf * len(a) * Pf for a in sets)
     assert useful == 4 * D * nh * T * C * Pf * Pf
+
+
+# ---------------------------------------------------------------- DynamicRad radial masks
+
+def _golden_radial(golden_dir, name):
+    rows = []
+    with open(os.path.join(golden_dir, name)) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                head, ids = line.split(":")
+                lam, t, j = head.split()
+                rows.append((float(lam), int(t), int(j), [int(x) for x in ids.split()]))
+    return rows
+
+
+@pytest.mark.parametrize("name,T,P", [("radial_T5_P4.txt", 5, 4), ("radial_T3_P3.txt", 3, 3)])
+def test_radial_hand_derived(golden_dir, name, T, P):
+    for lam, t, j, ids in _golden_radial(golden_dir, name):
+        kv_idx, kv_cnt = oracle.select_radial(T, P, lam)
+        i = t * P + j
+        assert list(kv_idx[0, i, :kv_cnt[0, i]]) == ids, (lam, t, j)
+
+
+@pytest.mark.parametrize("T,P,lam", [(61, 13, 0.0), (61, 13, 0.1), (9, 5, 0.3), (4, 1, 0.0), (33, 24, 0.05)])
+def test_radial_window_invariants(T, P, lam):
+    """Own frame kept whole; own position kept in every frame; each frame's
+    window is one contiguous run of tiles; widths never grow with distance
+    and halve (rounded up) each time d + 1 doubles, down to the lam floor."""
+    kv_idx, kv_cnt = oracle.select_radial(T, P, lam)
+    widths = [oracle.radial_width(d, P, lam) for d in range(T)]
+    assert widths[0] == P and all(a >= b for a, b in zip(widths, widths[1:]))
+    floor = max(1, int(np.ceil(lam * P)))
+    assert all(w >= floor for w in widths)
+    k = 0
+    while (1 << k) - 1 < T:                       # dyadic bands d + 1 in [2^k, 2^(k+1))
+        band = widths[(1 << k) - 1:min((2 << k) - 1, T)]
+        assert len(set(band)) == 1
+        if k > 0:
+            prev = widths[(1 << (k - 1)) - 1]
+            assert band[0] == max(-(-prev // 2), floor) or band[0] == floor
+        k += 1
+    for t in range(T):
+        for j in range(P):
+            i = t * P + j
+            ids = kv_idx[0, i, :kv_cnt[0, i]]
+            assert kv_cnt[0, i] == sum(widths[abs(t - f)] for f in range(T))
+            f_of, j_of = np.divmod(ids, P)
+            for f in range(T):
+                js = j_of[f_of == f]
+                assert j in js
+                assert np.array_equal(js, np.arange(js.min(), js.max() + 1))
+                assert js.size == widths[abs(t - f)]
+
+
+def test_radial_full_factor_is_dense():
+    kv_idx, kv_cnt = oracle.select_radial(6, 3, 1.0)
+    assert np.all(kv_cnt == 18)
+
+
+def test_radial_dynamic_union_and_threshold():
+    """The dynamic mode keeps the radial window plus every block whose logit
+    is within delta of the row's best (float32); delta = 0 adds the row's
+    best block(s), a huge delta keeps everything, and growing delta only adds."""
+    rng = np.random.default_rng(7)
+    T, P, nh = 6, 4, 2
+    nb = T * P
+    S = rng.standard_normal((nh, nb, nb)).astype(np.float32)
+    S[0, 3, 5] = S[0, 3].max()            # a tie for the row's best
+    base_idx, base_cnt = oracle.select_radial(T, P, 0.0)
+    prev = None
+    for delta in (0.0, 0.5, 1.5, 1e9):
+        kv_idx, kv_cnt = oracle.select_radial_dynamic(S, T, P, 0.0, delta)
+        sets = [[set(kv_idx[h, i, :kv_cnt[h, i]]) for i in range(nb)] for h in range(nh)]
+        for h in range(nh):
+            for i in range(nb):
+                base = set(base_idx[0, i, :base_cnt[0, i]])
+                strong = set(np.nonzero(S[h, i] >= np.float32(S[h, i].max()) - np.float32(delta))[0])
+                assert sets[h][i] == base | strong
+                assert int(np.argmax(S[h, i])) in sets[h][i]
+                if prev is not None:
+                    assert prev[h][i] <= sets[h][i]
+                if delta == 1e9:
+                    assert len(sets[h][i]) == nb
+        prev = sets
+    assert 5 in set(oracle.select_radial_dynamic(S, T, P, 0.0, 0.0)[0][0, 3])
