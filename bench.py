@@ -98,6 +98,11 @@ def _keep_text(w, L, nb, tiles_steps, nh):
     if w.select == "lvsa":
         return (f"LVSA C={w.C} frames, T_per={w.T_per}: {mean_per_row:.1f} of {nb} tiles per "
                 f"query tile (mean over {len(tiles_steps)} steps)")
+    if w.select == "radial":
+        return f"radial window, long-range factor {w.lam}: {mean_per_row:.1f} of {nb} tiles per query tile"
+    if w.select == "radial_dyn":
+        return (f"radial window (factor {w.lam}) + logits within {w.delta} of the row's best: "
+                f"{mean_per_row:.1f} of {nb} tiles per query tile")
     return (f"cumulative threshold tau={w.tau} + global budget: {mean_per_row:.1f} of {nb} blocks per "
             f"query block (mean over {len(tiles_steps)} steps)")
 
@@ -138,7 +143,7 @@ def main():
     esz = 2 if w.dtype == "bf16" else 4
     stream = torch.cuda.current_stream()
 
-    scored = w.select != "lvsa"
+    scored = L.S is not None
     # the diffusion step a timed step stands for: its budget (threshold mode)
     # or its anchor rotation (LVSA); top-k steps refresh the same way each time
     def step_of(i):
@@ -154,7 +159,7 @@ def main():
             ev[1].record(stream)
         if scored:
             qp, kp, _ = L.xp
-            hsa.hsa_score(qp, kp, L.blk_len, B, w.s, "mass", L.scale, out=L.S, pooled=L.pooled)
+            hsa.hsa_score(qp, kp, L.blk_len, B, w.s, L.agg, L.scale, out=L.S, pooled=L.pooled)
         if ev is not None:
             ev[2].record(stream)
         hsa.hsa_select(L.S, nh, nb, L.params(st, wl.budget_ratio(w, st)), L.max_kv,

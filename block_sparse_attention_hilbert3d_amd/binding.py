@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libhsa.so")
 HSA_F32, HSA_BF16 = 0, 1
 ORDERS = {"row": 0, "hilbert": 1, "frame": 2, "tile2d": 3, "cube3d": 4}
 AGGS = {"mass": 0, "max": 1}
-MODES = {"topk": 0, "thresh_global": 1, "lvsa": 2}
+MODES = {"topk": 0, "thresh_global": 1, "lvsa": 2, "radial": 3, "radial_dyn": 4}
 
 _c_i32, _c_i64, _c_f32, _c_sz, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -29,7 +29,8 @@ class SelectParams(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("k", ctypes.c_int32), ("tau", ctypes.c_double),
                 ("budget_ratio", ctypes.c_double), ("frames", ctypes.c_int32),
                 ("tiles_per_frame", ctypes.c_int32), ("C", ctypes.c_int32),
-                ("T_per", ctypes.c_int32), ("step", ctypes.c_int32)]
+                ("T_per", ctypes.c_int32), ("step", ctypes.c_int32), ("lam", ctypes.c_double),
+                ("delta", ctypes.c_double)]
 
 
 _SIGS = {
@@ -44,6 +45,7 @@ _SIGS = {
     "hsa_score_ws_size": (_c_sz, [_c_i32] * 4),
     "hsa_score": (ctypes.c_int, [_p, _p, _p, _p] + [_c_i32] * 7 + [_c_f32, _p, _p, _c_sz, _p]),
     "hsa_select_ws_size": (_c_sz, [_c_i32, _c_i32, ctypes.POINTER(SelectParams)]),
+    "hsa_select_list_width": (_c_i32, [_c_i32, _c_i32, ctypes.POINTER(SelectParams)]),
     "hsa_select": (ctypes.c_int, [_p, _c_i32, _c_i32, ctypes.POINTER(SelectParams), _p, _p, _c_i32, _p, _c_sz, _p]),
     "hsa_attn": (ctypes.c_int, [_p] * 9 + [_c_i32] * 7 + [_c_f32, _p]),
     "hsa_attn_order": (ctypes.c_int, [_p, _c_i32, _c_i32, _c_i32, _p, _p]),
@@ -172,18 +174,27 @@ def hsa_score(qp, kp, blk_len, B: int, s: int, agg: str = "mass", scale: float |
 
 
 def make_params(mode: str, k=0, tau=0.0, budget_ratio=0.0, frames=0, tiles_per_frame=0, C=0,
-                T_per=1, step=0) -> SelectParams:
+                T_per=1, step=0, lam=0.0, delta=0.0) -> SelectParams:
     return SelectParams(MODES[mode], int(k), float(tau), float(budget_ratio), int(frames),
-                        int(tiles_per_frame), int(C), int(T_per), int(step))
+                        int(tiles_per_frame), int(C), int(T_per), int(step), float(lam), float(delta))
+
+
+def hsa_select_list_width(nh: int, nb: int, params: SelectParams) -> int:
+    """Smallest max_kv hsa_select accepts for these parameters."""
+    n = lib().hsa_select_list_width(nh, nb, ctypes.byref(params))
+    if n < 1:
+        raise HsaError("hsa_select_list_width: invalid parameters")
+    return n
 
 
 def hsa_select(S, nh: int, nb: int, params: SelectParams, max_kv: int, device="cuda",
                outs=None, ws=None):
-    """-> (kv_idx int32 [G, nb, max_kv], kv_cnt int32 [G, nb]); G = 1 for LVSA."""
+    """-> (kv_idx int32 [G, nb, max_kv], kv_cnt int32 [G, nb]); G = 1 for the head-shared
+    modes (LVSA, RADIAL)."""
     if S is not None:
         _need_device(S)
         device = S.device
-    G = 1 if params.mode == MODES["lvsa"] else nh
+    G = 1 if params.mode in (MODES["lvsa"], MODES["radial"]) else nh
     if outs is None:
         outs = (torch.empty((G, nb, max_kv), dtype=torch.int32, device=device),
                 torch.empty((G, nb), dtype=torch.int32, device=device))

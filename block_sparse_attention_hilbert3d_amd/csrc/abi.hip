@@ -208,6 +208,55 @@ hsa_status_t hsa_score(const void *qp, const void *kp, const float *pooled,
                       static_cast<hipStream_t>(stream));
 }
 
+// Radial window width at temporal distance d (DynamicRad static ratio): the
+// frame's P tiles halved (rounded up) each time d + 1 doubles, floored at
+// ceil(lam * P) and 1.
+static int radial_w(int d, int P, int lam_tiles) {
+  int k = 0;
+  while ((2 << k) <= d + 1) ++k;
+  const int w = (P + (1 << k) - 1) >> k;
+  const int m = w > lam_tiles ? w : lam_tiles;
+  return m < 1 ? 1 : (m > P ? P : m);
+}
+
+static int radial_lam_tiles(double lam, int P) { return static_cast<int>(ceil(lam * P)); }
+
+static int radial_list_width(int T, int P, double lam) {
+  const int lt = radial_lam_tiles(lam, P);
+  int best = 0;
+  for (int t = 0; t < T; ++t) {
+    int n = 0;
+    for (int f = 0; f < T; ++f) n += radial_w(t > f ? t - f : f - t, P, lt);
+    best = n > best ? n : best;
+  }
+  return best;
+}
+
+static int lvsa_list_width(const hsa_select_params_t *p) {
+  const int rot = p->step % p->T_per;
+  const int anchors = rot < p->frames ? (p->frames - 1 - rot) / p->T_per + 1 : 0;
+  const int others = p->frames - anchors;
+  const int want = p->C - anchors > 1 ? p->C - anchors : 1;
+  const int nw = others < want ? others : want;
+  return (anchors + nw) * p->tiles_per_frame;
+}
+
+int32_t hsa_select_list_width(int32_t nh, int32_t nb, const hsa_select_params_t *p) {
+  if (!p || nh < 1 || nb < 1) return 0;
+  switch (p->mode) {
+    case HSA_SELECT_TOPK: return p->k;
+    case HSA_SELECT_THRESH_GLOBAL: return nb;
+    case HSA_SELECT_RADIAL_DYN: return nb;
+    case HSA_SELECT_LVSA:
+      if (p->frames < 1 || p->tiles_per_frame < 1 || p->T_per < 1 || p->step < 0 || p->C < 1) return 0;
+      return lvsa_list_width(p);
+    case HSA_SELECT_RADIAL:
+      if (p->frames < 1 || p->frames > 1024 || p->tiles_per_frame < 1 || !(p->lam >= 0.0) || !(p->lam <= 1.0)) return 0;
+      return radial_list_width(p->frames, p->tiles_per_frame, p->lam);
+    default: return 0;
+  }
+}
+
 size_t hsa_select_ws_size(int32_t nh, int32_t nb, const hsa_select_params_t *p) {
   if (!p || nh < 1 || nb < 1) return 0;
   return select_ws_bytes(nh, nb, p->mode);
@@ -243,12 +292,24 @@ hsa_status_t hsa_select(const float *S, int32_t nh, int32_t nb, const hsa_select
       if (static_cast<int64_t>(p->frames) * p->tiles_per_frame != nb) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: frames*tiles_per_frame != nb");
       if (p->C < 1 || p->T_per < 1 || p->step < 0) return fail(HSA_ERR_BAD_ARG, "hsa_select: C=%d T_per=%d step=%d", p->C, p->T_per, p->step);
       // largest |A(t)|: all anchors plus max(C - anchors, 1) window frames
-      const int rot = p->step % p->T_per;
-      const int anchors = rot < p->frames ? (p->frames - 1 - rot) / p->T_per + 1 : 0;
-      const int others = p->frames - anchors;
-      const int nw = others < (p->C - anchors > 1 ? p->C - anchors : 1) ? others : (p->C - anchors > 1 ? p->C - anchors : 1);
-      const int64_t need = static_cast<int64_t>(anchors + nw) * p->tiles_per_frame;
+      const int64_t need = lvsa_list_width(p);
       if (max_kv < need) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: max_kv %d < %lld tiles per list", max_kv, static_cast<long long>(need));
+      break;
+    }
+    case HSA_SELECT_RADIAL:
+    case HSA_SELECT_RADIAL_DYN: {
+      if (p->frames < 1 || p->frames > 1024 || p->tiles_per_frame < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: frames=%d tiles_per_frame=%d", p->frames, p->tiles_per_frame);
+      if (static_cast<int64_t>(p->frames) * p->tiles_per_frame != nb) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: frames*tiles_per_frame != nb");
+      if (!(p->lam >= 0.0) || !(p->lam <= 1.0)) return fail(HSA_ERR_BAD_ARG, "hsa_select: lam %g not in [0, 1]", p->lam);
+      if (p->mode == HSA_SELECT_RADIAL) {
+        const int need = radial_list_width(p->frames, p->tiles_per_frame, p->lam);
+        if (max_kv < need) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: max_kv %d < %d tiles per list", max_kv, need);
+      } else {
+        if (!S) return fail(HSA_ERR_NULL_PTR, "hsa_select: scores required");
+        if (!(p->delta >= 0.0) || !isfinite(p->delta)) return fail(HSA_ERR_BAD_ARG, "hsa_select: delta %g must be finite and >= 0", p->delta);
+        if (max_kv != nb) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: RADIAL_DYN needs max_kv == nb");
+        if (nb > 4096) return fail(HSA_ERR_UNSUPPORTED, "hsa_select: nb %d > 4096", nb);
+      }
       break;
     }
     default:

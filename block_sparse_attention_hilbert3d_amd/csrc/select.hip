@@ -366,6 +366,82 @@ lvsa_kernel(int T, int tiles, int C, int T_per, int step, int32_t *__restrict__ 
   if (lane == 0) kv_cnt[I] = before * tiles;
 }
 
+// DynamicRad radial window (static-ratio mode): width w(d) of the window in
+// a key frame at temporal distance d, and its first tile for query tile j.
+__device__ __forceinline__ int radial_width_dev(int d, int P, int lam_tiles) {
+  const int k = 31 - __clz(d + 1);  // floor(log2(d + 1))
+  const int w = (P + (1 << k) - 1) >> k;
+  return min(P, max(max(w, lam_tiles), 1));
+}
+__device__ __forceinline__ int radial_lo(int j, int w, int P) { return min(max(j - w / 2, 0), P - w); }
+
+// Static radial lists: one wave per query tile, key frames over the lanes;
+// a frame's window lands after the windows of all earlier frames.
+__global__ void __launch_bounds__(64)
+radial_kernel(int T, int P, int lam_tiles, int32_t *__restrict__ kv_idx, int32_t *__restrict__ kv_cnt,
+              int max_kv) {
+  const int I = blockIdx.x;
+  const int t = I / P, j = I - t * P;
+  const int lane = lane_id();
+  int32_t *out = kv_idx + static_cast<int64_t>(I) * max_kv;
+  int before = 0;
+  for (int f0 = 0; f0 < T; f0 += 64) {
+    const int f = f0 + lane;
+    const int w = f < T ? radial_width_dev(abs(t - f), P, lam_tiles) : 0;
+    // inclusive scan of w over the lanes
+    int incl = w;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    if (f < T) {
+      const int lo = radial_lo(j, w, P);
+      const int pos = before + incl - w;
+      for (int q = 0; q < w; ++q) out[pos + q] = f * P + lo + q;
+    }
+    before += __shfl(incl, 63, 64);
+  }
+  for (int p = before + lane; p < max_kv; p += 64) out[p] = -1;
+  if (lane == 0) kv_cnt[I] = before;
+}
+
+// Dynamic radial lists: one wave per (head, query tile): the row's best
+// logit, the float threshold best - delta, then every block inside the
+// radial window or at/above the threshold, ascending.
+__global__ void __launch_bounds__(256)
+radial_dyn_kernel(const float *__restrict__ S, int rows, int nb, int T, int P, int lam_tiles,
+                  float delta, int32_t *__restrict__ kv_idx, int32_t *__restrict__ kv_cnt, int max_kv) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = lane_id();
+  const int I = row % nb;
+  const int t = I / P, j = I - t * P;
+  const float *srow = S + static_cast<int64_t>(row) * nb;
+  float m = -INFINITY;
+  for (int J = lane; J < nb; J += 64) m = fmaxf(m, srow[J]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  const float thr = m - delta;
+  int32_t *out = kv_idx + static_cast<int64_t>(row) * max_kv;
+  int before = 0;
+  for (int J0 = 0; J0 < nb; J0 += 64) {
+    const int J = J0 + lane;
+    bool keep = false;
+    if (J < nb) {
+      const int f = J / P, jj = J - f * P;
+      const int w = radial_width_dev(abs(t - f), P, lam_tiles);
+      const int lo = radial_lo(j, w, P);
+      keep = (jj >= lo && jj < lo + w) || srow[J] >= thr;
+    }
+    const uint64_t b = __ballot(keep);
+    if (keep) out[before + popc64(b & lanemask_lt())] = J;
+    before += popc64(b);
+  }
+  for (int p = before + lane; p < max_kv; p += 64) out[p] = -1;
+  if (lane == 0) kv_cnt[row] = before;
+}
+
 }  // namespace hsa
 
 namespace hsa_host {
@@ -430,9 +506,20 @@ hsa_status_t launch_select(const float *S, int nh, int nb, const hsa_select_para
     }
     HSA_KPL_DISPATCH(nb, hsa::thresh_emit_kernel, grid, dim3(hsa::kSelThreads), S, nh, nb, row_thr,
                      st, kv_idx, kv_cnt, max_kv);
-  } else {
+  } else if (p->mode == HSA_SELECT_LVSA) {
     HSA_KPL_DISPATCH(p->frames, hsa::lvsa_kernel, dim3(nb), dim3(64), p->frames,
                      p->tiles_per_frame, p->C, p->T_per, p->step, kv_idx, kv_cnt, max_kv);
+  } else {
+    const int lam_tiles = static_cast<int>(ceil(p->lam * p->tiles_per_frame));
+    if (p->mode == HSA_SELECT_RADIAL) {
+      hipLaunchKernelGGL(hsa::radial_kernel, dim3(nb), dim3(64), 0, stream, p->frames,
+                         p->tiles_per_frame, lam_tiles, kv_idx, kv_cnt, max_kv);
+    } else {
+      const int rows = nh * nb;
+      hipLaunchKernelGGL(hsa::radial_dyn_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, S, rows,
+                         nb, p->frames, p->tiles_per_frame, lam_tiles, static_cast<float>(p->delta),
+                         kv_idx, kv_cnt, max_kv);
+    }
   }
   return check_launch("hsa_select");
 }

@@ -21,12 +21,14 @@ from . import binding as B_
 class SparseAttentionLayer:
     def __init__(self, T: int, H: int, W: int, heads: int, D: int, *, order: str, B: int,
                  select: str, s: int = 0, agg: str = "mass", k: int = 0, tau: float = 0.0,
-                 C: int = 0, T_per: int = 1, dtype=torch.bfloat16, device="cuda",
-                 want_lse: bool = True):
+                 C: int = 0, T_per: int = 1, lam: float = 0.0, delta: float = 0.0,
+                 dtype=torch.bfloat16, device="cuda", want_lse: bool = True):
         self.T, self.H, self.W, self.heads, self.D = T, H, W, heads, D
         self.N = T * H * W
         self.order, self.B, self.select, self.s, self.agg = order, B, select, s, agg
-        self.k, self.tau, self.C, self.T_per = k, tau, C, T_per
+        self.k, self.tau, self.C, self.T_per, self.lam, self.delta = k, tau, C, T_per, lam, delta
+        if select == "radial_dyn":
+            self.agg = "max"   # the dynamic threshold reads pre-softmax logits
         self.dtype, self.device = dtype, device
         self.scale = 1.0 / math.sqrt(D)
         self.perm, self.blk_len = B_.hsa_plan(T, H, W, order, B, device=device)
@@ -39,8 +41,9 @@ class SparseAttentionLayer:
         self.lse = torch.empty((heads, self.n_pad), dtype=torch.float32, device=device) if want_lse else None
         self.want_lse = want_lse
         self.o = torch.empty((1, self.N, heads, D), dtype=dtype, device=device)
-        if select == "lvsa":
-            self.max_kv = self._lvsa_width()
+        if select in ("lvsa", "radial"):   # geometry-only masks shared by all heads
+            self.max_kv = self._lvsa_width() if select == "lvsa" else \
+                B_.hsa_select_list_width(heads, self.nb, self.params(0, 0.0))
             G = 1
             self.S = None
             self.score_ws = None
@@ -56,7 +59,7 @@ class SparseAttentionLayer:
         self.kv_cnt = torch.empty((G, self.nb), dtype=torch.int32, device=device)
         # threshold lists differ in length from row to row: attend longest first
         self.order = (torch.arange(G * self.nb, dtype=torch.int32, device=device)
-                      if select == "thresh_global" else None)
+                      if select in ("thresh_global", "radial_dyn") else None)
         p = self.params(0, 0.0)
         n = B_.lib().hsa_select_ws_size(heads, self.nb, p)
         self.select_ws = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
@@ -73,11 +76,12 @@ class SparseAttentionLayer:
     def params(self, step: int, budget_ratio: float) -> B_.SelectParams:
         return B_.make_params(self.select, k=self.k, tau=self.tau, budget_ratio=budget_ratio,
                               frames=self.T, tiles_per_frame=self.tiles_per_frame, C=self.C,
+                              lam=self.lam, delta=self.delta,
                               T_per=self.T_per, step=step)
 
     def reorder(self, q, k, v, pool: bool = True):
         """Gather Q/K/V; on steps that refresh the mask also pool Q/K sub-blocks."""
-        if pool and self.select != "lvsa":
+        if pool and self.S is not None:
             B_.hsa_perm([q, k, v], self.perm, self.n_pad, outs=self.xp, pool_s=self.s,
                         pooled=self.pooled)
         else:
@@ -85,7 +89,7 @@ class SparseAttentionLayer:
 
     def make_mask(self, step: int = 0, budget_ratio: float = 0.0):
         qp, kp, _ = self.xp
-        if self.select != "lvsa":
+        if self.S is not None:
             B_.hsa_score(qp, kp, self.blk_len, self.B, self.s, self.agg, self.scale, out=self.S,
                          pooled=self.pooled)
         B_.hsa_select(self.S, self.heads, self.nb, self.params(step, budget_ratio), self.max_kv,
@@ -128,5 +132,6 @@ def layer_for_workload(w, device="cuda", want_lse=True) -> SparseAttentionLayer:
     if w.select == "topk":
         k = w.k if w.k > 0 else max(1, int(math.floor(w.keep_ratio * nb + 0.5)))
     return SparseAttentionLayer(w.T, w.H, w.W, w.heads, w.D, order=w.order, B=w.B,
-                                select=w.select, s=w.s, k=k, tau=w.tau, C=w.C, T_per=w.T_per,
-                                dtype=dtype, device=device, want_lse=want_lse)
+                                select=w.select, s=w.s, agg=w.agg, k=k, tau=w.tau, C=w.C,
+                                T_per=w.T_per, lam=w.lam, delta=w.delta, dtype=dtype,
+                                device=device, want_lse=want_lse)

@@ -72,7 +72,9 @@ typedef enum { HSA_AGG_MASS = 0, HSA_AGG_MAX = 1 } hsa_agg_t;
 typedef enum {
   HSA_SELECT_TOPK = 0,
   HSA_SELECT_THRESH_GLOBAL = 1,
-  HSA_SELECT_LVSA = 2
+  HSA_SELECT_LVSA = 2,
+  HSA_SELECT_RADIAL = 3,     /* DynamicRad static-ratio radial mask */
+  HSA_SELECT_RADIAL_DYN = 4  /* DynamicRad dynamic logit threshold */
 } hsa_select_mode_t;
 
 typedef void *hsa_stream_t; /* a hipStream_t */
@@ -83,11 +85,13 @@ typedef struct hsa_select_params {
   int32_t k;               /* TOPK: key blocks kept per query block, 1..nb */
   double tau;              /* THRESH_GLOBAL: cumulative score per query block, >= 0 */
   double budget_ratio;     /* THRESH_GLOBAL: head budget floor(ratio*nb*nb + 0.5) pairs */
-  int32_t frames;          /* LVSA: number of frames T (nb = frames*tiles_per_frame) */
-  int32_t tiles_per_frame; /* LVSA: tiles (blocks) per frame */
+  int32_t frames;          /* LVSA, RADIAL*: number of frames T (nb = frames*tiles_per_frame) */
+  int32_t tiles_per_frame; /* LVSA, RADIAL*: tiles (blocks) per frame */
   int32_t C;               /* LVSA: frame budget per query frame, >= 1 */
   int32_t T_per;           /* LVSA: anchor period in frames, >= 1 */
   int32_t step;            /* LVSA: denoising step index, >= 0 */
+  double lam;              /* RADIAL*: long-range factor in [0, 1] */
+  double delta;            /* RADIAL_DYN: logit margin below the row's best, >= 0 */
 } hsa_select_params_t;
 
 /* Library version (HSA_ABI_VERSION) and status strings. */
@@ -175,8 +179,15 @@ hsa_status_t hsa_score(const void *qp, const void *kp, const float *pooled,
                        int32_t D, int32_t dtype, int32_t agg, float scale, float *S, void *ws,
                        size_t ws_bytes, hsa_stream_t stream);
 
-/* Workspace bytes for hsa_select (0 for TOPK and LVSA). */
+/* Workspace bytes for hsa_select (0 for every mode but THRESH_GLOBAL). */
 size_t hsa_select_ws_size(int32_t nh, int32_t nb, const hsa_select_params_t *p);
+
+/*
+ * hsa_select_list_width -- host-only: the smallest max_kv hsa_select accepts
+ * for these parameters (k for TOPK; nb for THRESH_GLOBAL and RADIAL_DYN; the
+ * longest list for LVSA and RADIAL). Returns 0 for invalid parameters.
+ */
+int32_t hsa_select_list_width(int32_t nh, int32_t nb, const hsa_select_params_t *p);
 
 /*
  * hsa_select -- per-query-block ascending lists of key blocks.
@@ -195,6 +206,20 @@ size_t hsa_select_ws_size(int32_t nh, int32_t nb, const hsa_select_params_t *p);
  *   frames (ties to the earlier frame; at least one); every tile of frame t
  *   lists every tile of those frames. S is not read (may be NULL). One list
  *   set shared by all heads: kv_idx [nb][max_kv], kv_cnt [nb].
+ * RADIAL (DynamicRad section 2: static-ratio mode over a logarithmic radial
+ *   window with long-range factor lam): blocks are frame tiles (block
+ *   t*P + j is tile j of frame t, P = tiles_per_frame). Query tile (t, j)
+ *   keeps, in every frame f at distance d = |t - f|, the
+ *   w(d) = min(P, max(ceil(P / 2^floor(log2(d+1))), ceil(lam*P), 1)) tiles
+ *   nearest to position j (ties to the lower tile): the run starting at
+ *   clamp(j - floor(w/2), 0, P - w). S is not read (may be NULL). Shared by
+ *   all heads: kv_idx [nb][max_kv], kv_cnt [nb]; max_kv >= the width that
+ *   hsa_select_list_width reports.
+ * RADIAL_DYN (DynamicRad section 2: dynamic-threshold mode, pre-softmax
+ *   logits as importance): per head, the RADIAL window of each row plus
+ *   every block J with S[h][I][J] >= max_J S[h][I][J] - (float)delta,
+ *   formed and compared in float. S holds block logits (hsa_score with
+ *   HSA_AGG_MAX), finite. Lists [nh][nb][max_kv]; max_kv must be nb.
  * ws: device workspace of hsa_select_ws_size bytes.
  */
 hsa_status_t hsa_select(const float *S, int32_t nh, int32_t nb, const hsa_select_params_t *p,

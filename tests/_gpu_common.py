@@ -31,6 +31,10 @@ def oracle_select(w, S, nb, step, max_kv=None):
     if w.select == "thresh_global":
         return oracle.select_thresh_global(S, w.tau, wl.budget_ratio(w, step), max_kv)
     tiles = nb // w.T
+    if w.select == "radial":
+        return oracle.select_radial(w.T, tiles, w.lam, max_kv)
+    if w.select == "radial_dyn":
+        return oracle.select_radial_dynamic(S, w.T, tiles, w.lam, w.delta, max_kv)
     return oracle.select_lvsa(w.T, tiles, w.C, w.T_per, step, max_kv)
 
 

@@ -144,6 +144,26 @@ def test_select_validation(B):
     assert L.hsa_select(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 4, NULL, 0, NULL) == 6
 
 
+def test_radial_select_validation_and_width(B):
+    L = B.lib()
+    p = B.make_params("radial", frames=61, tiles_per_frame=13, lam=0.125)
+    width = L.hsa_select_list_width(12, 793, ctypes.byref(p))
+    assert width == 169
+    assert L.hsa_select(NULL, 12, 793, ctypes.byref(p), FAKE, FAKE, width - 1, NULL, 0, NULL) == 2
+    assert L.hsa_select(NULL, 12, 792, ctypes.byref(p), FAKE, FAKE, width, NULL, 0, NULL) == 2
+    p = B.make_params("radial", frames=61, tiles_per_frame=13, lam=1.5)
+    assert L.hsa_select(NULL, 12, 793, ctypes.byref(p), FAKE, FAKE, 793, NULL, 0, NULL) == 6
+    assert L.hsa_select_list_width(12, 793, ctypes.byref(p)) == 0
+    p = B.make_params("radial_dyn", frames=61, tiles_per_frame=13, lam=0.1, delta=1.0)
+    assert L.hsa_select_list_width(12, 793, ctypes.byref(p)) == 793
+    assert L.hsa_select(NULL, 12, 793, ctypes.byref(p), FAKE, FAKE, 793, NULL, 0, NULL) == 1   # S
+    assert L.hsa_select(FAKE, 12, 793, ctypes.byref(p), FAKE, FAKE, 792, NULL, 0, NULL) == 2   # max_kv
+    p = B.make_params("radial_dyn", frames=61, tiles_per_frame=13, lam=0.1, delta=-1.0)
+    assert L.hsa_select(FAKE, 12, 793, ctypes.byref(p), FAKE, FAKE, 793, NULL, 0, NULL) == 6
+    p = B.make_params("topk", k=7)
+    assert L.hsa_select_list_width(2, 16, ctypes.byref(p)) == 7
+
+
 def test_attn_and_unperm_validation(B):
     L = B.lib()
     a = [FAKE] * 8

@@ -244,7 +244,7 @@ def _check_layer(hsa, w, step, q, k, v, L, o, check_select=True):
     assert np.array_equal(perm, oracle.plan(w.T, w.H, w.W, w.order, w.B)[0])
     kv_idx, kv_cnt = L.kv_idx.cpu().numpy(), L.kv_cnt.cpu().numpy()
     if check_select:
-        S = None if w.select == "lvsa" else L.S.cpu().numpy().astype(np.float64)
+        S = None if L.S is None else L.S.cpu().numpy().astype(np.float64)
         ref = oracle_select(w, S, nb, step, max_kv=kv_idx.shape[2])
         assert lists_equal(kv_idx, kv_cnt, *ref)
     _say("  lists ok; oracle attention on the sampled rows")
@@ -271,7 +271,7 @@ def test_layer_all_rows(hsa, idx):
     _check_layer(hsa, w, 0, *_layer(hsa, w, 0))
 
 
-@pytest.mark.parametrize("idx,step", [(3, 0), (4, 0), (4, 5), (5, 0), (5, 9)])
+@pytest.mark.parametrize("idx,step", [(3, 0), (4, 0), (4, 5), (5, 0), (5, 9), (6, 0), (7, 0)])
 def test_layer_sampled_rows(hsa, idx, step):
     w = wl.get(idx)
     _say(f"layer workload {idx} step {step} (sampled rows)")
@@ -288,6 +288,35 @@ def test_layer_vmoba_partitions(hsa, idx, order, step):
     w = replace(wl.get(idx), order=order)
     _say(f"layer workload {idx} with {order} blocks, step {step}")
     _check_layer(hsa, w, step, *_layer(hsa, w, step))
+
+
+@pytest.mark.parametrize("T,P,lam", [(61, 13, 0.125), (61, 13, 0.0), (1, 1, 0.0), (5, 4, 0.5),
+                                     (100, 3, 0.0), (7, 70, 0.3), (130, 2, 1.0)])
+def test_radial_lists_bit_exact(hsa, T, P, lam):
+    """DynamicRad static-ratio lists from the GPU equal the oracle's."""
+    _say(f"radial lists T={T} P={P} lam={lam}")
+    nb = T * P
+    p = hsa.make_params("radial", frames=T, tiles_per_frame=P, lam=lam)
+    width = hsa.hsa_select_list_width(1, nb, p)
+    kv_idx, kv_cnt = hsa.hsa_select(None, 1, nb, p, width, device=dev())
+    ref = oracle.select_radial(T, P, lam, width)
+    assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), *ref)
+    assert width == int(ref[1].max())
+
+
+@pytest.mark.parametrize("T,P,delta", [(6, 4, 0.0), (6, 4, 0.7), (20, 13, 1.0), (3, 3, 1e6)])
+def test_radial_dynamic_lists_bit_exact(hsa, T, P, delta):
+    """The dynamic threshold on given float32 logits (ties included) equals
+    the oracle's float32 decision."""
+    _say(f"radial dynamic T={T} P={P} delta={delta}")
+    nh, nb = 3, T * P
+    rng = np.random.default_rng(T * 100 + P)
+    S = np.round(rng.standard_normal((nh, nb, nb)) * 4) / 4      # many exact ties
+    S = S.astype(np.float32)
+    p = hsa.make_params("radial_dyn", frames=T, tiles_per_frame=P, lam=0.1, delta=delta)
+    kv_idx, kv_cnt = hsa.hsa_select(torch.from_numpy(S).to(dev()), nh, nb, p, nb)
+    ref = oracle.select_radial_dynamic(S, T, P, 0.1, delta, nb)
+    assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), *ref)
 
 
 def test_cached_mask_step(hsa):

@@ -60,7 +60,7 @@ class Workload:
     order: str             # "row", "hilbert" or "frame"
     B: int                 # block (tile) size in tokens
     s: int                 # sub-block size used for scoring (0 = no scoring)
-    select: str            # "topk", "thresh_global" or "lvsa"
+    select: str            # "topk", "thresh_global", "lvsa", "radial" or "radial_dyn"
     keep_ratio: float = 0.0      # top-k budget as a fraction of blocks
     k: int = 0                   # explicit top-k (0 = derive from keep_ratio)
     tau: float = 0.0             # cumulative-mass threshold per query block
@@ -71,6 +71,9 @@ class Workload:
     steps: int = 1               # simulated denoising steps
     refresh: int = 1             # mask recomputed when step % refresh == 0
     sample_rows: int = 0         # 0 = compare every row
+    agg: str = "mass"            # block score aggregation ("max": pre-softmax logits)
+    lam: float = 0.0             # radial masks: long-range factor
+    delta: float = 0.0           # dynamic radial mask: logit margin below the row's best
     extra: dict = field(default_factory=dict, compare=False)
 
     @property
@@ -100,6 +103,16 @@ WORKLOADS = {
                 T=33, H=45, W=80, heads=24, D=128, dtype="bf16", qk="smooth",
                 order="hilbert", B=128, s=128, select="thresh_global", tau=0.25,
                 budget_start=0.30, budget_end=0.10, steps=10, sample_rows=4096),
+    6: Workload(6, "DynamicRad-style static radial mask: 61x30x52 frame tiles, 12 heads, d128, "
+                   "bf16, long-range factor 1/8",
+                T=61, H=30, W=52, heads=12, D=128, dtype="bf16", qk="smooth",
+                order="frame", B=128, s=0, select="radial", lam=0.125, sample_rows=4096),
+    7: Workload(7, "DynamicRad-style dynamic logit threshold: 61x30x52 frame tiles, 12 heads, "
+                   "d128, bf16, radial window (factor 1/8) + blocks within 1.0 of the row's best "
+                   "64-token sub-block logit",
+                T=61, H=30, W=52, heads=12, D=128, dtype="bf16", qk="smooth",
+                order="frame", B=128, s=64, select="radial_dyn", agg="max", lam=0.125,
+                delta=1.0, sample_rows=4096),
 }
 
 
