@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhsa.so")
 
 HSA_F32, HSA_BF16 = 0, 1
-ORDERS = {"row": 0, "hilbert": 1, "frame": 2, "tile2d": 3, "cube3d": 4}
+ORDERS = {"row": 0, "hilbert": 1, "frame": 2, "tile2d": 3, "cube3d": 4, "hilbert2d": 5}
 AGGS = {"mass": 0, "max": 1}
 MODES = {"topk": 0, "thresh_global": 1, "lvsa": 2, "radial": 3, "radial_dyn": 4}
 
@@ -50,6 +50,8 @@ _SIGS = {
     "hsa_attn": (ctypes.c_int, [_p] * 9 + [_c_i32] * 7 + [_c_f32, _p]),
     "hsa_attn_order": (ctypes.c_int, [_p, _c_i32, _c_i32, _c_i32, _p, _p]),
     "hsa_unperm": (ctypes.c_int, [_p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _p]),
+    "hsa_block_mass": (ctypes.c_int, [_p, _p, _p, _p] + [_c_i32] * 6 + [_c_f32, _p, _p, _c_i32, _c_i32,
+                                                                     _p, _p, _p]),
 }
 
 _lib = None
@@ -247,3 +249,25 @@ def hsa_unperm(op, perm, N: int, out=None):
     _check(lib().hsa_unperm(_ptr(op), _ptr(out), _ptr(perm), N, n_pad, nh, D, out.stride(1),
                             _dtype_code(op), _stream()), "hsa_unperm")
     return out
+
+
+def hsa_block_mass(qp, kp, blk_len, rows, B: int, scale: float | None = None, kv_idx=None,
+                   kv_cnt=None, want_mass: bool = True):
+    """Selection diagnostic. rows int32 [nh, n_rows] (slots) -> (mass float32 [nh, n_rows, nb]
+    or None, recall float32 [nh, n_rows] or None; recall needs kv_idx/kv_cnt)."""
+    _need_device(qp, kp, blk_len, rows, kv_idx, kv_cnt)
+    nh, n_pad, D = qp.shape
+    nb = n_pad // B
+    n_rows = rows.shape[1]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    mass = torch.empty((nh, n_rows, nb), dtype=torch.float32, device=qp.device) if want_mass else None
+    rec = None
+    shared, max_kv = 0, 0
+    if kv_idx is not None:
+        rec = torch.empty((nh, n_rows), dtype=torch.float32, device=qp.device)
+        shared = 1 if kv_idx.shape[0] == 1 and nh > 1 else 0
+        max_kv = kv_idx.shape[-1]
+    _check(lib().hsa_block_mass(_ptr(qp), _ptr(kp), _ptr(blk_len), _ptr(rows), n_rows, nh, nb, B, D,
+                                _dtype_code(qp), scale, _ptr(kv_idx), _ptr(kv_cnt), max_kv, shared,
+                                _ptr(mass), _ptr(rec), _stream()), "hsa_block_mass")
+    return mass, rec

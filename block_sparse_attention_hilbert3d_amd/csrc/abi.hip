@@ -28,7 +28,7 @@ hsa_status_t check_launch(const char *what) {
 }
 
 // Defined next to their kernels.
-size_t plan_hilbert_groups(int T, int H, int W, int &bits, uint32_t &cube);
+size_t plan_hilbert_groups(int T, int H, int W, int &bits, uint32_t &cube, int dims);
 hsa_status_t launch_plan(int T, int H, int W, int order, int B, int n_pad, int nb, int32_t *perm,
                          int32_t *blk_len, void *ws, hipStream_t stream);
 hsa_status_t launch_perm(int n, const void *const *xs, void *const *xps, const int32_t *perm,
@@ -48,6 +48,10 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                          const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
                          const int32_t *order, int max_kv, int kv_shared, int nh, int nb, int B,
                          int D, int dtype, float scale, hipStream_t stream);
+hsa_status_t launch_block_mass(const void *qp, const void *kp, const int32_t *blk_len, const int32_t *rows,
+                               int n_rows, int nh, int nb, int B, int D, int dtype, float scale,
+                               const int32_t *kv_idx, const int32_t *kv_cnt, int max_kv, int kv_shared,
+                               float *mass, float *recall, hipStream_t stream);
 hsa_status_t launch_attn_order(const int32_t *kv_cnt, int G, int nb, int max_kv, int32_t *order,
                                hipStream_t stream);
 
@@ -77,7 +81,7 @@ static hsa_status_t plan_size(int T, int H, int W, int order, int B, int32_t *n_
   if (B < 1 || B > 4096) return fail(HSA_ERR_BAD_SHAPE, "block size %d out of range", B);
   const int64_t N = static_cast<int64_t>(T) * H * W;
   int64_t np;
-  if (order == HSA_ORDER_ROW || order == HSA_ORDER_HILBERT3D) {
+  if (order == HSA_ORDER_ROW || order == HSA_ORDER_HILBERT3D || order == HSA_ORDER_HILBERT2D) {
     np = (N + B - 1) / B * B;
   } else if (order == HSA_ORDER_TILE2D || order == HSA_ORDER_CUBE3D) {
     const bool two = order == HSA_ORDER_TILE2D;
@@ -128,10 +132,12 @@ hsa_status_t hsa_plan_size(int32_t T, int32_t H, int32_t W, int32_t order, int32
 }
 
 size_t hsa_plan_ws_size(int32_t T, int32_t H, int32_t W, int32_t order) {
-  if (order != HSA_ORDER_HILBERT3D || T < 1 || H < 1 || W < 1 || T > 1024 || H > 1024 || W > 1024) return 0;
+  if ((order != HSA_ORDER_HILBERT3D && order != HSA_ORDER_HILBERT2D) || T < 1 || H < 1 || W < 1 ||
+      T > 1024 || H > 1024 || W > 1024)
+    return 0;
   int bits;
   uint32_t cube;
-  return plan_hilbert_groups(T, H, W, bits, cube) * sizeof(int32_t);
+  return plan_hilbert_groups(T, H, W, bits, cube, order == HSA_ORDER_HILBERT3D ? 3 : 2) * sizeof(int32_t);
 }
 
 hsa_status_t hsa_plan(int32_t T, int32_t H, int32_t W, int32_t order, int32_t B, int32_t *perm,
@@ -345,6 +351,26 @@ hsa_status_t hsa_attn_order(const int32_t *kv_cnt, int32_t G, int32_t nb, int32_
   if (max_kv > 4095) return fail(HSA_ERR_UNSUPPORTED, "hsa_attn_order: max_kv > 4095");
   if (!aligned4(kv_cnt) || !aligned4(order)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_order: arrays must be 4-byte aligned");
   return launch_attn_order(kv_cnt, G, nb, max_kv, order, static_cast<hipStream_t>(stream));
+}
+
+hsa_status_t hsa_block_mass(const void *qp, const void *kp, const int32_t *blk_len,
+                            const int32_t *rows, int32_t n_rows, int32_t nh, int32_t nb,
+                            int32_t B, int32_t D, int32_t dtype, float scale,
+                            const int32_t *kv_idx, const int32_t *kv_cnt, int32_t max_kv,
+                            int32_t kv_shared, float *mass, float *recall, hsa_stream_t stream) {
+  g_last_error.clear();
+  if (!qp || !kp || !blk_len || !rows) return fail(HSA_ERR_NULL_PTR, "hsa_block_mass: null input");
+  if (!mass && !recall) return fail(HSA_ERR_NULL_PTR, "hsa_block_mass: no output requested");
+  if (recall && (!kv_idx || !kv_cnt)) return fail(HSA_ERR_NULL_PTR, "hsa_block_mass: recall needs the lists");
+  hsa_status_t st;
+  if ((st = check_dtype(dtype)) != HSA_OK || (st = check_D(D)) != HSA_OK || (st = check_B(B)) != HSA_OK) return st;
+  if (n_rows < 1 || nh < 1 || nb < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_block_mass: n_rows=%d nh=%d nb=%d", n_rows, nh, nb);
+  if (recall && max_kv < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_block_mass: max_kv=%d", max_kv);
+  if (kv_shared != 0 && kv_shared != 1) return fail(HSA_ERR_BAD_ARG, "hsa_block_mass: kv_shared must be 0 or 1");
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(HSA_ERR_BAD_ARG, "hsa_block_mass: scale must be finite and positive");
+  if (!aligned16(qp) || !aligned16(kp)) return fail(HSA_ERR_BAD_ARG, "hsa_block_mass: tensors must be 16-byte aligned");
+  return launch_block_mass(qp, kp, blk_len, rows, n_rows, nh, nb, B, D, dtype, scale, kv_idx, kv_cnt, max_kv,
+                           kv_shared, mass, recall, static_cast<hipStream_t>(stream));
 }
 
 hsa_status_t hsa_unperm(const void *op, void *o, const int32_t *perm, int32_t N, int32_t n_pad,

@@ -57,9 +57,40 @@ __device__ __forceinline__ void hilbert_decode3(uint32_t h, int b, uint32_t &x0,
   x2 = a2;
 }
 
+// Cell (x0, x1) = (y, x) visited at curve index h on the 2^b square: the
+// same inverse transform in two dimensions.
+__device__ __forceinline__ void hilbert_decode2(uint32_t h, int b, uint32_t &x0, uint32_t &x1) {
+  uint32_t a0 = 0, a1 = 0;
+  for (int j = 0; j < b; ++j) {
+    a0 |= ((h >> (2 * j + 1)) & 1u) << j;
+    a1 |= ((h >> (2 * j)) & 1u) << j;
+  }
+  const uint32_t g = a1 >> 1;
+  a1 ^= a0;
+  a0 ^= g;
+  const uint32_t end = 2u << (b - 1);
+  for (uint32_t q = 2; q != end; q <<= 1) {
+    const uint32_t low = q - 1;
+    if (a1 & q) {
+      a0 ^= low;
+    } else {
+      const uint32_t sw = (a0 ^ a1) & low;
+      a0 ^= sw;
+      a1 ^= sw;
+    }
+    if (a0 & q) a0 ^= low;
+  }
+  x0 = a0;
+  x1 = a1;
+}
+
+// Curve index h -> token, if its cell lies in the grid. DIMS = 3: the
+// T x H x W grid in the 2^b cube; DIMS = 2: one H x W frame in the square.
+template <int DIMS>
 __device__ __forceinline__ bool in_grid(uint32_t h, int b, int T, int H, int W, int32_t &tok) {
-  uint32_t t, y, x;
-  hilbert_decode3(h, b, t, y, x);
+  uint32_t t = 0, y, x;
+  if constexpr (DIMS == 3) hilbert_decode3(h, b, t, y, x);
+  else hilbert_decode2(h, b, y, x);
   tok = static_cast<int32_t>((t * static_cast<uint32_t>(H) + y) * static_cast<uint32_t>(W) + x);
   return t < static_cast<uint32_t>(T) && y < static_cast<uint32_t>(H) &&
          x < static_cast<uint32_t>(W);
@@ -86,6 +117,7 @@ __device__ int block_exclusive_scan(int v, int &excl, int *sh /* kPlanThreads/64
   return total;
 }
 
+template <int DIMS>
 __global__ void __launch_bounds__(kPlanThreads)
 hilbert_count_kernel(int b, uint32_t cube, int T, int H, int W, int32_t *counts) {
   __shared__ int sh[kPlanThreads / 64 + 1];
@@ -94,13 +126,14 @@ hilbert_count_kernel(int b, uint32_t cube, int T, int H, int W, int32_t *counts)
   for (int j = 0; j < kPlanItems; ++j) {
     const uint32_t h = base + j;
     int32_t tok;
-    if (h < cube && in_grid(h, b, T, H, W, tok)) ++c;
+    if (h < cube && in_grid<DIMS>(h, b, T, H, W, tok)) ++c;
   }
   int excl;
   const int total = block_exclusive_scan(c, excl, sh);
   if (threadIdx.x == 0) counts[blockIdx.x] = total;
 }
 
+template <int DIMS>
 __global__ void __launch_bounds__(kPlanThreads)
 hilbert_write_kernel(int b, uint32_t cube, int T, int H, int W, const int32_t *counts,
                      int32_t *perm) {
@@ -120,7 +153,7 @@ hilbert_write_kernel(int b, uint32_t cube, int T, int H, int W, const int32_t *c
   for (int j = 0; j < kPlanItems; ++j) {
     const uint32_t h = base + j;
     int32_t tok;
-    if (h < cube && in_grid(h, b, T, H, W, tok)) ++c;
+    if (h < cube && in_grid<DIMS>(h, b, T, H, W, tok)) ++c;
   }
   int excl;
   block_exclusive_scan(c, excl, sh);
@@ -129,7 +162,7 @@ hilbert_write_kernel(int b, uint32_t cube, int T, int H, int W, const int32_t *c
   for (int j = 0; j < kPlanItems; ++j) {
     const uint32_t h = base + j;
     int32_t tok;
-    if (h < cube && in_grid(h, b, T, H, W, tok)) perm[k++] = tok;
+    if (h < cube && in_grid<DIMS>(h, b, T, H, W, tok)) perm[k++] = tok;
   }
 }
 
@@ -178,6 +211,10 @@ __global__ void plan_fill_kernel(int order, int T, int H, int W, int B, int n_pa
       perm[i] = (r < P) ? f * P + r : -1;
     } else if (order == HSA_ORDER_ROW) {
       perm[i] = (i < N) ? i : -1;
+    } else if (order == HSA_ORDER_HILBERT2D) {
+      // frame 0 was written in curve order; later frames repeat it
+      if (i >= N) perm[i] = -1;
+      else if (i >= P) perm[i] = (i / P) * P + perm[i % P];
     } else if (order == HSA_ORDER_TILE2D || order == HSA_ORDER_CUBE3D) {
       const Tiling g = tiling_of(order, T, H, W, B);
       const int k = i / B, r = i - k * B;
@@ -212,12 +249,12 @@ __global__ void plan_fill_kernel(int order, int T, int H, int W, int B, int n_pa
 
 namespace hsa_host {
 
-size_t plan_hilbert_groups(int T, int H, int W, int &bits, uint32_t &cube) {
-  const int m = max(T, max(H, W));
+size_t plan_hilbert_groups(int T, int H, int W, int &bits, uint32_t &cube, int dims) {
+  const int m = dims == 3 ? max(T, max(H, W)) : max(H, W);
   int b = 1;
   while ((1 << b) < m) ++b;
   bits = b;
-  cube = 1u << (3 * b);
+  cube = 1u << (dims * b);
   return (cube + hsa::kPlanCells - 1) / hsa::kPlanCells;
 }
 
@@ -226,12 +263,22 @@ hsa_status_t launch_plan(int T, int H, int W, int order, int B, int n_pad, int n
   if (order == HSA_ORDER_HILBERT3D) {
     int b;
     uint32_t cube;
-    const size_t groups = plan_hilbert_groups(T, H, W, b, cube);
+    const size_t groups = plan_hilbert_groups(T, H, W, b, cube, 3);
     int32_t *counts = static_cast<int32_t *>(ws);
-    hipLaunchKernelGGL(hsa::hilbert_count_kernel, dim3(groups), dim3(hsa::kPlanThreads), 0,
+    hipLaunchKernelGGL(hsa::hilbert_count_kernel<3>, dim3(groups), dim3(hsa::kPlanThreads), 0,
                        stream, b, cube, T, H, W, counts);
-    hipLaunchKernelGGL(hsa::hilbert_write_kernel, dim3(groups), dim3(hsa::kPlanThreads), 0,
+    hipLaunchKernelGGL(hsa::hilbert_write_kernel<3>, dim3(groups), dim3(hsa::kPlanThreads), 0,
                        stream, b, cube, T, H, W, counts, perm);
+  } else if (order == HSA_ORDER_HILBERT2D) {
+    // frame 0's cells in curve order; plan_fill_kernel repeats them per frame
+    int b;
+    uint32_t sq;
+    const size_t groups = plan_hilbert_groups(T, H, W, b, sq, 2);
+    int32_t *counts = static_cast<int32_t *>(ws);
+    hipLaunchKernelGGL(hsa::hilbert_count_kernel<2>, dim3(groups), dim3(hsa::kPlanThreads), 0,
+                       stream, b, sq, 1, H, W, counts);
+    hipLaunchKernelGGL(hsa::hilbert_write_kernel<2>, dim3(groups), dim3(hsa::kPlanThreads), 0,
+                       stream, b, sq, 1, H, W, counts, perm);
   }
   const int blocks = min((n_pad + 255) / 256, 4096);
   hipLaunchKernelGGL(hsa::plan_fill_kernel, dim3(blocks), dim3(256), 0, stream, order, T, H, W,

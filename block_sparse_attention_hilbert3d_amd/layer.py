@@ -105,6 +105,15 @@ class SparseAttentionLayer:
     def restore(self):
         return B_.hsa_unperm(self.op, self.perm, self.N, out=self.o)
 
+    def recall(self, rows):
+        """Attention recall of the current lists for sampled query slots
+        (rows int32 [heads, n] on the device): the share of each row's exact
+        attention mass that its query block's list keeps (hsa_block_mass)."""
+        qp, kp, _ = self.xp
+        _, rec = B_.hsa_block_mass(qp, kp, self.blk_len, rows, self.B, self.scale, self.kv_idx,
+                                   self.kv_cnt, want_mass=False)
+        return rec
+
     def step(self, q, k, v, step: int = 0, budget_ratio: float = 0.0, reuse_mask: bool = False):
         """One layer: returns the output [1, N, heads, D] (a buffer owned by the layer)."""
         self.reorder(q, k, v, pool=not reuse_mask)

@@ -66,7 +66,8 @@ typedef enum {
   HSA_ORDER_HILBERT3D = 1,
   HSA_ORDER_FRAME = 2,
   HSA_ORDER_TILE2D = 3, /* per-frame spatial tiles of 8 x (B/8) tokens */
-  HSA_ORDER_CUBE3D = 4  /* spatiotemporal cubes of (B/64) x 8 x 8 tokens */
+  HSA_ORDER_CUBE3D = 4, /* spatiotemporal cubes of (B/64) x 8 x 8 tokens */
+  HSA_ORDER_HILBERT2D = 5 /* frame-major, 2D Hilbert curve inside each frame */
 } hsa_order_t;
 typedef enum { HSA_AGG_MASS = 0, HSA_AGG_MAX = 1 } hsa_agg_t;
 typedef enum {
@@ -102,7 +103,7 @@ const char *hsa_last_error(void);
 
 /*
  * hsa_plan_size -- host-only: padded length and block count of a plan.
- * ROW / HILBERT3D: n_pad = ceil(N/B)*B. FRAME: n_pad = T*ceil(H*W/B)*B.
+ * ROW / HILBERT3D / HILBERT2D: n_pad = ceil(N/B)*B. FRAME: n_pad = T*ceil(H*W/B)*B.
  * TILE2D / CUBE3D with tiles tT x tH x tW: one block per tile,
  * nb = ceil(T/tT)*ceil(H/tH)*ceil(W/tW). Grid sides 1..1024, n_pad < 2^31.
  * TILE2D needs B a multiple of 8, CUBE3D a multiple of 64.
@@ -110,7 +111,7 @@ const char *hsa_last_error(void);
 hsa_status_t hsa_plan_size(int32_t T, int32_t H, int32_t W, int32_t order, int32_t B,
                            int32_t *n_pad, int32_t *nb);
 
-/* Workspace bytes hsa_plan needs (0 for every order but HILBERT3D). */
+/* Workspace bytes hsa_plan needs (0 for every order but HILBERT3D and HILBERT2D). */
 size_t hsa_plan_ws_size(int32_t T, int32_t H, int32_t W, int32_t order);
 
 /*
@@ -120,6 +121,9 @@ size_t hsa_plan_ws_size(int32_t T, int32_t H, int32_t W, int32_t order);
  * neighbourhoods. HILBERT3D walks the enclosing 2^b cube (b = ceil(log2 of
  * the longest side)) in curve order (Skilling's transpose construction, axes
  * (t, y, x), t most significant), keeps in-grid cells and pads the tail.
+ * HILBERT2D is frame-major with each frame's cells along the 2D curve of the
+ * enclosing square (b from max(H, W)), tail pads: the per-frame curve the
+ * global 3D curve is measured against.
  * ROW is row-major with tail pads; FRAME is frame-major with each frame's
  * tokens padded to whole blocks (LVSA section 2 attends frame by frame).
  * TILE2D and CUBE3D are the 2D and 3D block partitions that VMoBA (abstract:
@@ -274,6 +278,26 @@ hsa_status_t hsa_attn_order(const int32_t *kv_cnt, int32_t G, int32_t nb, int32_
 hsa_status_t hsa_unperm(const void *op, void *o, const int32_t *perm, int32_t N, int32_t n_pad,
                         int32_t nh, int32_t D, int64_t tok_stride, int32_t dtype,
                         hsa_stream_t stream);
+
+/*
+ * hsa_block_mass -- selection diagnostic (off the hot path): for sampled
+ *   query slots, the exact attention mass on every key block and the recall
+ *   of the selected lists. Block selection (DFSAttn, Methodology, designs 2-3;
+ *   VMoBA abstract; DynamicRad section 2) keeps the key blocks it estimates
+ *   to carry a query block's attention; this measures what they really carry.
+ * rows: int32 [nh][n_rows], slots of each head (values outside [0, nb*B) are
+ *   clamped; pad slots give a zero query, i.e. uniform attention).
+ * mass: optional float [nh][n_rows][nb]: the dense softmax of scale*q.k over
+ *   every real key, summed over the real keys of block J (rows sum to 1).
+ * recall: optional float [nh][n_rows]: the mass on the blocks listed for the
+ *   row's own query block (kv_idx/kv_cnt as hsa_attn, required with recall).
+ * At least one of mass and recall. Float arithmetic throughout.
+ */
+hsa_status_t hsa_block_mass(const void *qp, const void *kp, const int32_t *blk_len,
+                            const int32_t *rows, int32_t n_rows, int32_t nh, int32_t nb,
+                            int32_t B, int32_t D, int32_t dtype, float scale,
+                            const int32_t *kv_idx, const int32_t *kv_cnt, int32_t max_kv,
+                            int32_t kv_shared, float *mass, float *recall, hsa_stream_t stream);
 
 #ifdef __cplusplus
 }

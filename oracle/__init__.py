@@ -31,20 +31,20 @@ aggregation choice, the way threshold and global budget combine, the window
 tie order and the synthetic-field recipe are readings that only invariants
 pin, not values printed on the pages.
 """
-from .hilbert import hilbert_index, hilbert_order_bits
+from .hilbert import hilbert_index, hilbert_index_2d, hilbert_order_bits
 from .plan import plan, inverse_perm
 from .gather import gather, scatter
 from .score import pool, score_mass, score_max, score
 from .select import (select_topk, select_thresh_global, lvsa_frame_sets,
                      select_lvsa, thresh_fixed_point, budget_pairs, radial_width,
                      radial_window, select_radial, select_radial_dynamic)
-from .attn import attn_blocks, attn_dense
+from .attn import attn_blocks, attn_dense, block_mass, recall
 from .layer import run_layer
 
 __all__ = [
-    "hilbert_index", "hilbert_order_bits", "plan", "inverse_perm", "gather", "scatter",
+    "hilbert_index", "hilbert_index_2d", "hilbert_order_bits", "plan", "inverse_perm", "gather", "scatter",
     "pool", "score_mass", "score_max", "score", "select_topk", "select_thresh_global",
     "lvsa_frame_sets", "select_lvsa", "thresh_fixed_point", "budget_pairs",
     "radial_width", "radial_window", "select_radial", "select_radial_dynamic",
-    "attn_blocks", "attn_dense", "run_layer",
+    "attn_blocks", "attn_dense", "block_mass", "recall", "run_layer",
 ]

@@ -66,3 +66,40 @@ def attn_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float | None 
         e = np.exp(logits - m)
         out[0, :, h] = (e @ v[0, :, h]) / e.sum(axis=1, keepdims=True)
     return out
+
+
+def block_mass(qp: np.ndarray, kp: np.ndarray, perm: np.ndarray, B: int, rows: list,
+               scale: float | None = None) -> np.ndarray:
+    """Exact attention mass of query rows on key blocks (the quantity block
+    selection tries to keep: DFSAttn, Methodology, designs 2-3 estimate it from
+    pooled scores). For each head h and slot r = rows[h][i]: the dense softmax
+    over every real key, summed over the real keys of each block J.
+    Returns [heads, len(rows[h]), nb] float64."""
+    nh, n_pad, D = qp.shape
+    nb = n_pad // B
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    real = perm >= 0
+    keys = np.nonzero(real)[0]
+    out = np.zeros((nh, len(rows[0]), nb), dtype=np.float64)
+    for h in range(nh):
+        r = np.asarray(rows[h], dtype=np.int64)
+        logits = (qp[h, r] @ kp[h, keys].T) * scale
+        p = np.exp(logits - logits.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        np.add.at(out[h].T, keys // B, p.T)
+    return out
+
+
+def recall(mass: np.ndarray, rows: list, B: int, kv_idx: np.ndarray, kv_cnt: np.ndarray) -> np.ndarray:
+    """Attention recall of a selection: for each sampled row, the share of its
+    exact attention mass that falls on the key blocks listed for its query
+    block. [heads, rows]."""
+    nh = mass.shape[0]
+    out = np.zeros((nh, mass.shape[1]), dtype=np.float64)
+    for h in range(nh):
+        g = h if kv_idx.shape[0] > 1 else 0
+        for i, r in enumerate(np.asarray(rows[h], dtype=np.int64)):
+            I = r // B
+            out[h, i] = mass[h, i, kv_idx[g, I, :kv_cnt[g, I]]].sum()
+    return out

@@ -76,3 +76,38 @@ def hilbert_index(t, y, x, b: int) -> np.ndarray:
         for i in range(3):
             h = (h << 1) | ((X[i] >> level) & 1)
     return h
+
+
+def hilbert_index_2d(y, x, b: int) -> np.ndarray:
+    """Hilbert index of cells (y, x) on the (2**b)**2 square (vectorised), by
+    the same transpose construction in two dimensions: undo the excess work
+    level by level, Gray-encode, interleave the two words, y most significant."""
+    X = [np.array(y, dtype=np.int64, copy=True), np.array(x, dtype=np.int64, copy=True)]
+    if b < 1:
+        raise ValueError("b must be >= 1")
+    lim = 1 << b
+    for a in X:
+        if a.size and (a.min() < 0 or a.max() >= lim):
+            raise ValueError("coordinate outside the square")
+    top = 1 << (b - 1)
+    q = top
+    while q > 1:
+        low = q - 1
+        X[0] = np.where((X[0] & q) != 0, X[0] ^ low, X[0])
+        set_1 = (X[1] & q) != 0
+        swap = np.where(set_1, 0, (X[0] ^ X[1]) & low)
+        X[0] = X[0] ^ np.where(set_1, low, 0) ^ swap
+        X[1] = X[1] ^ swap
+        q >>= 1
+    X[1] = X[1] ^ X[0]
+    flip = np.zeros_like(X[0])
+    q = top
+    while q > 1:
+        flip = np.where((X[1] & q) != 0, flip ^ (q - 1), flip)
+        q >>= 1
+    X = [a ^ flip for a in X]
+    h = np.zeros_like(X[0])
+    for level in range(b - 1, -1, -1):
+        for i in range(2):
+            h = (h << 1) | ((X[i] >> level) & 1)
+    return h

@@ -14,6 +14,11 @@ Orders:
 * "frame": frame-major; each frame's H*W tokens in row-major order, padded up
   to whole tiles of B so no tile straddles two frames (LVSA, section 2: the
   attention unit is the frame).
+* "hilbert2d": frame-major; inside each frame the cells follow the 2D Hilbert
+  curve of the enclosing (2**b)**2 square (b from max(H, W)), out-of-grid
+  cells skipped; pads at the tail of the sequence. The per-frame curve the
+  3D curve is compared against (DFSAttn, Methodology, design 1, argues for a
+  global 3D curve).
 * "tile2d" / "cube3d": the 2D and 3D block partitions of VMoBA (abstract:
   layer-wise recurrent 1D-2D-3D partitions, "row" being the 1D one). The grid
   is cut into tiles of 1 x 8 x B/8 (2D) or B/64 x 8 x 8 (3D) cells, tiles at
@@ -26,7 +31,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .hilbert import hilbert_index, hilbert_order_bits
+from .hilbert import hilbert_index, hilbert_index_2d, hilbert_order_bits
 
 
 def _ceil_div(a: int, b: int) -> int:
@@ -53,6 +58,14 @@ def plan(T: int, H: int, W: int, order: str, B: int):
         n_pad = _ceil_div(N, B) * B
         perm = np.full(n_pad, -1, dtype=np.int64)
         perm[:N] = cells
+    elif order == "hilbert2d":
+        b = max(1, (max(H, W) - 1).bit_length())
+        y, x = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+        h2 = hilbert_index_2d(y.ravel(), x.ravel(), b)
+        frame_cells = np.argsort(h2, kind="stable")      # row-major cell ids in curve order
+        n_pad = _ceil_div(N, B) * B
+        perm = np.full(n_pad, -1, dtype=np.int64)
+        perm[:N] = (np.arange(T)[:, None] * (H * W) + frame_cells[None, :]).ravel()
     elif order == "frame":
         P = H * W
         tiles = _ceil_div(P, B)

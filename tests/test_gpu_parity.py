@@ -44,6 +44,8 @@ def _say(msg):
     ((3, 5, 7), "tile2d", 64), ((21, 30, 52), "tile2d", 128), ((2, 17, 40), "tile2d", 128),
     ((4, 16, 32), "tile2d", 128), ((3, 5, 7), "cube3d", 64), ((21, 30, 52), "cube3d", 128),
     ((5, 9, 17), "cube3d", 128), ((33, 45, 80), "cube3d", 128), ((1, 1, 1), "cube3d", 128),
+    ((3, 5, 7), "hilbert2d", 64), ((21, 30, 52), "hilbert2d", 128), ((33, 45, 80), "hilbert2d", 128),
+    ((2, 1, 1), "hilbert2d", 64), ((4, 600, 3), "hilbert2d", 128),
 ])
 def test_plan_bit_exact(hsa, shape, order, B):
     T, H, W = shape
@@ -317,6 +319,32 @@ def test_radial_dynamic_lists_bit_exact(hsa, T, P, delta):
     kv_idx, kv_cnt = hsa.hsa_select(torch.from_numpy(S).to(dev()), nh, nb, p, nb)
     ref = oracle.select_radial_dynamic(S, T, P, 0.1, delta, nb)
     assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), *ref)
+
+
+def test_block_mass_and_recall(hsa):
+    """The selection diagnostic: exact per-block attention mass of sampled rows
+    and the recall of the selected lists, against the oracle."""
+    w = wl.get(2)
+    _say("block mass / recall (workload 2)")
+    q, k, v, L, o = _layer(hsa, w, 0)
+    perm = L.perm.cpu().numpy().astype(np.int64)
+    real = np.nonzero(perm >= 0)[0]
+    rng = np.random.default_rng(12)
+    rows = np.stack([np.sort(rng.choice(real, 300, replace=False)) for _ in range(w.heads)]).astype(np.int32)
+    mass, rec = hsa.hsa_block_mass(*L.xp[:2], L.blk_len, torch.from_numpy(rows).to(dev()), w.B,
+                                   kv_idx=L.kv_idx, kv_cnt=L.kv_cnt)
+    torch.cuda.synchronize()
+    qp, kp = (oracle.gather(x.cpu(), perm) for x in (q, k))
+    ref = oracle.block_mass(qp, kp, perm, w.B, list(rows))
+    ref_rec = oracle.recall(ref, list(rows), w.B, L.kv_idx.cpu().numpy(), L.kv_cnt.cpu().numpy())
+    err = np.abs(mass.cpu().numpy() - ref).max()
+    rerr = np.abs(rec.cpu().numpy() - ref_rec).max()
+    _say(f"  mass err {err:.2e}, recall err {rerr:.2e}, mean recall {ref_rec.mean():.4f}")
+    # fp32 logits of D = 64 terms carry a relative error up to ~64 * 2^-24
+    # (4e-6); at logit magnitudes ~10 (log2 units) a block's weight moves by
+    # ~3e-5 relative, so masses (<= 1) and their sums agree to ~3e-5: 1e-4 bar
+    assert err <= 1e-4 and rerr <= 1e-4
+    assert torch.equal(rec, L.recall(torch.from_numpy(rows).to(dev())))
 
 
 def test_cached_mask_step(hsa):

@@ -110,3 +110,31 @@ def test_cached_mask_step_uses_step0_lists():
     op, _ = oracle.attn_blocks(qp, kp, vp, perm, w.B, r0["kv_idx"], r0["kv_cnt"])
     np.testing.assert_array_equal(r1["op"], op)
     assert r1["S"] is None
+
+
+def test_block_mass_pins():
+    """Exact per-block attention mass: every row sums to 1; averaged over the
+    rows of a query block it equals MASS scoring at sub-block size 1 (itself
+    pinned to brute-force softmax attention); full lists give recall 1 and a
+    list of one block gives that block's mass."""
+    rng = np.random.default_rng(11)
+    T, H, W, nh, D, B = 2, 4, 5, 2, 8, 8           # 40 tokens, ragged last block
+    perm, blk_len = oracle.plan(T, H, W, "row", B)
+    x = [rng.standard_normal((1, T * H * W, nh, D)) for _ in range(2)]
+    qp, kp = (oracle.gather(a, perm) for a in x)
+    nb = perm.size // B
+    real = np.nonzero(perm >= 0)[0]
+    rows = [real, real]
+    mass = oracle.block_mass(qp, kp, perm, B, rows)
+    np.testing.assert_allclose(mass.sum(axis=2), 1.0, atol=1e-12)
+    S1 = oracle.score_mass(qp, kp, perm, B, 1)
+    blocks = real // B
+    for h in range(nh):
+        for I in range(nb):
+            np.testing.assert_allclose(mass[h, blocks == I].mean(axis=0), S1[h, I], atol=1e-12)
+    full = np.tile(np.arange(nb, dtype=np.int32), (nh, nb, 1))
+    rec = oracle.recall(mass, rows, B, full, np.full((nh, nb), nb, dtype=np.int32))
+    np.testing.assert_allclose(rec, 1.0, atol=1e-12)
+    one = np.full((nh, nb, 1), 2, dtype=np.int32)
+    rec1 = oracle.recall(mass, rows, B, one, np.ones((nh, nb), dtype=np.int32))
+    np.testing.assert_allclose(rec1, mass[:, :, 2], atol=0)

@@ -259,3 +259,54 @@ def test_tiled_blocks_are_more_compact_than_raster():
 
     row = mean_box("row")
     assert mean_box("tile2d") * 2 < row and mean_box("cube3d") * 2 < row
+
+
+# ---------------------------------------------------------------- 2D Hilbert (per-frame) order
+
+def test_2d_order1_is_gray_code(golden_dir):
+    with open(os.path.join(golden_dir, "hilbert2d_order1.txt")) as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    for r in rows:
+        idx, y, x = int(r[0]), int(r[2]), int(r[3])
+        assert int(oracle.hilbert_index_2d(np.array([y]), np.array([x]), 1)[0]) == idx
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6])
+def test_2d_square_bijection_unit_steps_quadrants(b):
+    """A bijection onto [0, 4^b) with unit steps; every aligned run of 4^k
+    indices fills one aligned 2^k square; starts at (0, 0), ends at (2^b-1, 0)."""
+    S = 1 << b
+    y, x = np.meshgrid(np.arange(S), np.arange(S), indexing="ij")
+    h = oracle.hilbert_index_2d(y.ravel(), x.ravel(), b)
+    assert np.array_equal(np.sort(h), np.arange(S * S))
+    order = np.argsort(h)
+    yy, xx = y.ravel()[order], x.ravel()[order]
+    assert np.all(np.abs(np.diff(yy)) + np.abs(np.diff(xx)) == 1)
+    assert (yy[0], xx[0]) == (0, 0) and (yy[-1], xx[-1]) == (S - 1, 0)
+    for k in range(1, b):
+        run = 1 << (2 * k)
+        for s0 in range(0, S * S, run):
+            ys, xs = yy[s0:s0 + run], xx[s0:s0 + run]
+            assert ys.min() % (1 << k) == 0 and xs.min() % (1 << k) == 0
+            assert np.ptp(ys) == (1 << k) - 1 and np.ptp(xs) == (1 << k) - 1
+
+
+@pytest.mark.parametrize("shape,B", [((3, 5, 7), 64), ((21, 30, 52), 128), ((2, 16, 16), 64), ((1, 1, 1), 64)])
+def test_hilbert2d_plan(shape, B):
+    """Frame-major; each frame's in-grid cells in the order of the enclosing
+    square's curve (brute-force filter of the full square); tail pads."""
+    T, H, W = shape
+    N = T * H * W
+    perm, blk_len = oracle.plan(T, H, W, "hilbert2d", B)
+    assert perm.size == -(-N // B) * B and np.all(perm[N:] == -1) and blk_len.sum() == N
+    b = max(1, (max(H, W) - 1).bit_length())
+    S = 1 << b
+    yy, xx = np.meshgrid(np.arange(S), np.arange(S), indexing="ij")
+    cell_at = {int(h): (int(y), int(x)) for h, y, x in
+               zip(oracle.hilbert_index_2d(yy.ravel(), xx.ravel(), b), yy.ravel(), xx.ravel())}
+    frame = [cell_at[h][0] * W + cell_at[h][1] for h in range(S * S)
+             if cell_at[h][0] < H and cell_at[h][1] < W]         # walk the whole square, keep in-grid
+    for t in range(T):
+        assert np.array_equal(perm[t * H * W:(t + 1) * H * W], t * H * W + np.array(frame))
+    t, r = np.divmod(perm[:N], H * W)
+    assert np.array_equal(t, np.repeat(np.arange(T), H * W))
