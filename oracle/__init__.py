@@ -38,7 +38,7 @@ from .score import pool, score_mass, score_max, score
 from .select import (select_topk, select_thresh_global, lvsa_frame_sets,
                      select_lvsa, thresh_fixed_point, budget_pairs, radial_width,
                      radial_window, select_radial, select_radial_dynamic)
-from .attn import attn_blocks, attn_dense, block_mass, recall
+from .attn import attn_blocks, attn_blocks_bwd, attn_dense, block_mass, recall
 from .layer import run_layer
 
 __all__ = [
@@ -46,5 +46,5 @@ __all__ = [
     "pool", "score_mass", "score_max", "score", "select_topk", "select_thresh_global",
     "lvsa_frame_sets", "select_lvsa", "thresh_fixed_point", "budget_pairs",
     "radial_width", "radial_window", "select_radial", "select_radial_dynamic",
-    "attn_blocks", "attn_dense", "block_mass", "recall", "run_layer",
+    "attn_blocks", "attn_blocks_bwd", "attn_dense", "block_mass", "recall", "run_layer",
 ]

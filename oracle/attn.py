@@ -103,3 +103,41 @@ def recall(mass: np.ndarray, rows: list, B: int, kv_idx: np.ndarray, kv_cnt: np.
             I = r // B
             out[h, i] = mass[h, i, kv_idx[g, I, :kv_cnt[g, I]]].sum()
     return out
+
+
+def attn_blocks_bwd(qp: np.ndarray, kp: np.ndarray, vp: np.ndarray, dop: np.ndarray, perm: np.ndarray,
+                    B: int, kv_idx: np.ndarray, kv_cnt: np.ndarray, scale: float | None = None):
+    """Gradients of the block-sparse attention of attn_blocks (the same
+    attended key set per query block) with respect to Q, K and V, given the
+    output gradient dO. Plain softmax calculus per query row over its
+    attended keys, in float64:
+        P = softmax(scale * q K^T),  dV += P^T dO,  dP = dO V^T,
+        dS = P * (dP - rowsum(dP * P)),  dQ = scale * dS K,  dK += scale * dS^T Q.
+    Pad query rows and pad keys carry no gradient.
+    Returns (dq, dk, dv), each [heads, N_pad, D]."""
+    nh, n_pad, D = qp.shape
+    nb = n_pad // B
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    real = perm >= 0
+    dq, dk, dv = np.zeros_like(qp), np.zeros_like(kp), np.zeros_like(vp)
+    for h in range(nh):
+        g = h if kv_idx.shape[0] > 1 else 0
+        for I in range(nb):
+            qi = np.arange(I * B, (I + 1) * B)
+            qi = qi[real[qi]]
+            sel = kv_idx[g, I, :kv_cnt[g, I]].astype(np.int64)
+            if qi.size == 0 or sel.size == 0:
+                continue
+            keys = (sel[:, None] * B + np.arange(B)[None, :]).ravel()
+            keys = keys[real[keys]]
+            logits = (qp[h, qi] @ kp[h, keys].T) * scale
+            P = np.exp(logits - logits.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            dO = dop[h, qi]
+            dv[h, keys] += P.T @ dO
+            dP = dO @ vp[h, keys].T
+            dS = P * (dP - (dP * P).sum(axis=1, keepdims=True))
+            dq[h, qi] += scale * (dS @ kp[h, keys])
+            dk[h, keys] += scale * (dS.T @ qp[h, qi])
+    return dq, dk, dv

@@ -138,3 +138,49 @@ def test_block_mass_pins():
     one = np.full((nh, nb, 1), 2, dtype=np.int32)
     rec1 = oracle.recall(mass, rows, B, one, np.ones((nh, nb), dtype=np.int32))
     np.testing.assert_allclose(rec1, mass[:, :, 2], atol=0)
+
+
+def test_backward_full_keep_matches_autograd():
+    """Keeping every block, the gradients equal torch autograd of dense fp64
+    scaled-dot-product attention (an independent implementation)."""
+    import torch
+    rng = np.random.default_rng(21)
+    T, H, W, nh, D, B = 2, 4, 5, 2, 8, 16           # 40 tokens, ragged last block
+    perm, blk_len = oracle.plan(T, H, W, "hilbert", B)
+    q, k, v, do = (rng.standard_normal((1, T * H * W, nh, D)) for _ in range(4))
+    qp, kp, vp, dop = (oracle.gather(a, perm) for a in (q, k, v, do))
+    nb = perm.size // B
+    full = np.tile(np.arange(nb, dtype=np.int32), (nh, nb, 1))
+    dq, dk, dv = oracle.attn_blocks_bwd(qp, kp, vp, dop, perm, B, full, np.full((nh, nb), nb, np.int32))
+    tq, tk, tv = (torch.tensor(a[0].transpose(1, 0, 2), dtype=torch.float64, requires_grad=True)
+                  for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None])[0]
+    out.backward(torch.tensor(do[0].transpose(1, 0, 2)))
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        back = oracle.scatter(mine, perm, T * H * W)[0].transpose(1, 0, 2)
+        np.testing.assert_allclose(back, ref.numpy(), atol=1e-12)
+
+
+def test_backward_finite_differences_sparse_lists():
+    """With uneven sparse lists, the gradients match central finite
+    differences of the oracle's own forward loss <dO, O>."""
+    rng = np.random.default_rng(22)
+    T, H, W, nh, D, B = 1, 4, 6, 1, 4, 8             # 24 tokens, 3 blocks
+    perm, _ = oracle.plan(T, H, W, "row", B)
+    qp, kp, vp, dop = (rng.standard_normal((nh, perm.size, D)) for _ in range(4))
+    kv_idx = np.array([[[0, 2], [1, -1], [0, 1]]], dtype=np.int32)
+    kv_cnt = np.array([[2, 1, 2]], dtype=np.int32)
+    grads = oracle.attn_blocks_bwd(qp, kp, vp, dop, perm, B, kv_idx, kv_cnt)
+
+    def loss(q, k, v):
+        o, _ = oracle.attn_blocks(q, k, v, perm, B, kv_idx, kv_cnt)
+        return float((o * dop).sum())
+    eps = 1e-6
+    for which, g in enumerate(grads):
+        for (i, d) in [(0, 0), (5, 3), (9, 1), (17, 2), (23, 0)]:
+            args = [qp.copy(), kp.copy(), vp.copy()]
+            args[which][0, i, d] += eps
+            up = loss(*args)
+            args[which][0, i, d] -= 2 * eps
+            down = loss(*args)
+            assert abs((up - down) / (2 * eps) - g[0, i, d]) < 1e-7, (which, i, d)
