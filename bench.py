@@ -91,6 +91,37 @@ def _cpu_baseline(w, q, k, v, blocks_per_head=32):
                 nb=nb)
 
 
+def _time_backward(hsa, L, qkv, K, stream, flop_fwd):
+    """Attention backward on the layer's current lists: dQ, dK, dV for a seeded
+    output gradient. FLOP: the algorithmic 2.5x the forward (five products per
+    tile pair); the kernels compute seven (S and dP in both passes)."""
+    import torch
+    L.want_lse = True
+    if L.lse is None:
+        L.lse = torch.empty((L.heads, L.n_pad), dtype=torch.float32, device=L.op.device)
+    L.reorder(*qkv, pool=False)
+    L.attend()
+    g = torch.Generator(device=L.op.device).manual_seed(7)
+    dop = torch.randn(L.op.shape, generator=g, device=L.op.device).to(L.op.dtype)
+    outs = tuple(torch.empty_like(L.op) for _ in range(3))
+    ws = torch.empty(max(hsa.lib().hsa_attn_bwd_ws_size(L.heads, L.nb, L.B, int(L.kv_idx.shape[0] == 1)), 16),
+                     dtype=torch.uint8, device=L.op.device)
+    args = (*L.xp, L.op, dop, L.lse, L.blk_len, L.kv_idx, L.kv_cnt, L.B)
+    for _ in range(2):
+        hsa.hsa_attn_bwd(*args, outs=outs, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        hsa.hsa_attn_bwd(*args, outs=outs, ws=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    return {"ms": ms, "tflops_algorithmic": 2.5 * flop_fwd / (ms * 1e-3) / 1e12,
+            "tflops_computed": 3.5 * flop_fwd / (ms * 1e-3) / 1e12,
+            "frac_mfma_peak_algorithmic": 2.5 * flop_fwd / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+
+
 def _keep_text(w, L, nb, tiles_steps, nh):
     mean_per_row = float(sum(tiles_steps)) / len(tiles_steps) / (nh * nb)
     if w.select == "topk":
@@ -115,6 +146,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--order", choices=["row", "hilbert", "frame", "tile2d", "cube3d"], default=None,
                     help="token order instead of the workload's own (e.g. the VMoBA 2D/3D partitions)")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the attention backward (hsa_attn_bwd) on the layer's lists")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one device-to-device copy of this many MiB (a kernel of known "
@@ -313,6 +346,8 @@ def main():
                      "frac": achieved / peak, "traffic": _traffic(w.idx),
                      "kernel": "attn_bf16_pipe_kernel" if w.dtype == "bf16" else "attn_f32_kernel"},
     }
+    if args.backward:
+        out["backward"] = _time_backward(hsa, L, sets[0], K, stream, flop_tiles)
     if not args.no_cpu and w.select == "topk":
         cb = _cpu_baseline(w, *sets_cpu[0])
         out["cpu_baseline"] = {

@@ -50,6 +50,8 @@ _SIGS = {
     "hsa_attn": (ctypes.c_int, [_p] * 9 + [_c_i32] * 7 + [_c_f32, _p]),
     "hsa_attn_order": (ctypes.c_int, [_p, _c_i32, _c_i32, _c_i32, _p, _p]),
     "hsa_unperm": (ctypes.c_int, [_p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _p]),
+    "hsa_attn_bwd_ws_size": (_c_sz, [_c_i32] * 4),
+    "hsa_attn_bwd": (ctypes.c_int, [_p] * 9 + [_c_i32] * 7 + [_c_f32, _p, _p, _p, _p, _c_sz, _p]),
     "hsa_block_mass": (ctypes.c_int, [_p, _p, _p, _p] + [_c_i32] * 6 + [_c_f32, _p, _p, _c_i32, _c_i32,
                                                                      _p, _p, _p]),
 }
@@ -271,3 +273,25 @@ def hsa_block_mass(qp, kp, blk_len, rows, B: int, scale: float | None = None, kv
                                 _dtype_code(qp), scale, _ptr(kv_idx), _ptr(kv_cnt), max_kv, shared,
                                 _ptr(mass), _ptr(rec), _stream()), "hsa_block_mass")
     return mass, rec
+
+
+def hsa_attn_bwd(qp, kp, vp, op, dop, lse, blk_len, kv_idx, kv_cnt, B: int, scale: float | None = None,
+                 outs=None, ws=None):
+    """Gradients of hsa_attn -> (dqp, dkp, dvp), each [nh, n_pad, D] in the input dtype.
+    lse is the forward's log-sum-exp [nh, n_pad]."""
+    _need_device(qp, kp, vp, op, dop, lse, blk_len, kv_idx, kv_cnt)
+    nh, n_pad, D = qp.shape
+    nb = n_pad // B
+    shared = 1 if kv_idx.shape[0] == 1 and nh > 1 else 0
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if outs is None:
+        outs = tuple(torch.empty_like(qp) for _ in range(3))
+    dq, dk, dv = outs
+    n = lib().hsa_attn_bwd_ws_size(nh, nb, B, shared)
+    if ws is None:
+        ws = torch.empty(max(n, 16), dtype=torch.uint8, device=qp.device)
+    _check(lib().hsa_attn_bwd(_ptr(qp), _ptr(kp), _ptr(vp), _ptr(op), _ptr(dop), _ptr(lse), _ptr(blk_len),
+                              _ptr(kv_idx), _ptr(kv_cnt), kv_idx.shape[-1], shared, nh, nb, B, D,
+                              _dtype_code(qp), scale, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                              _stream()), "hsa_attn_bwd")
+    return dq, dk, dv

@@ -48,6 +48,12 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                          const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
                          const int32_t *order, int max_kv, int kv_shared, int nh, int nb, int B,
                          int D, int dtype, float scale, hipStream_t stream);
+size_t attn_bwd_ws_bytes(int nh, int nb, int B, int G);
+hsa_status_t launch_attn_bwd(const void *qp, const void *kp, const void *vp, const void *op, const void *dop,
+                             const float *lse, const int32_t *blk_len, const int32_t *kv_idx,
+                             const int32_t *kv_cnt, int max_kv, int kv_shared, int nh, int nb, int B, int D,
+                             int dtype, float scale, void *dqp, void *dkp, void *dvp, void *ws,
+                             hipStream_t stream);
 hsa_status_t launch_block_mass(const void *qp, const void *kp, const int32_t *blk_len, const int32_t *rows,
                                int n_rows, int nh, int nb, int B, int D, int dtype, float scale,
                                const int32_t *kv_idx, const int32_t *kv_cnt, int max_kv, int kv_shared,
@@ -351,6 +357,37 @@ hsa_status_t hsa_attn_order(const int32_t *kv_cnt, int32_t G, int32_t nb, int32_
   if (max_kv > 4095) return fail(HSA_ERR_UNSUPPORTED, "hsa_attn_order: max_kv > 4095");
   if (!aligned4(kv_cnt) || !aligned4(order)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_order: arrays must be 4-byte aligned");
   return launch_attn_order(kv_cnt, G, nb, max_kv, order, static_cast<hipStream_t>(stream));
+}
+
+size_t hsa_attn_bwd_ws_size(int32_t nh, int32_t nb, int32_t B, int32_t kv_shared) {
+  if (nh < 1 || nb < 1 || B < 1 || (kv_shared != 0 && kv_shared != 1)) return 0;
+  return attn_bwd_ws_bytes(nh, nb, B, kv_shared ? 1 : nh);
+}
+
+hsa_status_t hsa_attn_bwd(const void *qp, const void *kp, const void *vp, const void *op,
+                          const void *dop, const float *lse, const int32_t *blk_len,
+                          const int32_t *kv_idx, const int32_t *kv_cnt, int32_t max_kv,
+                          int32_t kv_shared, int32_t nh, int32_t nb, int32_t B, int32_t D,
+                          int32_t dtype, float scale, void *dqp, void *dkp, void *dvp, void *ws,
+                          size_t ws_bytes, hsa_stream_t stream) {
+  g_last_error.clear();
+  if (!qp || !kp || !vp || !op || !dop || !lse || !blk_len || !kv_idx || !kv_cnt)
+    return fail(HSA_ERR_NULL_PTR, "hsa_attn_bwd: null input (the forward's lse is required)");
+  if (!dqp || !dkp || !dvp) return fail(HSA_ERR_NULL_PTR, "hsa_attn_bwd: null output");
+  hsa_status_t st;
+  if ((st = check_dtype(dtype)) != HSA_OK || (st = check_D(D)) != HSA_OK || (st = check_B(B)) != HSA_OK) return st;
+  if (nh < 1 || nb < 1 || max_kv < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn_bwd: nh=%d nb=%d max_kv=%d", nh, nb, max_kv);
+  if (static_cast<int64_t>(nh) * nb * B >= (1ll << 31)) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn_bwd: too many slots");
+  if (kv_shared != 0 && kv_shared != 1) return fail(HSA_ERR_BAD_ARG, "hsa_attn_bwd: kv_shared must be 0 or 1");
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_bwd: scale must be finite and positive");
+  const void *ten[8] = {qp, kp, vp, op, dop, dqp, dkp, dvp};
+  for (const void *t : ten)
+    if (!aligned16(t)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_bwd: tensors must be 16-byte aligned");
+  const size_t need = attn_bwd_ws_bytes(nh, nb, B, kv_shared ? 1 : nh);
+  if (!ws || ws_bytes < need) return fail(HSA_ERR_WORKSPACE, "hsa_attn_bwd: workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (!aligned16(ws)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_bwd: workspace must be 16-byte aligned");
+  return launch_attn_bwd(qp, kp, vp, op, dop, lse, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, B, D,
+                         dtype, scale, dqp, dkp, dvp, ws, static_cast<hipStream_t>(stream));
 }
 
 hsa_status_t hsa_block_mass(const void *qp, const void *kp, const int32_t *blk_len,

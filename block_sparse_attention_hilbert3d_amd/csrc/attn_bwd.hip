@@ -1,0 +1,563 @@
+// Block-sparse attention backward: dQ, dK, dV over the forward's lists.
+//
+// VMoBA (abstract) trains video diffusion models natively with block-sparse
+// attention; this is the gradient of hsa_attn for the same attended key set
+// per query block (DFSAttn, Significance; DynamicRad, section 2 item 2: the
+// shared candidate set consumed block-wise). With P = softmax(scale q K^T)
+// over the real keys of the listed blocks and D_i = dO_i . O_i:
+//   dV_j = sum_i P_ij dO_i,   dS_ij = P_ij (dO_i . V_j - D_i),
+//   dQ_i = scale sum_j dS_ij K_j,   dK_j = scale sum_i dS_ij Q_i.
+// P is rebuilt from the forward's log-sum-exp, so nothing quadratic is
+// stored. Two kernels keep every sum in a fixed order (bit-reproducible):
+//  - dQ: one workgroup per (head, query block), over its list (as the
+//    forward), S^T = K Q^T and dP^T = V dO^T with one query per lane
+//    column, dQ^T += K^T dS^T with K^T read by ds_read_b64_tr_b16;
+//  - dK/dV: one workgroup per (head, key block), over the query blocks whose
+//    list holds it (a transposed list built first), S = Q K^T and
+//    dP = dO V^T with one key per lane column so P and dS feed
+//    dV^T += dO^T P and dK^T += Q^T dS straight from the accumulators.
+// bf16 runs on 32x32x16 matrix cores with float accumulation; P and dS are
+// rounded to bf16 for the products, as the forward rounds P. Float inputs use
+// plain one-thread-per-row loops. Pad query rows and pad keys get zero
+// gradient.
+#include "common.h"
+
+namespace hsa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// D_i = dO_i . O_i in float; zero for pad slots.
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+bwd_delta_kernel(const T *__restrict__ op, const T *__restrict__ dop, const int32_t *__restrict__ blk_len,
+                 int n_pad, int B, int64_t total, float *__restrict__ delta) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int slot = static_cast<int>(idx % n_pad);
+  const bool real = (slot % B) < blk_len[slot / B];
+  float s = 0.f;
+  if (real) {
+    const T *o = op + idx * D;
+    const T *d = dop + idx * D;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int c = 0; c < D; c += 8) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(o + c);
+        const uint4 b = *reinterpret_cast<const uint4 *>(d + c);
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s = fmaf(__uint_as_float(aw[j] << 16), __uint_as_float(bw[j] << 16), s);
+          s = fmaf(__uint_as_float(aw[j] & 0xFFFF0000u), __uint_as_float(bw[j] & 0xFFFF0000u), s);
+        }
+      }
+    } else {
+#pragma unroll 8
+      for (int c = 0; c < D; ++c) s = fmaf(o[c], d[c], s);
+    }
+  }
+  delta[idx] = s;
+}
+
+// Transposed lists: for list set g and key block J, the query blocks I whose
+// (ascending) list holds J, ascending. One wave per (g, J).
+__global__ void __launch_bounds__(64)
+bwd_transpose_kernel(const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt, int nb,
+                     int max_kv, int32_t *__restrict__ t_idx, int32_t *__restrict__ t_cnt) {
+  const int gJ = blockIdx.x;
+  const int g = gJ / nb, J = gJ - g * nb;
+  const int lane = lane_id();
+  int32_t *out = t_idx + static_cast<int64_t>(gJ) * nb;
+  int before = 0;
+  for (int I0 = 0; I0 < nb; I0 += 64) {
+    const int I = I0 + lane;
+    bool found = false;
+    if (I < nb) {
+      const int32_t *list = kv_idx + (static_cast<int64_t>(g) * nb + I) * max_kv;
+      int lo = 0, hi = kv_cnt[static_cast<int64_t>(g) * nb + I];
+      const int cnt = hi;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (list[mid] < J) lo = mid + 1;
+        else hi = mid;
+      }
+      found = lo < cnt && list[lo] == J;
+    }
+    const uint64_t b = __ballot(found);
+    if (found) out[before + popc64(b & lanemask_lt())] = I;
+    before += popc64(b);
+  }
+  if (lane == 0) t_cnt[gJ] = before;
+}
+
+// Per-lane fragment offsets, as in the forward kernel: b128 reads of a
+// K-swizzled tile (row ln of a 32-row slice, 8-element chunk 2*ks + g) and
+// ds_read_b64_tr_b16 reads of a V-swizzled tile.
+template <int D>
+struct FragOffsets {
+  static constexpr int CPR = D / 8, DK = D / 16, DM = D / 32;
+  int row[DK];  // element offset / 8 inside a 32-row slice
+  int tr[DM];   // byte offset of the first transposed read
+  __device__ __forceinline__ FragOffsets(int lane) {
+    const int g = lane >> 5, ln = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) row[ks] = ln * CPR + ((2 * ks + g) ^ (ln & (CPR - 1)));
+    const int q16 = lane >> 4, jj = lane & 15;
+#pragma unroll
+    for (int md = 0; md < DM; ++md) {
+      const int col = md * 32 + (q16 & 1) * 16 + 4 * (jj & 3);
+      const int chunk = (col >> 3) ^ ((jj & 12) & (CPR - 1));
+      tr[md] = ((g * 4 + (jj >> 2)) * CPR + chunk) * 16 + ((col >> 2) & 1) * 8;
+    }
+  }
+};
+
+// 8 bf16 of the transposed tile for k-step kk (16 rows) and d-slice md.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(lds_char_t *tile, int tr_ofs, int kk) {
+  constexpr int CPR = D / 8;
+  lds_i16x4_t *a0 = (lds_i16x4_t *)(tile + tr_ofs + kk * 16 * CPR * 16);
+  lds_i16x4_t *a1 = (lds_i16x4_t *)(tile + tr_ofs + (kk * 16 + 8) * CPR * 16);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1);
+  const i16x8_t both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+template <int D>
+__device__ __forceinline__ void load_row_frags(const uint16_t *row, int g, bf16x8 (&f)[D / 16]) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) f[ks] = *reinterpret_cast<const bf16x8 *>(row + g * 8 + ks * 16);
+}
+
+// Write a d x 32 accumulator (one column per lane) as rows of the output.
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t *row, const f32x16 (&acc)[D / 32], float mul, int g) {
+#pragma unroll
+  for (int md = 0; md < D / 32; ++md)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = md * 32 + i4 * 8 + g * 4;
+      const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(acc[md][i4 * 4 + 0] * mul)) |
+                          (static_cast<uint32_t>(f32_to_bf16(acc[md][i4 * 4 + 1] * mul)) << 16);
+      const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(acc[md][i4 * 4 + 2] * mul)) |
+                          (static_cast<uint32_t>(f32_to_bf16(acc[md][i4 * 4 + 3] * mul)) << 16);
+      *reinterpret_cast<uint2 *>(row + d0) = make_uint2(w0, w1);
+    }
+}
+
+template <int D, int BK>
+__global__ void __launch_bounds__(BK * 2, 1)
+attn_bwd_dq_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
+                   const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
+                   const float *__restrict__ lse, const float *__restrict__ delta,
+                   const int32_t *__restrict__ blk_len, const int32_t *__restrict__ kv_idx,
+                   const int32_t *__restrict__ kv_cnt, int max_kv, int kv_shared, int nh, int nb,
+                   float scale_log2, float scale, uint16_t *__restrict__ dqp) {
+  constexpr int NW = BK / 32, CPR = D / 8, DK = D / 16, DM = D / 32, MT = BK / 32, TILE = BK * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[TILE];   // b128 rows (K swizzle)
+  __shared__ __attribute__((aligned(1024))) uint16_t sKt[TILE];  // transposed reads (V swizzle)
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[TILE];   // b128 rows (K swizzle)
+  const int total = nh * nb;
+  const int bid = xcd_remap(blockIdx.x, total);
+  const int h = bid / nb, I = bid - h * nb;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, ln = lane & 31;
+  const int64_t n_pad = static_cast<int64_t>(nb) * BK;
+  const int64_t head_off = static_cast<int64_t>(h) * n_pad * D;
+  const int qslot = I * BK + w * 32 + ln;
+  const FragOffsets<D> fo(lane);
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    koff[i] = tile_lane_offset<D, false>(i, lane);
+    voff[i] = tile_lane_offset<D, true>(i, lane);
+  }
+  const uint32_t ldsK = lds_addr(sK), ldsKt = lds_addr(sKt), ldsV = lds_addr(sV);
+  lds_char_t *const ktl = to_lds(sKt);
+
+  bf16x8 qf[DK], dof[DK];
+  load_row_frags<D>(qp + head_off + static_cast<int64_t>(qslot) * D, g, qf);
+  load_row_frags<D>(dop + head_off + static_cast<int64_t>(qslot) * D, g, dof);
+  const float lq2 = lse[static_cast<int64_t>(h) * n_pad + qslot] * kLog2e;
+  const float dq_i = delta[static_cast<int64_t>(h) * n_pad + qslot];
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(dof[ks]));
+
+  f32x16 acc[DM];
+#pragma unroll
+  for (int md = 0; md < DM; ++md)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[md][i] = 0.f;
+
+  const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
+  const int cnt = kv_cnt[lrow];
+  const int32_t *list = kv_idx + lrow * max_kv;
+  for (int c = 0; c < cnt; ++c) {
+    const int J = list[c];
+    const int kvalid = blk_len[J];
+    const int64_t tile_off = head_off + static_cast<int64_t>(J) * BK * D;
+    __syncthreads();  // the previous block's tiles are no longer read
+    issue_tile<D, BK, NW>(kp + tile_off, ldsK, w, koff);
+    issue_tile<D, BK, NW>(kp + tile_off, ldsKt, w, voff);
+    issue_tile<D, BK, NW>(vp + tile_off, ldsV, w, koff);
+    wait_vmcnt<0>();
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = 0.f;
+        dp[i] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&sK[(mt * 32 * CPR + fo.row[ks]) * 8]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&sV[(mt * 32 * CPR + fo.row[ks]) * 8]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[ks], dp, 0, 0, 0);
+      }
+      // element i is key mt*32 + 8(i/4) + 4g + i%4 of block J, query = lane column
+      const int lim = kvalid - mt * 32 - g * 4;
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool real_key = (i >> 2) * 8 + (i & 3) < lim;
+        const float p = real_key ? __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -lq2)) : 0.f;
+        ds[i] = p * (dp[i] - dq_i);
+      }
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        bf16x8 dsf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dsf[j] = static_cast<__bf16>(ds[ks2 * 8 + j]);
+#pragma unroll
+        for (int md = 0; md < DM; ++md)
+          acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ktl, fo.tr[md], mt * 2 + ks2), dsf,
+                                                           acc[md], 0, 0, 0);
+      }
+    }
+  }
+  const bool real = (w * 32 + ln) < blk_len[I];
+  store_rows<D>(dqp + head_off + static_cast<int64_t>(qslot) * D, acc, real ? scale : 0.f, g);
+}
+
+template <int D, int BK>
+__global__ void __launch_bounds__(BK * 2, 1)
+attn_bwd_dkdv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
+                     const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
+                     const float *__restrict__ lse, const float *__restrict__ delta,
+                     const int32_t *__restrict__ blk_len, const int32_t *__restrict__ t_idx,
+                     const int32_t *__restrict__ t_cnt, int kv_shared, int nh, int nb, float scale_log2,
+                     float scale, uint16_t *__restrict__ dkp, uint16_t *__restrict__ dvp) {
+  constexpr int NW = BK / 32, CPR = D / 8, DK = D / 16, DM = D / 32, QT = BK / 32, TILE = BK * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ[TILE];    // b128 rows
+  __shared__ __attribute__((aligned(1024))) uint16_t sQt[TILE];   // transposed reads
+  __shared__ __attribute__((aligned(1024))) uint16_t sdO[TILE];   // b128 rows
+  __shared__ __attribute__((aligned(1024))) uint16_t sdOt[TILE];  // transposed reads
+  __shared__ __attribute__((aligned(16))) float sL[BK];           // lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[BK];           // D_i
+  const int total = nh * nb;
+  const int bid = xcd_remap(blockIdx.x, total);
+  const int h = bid / nb, J = bid - h * nb;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, ln = lane & 31;
+  const int64_t n_pad = static_cast<int64_t>(nb) * BK;
+  const int64_t head_off = static_cast<int64_t>(h) * n_pad * D;
+  const int kslot = J * BK + w * 32 + ln;
+  const FragOffsets<D> fo(lane);
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    koff[i] = tile_lane_offset<D, false>(i, lane);
+    voff[i] = tile_lane_offset<D, true>(i, lane);
+  }
+  const uint32_t ldsQ = lds_addr(sQ), ldsQt = lds_addr(sQt), ldsO = lds_addr(sdO), ldsOt = lds_addr(sdOt);
+  lds_char_t *const qtl = to_lds(sQt);
+  lds_char_t *const otl = to_lds(sdOt);
+
+  bf16x8 kf[DK], vf[DK];
+  load_row_frags<D>(kp + head_off + static_cast<int64_t>(kslot) * D, g, kf);
+  load_row_frags<D>(vp + head_off + static_cast<int64_t>(kslot) * D, g, vf);
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) asm volatile("" ::"v"(kf[ks]), "v"(vf[ks]));
+
+  f32x16 dk[DM], dv[DM];
+#pragma unroll
+  for (int md = 0; md < DM; ++md)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dk[md][i] = 0.f;
+      dv[md][i] = 0.f;
+    }
+
+  const int64_t lrow = kv_shared ? static_cast<int64_t>(J) : static_cast<int64_t>(h) * nb + J;
+  const int cnt = t_cnt[lrow];
+  const int32_t *tl = t_idx + lrow * nb;
+  for (int c = 0; c < cnt; ++c) {
+    const int I = tl[c];
+    const int qvalid = blk_len[I];
+    const int64_t tile_off = head_off + static_cast<int64_t>(I) * BK * D;
+    __syncthreads();
+    issue_tile<D, BK, NW>(qp + tile_off, ldsQ, w, koff);
+    issue_tile<D, BK, NW>(qp + tile_off, ldsQt, w, voff);
+    issue_tile<D, BK, NW>(dop + tile_off, ldsO, w, koff);
+    issue_tile<D, BK, NW>(dop + tile_off, ldsOt, w, voff);
+    if (tid < BK) {
+      const int64_t r = static_cast<int64_t>(h) * n_pad + static_cast<int64_t>(I) * BK + tid;
+      sL[tid] = lse[r] * kLog2e;
+      sD[tid] = delta[r];
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = 0.f;
+        dp[i] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(&sQ[(qt * 32 * CPR + fo.row[ks]) * 8]);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8 *>(&sdO[(qt * 32 * CPR + fo.row[ks]) * 8]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp, 0, 0, 0);
+      }
+      // element i is query qt*32 + 8(i/4) + 4g + i%4 of block I, key = lane column
+      float p[16], ds[16];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int q0 = qt * 32 + i4 * 8 + g * 4;
+        const float4 l4 = *reinterpret_cast<const float4 *>(&sL[q0]);
+        const float4 d4 = *reinterpret_cast<const float4 *>(&sD[q0]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = i4 * 4 + r;
+          const float pv = (q0 + r < qvalid) ? __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -lv[r])) : 0.f;
+          p[i] = pv;
+          ds[i] = pv * (dp[i] - dv4[r]);
+        }
+      }
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        bf16x8 pf, dsf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pf[j] = static_cast<__bf16>(p[ks2 * 8 + j]);
+          dsf[j] = static_cast<__bf16>(ds[ks2 * 8 + j]);
+        }
+#pragma unroll
+        for (int md = 0; md < DM; ++md) {
+          dv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(otl, fo.tr[md], qt * 2 + ks2), pf,
+                                                          dv[md], 0, 0, 0);
+          dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qtl, fo.tr[md], qt * 2 + ks2), dsf,
+                                                          dk[md], 0, 0, 0);
+        }
+      }
+    }
+  }
+  const bool real = (w * 32 + ln) < blk_len[J];
+  store_rows<D>(dkp + head_off + static_cast<int64_t>(kslot) * D, dk, real ? scale : 0.f, g);
+  store_rows<D>(dvp + head_off + static_cast<int64_t>(kslot) * D, dv, real ? 1.f : 0.f, g);
+}
+
+// Float inputs: one thread per query row (dQ) / per key row (dK, dV), tiles
+// of the other side in LDS.
+template <int D, int BK>
+__global__ void __launch_bounds__(BK)
+attn_bwd_dq_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp, const float *__restrict__ vp,
+                       const float *__restrict__ dop, const float *__restrict__ lse,
+                       const float *__restrict__ delta, const int32_t *__restrict__ blk_len,
+                       const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt, int max_kv,
+                       int kv_shared, int nh, int nb, float scale, float *__restrict__ dqp) {
+  __shared__ __attribute__((aligned(16))) float sK[BK * D];
+  __shared__ __attribute__((aligned(16))) float sV[BK * D];
+  const int h = blockIdx.x / nb, I = blockIdx.x % nb;
+  const int tid = threadIdx.x;
+  const int64_t n_pad = static_cast<int64_t>(nb) * BK;
+  const int64_t head_off = static_cast<int64_t>(h) * n_pad * D;
+  const int qslot = I * BK + tid;
+  float q[D], dq[D], dO[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    q[d] = qp[head_off + static_cast<int64_t>(qslot) * D + d];
+    dO[d] = dop[head_off + static_cast<int64_t>(qslot) * D + d];
+    dq[d] = 0.f;
+  }
+  const float L = lse[static_cast<int64_t>(h) * n_pad + qslot];
+  const float Di = delta[static_cast<int64_t>(h) * n_pad + qslot];
+  const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
+  const int cnt = kv_cnt[lrow];
+  const int32_t *list = kv_idx + lrow * max_kv;
+  for (int c = 0; c < cnt; ++c) {
+    const int J = list[c];
+    const int kvalid = blk_len[J];
+    const float4 *ks = reinterpret_cast<const float4 *>(kp + head_off + static_cast<int64_t>(J) * BK * D);
+    const float4 *vs = reinterpret_cast<const float4 *>(vp + head_off + static_cast<int64_t>(J) * BK * D);
+    __syncthreads();
+    for (int e = tid; e < BK * D / 4; e += BK) {
+      reinterpret_cast<float4 *>(sK)[e] = ks[e];
+      reinterpret_cast<float4 *>(sV)[e] = vs[e];
+    }
+    __syncthreads();
+    for (int key = 0; key < kvalid; ++key) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        s = fmaf(q[d], sK[key * D + d], s);
+        dp = fmaf(dO[d], sV[key * D + d], dp);
+      }
+      const float ds = expf(s * scale - L) * (dp - Di);
+#pragma unroll
+      for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, sK[key * D + d], dq[d]);
+    }
+  }
+  const bool real = tid < blk_len[I];
+#pragma unroll
+  for (int d = 0; d < D; ++d) dqp[head_off + static_cast<int64_t>(qslot) * D + d] = real ? dq[d] * scale : 0.f;
+}
+
+template <int D, int BK>
+__global__ void __launch_bounds__(BK)
+attn_bwd_dkdv_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp, const float *__restrict__ vp,
+                         const float *__restrict__ dop, const float *__restrict__ lse,
+                         const float *__restrict__ delta, const int32_t *__restrict__ blk_len,
+                         const int32_t *__restrict__ t_idx, const int32_t *__restrict__ t_cnt, int kv_shared,
+                         int nh, int nb, float scale, float *__restrict__ dkp, float *__restrict__ dvp) {
+  __shared__ __attribute__((aligned(16))) float sQ[BK * D];
+  __shared__ __attribute__((aligned(16))) float sO[BK * D];
+  __shared__ float sL[BK], sD[BK];
+  const int h = blockIdx.x / nb, J = blockIdx.x % nb;
+  const int tid = threadIdx.x;
+  const int64_t n_pad = static_cast<int64_t>(nb) * BK;
+  const int64_t head_off = static_cast<int64_t>(h) * n_pad * D;
+  const int kslot = J * BK + tid;
+  float k[D], v[D], dk[D], dv[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    k[d] = kp[head_off + static_cast<int64_t>(kslot) * D + d];
+    v[d] = vp[head_off + static_cast<int64_t>(kslot) * D + d];
+    dk[d] = 0.f;
+    dv[d] = 0.f;
+  }
+  const int64_t lrow = kv_shared ? static_cast<int64_t>(J) : static_cast<int64_t>(h) * nb + J;
+  const int cnt = t_cnt[lrow];
+  const int32_t *tl = t_idx + lrow * nb;
+  for (int c = 0; c < cnt; ++c) {
+    const int I = tl[c];
+    const int qvalid = blk_len[I];
+    const float4 *qs = reinterpret_cast<const float4 *>(qp + head_off + static_cast<int64_t>(I) * BK * D);
+    const float4 *os = reinterpret_cast<const float4 *>(dop + head_off + static_cast<int64_t>(I) * BK * D);
+    __syncthreads();
+    for (int e = tid; e < BK * D / 4; e += BK) {
+      reinterpret_cast<float4 *>(sQ)[e] = qs[e];
+      reinterpret_cast<float4 *>(sO)[e] = os[e];
+    }
+    sL[tid] = lse[static_cast<int64_t>(h) * n_pad + static_cast<int64_t>(I) * BK + tid];
+    sD[tid] = delta[static_cast<int64_t>(h) * n_pad + static_cast<int64_t>(I) * BK + tid];
+    __syncthreads();
+    for (int qi = 0; qi < qvalid; ++qi) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        s = fmaf(sQ[qi * D + d], k[d], s);
+        dp = fmaf(sO[qi * D + d], v[d], dp);
+      }
+      const float p = expf(s * scale - sL[qi]);
+      const float ds = p * (dp - sD[qi]);
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        dv[d] = fmaf(p, sO[qi * D + d], dv[d]);
+        dk[d] = fmaf(ds, sQ[qi * D + d], dk[d]);
+      }
+    }
+  }
+  const bool real = tid < blk_len[J];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    dkp[head_off + static_cast<int64_t>(kslot) * D + d] = real ? dk[d] * scale : 0.f;
+    dvp[head_off + static_cast<int64_t>(kslot) * D + d] = real ? dv[d] : 0.f;
+  }
+}
+
+}  // namespace hsa
+
+namespace hsa_host {
+
+static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+size_t attn_bwd_ws_bytes(int nh, int nb, int B, int G) {
+  return align256(static_cast<size_t>(nh) * nb * B * sizeof(float)) +
+         align256(static_cast<size_t>(G) * nb * nb * sizeof(int32_t)) +
+         align256(static_cast<size_t>(G) * nb * sizeof(int32_t));
+}
+
+hsa_status_t launch_attn_bwd(const void *qp, const void *kp, const void *vp, const void *op, const void *dop,
+                             const float *lse, const int32_t *blk_len, const int32_t *kv_idx,
+                             const int32_t *kv_cnt, int max_kv, int kv_shared, int nh, int nb, int B, int D,
+                             int dtype, float scale, void *dqp, void *dkp, void *dvp, void *ws,
+                             hipStream_t stream) {
+  const int G = kv_shared ? 1 : nh;
+  char *base = static_cast<char *>(ws);
+  float *delta = reinterpret_cast<float *>(base);
+  base += align256(static_cast<size_t>(nh) * nb * B * sizeof(float));
+  int32_t *t_idx = reinterpret_cast<int32_t *>(base);
+  base += align256(static_cast<size_t>(G) * nb * nb * sizeof(int32_t));
+  int32_t *t_cnt = reinterpret_cast<int32_t *>(base);
+  const int n_pad = nb * B;
+  const int64_t total = static_cast<int64_t>(nh) * n_pad;
+  const dim3 dgrid(static_cast<unsigned>((total + 255) / 256));
+  const bool bf = dtype == HSA_BF16;
+#define HSA_DELTA(TT, DD)                                                                          \
+  hipLaunchKernelGGL((hsa::bwd_delta_kernel<TT, DD>), dgrid, dim3(256), 0, stream,                 \
+                     static_cast<const TT *>(op), static_cast<const TT *>(dop), blk_len, n_pad, B, total, delta)
+  if (bf) { if (D == 128) HSA_DELTA(uint16_t, 128); else HSA_DELTA(uint16_t, 64); }
+  else { if (D == 128) HSA_DELTA(float, 128); else HSA_DELTA(float, 64); }
+#undef HSA_DELTA
+  hipLaunchKernelGGL(hsa::bwd_transpose_kernel, dim3(G * nb), dim3(64), 0, stream, kv_idx, kv_cnt, nb,
+                     max_kv, t_idx, t_cnt);
+  const dim3 grid(nh * nb);
+  const float sl2 = scale * hsa::kLog2e;
+  if (bf) {
+    const uint16_t *q = static_cast<const uint16_t *>(qp), *k = static_cast<const uint16_t *>(kp),
+                   *v = static_cast<const uint16_t *>(vp), *dO = static_cast<const uint16_t *>(dop);
+    uint16_t *dq = static_cast<uint16_t *>(dqp), *dk = static_cast<uint16_t *>(dkp), *dv = static_cast<uint16_t *>(dvp);
+#define HSA_BWD(DD, BB)                                                                                 \
+  do {                                                                                                  \
+    hipLaunchKernelGGL((hsa::attn_bwd_dq_kernel<DD, BB>), grid, dim3(BB * 2), 0, stream, q, k, v, dO, lse, \
+                       delta, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, sl2, scale, dq);        \
+    hipLaunchKernelGGL((hsa::attn_bwd_dkdv_kernel<DD, BB>), grid, dim3(BB * 2), 0, stream, q, k, v, dO,    \
+                       lse, delta, blk_len, t_idx, t_cnt, kv_shared, nh, nb, sl2, scale, dk, dv);         \
+  } while (0)
+    if (D == 128 && B == 128) HSA_BWD(128, 128);
+    else if (D == 64 && B == 128) HSA_BWD(64, 128);
+    else if (D == 128 && B == 64) HSA_BWD(128, 64);
+    else HSA_BWD(64, 64);
+#undef HSA_BWD
+  } else {
+    const float *q = static_cast<const float *>(qp), *k = static_cast<const float *>(kp),
+                *v = static_cast<const float *>(vp), *dO = static_cast<const float *>(dop);
+    float *dq = static_cast<float *>(dqp), *dk = static_cast<float *>(dkp), *dv = static_cast<float *>(dvp);
+#define HSA_BWD32(DD, BB)                                                                                  \
+  do {                                                                                                     \
+    hipLaunchKernelGGL((hsa::attn_bwd_dq_f32_kernel<DD, BB>), grid, dim3(BB), 0, stream, q, k, v, dO, lse,   \
+                       delta, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, scale, dq);              \
+    hipLaunchKernelGGL((hsa::attn_bwd_dkdv_f32_kernel<DD, BB>), grid, dim3(BB), 0, stream, q, k, v, dO, lse, \
+                       delta, blk_len, t_idx, t_cnt, kv_shared, nh, nb, scale, dk, dv);                    \
+  } while (0)
+    if (D == 128 && B == 128) HSA_BWD32(128, 128);
+    else if (D == 64 && B == 128) HSA_BWD32(64, 128);
+    else if (D == 128 && B == 64) HSA_BWD32(128, 64);
+    else HSA_BWD32(64, 64);
+#undef HSA_BWD32
+  }
+  return check_launch("hsa_attn_bwd");
+}
+
+}  // namespace hsa_host

@@ -15,6 +15,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
@@ -75,6 +81,46 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 __device__ __forceinline__ lds_char_t *to_lds(const void *p) { return (lds_char_t *)(p); }
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return static_cast<uint32_t>((uintptr_t)to_lds(p));
+}
+
+// Tile layouts in LDS: BK rows (keys) of CPR 16-byte chunks (D bf16 each).
+// K: chunk c of row r sits at slot c ^ (r mod CPR) so the 32 lanes reading a
+//    fragment (32 rows, one chunk) hit distinct banks.
+// V: chunk c of row r sits at slot c ^ ((4 (r mod 4)) mod CPR) so the
+//    transposed reads (4 rows x 4 chunks per half-wave) hit distinct banks.
+template <int CPR>
+__device__ __forceinline__ int k_slot(int r, int c) { return r * CPR + (c ^ (r & (CPR - 1))); }
+template <int CPR>
+__device__ __forceinline__ int v_slot(int r, int c) { return r * CPR + (c ^ (((r & 3) << 2) & (CPR - 1))); }
+
+// Per-lane byte offsets (within a 1 KB slice) of the direct tile loads.
+// A wave's i-th load fills LDS slots P = (w*NI + i)*64 + lane, i.e. rows
+// r = (w*NI + i)*(64/CPR) + lane/CPR, physical chunk lane%CPR; it reads the
+// logical chunk that the swizzle stores there. The swizzle key depends on
+// r mod CPR (K) or r mod 4 (V), which repeats every 4 loads (K) or never
+// changes (V), so 4 offsets cover every load.
+template <int D, bool IS_V>
+__device__ __forceinline__ uint32_t tile_lane_offset(int i, int lane) {
+  constexpr int CPR = D / 8;
+  const int r = i * (64 / CPR) + lane / CPR;   // row within the slice group, mod 16 exact
+  const int cs = lane & (CPR - 1);
+  const int c = IS_V ? (cs ^ (((r & 3) << 2) & (CPR - 1))) : (cs ^ (r & (CPR - 1)));
+  return static_cast<uint32_t>((lane / CPR) * D * 2 + c * 16);
+}
+
+// Issue the direct loads of one BKxD bf16 tile (row-major in HBM) into a
+// swizzled LDS tile; each wave moves NI consecutive 1 KB slices.
+template <int D, int BK, int NW>
+__device__ __forceinline__ void issue_tile(const uint16_t *gtile, uint32_t lds_tile, int w,
+                                           const uint32_t (&loff)[4]) {
+  constexpr int CPR = D / 8;
+  constexpr int NI = BK * CPR / (64 * NW);
+  static_assert(CPR == 8 || NI % 4 == 0, "the swizzle key must not depend on the wave");
+  const char *gbase = reinterpret_cast<const char *>(gtile) + w * NI * 1024;
+  const uint32_t lbase = lds_tile + w * NI * 1024;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    load_lds16(gbase + i * 1024, loff[i & 3], lbase + i * 1024);
 }
 
 }  // namespace hsa

@@ -272,6 +272,30 @@ hsa_status_t hsa_attn_order(const int32_t *kv_cnt, int32_t G, int32_t nb, int32_
                             int32_t *order, hsa_stream_t stream);
 
 /*
+ * hsa_attn_bwd -- gradients of hsa_attn (same lists, same attended keys) with
+ *   respect to the reordered Q, K and V, for block-sparse training (VMoBA
+ *   abstract: native training with block-sparse attention):
+ *     P = softmax(scale q K^T) over the row's attended keys,
+ *     dV = P^T dO,  dS = P * (dO V^T - rowsum(dO * O)),
+ *     dQ = scale dS K,  dK = scale dS^T Q.
+ * op: the forward output; lse: the forward's log-sum-exp (required); dop:
+ *   dO, reordered like op. dqp, dkp, dvp: outputs [nh][nb*B][D] in the input
+ *   dtype; rows of pad slots are zero, and pad rows of dop are ignored.
+ * BF16 computes in float on matrix cores with P and dS rounded to bf16 for
+ *   the products; F32 in float. Results are bit-reproducible (fixed sum
+ *   order, no atomics).
+ * ws: device workspace of hsa_attn_bwd_ws_size bytes (row deltas and the
+ *   transposed lists: for each key block, the query blocks that list it).
+ */
+size_t hsa_attn_bwd_ws_size(int32_t nh, int32_t nb, int32_t B, int32_t kv_shared);
+hsa_status_t hsa_attn_bwd(const void *qp, const void *kp, const void *vp, const void *op,
+                          const void *dop, const float *lse, const int32_t *blk_len,
+                          const int32_t *kv_idx, const int32_t *kv_cnt, int32_t max_kv,
+                          int32_t kv_shared, int32_t nh, int32_t nb, int32_t B, int32_t D,
+                          int32_t dtype, float scale, void *dqp, void *dkp, void *dvp, void *ws,
+                          size_t ws_bytes, hsa_stream_t stream);
+
+/*
  * hsa_unperm -- scatter back to token order: o[perm[i]][h][:] = op[h][i][:]
  * for every real slot i (pad slots are dropped). Layouts as hsa_perm.
  */

@@ -459,3 +459,100 @@ def test_deterministic(hsa):
         outs.append((o.clone(), L.S.clone(), L.kv_idx.clone(), L.lse.clone()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- backward
+
+def _bwd_case(hsa, T, H, W, nh, B, D, dtype, shared, seed):
+    g = torch.Generator().manual_seed(seed)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q, k, v, do = (torch.randn((1, T * H * W, nh, D), generator=g).to(tdt) for _ in range(4))
+    perm, blk_len = hsa.hsa_plan(T, H, W, "hilbert", B, device=dev())
+    nb = perm.numel() // B
+    qp, kp, vp, dop = hsa.hsa_perm([x.to(dev()) for x in (q, k, v, do)][:3], perm, perm.numel()) + \
+        hsa.hsa_perm([do.to(dev())], perm, perm.numel())
+    rng = np.random.default_rng(seed)
+    G = 1 if shared else nh
+    cnt = rng.integers(1, nb + 1, size=(G, nb)).astype(np.int32)
+    idx = np.full((G, nb, nb), -1, dtype=np.int32)
+    for h in range(G):
+        for i in range(nb):
+            idx[h, i, :cnt[h, i]] = np.sort(rng.choice(nb, cnt[h, i], replace=False))
+    kv_idx, kv_cnt = torch.from_numpy(idx).to(dev()), torch.from_numpy(cnt).to(dev())
+    op, lse = hsa.hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B)
+    grads = hsa.hsa_attn_bwd(qp, kp, vp, op, dop, lse, blk_len, kv_idx, kv_cnt, B)
+    torch.cuda.synchronize()
+    p = perm.cpu().numpy().astype(np.int64)
+    ref = oracle.attn_blocks_bwd(*(oracle.gather(x, p) for x in (q, k, v, do)), p, B, idx, cnt)
+    return grads, ref, p, (qp, kp, vp, op, dop, lse, blk_len, kv_idx, kv_cnt)
+
+
+# bf16: P and dS are rounded to bf16 (relative 2^-9) before their products and
+# the results are rounded to bf16 (2^-9 of the largest gradient); those
+# average out over many keys. D_i = dO_i . O_i uses the stored bf16 output,
+# whose rounding shifts every dS of a row coherently (dQ_i moves by about
+# 2^-9 |dO_i||O_i| times the attention-weighted mean key), which reaches ~1 %
+# of the largest dQ at the Wan shape; 2 % of the largest gradient magnitude
+# bounds every element. Float: 1e-4 of it (float sums of D terms).
+BWD_TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+@pytest.mark.parametrize("B,D,dtype,shared", [(64, 64, "bf16", False), (128, 128, "bf16", False),
+                                              (64, 128, "bf16", True), (128, 64, "bf16", False),
+                                              (64, 64, "f32", False), (128, 128, "f32", True)])
+def test_attn_bwd_matches_oracle(hsa, B, D, dtype, shared):
+    """dQ, dK, dV on every row of a ragged grid with uneven lists."""
+    _say(f"attention backward B={B} D={D} {dtype} shared={shared}")
+    grads, ref, p, _ = _bwd_case(hsa, 3, 9, 11 if B == 64 else 23, 2, B, D, dtype, shared, B + D)
+    for name, a, r in zip(("dq", "dk", "dv"), grads, ref):
+        a = to_np(a)
+        scale = float(np.abs(r).max())
+        err = float(np.abs(a - r).max())
+        _say(f"  {name}: max err {err:.3e} of max |ref| {scale:.3e} ({err / scale:.2e})")
+        assert err <= BWD_TOL[dtype] * scale
+        assert np.all(a[:, p < 0] == 0)
+
+
+def test_attn_bwd_deterministic(hsa):
+    _say("attention backward determinism")
+    grads, _, _, args = _bwd_case(hsa, 3, 9, 23, 2, 128, 128, "bf16", False, 5)
+    again = hsa.hsa_attn_bwd(*args, 128)
+    for a, b in zip(grads, again):
+        assert torch.equal(a, b)
+
+
+def test_attn_bwd_wan_shape_sampled(hsa):
+    """At the Wan 480p shape (two of its heads, top-38 lists from the real
+    scoring path), dQ of sampled query blocks and dK/dV of sampled key blocks
+    against the oracle, which is run only on the rows those gradients depend on."""
+    w = wl.get(3)
+    _say("attention backward at the Wan shape (sampled blocks)")
+    q, k, v = (x[:, :, :2].contiguous() for x in wl.make_qkv(w, 0))
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
+    from dataclasses import replace
+    w2 = replace(w, heads=2)
+    L = hsa.layer_for_workload(w2, device=dev())
+    L.step(q.to(dev()), k.to(dev()), v.to(dev()))
+    dop = hsa.hsa_perm([do.to(dev())], L.perm, L.n_pad)[0]
+    dq, dk, dv = hsa.hsa_attn_bwd(*L.xp, L.op, dop, L.lse, L.blk_len, L.kv_idx, L.kv_cnt, w.B)
+    torch.cuda.synchronize()
+    nb = L.nb
+    idx, cnt = L.kv_idx.cpu().numpy(), L.kv_cnt.cpu().numpy()
+    rng = np.random.default_rng(31)
+    qs = rng.choice(nb, 2, replace=False)
+    ks = rng.choice(nb, 1, replace=False)
+    keep_cnt = np.zeros_like(cnt)
+    for h in range(2):
+        for I in range(nb):
+            if I in qs or np.isin(idx[h, I, :cnt[h, I]], ks).any():
+                keep_cnt[h, I] = cnt[h, I]
+    p = L.perm.cpu().numpy().astype(np.int64)
+    ref = oracle.attn_blocks_bwd(*(oracle.gather(x, p) for x in (q, k, v, do)), p, w.B, idx, keep_cnt)
+    rows_q = (qs[:, None] * w.B + np.arange(w.B)).ravel()
+    rows_k = (ks[:, None] * w.B + np.arange(w.B)).ravel()
+    for name, a, r, rows in (("dq", dq, ref[0], rows_q), ("dk", dk, ref[1], rows_k), ("dv", dv, ref[2], rows_k)):
+        a = to_np(a)[:, rows]
+        r = r[:, rows]
+        err, scale = float(np.abs(a - r).max()), float(np.abs(r).max())
+        _say(f"  {name}: max err {err:.3e} of max |ref| {scale:.3e}")
+        assert err <= BWD_TOL["bf16"] * scale
