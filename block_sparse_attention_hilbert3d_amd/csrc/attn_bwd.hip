@@ -146,6 +146,10 @@ __device__ __forceinline__ void store_rows(uint16_t *row, const f32x16 (&acc)[D 
     }
 }
 
+// Stages of ST = 64 rows (half a 128-row block) are double-buffered in LDS:
+// the direct loads of stage t + 1 are issued before stage t is computed.
+constexpr int kBwdStage = 64;
+
 template <int D, int BK>
 __global__ void __launch_bounds__(BK * 2, 1)
 attn_bwd_dq_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
@@ -154,10 +158,12 @@ attn_bwd_dq_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__
                    const int32_t *__restrict__ blk_len, const int32_t *__restrict__ kv_idx,
                    const int32_t *__restrict__ kv_cnt, int max_kv, int kv_shared, int nh, int nb,
                    float scale_log2, float scale, uint16_t *__restrict__ dqp) {
-  constexpr int NW = BK / 32, CPR = D / 8, DK = D / 16, DM = D / 32, MT = BK / 32, TILE = BK * D;
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[TILE];   // b128 rows (K swizzle)
-  __shared__ __attribute__((aligned(1024))) uint16_t sKt[TILE];  // transposed reads (V swizzle)
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[TILE];   // b128 rows (K swizzle)
+  constexpr int ST = kBwdStage, NS = BK / ST;
+  constexpr int NW = BK / 32, CPR = D / 8, DK = D / 16, DM = D / 32, MT = ST / 32, TILE = ST * D;
+  constexpr int LOADS = 3 * (ST * CPR / (64 * NW));  // direct loads per wave per stage
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[2 * TILE];   // b128 rows (K swizzle)
+  __shared__ __attribute__((aligned(1024))) uint16_t sKt[2 * TILE];  // transposed reads (V swizzle)
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[2 * TILE];   // b128 rows (K swizzle)
   const int total = nh * nb;
   const int bid = xcd_remap(blockIdx.x, total);
   const int h = bid / nb, I = bid - h * nb;
@@ -184,6 +190,7 @@ attn_bwd_dq_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__
   const float dq_i = delta[static_cast<int64_t>(h) * n_pad + qslot];
 #pragma unroll
   for (int ks = 0; ks < DK; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(dof[ks]));
+  asm volatile("" ::"v"(lq2), "v"(dq_i));
 
   f32x16 acc[DM];
 #pragma unroll
@@ -192,18 +199,26 @@ attn_bwd_dq_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__
     for (int i = 0; i < 16; ++i) acc[md][i] = 0.f;
 
   const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
-  const int cnt = kv_cnt[lrow];
+  const int nst = kv_cnt[lrow] * NS;
   const int32_t *list = kv_idx + lrow * max_kv;
-  for (int c = 0; c < cnt; ++c) {
-    const int J = list[c];
-    const int kvalid = blk_len[J];
-    const int64_t tile_off = head_off + static_cast<int64_t>(J) * BK * D;
-    __syncthreads();  // the previous block's tiles are no longer read
-    issue_tile<D, BK, NW>(kp + tile_off, ldsK, w, koff);
-    issue_tile<D, BK, NW>(kp + tile_off, ldsKt, w, voff);
-    issue_tile<D, BK, NW>(vp + tile_off, ldsV, w, koff);
-    wait_vmcnt<0>();
-    __syncthreads();
+  auto issue = [&](int t) {
+    const int64_t off = head_off + (static_cast<int64_t>(list[t / NS]) * BK + (t % NS) * ST) * D;
+    const uint32_t b = static_cast<uint32_t>((t & 1) * TILE * 2);
+    issue_tile<D, ST, NW>(kp + off, ldsK + b, w, koff);
+    issue_tile<D, ST, NW>(kp + off, ldsKt + b, w, voff);
+    issue_tile<D, ST, NW>(vp + off, ldsV + b, w, koff);
+  };
+  if (nst > 0) issue(0);
+  for (int t = 0; t < nst; ++t) {
+    const int buf = t & 1;
+    const int kvalid = min(max(blk_len[list[t / NS]] - (t % NS) * ST, 0), ST);
+    if (t + 1 < nst) {
+      issue(t + 1);  // its buffer was released by the barrier closing iteration t - 1
+      wait_vmcnt<LOADS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();  // stage t is in LDS for every wave
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       f32x16 s, dp;
@@ -214,12 +229,12 @@ attn_bwd_dq_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__
       }
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&sK[(mt * 32 * CPR + fo.row[ks]) * 8]);
-        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&sV[(mt * 32 * CPR + fo.row[ks]) * 8]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&sK[buf * TILE + (mt * 32 * CPR + fo.row[ks]) * 8]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&sV[buf * TILE + (mt * 32 * CPR + fo.row[ks]) * 8]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[ks], dp, 0, 0, 0);
       }
-      // element i is key mt*32 + 8(i/4) + 4g + i%4 of block J, query = lane column
+      // element i is key mt*32 + 8(i/4) + 4g + i%4 of the stage, query = lane column
       const int lim = kvalid - mt * 32 - g * 4;
       float ds[16];
 #pragma unroll
@@ -235,10 +250,11 @@ attn_bwd_dq_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__
         for (int j = 0; j < 8; ++j) dsf[j] = static_cast<__bf16>(ds[ks2 * 8 + j]);
 #pragma unroll
         for (int md = 0; md < DM; ++md)
-          acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ktl, fo.tr[md], mt * 2 + ks2), dsf,
-                                                           acc[md], 0, 0, 0);
+          acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_frag<D>(ktl + buf * TILE * 2, fo.tr[md], mt * 2 + ks2), dsf, acc[md], 0, 0, 0);
       }
     }
+    __syncthreads();  // every wave is done with buffer t & 1
   }
   const bool real = (w * 32 + ln) < blk_len[I];
   store_rows<D>(dqp + head_off + static_cast<int64_t>(qslot) * D, acc, real ? scale : 0.f, g);
@@ -252,13 +268,17 @@ attn_bwd_dkdv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict
                      const int32_t *__restrict__ blk_len, const int32_t *__restrict__ t_idx,
                      const int32_t *__restrict__ t_cnt, int kv_shared, int nh, int nb, float scale_log2,
                      float scale, uint16_t *__restrict__ dkp, uint16_t *__restrict__ dvp) {
-  constexpr int NW = BK / 32, CPR = D / 8, DK = D / 16, DM = D / 32, QT = BK / 32, TILE = BK * D;
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ[TILE];    // b128 rows
-  __shared__ __attribute__((aligned(1024))) uint16_t sQt[TILE];   // transposed reads
-  __shared__ __attribute__((aligned(1024))) uint16_t sdO[TILE];   // b128 rows
-  __shared__ __attribute__((aligned(1024))) uint16_t sdOt[TILE];  // transposed reads
-  __shared__ __attribute__((aligned(16))) float sL[BK];           // lse * log2(e)
-  __shared__ __attribute__((aligned(16))) float sD[BK];           // D_i
+  constexpr int ST = kBwdStage, NS = BK / ST;
+  constexpr int NW = BK / 32, CPR = D / 8, DK = D / 16, DM = D / 32, QT = ST / 32, TILE = ST * D;
+  // four tiles per stage, plus the stage's lse and D rows (one load each)
+  constexpr int LOADS = 4 * (ST * CPR / (64 * NW)) + 2;
+  __shared__ __attribute__((aligned(1024))) uint16_t sQ[2 * TILE];    // b128 rows
+  __shared__ __attribute__((aligned(1024))) uint16_t sQt[2 * TILE];   // transposed reads
+  __shared__ __attribute__((aligned(1024))) uint16_t sdO[2 * TILE];   // b128 rows
+  __shared__ __attribute__((aligned(1024))) uint16_t sdOt[2 * TILE];  // transposed reads
+  // per wave and buffer: 64 lse values then 64 D values (each 1 KB load
+  // fills 256 B of data; the other lanes repeat it)
+  __shared__ __attribute__((aligned(1024))) float sLD[NW][2][2][256];
   const int total = nh * nb;
   const int bid = xcd_remap(blockIdx.x, total);
   const int h = bid / nb, J = bid - h * nb;
@@ -276,6 +296,7 @@ attn_bwd_dkdv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict
     voff[i] = tile_lane_offset<D, true>(i, lane);
   }
   const uint32_t ldsQ = lds_addr(sQ), ldsQt = lds_addr(sQt), ldsO = lds_addr(sdO), ldsOt = lds_addr(sdOt);
+  const uint32_t ldsLD = __builtin_amdgcn_readfirstlane(lds_addr(&sLD[w][0][0][0]));
   lds_char_t *const qtl = to_lds(sQt);
   lds_char_t *const otl = to_lds(sdOt);
 
@@ -295,24 +316,35 @@ attn_bwd_dkdv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict
     }
 
   const int64_t lrow = kv_shared ? static_cast<int64_t>(J) : static_cast<int64_t>(h) * nb + J;
-  const int cnt = t_cnt[lrow];
+  const int nst = t_cnt[lrow] * NS;
   const int32_t *tl = t_idx + lrow * nb;
-  for (int c = 0; c < cnt; ++c) {
-    const int I = tl[c];
-    const int qvalid = blk_len[I];
-    const int64_t tile_off = head_off + static_cast<int64_t>(I) * BK * D;
-    __syncthreads();
-    issue_tile<D, BK, NW>(qp + tile_off, ldsQ, w, koff);
-    issue_tile<D, BK, NW>(qp + tile_off, ldsQt, w, voff);
-    issue_tile<D, BK, NW>(dop + tile_off, ldsO, w, koff);
-    issue_tile<D, BK, NW>(dop + tile_off, ldsOt, w, voff);
-    if (tid < BK) {
-      const int64_t r = static_cast<int64_t>(h) * n_pad + static_cast<int64_t>(I) * BK + tid;
-      sL[tid] = lse[r] * kLog2e;
-      sD[tid] = delta[r];
+  const uint32_t ld_off = static_cast<uint32_t>((lane & 15) * 16);  // 16 lanes x 16 B = 64 floats
+  auto issue = [&](int t) {
+    const int64_t row0 = static_cast<int64_t>(tl[t / NS]) * BK + (t % NS) * ST;
+    const int64_t off = head_off + row0 * D;
+    const uint32_t b = static_cast<uint32_t>((t & 1) * TILE * 2);
+    issue_tile<D, ST, NW>(qp + off, ldsQ + b, w, koff);
+    issue_tile<D, ST, NW>(qp + off, ldsQt + b, w, voff);
+    issue_tile<D, ST, NW>(dop + off, ldsO + b, w, koff);
+    issue_tile<D, ST, NW>(dop + off, ldsOt + b, w, voff);
+    const int64_t r = static_cast<int64_t>(h) * n_pad + row0;
+    const uint32_t lb = ldsLD + static_cast<uint32_t>((t & 1) * 2 * 256 * 4);
+    load_lds16(lse + r, ld_off, lb);
+    load_lds16(delta + r, ld_off, lb + 256 * 4);
+  };
+  if (nst > 0) issue(0);
+  for (int t = 0; t < nst; ++t) {
+    const int buf = t & 1;
+    const int qvalid = min(max(blk_len[tl[t / NS]] - (t % NS) * ST, 0), ST);
+    if (t + 1 < nst) {
+      issue(t + 1);
+      wait_vmcnt<LOADS>();
+    } else {
+      wait_vmcnt<0>();
     }
-    wait_vmcnt<0>();
     __syncthreads();
+    const float *sL = &sLD[w][buf][0][0];
+    const float *sD = &sLD[w][buf][1][0];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       f32x16 s, dp;
@@ -323,19 +355,20 @@ attn_bwd_dkdv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict
       }
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(&sQ[(qt * 32 * CPR + fo.row[ks]) * 8]);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8 *>(&sdO[(qt * 32 * CPR + fo.row[ks]) * 8]);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(&sQ[buf * TILE + (qt * 32 * CPR + fo.row[ks]) * 8]);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8 *>(&sdO[buf * TILE + (qt * 32 * CPR + fo.row[ks]) * 8]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp, 0, 0, 0);
       }
-      // element i is query qt*32 + 8(i/4) + 4g + i%4 of block I, key = lane column
+      // element i is query qt*32 + 8(i/4) + 4g + i%4 of the stage, key = lane column
       float p[16], ds[16];
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int q0 = qt * 32 + i4 * 8 + g * 4;
         const float4 l4 = *reinterpret_cast<const float4 *>(&sL[q0]);
         const float4 d4 = *reinterpret_cast<const float4 *>(&sD[q0]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = i4 * 4 + r;
@@ -354,13 +387,14 @@ attn_bwd_dkdv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict
         }
 #pragma unroll
         for (int md = 0; md < DM; ++md) {
-          dv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(otl, fo.tr[md], qt * 2 + ks2), pf,
-                                                          dv[md], 0, 0, 0);
-          dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qtl, fo.tr[md], qt * 2 + ks2), dsf,
-                                                          dk[md], 0, 0, 0);
+          dv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_frag<D>(otl + buf * TILE * 2, fo.tr[md], qt * 2 + ks2), pf, dv[md], 0, 0, 0);
+          dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_frag<D>(qtl + buf * TILE * 2, fo.tr[md], qt * 2 + ks2), dsf, dk[md], 0, 0, 0);
         }
       }
     }
+    __syncthreads();
   }
   const bool real = (w * 32 + ln) < blk_len[J];
   store_rows<D>(dkp + head_off + static_cast<int64_t>(kslot) * D, dk, real ? scale : 0.f, g);
