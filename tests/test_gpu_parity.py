@@ -556,3 +556,76 @@ def test_attn_bwd_wan_shape_sampled(hsa):
         err, scale = float(np.abs(a - r).max()), float(np.abs(r).max())
         _say(f"  {name}: max err {err:.3e} of max |ref| {scale:.3e}")
         assert err <= BWD_TOL["bf16"] * scale
+
+
+# ---------------------------------------------------------------- edge cases
+
+def test_empty_lists_forward_backward(hsa):
+    """Query blocks with an empty list (kv_cnt = 0) attend to nothing: their
+    output rows and log-sum-exp are zero, and they pass no gradient; the
+    other rows match the oracle (per-head and shared lists, with and without
+    a processing order)."""
+    _say("empty lists")
+    T, H, W, nh, B, D = 4, 16, 16, 2, 64, 64
+    g = torch.Generator().manual_seed(41)
+    q, k, v, do = (torch.randn((1, T * H * W, nh, D), generator=g).to(torch.bfloat16) for _ in range(4))
+    perm, blk_len = hsa.hsa_plan(T, H, W, "hilbert", B, device=dev())
+    nb = perm.numel() // B
+    qp, kp, vp = hsa.hsa_perm([x.to(dev()) for x in (q, k, v)], perm, perm.numel())
+    dop = hsa.hsa_perm([do.to(dev())], perm, perm.numel())[0]
+    p = perm.cpu().numpy().astype(np.int64)
+    rng = np.random.default_rng(42)
+    for G in (nh, 1):
+        cnt = rng.integers(0, 4, size=(G, nb)).astype(np.int32)
+        cnt[:, :3] = 0
+        idx = np.full((G, nb, 4), -1, dtype=np.int32)
+        for h in range(G):
+            for i in range(nb):
+                idx[h, i, :cnt[h, i]] = np.sort(rng.choice(nb, cnt[h, i], replace=False))
+        kv_idx, kv_cnt = torch.from_numpy(idx).to(dev()), torch.from_numpy(cnt).to(dev())
+        order = hsa.hsa_attn_order(kv_cnt, 4)
+        for o in (None, order):
+            op, lse = hsa.hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B, order=o)
+            dq, dk, dv = hsa.hsa_attn_bwd(qp, kp, vp, op, dop, lse, blk_len, kv_idx, kv_cnt, B)
+            torch.cuda.synchronize()
+            ref_op, ref_lse = oracle.attn_blocks(*(oracle.gather(x, p) for x in (q, k, v)), p, B, idx, cnt)
+            assert np.abs(to_np(op) - ref_op).max() <= TOL["bf16"]
+            assert np.abs(to_np(lse) - ref_lse).max() <= 1e-3
+            empty = np.repeat(cnt[0 if G == 1 else slice(None)] == 0, B, axis=-1)
+            empty = np.broadcast_to(empty, (nh, nb * B)) if G == 1 else empty
+            assert np.all(to_np(op)[empty] == 0) and np.all(to_np(lse)[empty] == 0)
+            assert np.all(to_np(dq)[empty] == 0)
+            ref = oracle.attn_blocks_bwd(*(oracle.gather(x, p) for x in (q, k, v, do)), p, B, idx, cnt)
+            for a, r in zip((dq, dk, dv), ref):
+                assert np.abs(to_np(a) - r).max() <= BWD_TOL["bf16"] * max(float(np.abs(r).max()), 1e-6)
+
+
+@pytest.mark.parametrize("shape,order,B", [((1, 1024, 1024), "hilbert", 128), ((1024, 1, 1), "hilbert", 64),
+                                           ((1024, 1, 3), "row", 128), ((2, 1024, 3), "hilbert2d", 128),
+                                           ((64, 64, 64), "cube3d", 128), ((1, 1024, 1000), "tile2d", 128)])
+def test_plan_maximum_sides(hsa, shape, order, B):
+    """Plans at the largest grid sides the boundary accepts (1024)."""
+    T, H, W = shape
+    _say(f"plan at maximum side {shape} {order}")
+    perm, blk_len = hsa.hsa_plan(T, H, W, order, B, device=dev())
+    torch.cuda.synchronize()
+    ref, ref_len = oracle.plan(T, H, W, order, B)
+    assert np.array_equal(perm.cpu().numpy(), ref) and np.array_equal(blk_len.cpu().numpy(), ref_len)
+
+
+def test_score_at_the_subblock_limit(hsa):
+    """2048 sub-blocks per head (Wan grid, s = 16), MASS and MAX."""
+    w = wl.get(3)
+    _say("score with 2048 sub-blocks")
+    q, k, _ = (x[:, :, :2].contiguous() for x in wl.make_qkv(w, 0))
+    perm, blk_len = hsa.hsa_plan(w.T, w.H, w.W, "hilbert", w.B, device=dev())
+    qp, kp = hsa.hsa_perm([q.to(dev()), k.to(dev())], perm, perm.numel())
+    p = perm.cpu().numpy().astype(np.int64)
+    qo, ko = oracle.gather(q, p), oracle.gather(k, p)
+    for agg in ("mass", "max"):
+        S = hsa.hsa_score(qp, kp, blk_len, w.B, 16, agg)
+        torch.cuda.synchronize()
+        ref = oracle.score(qo, ko, p, w.B, 16, agg=agg)
+        err = float(np.abs(S.cpu().numpy() - ref).max())
+        _say(f"  {agg}: max err {err:.2e}")
+        assert err <= SCORE_TOL[agg]
