@@ -179,3 +179,16 @@ def test_attn_and_unperm_validation(B):
     assert L.hsa_attn_order(FAKE, 1 << 16, 1 << 16, 4, FAKE, NULL) == 4                          # G*nb
     assert L.hsa_unperm(FAKE, FAKE, FAKE, 10, 8, 2, 64, 128, 1, NULL) == 2
     assert L.hsa_unperm(FAKE, NULL, FAKE, 10, 16, 2, 64, 128, 1, NULL) == 1
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """A C99 program includes the header, links the library and calls it."""
+    exe = tmp_path / "abi_smoke"
+    src = os.path.join(ROOT, "tests", "c", "abi_smoke.c")
+    build = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), src,
+                            "-o", str(exe), "-L", os.path.dirname(LIB), "-lhsa",
+                            "-Wl,-rpath," + os.path.dirname(LIB)], capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
+    assert run.stdout.startswith("ok 3 workspace too small")
