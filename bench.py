@@ -271,6 +271,29 @@ def main():
 
     flop_tiles = 4.0 * B * B * D * float(np.mean(tiles_steps))
     # useful pairs of the last timed step's lists, scaled to the mean tile count
+    # the same refresh step captured once in a HIP graph and replayed (no
+    # per-kernel launch cost); one graph per input set
+    graphs = []
+    for i in range(2):
+        L.step(*sets[i], step=0, budget_ratio=wl.budget_ratio(w, 0))
+        torch.cuda.synchronize()
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            L.step(*sets[i], step=0, budget_ratio=wl.budget_ratio(w, 0))
+        graphs.append(gph)
+    torch.cuda.synchronize()
+    for gph in graphs:
+        gph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for i in range(K):
+        graphs[i % 2].replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    ms_graph = g0.elapsed_time(g1) / K
+    del graphs
+
     kv_cnt = L.kv_cnt.cpu().numpy()
     blk_len = L.blk_len.cpu().numpy().astype(np.int64)
     kv_idx = L.kv_idx.cpu().numpy()
@@ -337,6 +360,7 @@ def main():
                    "batch": 1},
         "ms_per_step_p10_p50_p90": [float(np.percentile(per_step, p)) for p in (10, 50, 90)],
         "ms_per_layer_cached_mask": ms_cached,
+        "ms_per_step_hip_graph": ms_graph,
         "ms_per_layer_refresh_cycle": cycle_ms,
         "refresh_interval": w.refresh,
         "stages": stages,

@@ -629,3 +629,36 @@ def test_score_at_the_subblock_limit(hsa):
         err = float(np.abs(S.cpu().numpy() - ref).max())
         _say(f"  {agg}: max err {err:.2e}")
         assert err <= SCORE_TOL[agg]
+
+
+@pytest.mark.parametrize("idx", [2, 5])
+def test_layer_step_in_a_hip_graph(hsa, idx):
+    """A whole layer step (reorder, score, select, order, attend, restore) is
+    captured into a HIP graph (the library never allocates, synchronises or
+    clears memory with memset); every replay, with fresh inputs copied in
+    eagerly and synchronisations between replays, equals the eager step."""
+    w = wl.get(idx)
+    _say(f"layer step in a HIP graph (workload {idx})")
+    L = hsa.layer_for_workload(w, device=dev())
+    inputs = [tuple(x.to(dev()) for x in wl.make_qkv(w, s)) for s in range(3)]
+    static = tuple(torch.empty_like(x) for x in inputs[0])
+    for x, y in zip(static, inputs[0]):
+        x.copy_(y)
+    br = wl.budget_ratio(w, 0)
+    L.step(*static, budget_ratio=br)                       # warm up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        L.step(*static, budget_ratio=br)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        src = inputs[rep % 3]
+        for x, y in zip(static, src):
+            x.copy_(y)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (L.o.clone(), L.kv_idx.clone(), L.kv_cnt.clone())
+        L.step(*static, budget_ratio=br)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], L.o) and torch.equal(got[1], L.kv_idx) and torch.equal(got[2], L.kv_cnt), rep
