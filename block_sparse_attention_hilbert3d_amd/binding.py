@@ -48,6 +48,8 @@ _SIGS = {
     "hsa_select_list_width": (_c_i32, [_c_i32, _c_i32, ctypes.POINTER(SelectParams)]),
     "hsa_select": (ctypes.c_int, [_p, _c_i32, _c_i32, ctypes.POINTER(SelectParams), _p, _p, _c_i32, _p, _c_sz, _p]),
     "hsa_attn": (ctypes.c_int, [_p] * 9 + [_c_i32] * 7 + [_c_f32, _p]),
+    "hsa_attn_tokens": (ctypes.c_int, [_p, _c_i64, _p, _p, _p, _c_i64, _p, _p, _c_i32, _p, _p, _p, _p]
+                        + [_c_i32] * 7 + [_c_f32, _p]),
     "hsa_attn_order": (ctypes.c_int, [_p, _c_i32, _c_i32, _c_i32, _p, _p]),
     "hsa_unperm": (ctypes.c_int, [_p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _p]),
     "hsa_attn_bwd_ws_size": (_c_sz, [_c_i32] * 4),
@@ -130,7 +132,8 @@ def hsa_plan(T: int, H: int, W: int, order: str, B: int, device="cuda"):
 def hsa_perm(xs, perm: torch.Tensor, n_pad: int, outs=None, pool_s: int = 0, pooled=None):
     """xs: list of [1, N, nh, D] (token stride may exceed nh*D) -> list of [nh, n_pad, D].
     With pool_s > 0 also fills `pooled` (float32 [2, nh, n_pad // pool_s, D], allocated if
-    None) with the sub-block means of xs[0] and xs[1]; returns (outs, pooled) then."""
+    None) with the sub-block means of xs[0] and xs[1]; returns (outs, pooled) then. When
+    pooling, outs[0] or outs[1] may be None: that tensor is pooled but not stored."""
     xs = list(xs)
     x0 = xs[0]
     _, N, nh, D = x0.shape
@@ -147,7 +150,7 @@ def hsa_perm(xs, perm: torch.Tensor, n_pad: int, outs=None, pool_s: int = 0, poo
     if pool_s and pooled is None:
         pooled = torch.empty((2, nh, n_pad // pool_s, D), dtype=torch.float32, device=x0.device)
     src = (ctypes.c_void_p * len(xs))(*[x.data_ptr() for x in xs])
-    dst = (ctypes.c_void_p * len(xs))(*[y.data_ptr() for y in outs])
+    dst = (ctypes.c_void_p * len(xs))(*[None if y is None else y.data_ptr() for y in outs])
     _check(lib().hsa_perm(len(xs), src, dst, _ptr(perm), N, n_pad, nh, D, x0.stride(1),
                           _dtype_code(x0), int(pool_s), _ptr(pooled if pool_s else None),
                           _stream()), "hsa_perm")
@@ -237,6 +240,33 @@ def hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B: int, scale: float | None = 
     _check(lib().hsa_attn(_ptr(qp), _ptr(kp), _ptr(vp), _ptr(out), _ptr(lse if want_lse else None),
                           _ptr(blk_len), _ptr(kv_idx), _ptr(kv_cnt), _ptr(order), kv_idx.shape[-1], shared,
                           nh, nb, B, D, _dtype_code(qp), scale, _stream()), "hsa_attn")
+    return out, (lse if want_lse else None)
+
+
+def hsa_attn_tokens(q, kp, vp, perm, blk_len, kv_idx, kv_cnt, B: int, scale: float | None = None,
+                    want_lse: bool = True, out=None, lse=None, order=None):
+    """q [1, N, nh, D] token-major (token stride may exceed nh*D, e.g. a slice of a fused QKV
+    buffer); kp, vp [nh, n_pad, D] reordered -> (o [1, N, nh, D], lse float32 [nh, n_pad] or
+    None). Equals hsa_unperm(hsa_attn(Qp, kp, vp, ...)) with the reorder of Q and the inverse
+    reorder of the output done inside the attention kernel."""
+    _need_device(kp, vp, perm, blk_len, kv_idx, kv_cnt, order)
+    _, N, nh, D = q.shape
+    if not q.is_cuda or q.stride(3) != 1 or q.stride(2) != D:
+        raise HsaError("hsa_attn_tokens: q must be a device tensor with contiguous heads and head dim")
+    n_pad = kp.shape[1]
+    nb = n_pad // B
+    shared = 1 if kv_idx.shape[0] == 1 and nh > 1 else 0
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty((1, N, nh, D), dtype=q.dtype, device=q.device)
+    if out.stride(3) != 1 or out.stride(2) != D:
+        raise HsaError("hsa_attn_tokens: heads and head dim of the output must be contiguous")
+    if want_lse and lse is None:
+        lse = torch.empty((nh, n_pad), dtype=torch.float32, device=q.device)
+    _check(lib().hsa_attn_tokens(_ptr(q), q.stride(1), _ptr(kp), _ptr(vp), _ptr(out), out.stride(1),
+                                 _ptr(lse if want_lse else None), _ptr(perm), N, _ptr(blk_len),
+                                 _ptr(kv_idx), _ptr(kv_cnt), _ptr(order), kv_idx.shape[-1], shared,
+                                 nh, nb, B, D, _dtype_code(q), scale, _stream()), "hsa_attn_tokens")
     return out, (lse if want_lse else None)
 
 

@@ -47,7 +47,8 @@ hsa_status_t launch_select(const float *S, int nh, int nb, const hsa_select_para
 hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *op, float *lse,
                          const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
                          const int32_t *order, int max_kv, int kv_shared, int nh, int nb, int B,
-                         int D, int dtype, float scale, hipStream_t stream);
+                         int D, int dtype, float scale, const int32_t *perm, int64_t q_stride,
+                         int64_t o_stride, hipStream_t stream);
 size_t attn_bwd_ws_bytes(int nh, int nb, int B, int G);
 hsa_status_t launch_attn_bwd(const void *qp, const void *kp, const void *vp, const void *op, const void *dop,
                              const float *lse, const int32_t *blk_len, const int32_t *kv_idx,
@@ -166,8 +167,11 @@ hsa_status_t hsa_perm(int32_t n_tensors, const void *const *xs, void *const *xps
   g_last_error.clear();
   if (n_tensors < 1 || n_tensors > 3) return fail(HSA_ERR_BAD_ARG, "hsa_perm: n_tensors %d not in 1..3", n_tensors);
   if (!xs || !xps || !perm) return fail(HSA_ERR_NULL_PTR, "hsa_perm: null pointer array or perm");
-  for (int i = 0; i < n_tensors; ++i)
-    if (!xs[i] || !xps[i]) return fail(HSA_ERR_NULL_PTR, "hsa_perm: tensor %d is null", i);
+  for (int i = 0; i < n_tensors; ++i) {
+    if (!xs[i]) return fail(HSA_ERR_NULL_PTR, "hsa_perm: input %d is null", i);
+    // a null output is allowed for a pooled tensor (0 or 1): pooled, not stored
+    if (!xps[i] && !(pooled && i < 2)) return fail(HSA_ERR_NULL_PTR, "hsa_perm: output %d is null", i);
+  }
   hsa_status_t st;
   if ((st = check_dtype(dtype)) != HSA_OK || (st = check_D(D)) != HSA_OK) return st;
   if (N < 1 || n_pad < N || nh < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_perm: N=%d n_pad=%d nh=%d", N, n_pad, nh);
@@ -177,7 +181,7 @@ hsa_status_t hsa_perm(int32_t n_tensors, const void *const *xs, void *const *xps
   if (static_cast<int64_t>(nh) * n_pad * D >= (1ll << 40)) return fail(HSA_ERR_BAD_SHAPE, "hsa_perm: tensor too large");
   if (static_cast<int64_t>(nh) * D * es / 16 > 1024) return fail(HSA_ERR_UNSUPPORTED, "hsa_perm: nh*D*elem_size must be <= 16 KB");
   for (int i = 0; i < n_tensors; ++i)
-    if (!aligned16(xs[i]) || !aligned16(xps[i])) return fail(HSA_ERR_BAD_ARG, "hsa_perm: tensor %d not 16-byte aligned", i);
+    if (!aligned16(xs[i]) || (xps[i] && !aligned16(xps[i]))) return fail(HSA_ERR_BAD_ARG, "hsa_perm: tensor %d not 16-byte aligned", i);
   if (pooled) {
     if (pool_s != 16 && pool_s != 32 && pool_s != 64 && pool_s != 128) return fail(HSA_ERR_UNSUPPORTED, "hsa_perm: pool_s %d not in {16,32,64,128}", pool_s);
     if (n_pad % pool_s) return fail(HSA_ERR_BAD_SHAPE, "hsa_perm: pool_s %d does not divide n_pad %d", pool_s, n_pad);
@@ -345,7 +349,36 @@ hsa_status_t hsa_attn(const void *qp, const void *kp, const void *vp, void *op, 
   if (!(scale > 0.f) || !isfinite(scale)) return fail(HSA_ERR_BAD_ARG, "hsa_attn: scale must be finite and positive");
   if (!aligned16(qp) || !aligned16(kp) || !aligned16(vp) || !aligned16(op)) return fail(HSA_ERR_BAD_ARG, "hsa_attn: tensors must be 16-byte aligned");
   if (order && !aligned4(order)) return fail(HSA_ERR_BAD_ARG, "hsa_attn: order must be 4-byte aligned");
-  return launch_attn(qp, kp, vp, op, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, B, D, dtype, scale, static_cast<hipStream_t>(stream));
+  return launch_attn(qp, kp, vp, op, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, B, D, dtype, scale,
+                     nullptr, 0, 0, static_cast<hipStream_t>(stream));
+}
+
+hsa_status_t hsa_attn_tokens(const void *q, int64_t q_stride, const void *kp, const void *vp, void *o,
+                             int64_t o_stride, float *lse, const int32_t *perm, int32_t N,
+                             const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
+                             const int32_t *order, int32_t max_kv, int32_t kv_shared, int32_t nh,
+                             int32_t nb, int32_t B, int32_t D, int32_t dtype, float scale,
+                             hsa_stream_t stream) {
+  g_last_error.clear();
+  if (!q || !kp || !vp || !o || !perm || !blk_len || !kv_idx || !kv_cnt) return fail(HSA_ERR_NULL_PTR, "hsa_attn_tokens: null input or output");
+  hsa_status_t st;
+  if ((st = check_dtype(dtype)) != HSA_OK || (st = check_D(D)) != HSA_OK || (st = check_B(B)) != HSA_OK) return st;
+  if (nh < 1 || nb < 1 || max_kv < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn_tokens: nh=%d nb=%d max_kv=%d", nh, nb, max_kv);
+  if (static_cast<int64_t>(nh) * nb >= (1ll << 31)) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn_tokens: too many blocks");
+  if (N < 1 || static_cast<int64_t>(N) > static_cast<int64_t>(nb) * B) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn_tokens: N=%d outside 1..nb*B", N);
+  const int es = esize_of(dtype);
+  const int64_t strides[2] = {q_stride, o_stride};
+  for (const int64_t ts : strides) {
+    if (ts < static_cast<int64_t>(nh) * D) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn_tokens: token stride %lld < nh*D", static_cast<long long>(ts));
+    if ((ts * es) % 16 != 0) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: token strides must be multiples of 16 bytes");
+    if (ts >= (1ll << 40) / N) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn_tokens: tensor too large");
+  }
+  if (kv_shared != 0 && kv_shared != 1) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: kv_shared must be 0 or 1");
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: scale must be finite and positive");
+  if (!aligned16(q) || !aligned16(kp) || !aligned16(vp) || !aligned16(o)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: tensors must be 16-byte aligned");
+  if (!aligned4(perm) || (order && !aligned4(order))) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: perm and order must be 4-byte aligned");
+  return launch_attn(q, kp, vp, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, B, D, dtype, scale,
+                     perm, q_stride, o_stride, static_cast<hipStream_t>(stream));
 }
 
 hsa_status_t hsa_attn_order(const int32_t *kv_cnt, int32_t G, int32_t nb, int32_t max_kv,

@@ -28,6 +28,10 @@
 //    with v_readlane, keeping scalar memory round trips out of the loop;
 //  - epilogue divides by the row sum, rounds to bf16, zeroes pad rows and
 //    writes the natural-log log-sum-exp (from an unrounded fp32 sum).
+// Token-layout I/O (TOK): Q rows are read from, and output rows written to,
+// the token-major tensors through the slot -> token map, so the reorder of Q
+// and the inverse reorder of O happen inside this kernel's first loads and
+// last stores; pad slots take zero query rows and store nothing.
 // f32 kernel: a plain one-thread-per-query online-softmax loop with K/V tiles
 // in LDS, for float inputs (small shapes).
 #include "common.h"
@@ -67,14 +71,15 @@ __device__ __forceinline__ void block_of(int b, const int32_t *order, int kv_sha
 // the wave then needs about 400 registers, so each SIMD runs one wave and the
 // overlap of matrix and vector work comes from the pipelining alone. With
 // QT = 1 two workgroups of four waves share a CU, two waves per SIMD.
-template <int D, int BK, int ST, int QT, bool LSE>
+template <int D, int BK, int ST, int QT, bool LSE, bool TOK>
 __global__ void __launch_bounds__(BK * 2 / QT, QT == 1 ? 2 : 1)
 attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
                       const uint16_t *__restrict__ vp, uint16_t *__restrict__ op,
                       float *__restrict__ lse, const int32_t *__restrict__ blk_len,
                       const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt,
                       const int32_t *__restrict__ order, int max_kv, int kv_shared, int nh,
-                      int nb, float scale_log2) {
+                      int nb, float scale_log2, const int32_t *__restrict__ perm,
+                      int64_t q_stride, int64_t o_stride) {
   constexpr int NW = BK / (32 * QT);
   constexpr int CPR = D / 8;
   constexpr int NS = BK / ST;   // stages per key block
@@ -153,12 +158,29 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     }
   };
 
+  // Q rows: reordered layout, or the token-major tensor through perm
+  int qtok[QT];
   bf16x8 qf[QT][DK];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const uint16_t *qrow = qp + head_off + static_cast<int64_t>(I * BK + qrow0 + qt * 32) * D + g * 8;
+    const int qslot = I * BK + qrow0 + qt * 32;
+    const uint16_t *qrow;
+    if constexpr (TOK) {
+      qtok[qt] = perm[qslot];
+      qrow = qp + static_cast<int64_t>(max(qtok[qt], 0)) * q_stride + h * D + g * 8;
+    } else {
+      qtok[qt] = 0;
+      qrow = qp + head_off + static_cast<int64_t>(qslot) * D + g * 8;
+    }
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) qf[qt][ks] = *reinterpret_cast<const bf16x8 *>(qrow + ks * 16);
+    // Pad query rows are zero, as in the reordered layout: their scores then
+    // never trigger the wave-wide lazy rescale, so real rows round exactly as
+    // they do there.
+    if (TOK && qtok[qt] < 0) {
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) qf[qt][ks] = bf16x8{};
+    }
   }
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt)
@@ -335,18 +357,22 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     const float l_tot = l_run[qt] + __shfl_xor(l_run[qt], 32, 64);
     const bool real = row < blk_len[I];
     const float inv = (real && l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    uint16_t *orow = op + head_off + static_cast<int64_t>(qslot) * D;
+    uint16_t *orow = TOK ? op + static_cast<int64_t>(max(qtok[qt], 0)) * o_stride + h * D
+                         : op + head_off + static_cast<int64_t>(qslot) * D;
+    // the token layout has no pad rows: only real slots store
+    if (!TOK || (real && qtok[qt] >= 0)) {
 #pragma unroll
-    for (int md = 0; md < DM; ++md)
+      for (int md = 0; md < DM; ++md)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d0 = md * 32 + i4 * 8 + g * 4;
-        const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(oacc[qt][md][i4 * 4 + 0] * inv)) |
-                            (static_cast<uint32_t>(f32_to_bf16(oacc[qt][md][i4 * 4 + 1] * inv)) << 16);
-        const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(oacc[qt][md][i4 * 4 + 2] * inv)) |
-                            (static_cast<uint32_t>(f32_to_bf16(oacc[qt][md][i4 * 4 + 3] * inv)) << 16);
-        *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(w0, w1);
-      }
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = md * 32 + i4 * 8 + g * 4;
+          const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(oacc[qt][md][i4 * 4 + 0] * inv)) |
+                              (static_cast<uint32_t>(f32_to_bf16(oacc[qt][md][i4 * 4 + 1] * inv)) << 16);
+          const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(oacc[qt][md][i4 * 4 + 2] * inv)) |
+                              (static_cast<uint32_t>(f32_to_bf16(oacc[qt][md][i4 * 4 + 3] * inv)) << 16);
+          *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(w0, w1);
+        }
+    }
     if constexpr (LSE) {
       const float e_tot = e_run[qt] + __shfl_xor(e_run[qt], 32, 64);
       if (g == 0) {
@@ -364,7 +390,8 @@ attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
                 const float *__restrict__ vp, float *__restrict__ op, float *__restrict__ lse,
                 const int32_t *__restrict__ blk_len, const int32_t *__restrict__ kv_idx,
                 const int32_t *__restrict__ kv_cnt, const int32_t *__restrict__ order, int max_kv,
-                int kv_shared, int nh, int nb, float scale_log2) {
+                int kv_shared, int nh, int nb, float scale_log2, const int32_t *__restrict__ perm,
+                int64_t q_stride, int64_t o_stride) {
   __shared__ __attribute__((aligned(16))) float sK[BK * D];
   __shared__ __attribute__((aligned(16))) float sV[BK * D];
   int h, I;
@@ -372,10 +399,16 @@ attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
   const int tid = threadIdx.x;
   const int64_t head_off = static_cast<int64_t>(h) * nb * BK * D;
   const int qslot = I * BK + tid;
+  // token-layout I/O when perm is given (pad slots: zero query, no store)
+  const int tok = perm ? perm[qslot] : 0;
+  const int64_t qofs = perm ? static_cast<int64_t>(max(tok, 0)) * q_stride + h * D
+                            : head_off + static_cast<int64_t>(qslot) * D;
+  const int64_t oofs = perm ? static_cast<int64_t>(max(tok, 0)) * o_stride + h * D
+                            : head_off + static_cast<int64_t>(qslot) * D;
   float q[D], o[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    q[d] = qp[head_off + static_cast<int64_t>(qslot) * D + d] * scale_log2;
+    q[d] = (perm && tok < 0) ? 0.f : qp[qofs + d] * scale_log2;
     o[d] = 0.f;
   }
   float m = -1e30f, l = 0.f;
@@ -412,8 +445,10 @@ attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
   }
   const bool real = tid < blk_len[I];
   const float inv = (real && l > 0.f) ? 1.f / l : 0.f;
+  if (!perm || (real && tok >= 0)) {
 #pragma unroll
-  for (int d = 0; d < D; ++d) op[head_off + static_cast<int64_t>(qslot) * D + d] = o[d] * inv;
+    for (int d = 0; d < D; ++d) op[oofs + d] = o[d] * inv;
+  }
   if (lse != nullptr) lse[static_cast<int64_t>(h) * nb * BK + qslot] = real ? (m + log2f(l)) * 0.6931471805599453f : 0.f;
 }
 
@@ -485,7 +520,8 @@ static void launch_k(K kernel, dim3 grid, dim3 block, hipStream_t stream, A... a
 hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *op, float *lse,
                          const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
                          const int32_t *order, int max_kv, int kv_shared, int nh, int nb, int B,
-                         int D, int dtype, float scale, hipStream_t stream) {
+                         int D, int dtype, float scale, const int32_t *perm, int64_t q_stride,
+                         int64_t o_stride, hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid(nh * nb);
   if (dtype == HSA_BF16) {
@@ -493,24 +529,30 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                    *v = static_cast<const uint16_t *>(vp);
     uint16_t *o = static_cast<uint16_t *>(op);
     const dim3 block(B * 2);
-#define HSA_ATTN_BF16(DD, BB, QQ, L)                                                          \
-  launch_k(hsa::attn_bf16_pipe_kernel<DD, BB, (QQ == 2 ? 32 : 64), QQ, L>, grid, dim3(BB * 2 / QQ), stream, q, k, v, o, \
-           lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2)
+#define HSA_ATTN_BF16(DD, BB, QQ, L, TK)                                                      \
+  launch_k(hsa::attn_bf16_pipe_kernel<DD, BB, (QQ == 2 ? 32 : 64), QQ, L, TK>, grid, dim3(BB * 2 / QQ), stream, q, \
+           k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, o_stride)
+#define HSA_ATTN_BF16_IO(DD, BB)                                      \
+  do {                                                                \
+    if (perm) { if (L) HSA_ATTN_BF16(DD, BB, 1, true, true); else HSA_ATTN_BF16(DD, BB, 1, false, true); } \
+    else { if (L) HSA_ATTN_BF16(DD, BB, 1, true, false); else HSA_ATTN_BF16(DD, BB, 1, false, false); }    \
+  } while (0)
     const bool L = lse != nullptr;
-    if (D == 128 && B == 128) { if (L) HSA_ATTN_BF16(128, 128, 1, true); else HSA_ATTN_BF16(128, 128, 1, false); }
-    else if (D == 64 && B == 128) { if (L) HSA_ATTN_BF16(64, 128, 1, true); else HSA_ATTN_BF16(64, 128, 1, false); }
-    else if (D == 128 && B == 64) { if (L) HSA_ATTN_BF16(128, 64, 1, true); else HSA_ATTN_BF16(128, 64, 1, false); }
-    else { if (L) HSA_ATTN_BF16(64, 64, 1, true); else HSA_ATTN_BF16(64, 64, 1, false); }
+    if (D == 128 && B == 128) HSA_ATTN_BF16_IO(128, 128);
+    else if (D == 64 && B == 128) HSA_ATTN_BF16_IO(64, 128);
+    else if (D == 128 && B == 64) HSA_ATTN_BF16_IO(128, 64);
+    else HSA_ATTN_BF16_IO(64, 64);
+#undef HSA_ATTN_BF16_IO
 #undef HSA_ATTN_BF16
   } else {
     const float *q = static_cast<const float *>(qp), *k = static_cast<const float *>(kp),
                 *v = static_cast<const float *>(vp);
     float *o = static_cast<float *>(op);
     const dim3 block(B);
-    if (D == 128 && B == 128) launch_k(hsa::attn_f32_kernel<128, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2);
-    else if (D == 64 && B == 128) launch_k(hsa::attn_f32_kernel<64, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2);
-    else if (D == 128 && B == 64) launch_k(hsa::attn_f32_kernel<128, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2);
-    else launch_k(hsa::attn_f32_kernel<64, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2);
+    if (D == 128 && B == 128) launch_k(hsa::attn_f32_kernel<128, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, o_stride);
+    else if (D == 64 && B == 128) launch_k(hsa::attn_f32_kernel<64, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, o_stride);
+    else if (D == 128 && B == 64) launch_k(hsa::attn_f32_kernel<128, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, o_stride);
+    else launch_k(hsa::attn_f32_kernel<64, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, o_stride);
   }
   return check_launch("hsa_attn");
 }

@@ -88,9 +88,11 @@ perm_gather_kernel(PermArgs a, const int32_t *__restrict__ perm, int n_pad, int 
       const int j = j0 + u;
       if (j < slots) {
         const int64_t row = static_cast<int64_t>(slot0 + j) * cpr * 16;
+        if (dst != nullptr) {  // null: the tensor is only pooled
 #pragma unroll
-        for (int k = 0; k < NP; ++k)
-          if (pos[k] < P) *reinterpret_cast<uint4 *>(dst + dofs[k] + row) = v[u][k];
+          for (int k = 0; k < NP; ++k)
+            if (pos[k] < P) *reinterpret_cast<uint4 *>(dst + dofs[k] + row) = v[u][k];
+        }
         if (pool) {
           real += tok[u] >= 0;
 #pragma unroll

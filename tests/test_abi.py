@@ -50,7 +50,7 @@ def _err(B, status):
 
 def test_version_and_strings(B):
     L = B.lib()
-    assert L.hsa_abi_version() == 3
+    assert L.hsa_abi_version() == 4
     assert L.hsa_status_str(0) == b"ok"
     assert L.hsa_status_str(5) == b"workspace too small"
 
@@ -95,6 +95,11 @@ def test_perm_validation(B):
     assert L.hsa_perm(2, arr, arr, FAKE, 10, 16, 2, 64, 128, 1, 24, FAKE, NULL) == 4    # pool_s
     assert L.hsa_perm(2, arr, arr, FAKE, 10, 24, 2, 64, 128, 1, 16, FAKE, NULL) == 2    # pool_s | n_pad
     assert L.hsa_perm(1, arr, arr, FAKE, 10, 16, 2, 64, 128, 1, 16, FAKE, NULL) == 6    # needs Q and K
+    # a null output is a pooled-only tensor: allowed for tensors 0 and 1 when pooling, never else
+    some_null = (ctypes.c_void_p * 3)(None, FAKE.value, FAKE.value)
+    assert L.hsa_perm(3, arr, some_null, FAKE, 10, 16, 2, 64, 128, 1, *P, NULL) == 1
+    last_null = (ctypes.c_void_p * 3)(FAKE.value, FAKE.value, None)
+    assert L.hsa_perm(3, arr, last_null, FAKE, 10, 16, 2, 64, 128, 1, 16, FAKE, NULL) == 1
 
 
 def test_score_validation(B):
@@ -177,6 +182,17 @@ def test_attn_and_unperm_validation(B):
     assert L.hsa_attn_order(FAKE, 0, 4, 4, FAKE, NULL) == 2
     assert L.hsa_attn_order(FAKE, 2, 4, 4096, FAKE, NULL) == 4                                   # max_kv
     assert L.hsa_attn_order(FAKE, 1 << 16, 1 << 16, 4, FAKE, NULL) == 4                          # G*nb
+    # hsa_attn_tokens(q, q_stride, kp, vp, o, o_stride, lse, perm, N, blk_len, kv_idx, kv_cnt,
+    #                 order, max_kv, kv_shared, nh, nb, B, D, dtype, scale, stream)
+    def tok(q_stride=128, o_stride=128, perm=FAKE, N=200, B_=64, order=NULL):
+        return L.hsa_attn_tokens(FAKE, q_stride, FAKE, FAKE, FAKE, o_stride, NULL, perm, N, FAKE, FAKE,
+                                 FAKE, order, 4, 0, 2, 4, B_, 64, 1, 0.125, NULL)
+    assert tok(perm=NULL) == 1
+    assert tok(N=0) == 2 and tok(N=257) == 2                                                     # N vs nb*B
+    assert tok(q_stride=100) == 2 and tok(o_stride=64) == 2                                      # stride < nh*D
+    assert tok(q_stride=132) == 6 and tok(o_stride=132) == 6                                     # 16-byte rows
+    assert tok(B_=96) == 4
+    assert tok(order=ctypes.c_void_p(0x10002)) == 6
     assert L.hsa_unperm(FAKE, FAKE, FAKE, 10, 8, 2, 64, 128, 1, NULL) == 2
     assert L.hsa_unperm(FAKE, NULL, FAKE, 10, 16, 2, 64, 128, 1, NULL) == 1
 
@@ -191,4 +207,4 @@ def test_header_is_plain_c_and_links(tmp_path):
     assert build.returncode == 0, build.stderr
     run = subprocess.run([str(exe)], capture_output=True, text=True)
     assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
-    assert run.stdout.startswith("ok 3 workspace too small")
+    assert run.stdout.startswith("ok 4 workspace too small")

@@ -223,10 +223,10 @@ def test_select_ties_and_edges(hsa):
 
 # ---------------------------------------------------------------- attention / layer
 
-def _layer(hsa, w, step, mask=None):
+def _layer(hsa, w, step, mask=None, fused_io=True):
     _say(f"  generating inputs for workload {w.idx} step {step}")
     q, k, v = (x.to(dev()) for x in wl.make_qkv(w, step))
-    L = hsa.layer_for_workload(w, device=dev())
+    L = hsa.layer_for_workload(w, device=dev(), fused_io=fused_io)
     if mask is not None:
         L.reorder(q, k, v)
         L.kv_idx.copy_(mask[0])
@@ -253,7 +253,8 @@ def _check_layer(hsa, w, step, q, k, v, L, o, check_select=True):
     qp, kp, vp = (oracle.gather(x.cpu(), perm) for x in (q, k, v))
     rows = attn_rows(w, step, perm)
     ref_op, ref_lse = oracle.attn_blocks(qp, kp, vp, perm, w.B, kv_idx, kv_cnt, rows=rows)
-    op = to_np(L.op)
+    # with token-layout I/O the kernel wrote token order: view it per slot
+    op = oracle.gather(to_np(o), perm) if L.fused_io else to_np(L.op)
     err = max_err_rows(op, ref_op, rows)
     lse_err = max_err_rows(to_np(L.lse)[:, :, None], ref_lse[:, :, None], rows)
     omax = max(float(np.abs(ref_op[h, r]).max()) for h, r in enumerate(rows))
@@ -261,9 +262,10 @@ def _check_layer(hsa, w, step, q, k, v, L, o, check_select=True):
          f"lse err = {lse_err:.3e}, rows/head = {len(rows[0])}")
     assert err <= TOL[w.dtype]
     assert lse_err <= (1e-4 if w.dtype == "f32" else 1e-3)
-    assert np.all(op[:, perm < 0] == 0), "pad query rows must be zero"
-    # the restored output is exactly the reordered output scattered back
-    assert np.array_equal(to_np(o), oracle.scatter(op, perm, w.N))
+    if not L.fused_io:
+        assert np.all(op[:, perm < 0] == 0), "pad query rows must be zero"
+        # the restored output is exactly the reordered output scattered back
+        assert np.array_equal(to_np(o), oracle.scatter(op, perm, w.N))
 
 
 @pytest.mark.parametrize("idx", [1, 2])
@@ -326,7 +328,7 @@ def test_block_mass_and_recall(hsa):
     and the recall of the selected lists, against the oracle."""
     w = wl.get(2)
     _say("block mass / recall (workload 2)")
-    q, k, v, L, o = _layer(hsa, w, 0)
+    q, k, v, L, o = _layer(hsa, w, 0, fused_io=False)
     perm = L.perm.cpu().numpy().astype(np.int64)
     real = np.nonzero(perm >= 0)[0]
     rng = np.random.default_rng(12)
@@ -361,6 +363,46 @@ def test_cached_mask_step(hsa):
     torch.cuda.synchronize()
     assert torch.equal(L.kv_idx, mask0[0])
     _check_layer(hsa, w, 2, q2, k2, v2, L, o, check_select=False)
+
+
+@pytest.mark.parametrize("idx,step", [(1, 0), (2, 0), (3, 0), (4, 3), (5, 9), (6, 0)])
+def test_token_io_equals_five_passes(hsa, idx, step):
+    """hsa_attn_tokens (Q gathered and O scattered inside the attention
+    kernel) gives bit for bit the output of hsa_perm(Q) -> hsa_attn ->
+    hsa_unperm on the same lists, and the same lse."""
+    w = wl.get(idx)
+    _say(f"token-layout I/O vs five passes, workload {idx} step {step}")
+    q, k, v, L, o = _layer(hsa, w, step, fused_io=False)
+    o5 = o.clone()
+    lse5 = L.lse.clone()
+    L.fused_io = True
+    L.lse.fill_(float("nan"))
+    o.fill_(float("nan"))
+    L.reorder(q, k, v, pool=False)   # K and V only; Q stays in token order
+    L.attend()
+    ot = L.restore()
+    torch.cuda.synchronize()
+    assert ot.data_ptr() == o.data_ptr()
+    assert torch.equal(ot, o5)
+    real = (L.perm >= 0)
+    assert torch.equal(L.lse[:, real], lse5[:, real])
+
+
+def test_token_io_strided_buffers(hsa):
+    """Q read in place from a fused [N, 3, heads, D] projection buffer and the
+    output written into every other row group of a wider buffer: the rows in
+    between stay untouched."""
+    w = wl.get(2)
+    _say("token-layout I/O with strided Q and output")
+    q, k, v, L, o = _layer(hsa, w, 0, fused_io=False)
+    fused = torch.stack([q[0], k[0], v[0]], dim=1)[None]          # [1, N, 3, nh, D]
+    wide = torch.full((1, w.N, 2, w.heads, w.D), 7.0, dtype=q.dtype, device=dev())
+    out, _ = hsa.hsa_attn_tokens(fused[:, :, 0], L.xp[1], L.xp[2], L.perm, L.blk_len, L.kv_idx,
+                                 L.kv_cnt, w.B, want_lse=False, out=wide[:, :, 1])
+    torch.cuda.synchronize()
+    assert out.stride(1) == 2 * w.heads * w.D
+    assert torch.equal(wide[:, :, 1], o)
+    assert torch.all(wide[:, :, 0] == 7.0)
 
 
 @pytest.mark.parametrize("B,D,dtype", [(64, 64, "bf16"), (128, 128, "bf16"), (64, 128, "bf16"),
@@ -531,7 +573,7 @@ def test_attn_bwd_wan_shape_sampled(hsa):
     do = torch.randn(q.shape, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
     from dataclasses import replace
     w2 = replace(w, heads=2)
-    L = hsa.layer_for_workload(w2, device=dev())
+    L = hsa.layer_for_workload(w2, device=dev(), fused_io=False)
     L.step(q.to(dev()), k.to(dev()), v.to(dev()))
     dop = hsa.hsa_perm([do.to(dev())], L.perm, L.n_pad)[0]
     dq, dk, dv = hsa.hsa_attn_bwd(*L.xp, L.op, dop, L.lse, L.blk_len, L.kv_idx, L.kv_cnt, w.B)
