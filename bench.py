@@ -97,7 +97,7 @@ def _time_backward(hsa, L, qkv, K, stream, flop_fwd):
     tile pair); the kernels compute seven (S and dP in both passes)."""
     import torch
     L.want_lse = True
-    L.fused_io = False   # the backward reads Qp and Op in the reordered layout
+    L.io = "reordered"   # the backward reads Qp, Kp, Vp and Op in the reordered layout
     if L.lse is None:
         L.lse = torch.empty((L.heads, L.n_pad), dtype=torch.float32, device=L.op.device)
     L.reorder(*qkv, pool=False)
@@ -150,9 +150,10 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="also time the attention backward (hsa_attn_bwd) on the layer's lists")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--unfused", action="store_true",
-                    help="five separate passes: reorder Q too and restore with hsa_unperm "
-                         "instead of the attention kernel's token-layout loads and stores")
+    ap.add_argument("--io", choices=["reordered", "tokens_qo", "tokens"], default="tokens_qo",
+                    help="where the reorders happen: five separate passes (reordered), the "
+                         "attention kernel reading Q / writing O in token order (tokens_qo), "
+                         "or also gathering K/V rows itself (tokens)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one device-to-device copy of this many MiB (a kernel of known "
                          "traffic, to scale hardware byte counters)")
@@ -175,7 +176,7 @@ def main():
     dev = torch.device("cuda:0")
     sets_cpu = [wl.make_qkv(w, s) for s in range(2)]
     sets = [tuple(x.to(dev) for x in s) for s in sets_cpu]
-    L = hsa.layer_for_workload(w, device=dev, want_lse=False, fused_io=not args.unfused)
+    L = hsa.layer_for_workload(w, device=dev, want_lse=False, io=args.io)
     nb, B, D, nh, N = L.nb, w.B, w.D, w.heads, w.N
     esz = 2 if w.dtype == "bf16" else 4
     stream = torch.cuda.current_stream()
@@ -312,13 +313,15 @@ def main():
     U = L.n_pad // w.s if scored else 0
     pooled_bytes = 2 * nh * U * D * 4
     G = L.kv_idx.shape[0]
-    fused = L.fused_io
+    io = L.io
     stage_bytes = {
-        # Q, K, V read and written once, plus the Q/K sub-block means; with
-        # token-layout attention I/O only K and V are written (Q is read for
-        # its means on refresh steps, and by the attention kernel itself)
-        "perm": ((4 * row + (row + pooled_bytes if scored else 0)) if fused
-                 else 3 * 2 * row + pooled_bytes),
+        # reordered: Q, K, V read and written once, plus the Q/K sub-block
+        # means. tokens_qo: only K and V are reordered (Q is read for its
+        # means on refresh steps). tokens: nothing is reordered; Q and K are
+        # read for their means on refresh steps only.
+        "perm": {"reordered": 3 * 2 * row + pooled_bytes,
+                 "tokens_qo": 4 * row + ((row + pooled_bytes) if scored else 0),
+                 "tokens": (2 * row + pooled_bytes) if scored else 0}[io],
         "score": pooled_bytes + nh * nb * nb * 4,
         # S read (scored modes) and the lists written
         "select": (nh * nb * nb * 4 if scored else 0) + G * nb * (L.max_kv + 1) * 4,
@@ -328,7 +331,8 @@ def main():
     stages = {}
     for n in names:
         t = stage_ms[n] * 1e-3
-        if (n == "score" and not scored) or (n == "unperm" and fused):
+        if ((n == "score" and not scored) or (n == "unperm" and io != "reordered")
+                or (n == "perm" and stage_bytes["perm"] == 0)):
             continue
         if n == "attn":
             stages[n] = {"ms": stage_ms[n], "tflops_computed_tiles": achieved,
@@ -365,8 +369,10 @@ def main():
                                if w.idx == 3 else w.name,
                    "tokens": N, "heads": nh, "head_dim": D, "block": B, "sub_block": w.s,
                    "order": w.order, "keep": _keep_text(w, L, nb, tiles_steps, nh),
-                   "io": ("attention reads Q and writes O in token order (no unperm pass)"
-                          if fused else "five passes (reorder Q/K/V, attention, unperm)"),
+                   "io": {"reordered": "five passes (reorder Q/K/V, attention, unperm)",
+                          "tokens_qo": "K/V reordered; attention reads Q and writes O in token order",
+                          "tokens": "attention gathers Q/K/V rows and writes O in token order; "
+                                    "the reorder pass only pools Q/K on refresh steps"}[io],
                    "batch": 1},
         "ms_per_step_p10_p50_p90": [float(np.percentile(per_step, p)) for p in (10, 50, 90)],
         "ms_per_layer_cached_mask": ms_cached,

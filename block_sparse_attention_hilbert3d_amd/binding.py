@@ -48,7 +48,7 @@ _SIGS = {
     "hsa_select_list_width": (_c_i32, [_c_i32, _c_i32, ctypes.POINTER(SelectParams)]),
     "hsa_select": (ctypes.c_int, [_p, _c_i32, _c_i32, ctypes.POINTER(SelectParams), _p, _p, _c_i32, _p, _c_sz, _p]),
     "hsa_attn": (ctypes.c_int, [_p] * 9 + [_c_i32] * 7 + [_c_f32, _p]),
-    "hsa_attn_tokens": (ctypes.c_int, [_p, _c_i64, _p, _p, _p, _c_i64, _p, _p, _c_i32, _p, _p, _p, _p]
+    "hsa_attn_tokens": (ctypes.c_int, [_p] * 4 + [_c_i64] * 3 + [_p, _p, _c_i32, _p, _p, _p, _p]
                         + [_c_i32] * 7 + [_c_f32, _p]),
     "hsa_attn_order": (ctypes.c_int, [_p, _c_i32, _c_i32, _c_i32, _p, _p]),
     "hsa_unperm": (ctypes.c_int, [_p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _p]),
@@ -243,18 +243,26 @@ def hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B: int, scale: float | None = 
     return out, (lse if want_lse else None)
 
 
-def hsa_attn_tokens(q, kp, vp, perm, blk_len, kv_idx, kv_cnt, B: int, scale: float | None = None,
+def hsa_attn_tokens(q, k, v, perm, blk_len, kv_idx, kv_cnt, B: int, scale: float | None = None,
                     want_lse: bool = True, out=None, lse=None, order=None):
     """q [1, N, nh, D] token-major (token stride may exceed nh*D, e.g. a slice of a fused QKV
-    buffer); kp, vp [nh, n_pad, D] reordered -> (o [1, N, nh, D], lse float32 [nh, n_pad] or
-    None). Equals hsa_unperm(hsa_attn(Qp, kp, vp, ...)) with the reorder of Q and the inverse
-    reorder of the output done inside the attention kernel."""
-    _need_device(kp, vp, perm, blk_len, kv_idx, kv_cnt, order)
+    buffer); k, v either token-major like q (same token stride) or reordered [nh, n_pad, D]
+    (hsa_perm outputs) -> (o [1, N, nh, D], lse float32 [nh, n_pad] or None). Equals
+    hsa_unperm(hsa_attn(Qp, Kp, Vp, ...)) with the reorders done inside the attention kernel."""
+    _need_device(perm, blk_len, kv_idx, kv_cnt, order)
     _, N, nh, D = q.shape
-    if not q.is_cuda or q.stride(3) != 1 or q.stride(2) != D:
-        raise HsaError("hsa_attn_tokens: q must be a device tensor with contiguous heads and head dim")
-    n_pad = kp.shape[1]
+    for x in (q, k, v):
+        if not x.is_cuda or x.stride(-1) != 1 or (x.dim() == 4 and x.stride(2) != D):
+            raise HsaError("hsa_attn_tokens: device tensors with contiguous heads and head dim")
+    n_pad = perm.numel()
     nb = n_pad // B
+    if k.dim() == 4:
+        if k.stride(1) != v.stride(1) or k.shape != q.shape or v.shape != q.shape:
+            raise HsaError("hsa_attn_tokens: token-major k and v must match q and share a stride")
+        kv_stride = k.stride(1)
+    else:
+        _need_device(k, v)
+        kv_stride = 0
     shared = 1 if kv_idx.shape[0] == 1 and nh > 1 else 0
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     if out is None:
@@ -263,10 +271,11 @@ def hsa_attn_tokens(q, kp, vp, perm, blk_len, kv_idx, kv_cnt, B: int, scale: flo
         raise HsaError("hsa_attn_tokens: heads and head dim of the output must be contiguous")
     if want_lse and lse is None:
         lse = torch.empty((nh, n_pad), dtype=torch.float32, device=q.device)
-    _check(lib().hsa_attn_tokens(_ptr(q), q.stride(1), _ptr(kp), _ptr(vp), _ptr(out), out.stride(1),
-                                 _ptr(lse if want_lse else None), _ptr(perm), N, _ptr(blk_len),
-                                 _ptr(kv_idx), _ptr(kv_cnt), _ptr(order), kv_idx.shape[-1], shared,
-                                 nh, nb, B, D, _dtype_code(q), scale, _stream()), "hsa_attn_tokens")
+    _check(lib().hsa_attn_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(out), q.stride(1), kv_stride,
+                                 out.stride(1), _ptr(lse if want_lse else None), _ptr(perm), N,
+                                 _ptr(blk_len), _ptr(kv_idx), _ptr(kv_cnt), _ptr(order),
+                                 kv_idx.shape[-1], shared, nh, nb, B, D, _dtype_code(q), scale,
+                                 _stream()), "hsa_attn_tokens")
     return out, (lse if want_lse else None)
 
 

@@ -48,7 +48,7 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                          const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
                          const int32_t *order, int max_kv, int kv_shared, int nh, int nb, int B,
                          int D, int dtype, float scale, const int32_t *perm, int64_t q_stride,
-                         int64_t o_stride, hipStream_t stream);
+                         int64_t kv_stride, int64_t o_stride, hipStream_t stream);
 size_t attn_bwd_ws_bytes(int nh, int nb, int B, int G);
 hsa_status_t launch_attn_bwd(const void *qp, const void *kp, const void *vp, const void *op, const void *dop,
                              const float *lse, const int32_t *blk_len, const int32_t *kv_idx,
@@ -350,35 +350,39 @@ hsa_status_t hsa_attn(const void *qp, const void *kp, const void *vp, void *op, 
   if (!aligned16(qp) || !aligned16(kp) || !aligned16(vp) || !aligned16(op)) return fail(HSA_ERR_BAD_ARG, "hsa_attn: tensors must be 16-byte aligned");
   if (order && !aligned4(order)) return fail(HSA_ERR_BAD_ARG, "hsa_attn: order must be 4-byte aligned");
   return launch_attn(qp, kp, vp, op, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, B, D, dtype, scale,
-                     nullptr, 0, 0, static_cast<hipStream_t>(stream));
+                     nullptr, 0, 0, 0, static_cast<hipStream_t>(stream));
 }
 
-hsa_status_t hsa_attn_tokens(const void *q, int64_t q_stride, const void *kp, const void *vp, void *o,
-                             int64_t o_stride, float *lse, const int32_t *perm, int32_t N,
-                             const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
-                             const int32_t *order, int32_t max_kv, int32_t kv_shared, int32_t nh,
-                             int32_t nb, int32_t B, int32_t D, int32_t dtype, float scale,
-                             hsa_stream_t stream) {
+hsa_status_t hsa_attn_tokens(const void *q, const void *k, const void *v, void *o, int64_t q_stride,
+                             int64_t kv_stride, int64_t o_stride, float *lse, const int32_t *perm,
+                             int32_t N, const int32_t *blk_len, const int32_t *kv_idx,
+                             const int32_t *kv_cnt, const int32_t *order, int32_t max_kv,
+                             int32_t kv_shared, int32_t nh, int32_t nb, int32_t B, int32_t D,
+                             int32_t dtype, float scale, hsa_stream_t stream) {
   g_last_error.clear();
-  if (!q || !kp || !vp || !o || !perm || !blk_len || !kv_idx || !kv_cnt) return fail(HSA_ERR_NULL_PTR, "hsa_attn_tokens: null input or output");
+  if (!q || !k || !v || !o || !perm || !blk_len || !kv_idx || !kv_cnt) return fail(HSA_ERR_NULL_PTR, "hsa_attn_tokens: null input or output");
   hsa_status_t st;
   if ((st = check_dtype(dtype)) != HSA_OK || (st = check_D(D)) != HSA_OK || (st = check_B(B)) != HSA_OK) return st;
   if (nh < 1 || nb < 1 || max_kv < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn_tokens: nh=%d nb=%d max_kv=%d", nh, nb, max_kv);
   if (static_cast<int64_t>(nh) * nb >= (1ll << 31)) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn_tokens: too many blocks");
   if (N < 1 || static_cast<int64_t>(N) > static_cast<int64_t>(nb) * B) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn_tokens: N=%d outside 1..nb*B", N);
   const int es = esize_of(dtype);
-  const int64_t strides[2] = {q_stride, o_stride};
+  const int64_t strides[3] = {q_stride, o_stride, kv_stride > 0 ? kv_stride : static_cast<int64_t>(nh) * D};
   for (const int64_t ts : strides) {
     if (ts < static_cast<int64_t>(nh) * D) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn_tokens: token stride %lld < nh*D", static_cast<long long>(ts));
     if ((ts * es) % 16 != 0) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: token strides must be multiples of 16 bytes");
     if (ts >= (1ll << 40) / N) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn_tokens: tensor too large");
   }
+  if (kv_stride < 0) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: kv_stride must be 0 (reordered K/V) or a token stride");
+  // gathered rows are addressed with 32-bit byte offsets from the tensor start
+  if (kv_stride > 0 && static_cast<int64_t>(N) * kv_stride * es > (1ll << 32) - 1)
+    return fail(HSA_ERR_UNSUPPORTED, "hsa_attn_tokens: token-major K/V span more than 4 GiB; reorder them with hsa_perm");
   if (kv_shared != 0 && kv_shared != 1) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: kv_shared must be 0 or 1");
   if (!(scale > 0.f) || !isfinite(scale)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: scale must be finite and positive");
-  if (!aligned16(q) || !aligned16(kp) || !aligned16(vp) || !aligned16(o)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: tensors must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: tensors must be 16-byte aligned");
   if (!aligned4(perm) || (order && !aligned4(order))) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: perm and order must be 4-byte aligned");
-  return launch_attn(q, kp, vp, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, B, D, dtype, scale,
-                     perm, q_stride, o_stride, static_cast<hipStream_t>(stream));
+  return launch_attn(q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, B, D, dtype, scale,
+                     perm, q_stride, kv_stride, o_stride, static_cast<hipStream_t>(stream));
 }
 
 hsa_status_t hsa_attn_order(const int32_t *kv_cnt, int32_t G, int32_t nb, int32_t max_kv,

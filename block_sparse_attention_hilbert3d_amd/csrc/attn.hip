@@ -28,10 +28,13 @@
 //    with v_readlane, keeping scalar memory round trips out of the loop;
 //  - epilogue divides by the row sum, rounds to bf16, zeroes pad rows and
 //    writes the natural-log log-sum-exp (from an unrounded fp32 sum).
-// Token-layout I/O (TOK): Q rows are read from, and output rows written to,
-// the token-major tensors through the slot -> token map, so the reorder of Q
-// and the inverse reorder of O happen inside this kernel's first loads and
-// last stores; pad slots take zero query rows and store nothing.
+// Token-layout I/O: Q rows are read from, and output rows written to, the
+// token-major tensors through the slot -> token map, so the reorder of Q and
+// the inverse reorder of O happen inside this kernel's first loads and last
+// stores; pad slots take zero query rows and store nothing. With gathered
+// K/V the direct LDS loads also fetch key/value rows from the token-major
+// tensors (each lane's source rows for a stage are looked up in the map one
+// iteration ahead), so no reordered copy of Q, K or V is made at all.
 // f32 kernel: a plain one-thread-per-query online-softmax loop with K/V tiles
 // in LDS, for float inputs (small shapes).
 #include "common.h"
@@ -71,7 +74,8 @@ __device__ __forceinline__ void block_of(int b, const int32_t *order, int kv_sha
 // the wave then needs about 400 registers, so each SIMD runs one wave and the
 // overlap of matrix and vector work comes from the pipelining alone. With
 // QT = 1 two workgroups of four waves share a CU, two waves per SIMD.
-template <int D, int BK, int ST, int QT, bool LSE, bool TOK>
+// IO: 0 reordered Q/K/V/O; 1 token-major Q and O; 2 token-major Q, K, V, O.
+template <int D, int BK, int ST, int QT, bool LSE, int IO>
 __global__ void __launch_bounds__(BK * 2 / QT, QT == 1 ? 2 : 1)
 attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
                       const uint16_t *__restrict__ vp, uint16_t *__restrict__ op,
@@ -79,7 +83,8 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
                       const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt,
                       const int32_t *__restrict__ order, int max_kv, int kv_shared, int nh,
                       int nb, float scale_log2, const int32_t *__restrict__ perm,
-                      int64_t q_stride, int64_t o_stride) {
+                      int64_t q_stride, int64_t kv_stride, int64_t o_stride) {
+  constexpr bool TOK = IO >= 1, GKV = IO == 2;
   constexpr int NW = BK / (32 * QT);
   constexpr int CPR = D / 8;
   constexpr int NS = BK / ST;   // stages per key block
@@ -106,14 +111,15 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   uint32_t koff[4], voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    koff[i] = tile_lane_offset<D, false>(i, lane);
-    voff[i] = tile_lane_offset<D, true>(i, lane);
+    koff[i] = GKV ? tile_lane_chunk<D, false>(i, lane) : tile_lane_offset<D, false>(i, lane);
+    voff[i] = GKV ? tile_lane_chunk<D, true>(i, lane) : tile_lane_offset<D, true>(i, lane);
   }
   const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
   const int cnt = kv_cnt[lrow];
   const int32_t *list = kv_idx + lrow * max_kv;
-  const uint16_t *kbase = kp + head_off;
-  const uint16_t *vbase = vp + head_off;
+  const uint16_t *kbase = GKV ? kp + h * D : kp + head_off;
+  const uint16_t *vbase = GKV ? vp + h * D : vp + head_off;
+  const uint32_t kv_row_bytes = static_cast<uint32_t>(kv_stride * 2);
   // Stage t covers keys (t % NS)*ST .. +ST of listed block t / NS. The
   // listed blocks and their real lengths sit in lanes (lane i of the lo/hi
   // pair holds entry mbase + i / mbase + 64 + i), so a stage's address and
@@ -146,6 +152,23 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     int J, L;
     entry(t / NS, J, L);
     return min(max(L - (t % NS) * ST, 0), ST);
+  };
+  // Gathered K/V: the token rows this lane's loads of stage t read (raw map
+  // entries; clamped to >= 0 before use). Uniform base, unsigned lane offset.
+  using TL = TileLoads<D, ST, NW>;
+  uint32_t prow[TL::NI];
+#pragma unroll
+  for (int i = 0; i < TL::NI; ++i) prow[i] = static_cast<uint32_t>(TL::row(w, i, lane));
+  auto stage_rows = [&](int t, int (&tok)[TL::NI]) {
+    int J, L;
+    entry(t / NS, J, L);
+    const int32_t *pr = perm + (J * BK + (t % NS) * ST);
+#pragma unroll
+    for (int i = 0; i < TL::NI; ++i) tok[i] = pr[prow[i]];
+  };
+  auto clamp_rows = [&](int (&tok)[TL::NI]) {
+#pragma unroll
+    for (int i = 0; i < TL::NI; ++i) tok[i] = max(tok[i], 0);
   };
   // keep entries (c + 1) / NS .. (c + 2) / NS inside the window
   auto slide = [&](int c) {
@@ -314,14 +337,39 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     }
   };
 
+  // Gathered K/V: source rows of the V stage issued next (rv), of the K
+  // stage issued next (rk) and of the stage after it (rn, in flight).
+  int rv[TL::NI], rk[TL::NI], rn[TL::NI];
+#pragma unroll
+  for (int i = 0; i < TL::NI; ++i) rv[i] = rk[i] = rn[i] = 0;
+
   // Prologue: K(0), V(0) and K(1) in flight, S(0) once all three landed.
   f32x16 sA[MT][QT], sB[MT][QT];
   if (nst > 0) {
-    issue_tile<D, ST, NW>(kbase + stage_ofs(0), ldsK, w, koff);
-    issue_tile<D, ST, NW>(vbase + stage_ofs(0), ldsV, w, voff);
-    if (nst > 1) issue_tile<D, ST, NW>(kbase + stage_ofs(1), ldsK + TILE * 2, w, koff);
+    if constexpr (GKV) {
+      stage_rows(0, rv);
+      if (nst > 1) stage_rows(1, rk);
+      wait_vmcnt<0>();
+      clamp_rows(rv);
+      clamp_rows(rk);
+      issue_tile_rows<D, ST, NW>(kbase, kv_row_bytes, ldsK, w, koff, rv);
+      issue_tile_rows<D, ST, NW>(vbase, kv_row_bytes, ldsV, w, voff, rv);
+      if (nst > 1) issue_tile_rows<D, ST, NW>(kbase, kv_row_bytes, ldsK + TILE * 2, w, koff, rk);
+      if (nst > 2) stage_rows(2, rn);
+    } else {
+      issue_tile<D, ST, NW>(kbase + stage_ofs(0), ldsK, w, koff);
+      issue_tile<D, ST, NW>(vbase + stage_ofs(0), ldsV, w, voff);
+      if (nst > 1) issue_tile<D, ST, NW>(kbase + stage_ofs(1), ldsK + TILE * 2, w, koff);
+    }
     // iteration 0 reads K(1) as well, so all three stages must have landed
     wait_vmcnt<0>();
+    if constexpr (GKV) {
+#pragma unroll
+      for (int i = 0; i < TL::NI; ++i) {
+        rv[i] = rk[i];            // V(1)
+        rk[i] = max(rn[i], 0);    // K(2)
+      }
+    }
     __syncthreads();
     compute_s(sA, 0);
     mask_and_rescale(sA, stage_valid(0));
@@ -332,8 +380,14 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     const bool has1 = c + 1 < nst, has2 = c + 2 < nst;
     __syncthreads();  // K(c) and V(c-1) buffers are free, K(c+1) and V(c) visible
     slide(c);
-    if (has2) issue_tile<D, ST, NW>(kbase + stage_ofs(c + 2), ldsK + (c & 1) * TILE * 2, w, koff);
-    if (has1) issue_tile<D, ST, NW>(vbase + stage_ofs(c + 1), ldsV + ((c + 1) & 1) * TILE * 2, w, voff);
+    if constexpr (GKV) {
+      if (c + 3 < nst) stage_rows(c + 3, rn);
+      if (has2) issue_tile_rows<D, ST, NW>(kbase, kv_row_bytes, ldsK + (c & 1) * TILE * 2, w, koff, rk);
+      if (has1) issue_tile_rows<D, ST, NW>(vbase, kv_row_bytes, ldsV + ((c + 1) & 1) * TILE * 2, w, voff, rv);
+    } else {
+      if (has2) issue_tile<D, ST, NW>(kbase + stage_ofs(c + 2), ldsK + (c & 1) * TILE * 2, w, koff);
+      if (has1) issue_tile<D, ST, NW>(vbase + stage_ofs(c + 1), ldsV + ((c + 1) & 1) * TILE * 2, w, voff);
+    }
     // Unconditional so it shares a scheduling region with exp_pv; on the
     // last stage it reads an idle buffer (no load in flight) and is unused.
     compute_s(nxt, (c + 1) & 1);
@@ -344,6 +398,13 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     // an empty mask on the last stage leaves the running max untouched
     mask_and_rescale(nxt, has1 ? stage_valid(c + 1) : 0);
     wait_vmcnt<0>();
+    if constexpr (GKV) {
+#pragma unroll
+      for (int i = 0; i < TL::NI; ++i) {
+        rv[i] = rk[i];            // V(c+2) reads K(c+2)'s rows
+        rk[i] = max(rn[i], 0);    // K(c+3)
+      }
+    }
   };
   for (int c = 0; c < nst; c += 2) {
     body(c, sA, sB);
@@ -391,7 +452,7 @@ attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
                 const int32_t *__restrict__ blk_len, const int32_t *__restrict__ kv_idx,
                 const int32_t *__restrict__ kv_cnt, const int32_t *__restrict__ order, int max_kv,
                 int kv_shared, int nh, int nb, float scale_log2, const int32_t *__restrict__ perm,
-                int64_t q_stride, int64_t o_stride) {
+                int64_t q_stride, int64_t kv_stride, int64_t o_stride) {
   __shared__ __attribute__((aligned(16))) float sK[BK * D];
   __shared__ __attribute__((aligned(16))) float sV[BK * D];
   int h, I;
@@ -418,11 +479,20 @@ attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
   for (int c = 0; c < cnt; ++c) {
     const int J = list[c];
     const int kvalid = blk_len[J];
-    const float4 *ks = reinterpret_cast<const float4 *>(kp + head_off + static_cast<int64_t>(J) * BK * D);
-    const float4 *vs = reinterpret_cast<const float4 *>(vp + head_off + static_cast<int64_t>(J) * BK * D);
-    for (int i = tid; i < BK * D / 4; i += BK) {
-      reinterpret_cast<float4 *>(sK)[i] = ks[i];
-      reinterpret_cast<float4 *>(sV)[i] = vs[i];
+    if (perm && kv_stride > 0) {  // K/V rows gathered from the token-major tensors
+      for (int i = tid; i < BK * D / 4; i += BK) {
+        const int r = i / (D / 4), c4 = i - r * (D / 4);
+        const int64_t src = static_cast<int64_t>(max(perm[J * BK + r], 0)) * kv_stride + h * D + c4 * 4;
+        reinterpret_cast<float4 *>(sK)[i] = *reinterpret_cast<const float4 *>(kp + src);
+        reinterpret_cast<float4 *>(sV)[i] = *reinterpret_cast<const float4 *>(vp + src);
+      }
+    } else {
+      const float4 *ks = reinterpret_cast<const float4 *>(kp + head_off + static_cast<int64_t>(J) * BK * D);
+      const float4 *vs = reinterpret_cast<const float4 *>(vp + head_off + static_cast<int64_t>(J) * BK * D);
+      for (int i = tid; i < BK * D / 4; i += BK) {
+        reinterpret_cast<float4 *>(sK)[i] = ks[i];
+        reinterpret_cast<float4 *>(sV)[i] = vs[i];
+      }
     }
     __syncthreads();
     for (int key = 0; key < kvalid; ++key) {
@@ -521,7 +591,7 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                          const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
                          const int32_t *order, int max_kv, int kv_shared, int nh, int nb, int B,
                          int D, int dtype, float scale, const int32_t *perm, int64_t q_stride,
-                         int64_t o_stride, hipStream_t stream) {
+                         int64_t kv_stride, int64_t o_stride, hipStream_t stream) {
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid(nh * nb);
   if (dtype == HSA_BF16) {
@@ -529,14 +599,17 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                    *v = static_cast<const uint16_t *>(vp);
     uint16_t *o = static_cast<uint16_t *>(op);
     const dim3 block(B * 2);
-#define HSA_ATTN_BF16(DD, BB, QQ, L, TK)                                                      \
-  launch_k(hsa::attn_bf16_pipe_kernel<DD, BB, (QQ == 2 ? 32 : 64), QQ, L, TK>, grid, dim3(BB * 2 / QQ), stream, q, \
-           k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, o_stride)
+#define HSA_ATTN_BF16(DD, BB, QQ, L, IO)                                                      \
+  launch_k(hsa::attn_bf16_pipe_kernel<DD, BB, (QQ == 2 ? 32 : 64), QQ, L, IO>, grid, dim3(BB * 2 / QQ), stream, q, \
+           k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, \
+           kv_stride, o_stride)
 #define HSA_ATTN_BF16_IO(DD, BB)                                      \
   do {                                                                \
-    if (perm) { if (L) HSA_ATTN_BF16(DD, BB, 1, true, true); else HSA_ATTN_BF16(DD, BB, 1, false, true); } \
-    else { if (L) HSA_ATTN_BF16(DD, BB, 1, true, false); else HSA_ATTN_BF16(DD, BB, 1, false, false); }    \
+    if (io == 2) { if (L) HSA_ATTN_BF16(DD, BB, 1, true, 2); else HSA_ATTN_BF16(DD, BB, 1, false, 2); }      \
+    else if (io == 1) { if (L) HSA_ATTN_BF16(DD, BB, 1, true, 1); else HSA_ATTN_BF16(DD, BB, 1, false, 1); } \
+    else { if (L) HSA_ATTN_BF16(DD, BB, 1, true, 0); else HSA_ATTN_BF16(DD, BB, 1, false, 0); }             \
   } while (0)
+    const int io = perm == nullptr ? 0 : (kv_stride > 0 ? 2 : 1);
     const bool L = lse != nullptr;
     if (D == 128 && B == 128) HSA_ATTN_BF16_IO(128, 128);
     else if (D == 64 && B == 128) HSA_ATTN_BF16_IO(64, 128);
@@ -549,10 +622,10 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                 *v = static_cast<const float *>(vp);
     float *o = static_cast<float *>(op);
     const dim3 block(B);
-    if (D == 128 && B == 128) launch_k(hsa::attn_f32_kernel<128, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, o_stride);
-    else if (D == 64 && B == 128) launch_k(hsa::attn_f32_kernel<64, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, o_stride);
-    else if (D == 128 && B == 64) launch_k(hsa::attn_f32_kernel<128, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, o_stride);
-    else launch_k(hsa::attn_f32_kernel<64, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, o_stride);
+    if (D == 128 && B == 128) launch_k(hsa::attn_f32_kernel<128, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
+    else if (D == 64 && B == 128) launch_k(hsa::attn_f32_kernel<64, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
+    else if (D == 128 && B == 64) launch_k(hsa::attn_f32_kernel<128, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
+    else launch_k(hsa::attn_f32_kernel<64, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
   }
   return check_launch("hsa_attn");
 }

@@ -108,6 +108,43 @@ __device__ __forceinline__ uint32_t tile_lane_offset(int i, int lane) {
   return static_cast<uint32_t>((lane / CPR) * D * 2 + c * 16);
 }
 
+// The logical chunk's byte offset within its row for load i of this lane
+// (the chunk part of tile_lane_offset), for tiles gathered row by row.
+template <int D, bool IS_V>
+__device__ __forceinline__ uint32_t tile_lane_chunk(int i, int lane) {
+  constexpr int CPR = D / 8;
+  const int r = i * (64 / CPR) + lane / CPR;
+  const int cs = lane & (CPR - 1);
+  const int c = IS_V ? (cs ^ (((r & 3) << 2) & (CPR - 1))) : (cs ^ (r & (CPR - 1)));
+  return static_cast<uint32_t>(c * 16);
+}
+
+// Loads per wave of one BKxD bf16 tile and the tile row that load i of a lane
+// covers: row (w*NI + i)*(64/CPR) + lane/CPR.
+template <int D, int BK, int NW>
+struct TileLoads {
+  static constexpr int CPR = D / 8;
+  static constexpr int NI = BK * CPR / (64 * NW);
+  static constexpr int RPL = 64 / CPR;  // rows per load instruction
+  __device__ static __forceinline__ int row(int w, int i, int lane) { return (w * NI + i) * RPL + lane / CPR; }
+};
+
+// Issue the direct loads of one BKxD bf16 tile whose rows are gathered:
+// this lane's load i reads gbase + tok[i] * row_bytes + coff[i & 3], where
+// tok[i] >= 0 is the source row of the tile row it fills. Offsets are 32-bit
+// (24-bit multiply: tok and row_bytes below 2^24, product below 2^32).
+template <int D, int BK, int NW>
+__device__ __forceinline__ void issue_tile_rows(const uint16_t *gbase, uint32_t row_bytes, uint32_t lds_tile,
+                                                int w, const uint32_t (&coff)[4],
+                                                const int (&tok)[TileLoads<D, BK, NW>::NI]) {
+  constexpr int NI = TileLoads<D, BK, NW>::NI;
+  static_assert(D / 8 == 8 || NI % 4 == 0, "the swizzle key must not depend on the wave");
+  const uint32_t lbase = lds_tile + w * NI * 1024;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    load_lds16(gbase, __umul24(static_cast<uint32_t>(tok[i]), row_bytes) + coff[i & 3], lbase + i * 1024);
+}
+
 // Issue the direct loads of one BKxD bf16 tile (row-major in HBM) into a
 // swizzled LDS tile; each wave moves NI consecutive 1 KB slices.
 template <int D, int BK, int NW>

@@ -5,10 +5,17 @@ reorder (hsa_perm) -> score (hsa_score) -> select (hsa_select) -> attend
 grid shape (hsa_plan). Buffers and workspaces are allocated once per layer
 so a step enqueues kernels only.
 
-With ``fused_io`` (the default) the reorder of Q and the restore of the
-output move into the attention kernel (hsa_attn_tokens): hsa_perm reorders
-K and V and only pools Q, and no hsa_unperm pass runs. The output is
-bit-identical to the five-pass form.
+``io`` chooses where the reorders happen; the output is bit-identical in
+all three forms:
+  "reordered"  the five passes above;
+  "tokens_qo"  (default) the attention kernel reads Q and writes the output
+               in token order (hsa_attn_tokens); hsa_perm reorders K and V
+               and only pools Q; no hsa_unperm pass;
+  "tokens"     the attention kernel also gathers K and V rows from the
+               token-major tensors; hsa_perm runs on refresh steps only, to
+               pool the Q/K sub-blocks that scoring needs. The per-stage row
+               lookups cost the attention kernel ~4 %, so this pays only
+               when lists are short (the reorder pass is then a larger share).
 
 Mask caching (DFSAttn, Methodology, design 3): ``step(..., reuse_mask=True)``
 skips scoring and selection and attends with the lists kept from the last
@@ -22,13 +29,15 @@ import torch
 
 from . import binding as B_
 
+IO_FORMS = ("reordered", "tokens_qo", "tokens")
+
 
 class SparseAttentionLayer:
     def __init__(self, T: int, H: int, W: int, heads: int, D: int, *, order: str, B: int,
                  select: str, s: int = 0, agg: str = "mass", k: int = 0, tau: float = 0.0,
                  C: int = 0, T_per: int = 1, lam: float = 0.0, delta: float = 0.0,
                  dtype=torch.bfloat16, device="cuda", want_lse: bool = True,
-                 fused_io: bool = True):
+                 io: str = "tokens_qo"):
         self.T, self.H, self.W, self.heads, self.D = T, H, W, heads, D
         self.N = T * H * W
         self.order, self.B, self.select, self.s, self.agg = order, B, select, s, agg
@@ -36,8 +45,10 @@ class SparseAttentionLayer:
         if select == "radial_dyn":
             self.agg = "max"   # the dynamic threshold reads pre-softmax logits
         self.dtype, self.device = dtype, device
-        self.fused_io = fused_io
-        self._q = None
+        if io not in IO_FORMS:
+            raise ValueError(f"io must be one of {IO_FORMS}")
+        self.io = io
+        self._qkv = None
         self.scale = 1.0 / math.sqrt(D)
         self.perm, self.blk_len = B_.hsa_plan(T, H, W, order, B, device=device)
         self.n_pad = self.perm.numel()
@@ -88,11 +99,15 @@ class SparseAttentionLayer:
                               T_per=self.T_per, step=step)
 
     def reorder(self, q, k, v, pool: bool = True):
-        """Gather Q/K/V (K/V only with fused_io); on steps that refresh the mask
-        also pool Q/K sub-blocks."""
-        self._q = q
+        """Gather what the io form keeps reordered; on steps that refresh the
+        mask also pool Q/K sub-blocks."""
+        self._qkv = (q, k, v)
         pool = pool and self.S is not None
-        if self.fused_io:
+        if self.io == "tokens":
+            if pool:
+                B_.hsa_perm([q, k], self.perm, self.n_pad, outs=[None, None], pool_s=self.s,
+                            pooled=self.pooled)
+        elif self.io == "tokens_qo":
             if pool:
                 B_.hsa_perm([q, k, v], self.perm, self.n_pad, outs=[None, self.xp[1], self.xp[2]],
                             pool_s=self.s, pooled=self.pooled)
@@ -116,8 +131,11 @@ class SparseAttentionLayer:
 
     def attend(self):
         qp, kp, vp = self.xp
-        if self.fused_io:
-            B_.hsa_attn_tokens(self._q, kp, vp, self.perm, self.blk_len, self.kv_idx, self.kv_cnt,
+        if self.io != "reordered":
+            q, k, v = self._qkv
+            if self.io == "tokens_qo":
+                k, v = kp, vp
+            B_.hsa_attn_tokens(q, k, v, self.perm, self.blk_len, self.kv_idx, self.kv_cnt,
                                self.B, self.scale, want_lse=self.want_lse, out=self.o,
                                lse=self.lse, order=self.order)
         else:
@@ -125,7 +143,7 @@ class SparseAttentionLayer:
                         want_lse=self.want_lse, out=self.op, lse=self.lse, order=self.order)
 
     def restore(self):
-        if self.fused_io:
+        if self.io != "reordered":
             return self.o   # written by the attention kernel
         return B_.hsa_unperm(self.op, self.perm, self.N, out=self.o)
 
@@ -134,8 +152,10 @@ class SparseAttentionLayer:
         (rows int32 [heads, n] on the device): the share of each row's exact
         attention mass that its query block's list keeps (hsa_block_mass)."""
         qp, kp, _ = self.xp
-        if self.fused_io:   # Q is not kept reordered: gather it for the diagnostic
-            B_.hsa_perm([self._q], self.perm, self.n_pad, outs=[qp])
+        if self.io == "tokens_qo":   # Q is not kept reordered: gather it for the diagnostic
+            B_.hsa_perm([self._qkv[0]], self.perm, self.n_pad, outs=[qp])
+        elif self.io == "tokens":
+            B_.hsa_perm(list(self._qkv[:2]), self.perm, self.n_pad, outs=[qp, kp])
         _, rec = B_.hsa_block_mass(qp, kp, self.blk_len, rows, self.B, self.scale, self.kv_idx,
                                    self.kv_cnt, want_mass=False)
         return rec
@@ -159,7 +179,7 @@ def vmoba_order(layer_index: int) -> str:
     return VMOBA_CYCLE[layer_index % 3]
 
 
-def layer_for_workload(w, device="cuda", want_lse=True, fused_io=True) -> SparseAttentionLayer:
+def layer_for_workload(w, device="cuda", want_lse=True, io="tokens_qo") -> SparseAttentionLayer:
     """Layer configured for one of the synthetic workloads (workloads.Workload)."""
     dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
     nb = B_.hsa_plan_size(w.T, w.H, w.W, w.order, w.B)[1]
@@ -169,4 +189,4 @@ def layer_for_workload(w, device="cuda", want_lse=True, fused_io=True) -> Sparse
     return SparseAttentionLayer(w.T, w.H, w.W, w.heads, w.D, order=w.order, B=w.B,
                                 select=w.select, s=w.s, agg=w.agg, k=k, tau=w.tau, C=w.C,
                                 T_per=w.T_per, lam=w.lam, delta=w.delta, dtype=dtype,
-                                device=device, want_lse=want_lse, fused_io=fused_io)
+                                device=device, want_lse=want_lse, io=io)

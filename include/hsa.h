@@ -10,7 +10,7 @@
  *               global budget, or the LVSA frame mask)
  *   hsa_attn    block-sparse flash attention over the listed key blocks
  *   hsa_unperm  scatter the output back to the original token order
- *   (hsa_attn_tokens fuses the Q gather and this scatter into attention)
+ *   (hsa_attn_tokens fuses the gathers and this scatter into attention)
  *
  * Conventions shared by every entry point
  *  - The caller owns every buffer. Device buffers are device pointers (for
@@ -155,7 +155,7 @@ hsa_status_t hsa_plan(int32_t T, int32_t H, int32_t W, int32_t order, int32_t B,
  * u*pool_s + pool_s - 1) of x_j[perm[slot]][h][d], 0 for an empty sub-block.
  * pool_s in {16, 32, 64, 128} must divide n_pad; needs n_tensors >= 2.
  * With pooled given, xps[0] or xps[1] may be NULL: that tensor is pooled but
- * not stored (hsa_attn_tokens reads Q in the token layout itself).
+ * not stored (hsa_attn_tokens reads token-major tensors itself).
  */
 hsa_status_t hsa_perm(int32_t n_tensors, const void *const *xs, void *const *xps,
                       const int32_t *perm, int32_t N, int32_t n_pad, int32_t nh, int32_t D,
@@ -259,30 +259,33 @@ hsa_status_t hsa_attn(const void *qp, const void *kp, const void *vp, void *op, 
                       hsa_stream_t stream);
 
 /*
- * hsa_attn_tokens -- hsa_attn with Q read from, and the output written to,
- *   the token-major layout: the reorder of Q (DFSAttn, Methodology, design
- *   1) and the inverse reorder of the output happen in the attention
- *   kernel's own loads and stores, so the caller skips Qp and hsa_unperm.
- *   Results are bit-identical to hsa_attn on hsa_perm's Qp followed by
- *   hsa_unperm.
- * q: token-major [N][nh][D] with q_stride elements between tokens, for
- *   example the Q slice of a fused QKV buffer; o: token-major output with
- *   o_stride elements between tokens. Each stride is >= nh*D and a multiple
- *   of 16 bytes. Every real token's rows of o are written once; nothing else
- *   in o is touched.
- * kp, vp: reordered [nh][nb*B][D] (hsa_perm; hsa_perm can pool Q without
- *   storing it, see there). perm: the plan's int32 [nb*B] slot -> token map;
- *   entries must be -1 or < N and a slot must be real exactly when it lies
- *   in the first blk_len[I] slots of its block (as hsa_plan writes them).
+ * hsa_attn_tokens -- hsa_attn on token-major tensors: the reorder (DFSAttn,
+ *   Methodology, design 1) of Q, optionally of K and V, and the inverse
+ *   reorder of the output happen in the attention kernel's own loads and
+ *   stores (rows are looked up in perm), so no reordered copy of those
+ *   tensors is made and no hsa_unperm pass runs. Results are bit-identical
+ *   to hsa_perm -> hsa_attn -> hsa_unperm on the same lists.
+ * q: token-major [N][nh][D], q_stride elements between tokens (for example
+ *   the Q slice of a fused QKV buffer). o: token-major output, o_stride
+ *   elements between tokens; every real token's row is written once and
+ *   nothing else in o is touched.
+ * k, v: kv_stride > 0: token-major like q with that token stride (the byte
+ *   span N*kv_stride*element size must stay below 4 GiB); kv_stride = 0:
+ *   reordered [nh][nb*B][D] from hsa_perm.
+ * Strides are >= nh*D elements and multiples of 16 bytes.
+ * perm: the plan's int32 [nb*B] slot -> token map; entries are -1 or < N,
+ *   and a slot is real exactly when it lies in the first blk_len[I] slots of
+ *   its block (as hsa_plan writes them). Pad slots get zero query rows; pad
+ *   key rows read token 0 and are masked.
  * lse, lists, order, scale, dtype: as for hsa_attn (lse stays in the
  *   reordered layout [nh][nb*B]).
  */
-hsa_status_t hsa_attn_tokens(const void *q, int64_t q_stride, const void *kp, const void *vp, void *o,
-                             int64_t o_stride, float *lse, const int32_t *perm, int32_t N,
-                             const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
-                             const int32_t *order, int32_t max_kv, int32_t kv_shared, int32_t nh,
-                             int32_t nb, int32_t B, int32_t D, int32_t dtype, float scale,
-                             hsa_stream_t stream);
+hsa_status_t hsa_attn_tokens(const void *q, const void *k, const void *v, void *o, int64_t q_stride,
+                             int64_t kv_stride, int64_t o_stride, float *lse, const int32_t *perm,
+                             int32_t N, const int32_t *blk_len, const int32_t *kv_idx,
+                             const int32_t *kv_cnt, const int32_t *order, int32_t max_kv,
+                             int32_t kv_shared, int32_t nh, int32_t nb, int32_t B, int32_t D,
+                             int32_t dtype, float scale, hsa_stream_t stream);
 
 /*
  * hsa_attn_order -- a processing order for hsa_attn that dispatches each

@@ -23,8 +23,8 @@ int main(void) {
   if (hsa_attn(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 4, 0, 2, 4, 64, 64, HSA_BF16,
                0.125f, NULL) != HSA_ERR_NULL_PTR)
     return 7;
-  if (hsa_attn_tokens(NULL, 256, NULL, NULL, NULL, 256, NULL, NULL, 100, NULL, NULL, NULL, NULL, 4, 0,
-                      2, 4, 64, 64, HSA_BF16, 0.125f, NULL) != HSA_ERR_NULL_PTR)
+  if (hsa_attn_tokens(NULL, NULL, NULL, NULL, 256, 0, 256, NULL, NULL, 100, NULL, NULL, NULL, NULL, 4,
+                      0, 2, 4, 64, 64, HSA_BF16, 0.125f, NULL) != HSA_ERR_NULL_PTR)
     return 8;
   printf("ok %d %s\n", hsa_abi_version(), hsa_status_str(HSA_ERR_WORKSPACE));
   return 0;

@@ -182,17 +182,21 @@ def test_attn_and_unperm_validation(B):
     assert L.hsa_attn_order(FAKE, 0, 4, 4, FAKE, NULL) == 2
     assert L.hsa_attn_order(FAKE, 2, 4, 4096, FAKE, NULL) == 4                                   # max_kv
     assert L.hsa_attn_order(FAKE, 1 << 16, 1 << 16, 4, FAKE, NULL) == 4                          # G*nb
-    # hsa_attn_tokens(q, q_stride, kp, vp, o, o_stride, lse, perm, N, blk_len, kv_idx, kv_cnt,
-    #                 order, max_kv, kv_shared, nh, nb, B, D, dtype, scale, stream)
-    def tok(q_stride=128, o_stride=128, perm=FAKE, N=200, B_=64, order=NULL):
-        return L.hsa_attn_tokens(FAKE, q_stride, FAKE, FAKE, FAKE, o_stride, NULL, perm, N, FAKE, FAKE,
-                                 FAKE, order, 4, 0, 2, 4, B_, 64, 1, 0.125, NULL)
+    # hsa_attn_tokens(q, k, v, o, q_stride, kv_stride, o_stride, lse, perm, N, blk_len, kv_idx,
+    #                 kv_cnt, order, max_kv, kv_shared, nh, nb, B, D, dtype, scale, stream)
+    def tok(q_stride=128, kv_stride=0, o_stride=128, perm=FAKE, N=200, B_=64, order=NULL, nh=2):
+        return L.hsa_attn_tokens(FAKE, FAKE, FAKE, FAKE, q_stride, kv_stride, o_stride, NULL, perm, N,
+                                 FAKE, FAKE, FAKE, order, 4, 0, nh, 4, B_, 64, 1, 0.125, NULL)
     assert tok(perm=NULL) == 1
     assert tok(N=0) == 2 and tok(N=257) == 2                                                     # N vs nb*B
-    assert tok(q_stride=100) == 2 and tok(o_stride=64) == 2                                      # stride < nh*D
-    assert tok(q_stride=132) == 6 and tok(o_stride=132) == 6                                     # 16-byte rows
+    assert tok(q_stride=100) == 2 and tok(o_stride=64) == 2 and tok(kv_stride=64) == 2           # stride < nh*D
+    assert tok(q_stride=132) == 6 and tok(o_stride=132) == 6 and tok(kv_stride=132) == 6         # 16-byte rows
+    assert tok(kv_stride=-8) == 6                                                                # negative
     assert tok(B_=96) == 4
     assert tok(order=ctypes.c_void_p(0x10002)) == 6
+    # gathered K/V rows use 32-bit byte offsets: a 4 GiB token-major span is refused
+    assert L.hsa_attn_tokens(FAKE, FAKE, FAKE, FAKE, 1 << 14, 1 << 14, 1 << 14, NULL, FAKE, 1 << 17,
+                             FAKE, FAKE, FAKE, NULL, 4, 0, 128, 1024, 128, 128, 1, 0.125, NULL) == 4
     assert L.hsa_unperm(FAKE, FAKE, FAKE, 10, 8, 2, 64, 128, 1, NULL) == 2
     assert L.hsa_unperm(FAKE, NULL, FAKE, 10, 16, 2, 64, 128, 1, NULL) == 1
 

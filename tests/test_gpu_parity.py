@@ -223,10 +223,10 @@ def test_select_ties_and_edges(hsa):
 
 # ---------------------------------------------------------------- attention / layer
 
-def _layer(hsa, w, step, mask=None, fused_io=True):
+def _layer(hsa, w, step, mask=None, io="tokens_qo"):
     _say(f"  generating inputs for workload {w.idx} step {step}")
     q, k, v = (x.to(dev()) for x in wl.make_qkv(w, step))
-    L = hsa.layer_for_workload(w, device=dev(), fused_io=fused_io)
+    L = hsa.layer_for_workload(w, device=dev(), io=io)
     if mask is not None:
         L.reorder(q, k, v)
         L.kv_idx.copy_(mask[0])
@@ -254,7 +254,7 @@ def _check_layer(hsa, w, step, q, k, v, L, o, check_select=True):
     rows = attn_rows(w, step, perm)
     ref_op, ref_lse = oracle.attn_blocks(qp, kp, vp, perm, w.B, kv_idx, kv_cnt, rows=rows)
     # with token-layout I/O the kernel wrote token order: view it per slot
-    op = oracle.gather(to_np(o), perm) if L.fused_io else to_np(L.op)
+    op = oracle.gather(to_np(o), perm) if L.io != "reordered" else to_np(L.op)
     err = max_err_rows(op, ref_op, rows)
     lse_err = max_err_rows(to_np(L.lse)[:, :, None], ref_lse[:, :, None], rows)
     omax = max(float(np.abs(ref_op[h, r]).max()) for h, r in enumerate(rows))
@@ -262,7 +262,7 @@ def _check_layer(hsa, w, step, q, k, v, L, o, check_select=True):
          f"lse err = {lse_err:.3e}, rows/head = {len(rows[0])}")
     assert err <= TOL[w.dtype]
     assert lse_err <= (1e-4 if w.dtype == "f32" else 1e-3)
-    if not L.fused_io:
+    if L.io == "reordered":
         assert np.all(op[:, perm < 0] == 0), "pad query rows must be zero"
         # the restored output is exactly the reordered output scattered back
         assert np.array_equal(to_np(o), oracle.scatter(op, perm, w.N))
@@ -280,6 +280,15 @@ def test_layer_sampled_rows(hsa, idx, step):
     w = wl.get(idx)
     _say(f"layer workload {idx} step {step} (sampled rows)")
     _check_layer(hsa, w, step, *_layer(hsa, w, step))
+
+
+@pytest.mark.parametrize("idx,step", [(1, 0), (2, 0), (3, 0), (5, 9)])
+def test_layer_gathered_kv(hsa, idx, step):
+    """The layer with io="tokens": no reordered copy of Q, K or V at all (the
+    attention kernel gathers their rows itself), against the oracle."""
+    w = wl.get(idx)
+    _say(f"layer workload {idx} step {step}, K/V gathered in attention")
+    _check_layer(hsa, w, step, *_layer(hsa, w, step, io="tokens"))
 
 
 @pytest.mark.parametrize("idx,order,step", [(2, "tile2d", 0), (2, "cube3d", 0), (3, "tile2d", 0),
@@ -328,7 +337,7 @@ def test_block_mass_and_recall(hsa):
     and the recall of the selected lists, against the oracle."""
     w = wl.get(2)
     _say("block mass / recall (workload 2)")
-    q, k, v, L, o = _layer(hsa, w, 0, fused_io=False)
+    q, k, v, L, o = _layer(hsa, w, 0, io="reordered")
     perm = L.perm.cpu().numpy().astype(np.int64)
     real = np.nonzero(perm >= 0)[0]
     rng = np.random.default_rng(12)
@@ -365,20 +374,22 @@ def test_cached_mask_step(hsa):
     _check_layer(hsa, w, 2, q2, k2, v2, L, o, check_select=False)
 
 
+@pytest.mark.parametrize("io", ["tokens_qo", "tokens"])
 @pytest.mark.parametrize("idx,step", [(1, 0), (2, 0), (3, 0), (4, 3), (5, 9), (6, 0)])
-def test_token_io_equals_five_passes(hsa, idx, step):
-    """hsa_attn_tokens (Q gathered and O scattered inside the attention
-    kernel) gives bit for bit the output of hsa_perm(Q) -> hsa_attn ->
-    hsa_unperm on the same lists, and the same lse."""
+def test_token_io_equals_five_passes(hsa, idx, step, io):
+    """hsa_attn_tokens (Q, and with io="tokens" also K and V, gathered and the
+    output scattered inside the attention kernel) gives bit for bit the
+    output of hsa_perm -> hsa_attn -> hsa_unperm on the same lists, and the
+    same lse."""
     w = wl.get(idx)
-    _say(f"token-layout I/O vs five passes, workload {idx} step {step}")
-    q, k, v, L, o = _layer(hsa, w, step, fused_io=False)
+    _say(f"{io} I/O vs five passes, workload {idx} step {step}")
+    q, k, v, L, o = _layer(hsa, w, step, io="reordered")
     o5 = o.clone()
     lse5 = L.lse.clone()
-    L.fused_io = True
+    L.io = io
     L.lse.fill_(float("nan"))
     o.fill_(float("nan"))
-    L.reorder(q, k, v, pool=False)   # K and V only; Q stays in token order
+    L.reorder(q, k, v, pool=False)
     L.attend()
     ot = L.restore()
     torch.cuda.synchronize()
@@ -388,16 +399,18 @@ def test_token_io_equals_five_passes(hsa, idx, step):
     assert torch.equal(L.lse[:, real], lse5[:, real])
 
 
-def test_token_io_strided_buffers(hsa):
-    """Q read in place from a fused [N, 3, heads, D] projection buffer and the
-    output written into every other row group of a wider buffer: the rows in
-    between stay untouched."""
+@pytest.mark.parametrize("kv", ["reordered", "tokens"])
+def test_token_io_strided_buffers(hsa, kv):
+    """Q (and K, V) read in place from a fused [N, 3, heads, D] projection
+    buffer and the output written into every other row group of a wider
+    buffer: the rows in between stay untouched."""
     w = wl.get(2)
-    _say("token-layout I/O with strided Q and output")
-    q, k, v, L, o = _layer(hsa, w, 0, fused_io=False)
+    _say(f"token-layout I/O with strided buffers, K/V {kv}")
+    q, k, v, L, o = _layer(hsa, w, 0, io="reordered")
     fused = torch.stack([q[0], k[0], v[0]], dim=1)[None]          # [1, N, 3, nh, D]
     wide = torch.full((1, w.N, 2, w.heads, w.D), 7.0, dtype=q.dtype, device=dev())
-    out, _ = hsa.hsa_attn_tokens(fused[:, :, 0], L.xp[1], L.xp[2], L.perm, L.blk_len, L.kv_idx,
+    kk, vv = (fused[:, :, 1], fused[:, :, 2]) if kv == "tokens" else (L.xp[1], L.xp[2])
+    out, _ = hsa.hsa_attn_tokens(fused[:, :, 0], kk, vv, L.perm, L.blk_len, L.kv_idx,
                                  L.kv_cnt, w.B, want_lse=False, out=wide[:, :, 1])
     torch.cuda.synchronize()
     assert out.stride(1) == 2 * w.heads * w.D
@@ -573,7 +586,7 @@ def test_attn_bwd_wan_shape_sampled(hsa):
     do = torch.randn(q.shape, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
     from dataclasses import replace
     w2 = replace(w, heads=2)
-    L = hsa.layer_for_workload(w2, device=dev(), fused_io=False)
+    L = hsa.layer_for_workload(w2, device=dev(), io="reordered")
     L.step(q.to(dev()), k.to(dev()), v.to(dev()))
     dop = hsa.hsa_perm([do.to(dev())], L.perm, L.n_pad)[0]
     dq, dk, dv = hsa.hsa_attn_bwd(*L.xp, L.op, dop, L.lse, L.blk_len, L.kv_idx, L.kv_cnt, w.B)
