@@ -11,11 +11,14 @@
 //  THRESH_GLOBAL VMoBA abstract: threshold selection by cumulative
 //                similarity, then global selection over the head, under a
 //                budget that shrinks across steps (DFSAttn design 3).
-//                Per row: bitwise search for the boundary key of the
-//                shortest prefix reaching tau, with exact 2^-62 fixed-point
-//                sums. Per head: an 8-pass MSB-first radix select (8-bit
-//                digits, integer histograms) of the remaining budget among
-//                pairs outside the row prefixes. Then a compaction pass.
+//                Per row: MSB-first radix search (8-bit digits, exact 2^-62
+//                fixed-point mass histograms in LDS) for the boundary key of
+//                the shortest prefix reaching tau. Per head: an MSB-first
+//                radix select (11-bit digits, count histograms) of the
+//                remaining budget among pairs outside the row prefixes, a
+//                small pick kernel choosing each digit; the search stops as
+//                soon as the boundary digit's pairs are all taken (three
+//                passes unless scores tie exactly). Then a compaction pass.
 //  LVSA          LVSA section 2, A(t) = G_s u W(t): rotating anchors plus the
 //                nearest non-anchor frames; tile lists shared by all heads.
 #include "common.h"
@@ -120,6 +123,7 @@ template <int KPL>
 __global__ void __launch_bounds__(kSelThreads)
 thresh_row_kernel(const float *__restrict__ S, int rows, int nb, uint64_t target,
                   uint64_t *__restrict__ row_thr, int32_t *__restrict__ row_cnt) {
+  __shared__ uint64_t row_hist[kSelThreads / 64][256];
   const int row = blockIdx.x * (kSelThreads / 64) + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int lane = lane_id();
@@ -156,14 +160,55 @@ thresh_row_kernel(const float *__restrict__ S, int rows, int nb, uint64_t target
   } else {
     // Largest order key thr whose tail sum F(thr) = sum_{key >= thr} fx
     // still reaches the target: the boundary value of the shortest prefix.
+    // Radix search from the top byte: with the higher bytes fixed to P and
+    // A = mass of the keys above P, the next byte is the highest digit d
+    // with A + (mass of digits >= d under P) >= target.
+    uint64_t *mh = row_hist[threadIdx.x >> 6];
     uint32_t thr = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = thr | (1u << bit);
-      uint64_t f = 0;
+    uint64_t A = 0;
+#pragma unroll 1
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      const uint32_t pmask = shift == 24 ? 0u : (~0u << (shift + 8));
 #pragma unroll
-      for (int r = 0; r < KPL; ++r) f += (key[r] >= cand) ? fx[r] : 0ull;
-      f = wave_sum_u64(f);
-      if (f >= target) thr = cand;
+      for (int j = 0; j < 4; ++j) mh[lane * 4 + j] = 0;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int r = 0; r < KPL; ++r)
+        if (lane + 64 * r < nb && (key[r] & pmask) == thr)
+          atomicAdd(reinterpret_cast<unsigned long long *>(&mh[(key[r] >> shift) & 255]),
+                    static_cast<unsigned long long>(fx[r]));
+      __builtin_amdgcn_wave_barrier();
+      // lane l holds digits 255 - 4l - j (j = 0..3): lanes run from the top
+      uint64_t v[4], loc = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = mh[255 - 4 * lane - j];
+        loc += v[j];
+      }
+      uint64_t incl = loc;  // inclusive prefix over lanes (higher digits first)
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint64_t o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      uint64_t c = A + incl - loc;  // mass of the digits above this lane's
+      int jhit = 4;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {  // highest digit of the lane that reaches the target
+        if (c + v[0] + (j >= 1 ? v[1] : 0) + (j >= 2 ? v[2] : 0) + (j >= 3 ? v[3] : 0) >= target) jhit = j;
+      }
+      const uint64_t hit = __ballot(jhit < 4);
+      const int src = __builtin_ctzll(hit);  // the crossing lies in the first lane that reaches it
+      const int jsel = __shfl(jhit, src, 64);
+      uint64_t above_d = c;                  // mass of the digits above the chosen one
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (j < jhit) above_d += v[j];
+      above_d = __shfl(above_d, src, 64);
+      const uint32_t d = 255u - 4u * static_cast<uint32_t>(src) - static_cast<uint32_t>(jsel);
+      thr |= d << shift;
+      A = above_d;
+      __builtin_amdgcn_wave_barrier();
     }
     uint64_t above = 0;
     int n_above = 0;
@@ -204,13 +249,25 @@ thresh_row_kernel(const float *__restrict__ S, int rows, int nb, uint64_t target
   }
 }
 
+// Global fill: MSB-first radix select over 52-bit pair keys (score order key,
+// then lower linear index first; nb <= 1024 so I*nb+J < 2^20) in 11-bit
+// digits: three passes fix the score bits, two more break exact ties.
+constexpr int kGDigit = 11;
+constexpr int kGBins = 1 << kGDigit;
+constexpr int kGKeyBits = 52;
+constexpr int kGPasses = 5;  // 5 x 11 bits cover the 52-bit key
+
+__host__ __device__ constexpr int gfill_hi(int pass) { return kGKeyBits - 1 - kGDigit * pass; }
+__host__ __device__ constexpr int gfill_lo(int pass) { return gfill_hi(pass) - kGDigit + 1 > 0 ? gfill_hi(pass) - kGDigit + 1 : 0; }
+
 struct GlobalState {
-  uint64_t prefix;    // digits fixed so far
-  int64_t remaining;  // rank still to find within the matching keys
-  int32_t active;     // 1 if the head needs a global fill
-  int32_t pad;
+  uint64_t prefix;    // digits fixed so far; once done: the smallest selected key
+  int64_t remaining;  // rank still to find among the keys matching prefix
+  int32_t fill;       // 1 if the head adds pairs beyond its row prefixes
+  int32_t active;     // 1 while digits remain to be searched
 };
 
+// Per head: budget minus the row prefixes' size; clears the pass histograms.
 __global__ void __launch_bounds__(256)
 gfill_init_kernel(const int32_t *__restrict__ row_cnt, int nb, int64_t budget,
                   GlobalState *__restrict__ st, uint32_t *__restrict__ hist) {
@@ -221,35 +278,42 @@ gfill_init_kernel(const int32_t *__restrict__ row_cnt, int nb, int64_t budget,
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) c += __shfl_xor(c, off, 64);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
-  hist[h * 256 + threadIdx.x] = 0;
+  uint32_t *hh = hist + static_cast<int64_t>(h) * kGPasses * kGBins;
+  for (int i = threadIdx.x; i < kGPasses * kGBins; i += 256) hh[i] = 0;
   __syncthreads();
   if (threadIdx.x == 0) {
     const int64_t t = part[0] + part[1] + part[2] + part[3];
     const int64_t rem = budget - t;
     st[h].prefix = 0;
     st[h].remaining = rem > 0 ? rem : 0;
+    st[h].fill = rem > 0 ? 1 : 0;
     st[h].active = rem > 0 ? 1 : 0;
   }
 }
 
-// Global key of pair (I, J): order key of the score, then lower I*nb+J first.
+// Global key of pair (I, J): order key of the score, then lower I*nb+J first
+// (lin < 2^20).
 __device__ __forceinline__ uint64_t gkey(uint32_t ok, uint32_t lin) {
-  return (static_cast<uint64_t>(ok) << 32) | (0xFFFFFFFFu - lin);
+  return (static_cast<uint64_t>(ok) << 20) | (0xFFFFFu - lin);
 }
 
+// One digit of the global radix select: every workgroup counts the digits
+// of the matching keys outside the row prefixes (LDS histogram, then global
+// atomics into this pass's histogram).
 template <int KPL>
 __global__ void __launch_bounds__(kSelThreads)
 gfill_hist_kernel(const float *__restrict__ S, int nb, int pass,
                   const uint64_t *__restrict__ row_thr, const GlobalState *__restrict__ st,
                   uint32_t *__restrict__ hist) {
-  __shared__ uint32_t lh[256];
+  __shared__ uint32_t lh[kGBins];
   const int h = blockIdx.y;
   if (!st[h].active) return;  // uniform across the workgroup
-  lh[threadIdx.x] = 0;
+  for (int i = threadIdx.x; i < kGBins; i += kSelThreads) lh[i] = 0;
   __syncthreads();
-  const int shift = 56 - 8 * pass;
+  const int hi = gfill_hi(pass), lo = gfill_lo(pass);
+  const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
   const uint64_t prefix = st[h].prefix;
-  const uint64_t himask = (pass == 0) ? 0ull : (~0ull << (shift + 8));
+  const uint64_t himask = (pass == 0) ? 0ull : (~0ull << (hi + 1));
   const int I = blockIdx.x * (kSelThreads / 64) + (threadIdx.x >> 6);
   const int lane = lane_id();
   if (I < nb) {
@@ -263,37 +327,70 @@ gfill_hist_kernel(const float *__restrict__ S, int nb, int pass,
         const uint32_t ok = float_order_key(src[j]);
         if (key64(ok, j) < K) {  // not already in the row prefix
           const uint64_t g = gkey(ok, static_cast<uint32_t>(I * nb + j));
-          if ((g & himask) == (prefix & himask)) atomicAdd(&lh[(g >> shift) & 0xFF], 1u);
+          if ((g & himask) == (prefix & himask)) atomicAdd(&lh[static_cast<uint32_t>(g >> lo) & dmask], 1u);
         }
       }
     }
   }
   __syncthreads();
-  const uint32_t c = lh[threadIdx.x];
-  if (c) atomicAdd(&hist[h * 256 + threadIdx.x], c);
+  uint32_t *gh = hist + (static_cast<int64_t>(h) * kGPasses + pass) * kGBins;
+  for (int i = threadIdx.x; i < kGBins; i += kSelThreads)
+    if (lh[i]) atomicAdd(&gh[i], lh[i]);
 }
 
-// Choose the digit holding the remaining-th largest matching key.
-__global__ void __launch_bounds__(64)
-gfill_pick_kernel(int pass, GlobalState *__restrict__ st, uint32_t *__restrict__ hist) {
+// Pick the digit that holds the remaining-th largest matching key (one
+// workgroup per head, a scan from the top digit) and advance the state. The
+// search is over once the picked digit's keys are all taken (count <=
+// remaining) or the last digit is fixed.
+__global__ void __launch_bounds__(kSelThreads)
+gfill_pick_kernel(int pass, GlobalState *__restrict__ st, const uint32_t *__restrict__ hist) {
+  __shared__ uint32_t part[kSelThreads];
   const int h = blockIdx.x;
   if (!st[h].active) return;
-  __shared__ uint32_t hs[256];
-  for (int i = threadIdx.x; i < 256; i += 64) {
-    hs[i] = hist[h * 256 + i];
-    hist[h * 256 + i] = 0;
+  const int hi = gfill_hi(pass), lo = gfill_lo(pass);
+  const int nd = 1 << (hi - lo + 1);
+  const uint64_t himask = (pass == 0) ? 0ull : (~0ull << (hi + 1));
+  const uint64_t prefix = st[h].prefix;
+  const int64_t rem = st[h].remaining;
+  const uint32_t *gh = hist + (static_cast<int64_t>(h) * kGPasses + pass) * kGBins;
+  // thread t owns digits nd-1-8t .. nd-8-8t (top digits first)
+  constexpr int kPer = kGBins / kSelThreads;
+  uint32_t v[kPer];
+  uint32_t loc = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int d = nd - 1 - (threadIdx.x * kPer + j);
+    v[j] = d >= 0 ? gh[d] : 0u;
+    loc += v[j];
   }
+  part[threadIdx.x] = loc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t rem = st[h].remaining;
-    int d = 255;
-    for (; d > 0; --d) {
-      if (static_cast<int64_t>(hs[d]) >= rem) break;
-      rem -= hs[d];
+  for (int off = 1; off < kSelThreads; off <<= 1) {  // inclusive scan
+    const uint32_t o = threadIdx.x >= off ? part[threadIdx.x - off] : 0u;
+    __syncthreads();
+    part[threadIdx.x] += o;
+    __syncthreads();
+  }
+  const int64_t total = part[kSelThreads - 1];
+  int64_t cum = static_cast<int64_t>(part[threadIdx.x]) - loc;  // keys in higher digits
+  __syncthreads();  // every thread has read st[h] before it is rewritten
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int d = nd - 1 - (threadIdx.x * kPer + j);
+    // the digit whose cumulative count first reaches rem; with fewer matching
+    // keys than rem (all taken) the lowest digit
+    const bool hit = (cum < rem && cum + v[j] >= rem) || (total < rem && d == 0);
+    if (d >= 0 && hit) {
+      const int64_t r = rem - cum;  // rank within digit d
+      GlobalState ns;
+      ns.prefix = (prefix & himask) | (static_cast<uint64_t>(d) << lo);
+      ns.remaining = r;
+      ns.fill = 1;
+      // done: the smallest selected key is prefix with the lower bits zero
+      ns.active = (static_cast<int64_t>(v[j]) <= r || lo == 0) ? 0 : 1;
+      st[h] = ns;
     }
-    const int shift = 56 - 8 * pass;
-    st[h].prefix |= static_cast<uint64_t>(d) << shift;
-    st[h].remaining = rem;
+    cum += v[j];
   }
 }
 
@@ -307,8 +404,8 @@ thresh_emit_kernel(const float *__restrict__ S, int nh, int nb,
   const int h = row / nb, I = row - h * nb;
   const int lane = lane_id();
   const uint64_t K = row_thr[row];
-  const bool fill = st[h].active != 0;
-  const uint64_t lam = st[h].prefix;  // the budget-th largest outside key
+  const bool fill = st[h].fill != 0;
+  const uint64_t lam = st[h].prefix;  // the smallest outside key selected
   const float *src = S + static_cast<int64_t>(row) * nb;
   bool sel[KPL];
 #pragma unroll
@@ -456,7 +553,7 @@ size_t select_ws_bytes(int nh, int nb, int mode) {
   b = (b + 255) & ~static_cast<size_t>(255);
   b += static_cast<size_t>(nh) * sizeof(hsa::GlobalState);
   b = (b + 255) & ~static_cast<size_t>(255);
-  b += static_cast<size_t>(nh) * 256 * sizeof(uint32_t);  // histograms
+  b += static_cast<size_t>(nh) * hsa::kGPasses * hsa::kGBins * sizeof(uint32_t);  // histograms
   return b;
 }
 
@@ -499,10 +596,11 @@ hsa_status_t launch_select(const float *S, int nh, int nb, const hsa_select_para
     hipLaunchKernelGGL(hsa::gfill_init_kernel, dim3(nh), dim3(256), 0, stream, row_cnt, nb, budget,
                        st, hist);
     const dim3 hgrid((nb + rows_per_wg - 1) / rows_per_wg, nh);
-    for (int pass = 0; pass < 8; ++pass) {
+    for (int pass = 0; pass < hsa::kGPasses; ++pass) {  // passes after the search ends return at once
       HSA_KPL_DISPATCH(nb, hsa::gfill_hist_kernel, hgrid, dim3(hsa::kSelThreads), S, nb, pass,
                        row_thr, st, hist);
-      hipLaunchKernelGGL(hsa::gfill_pick_kernel, dim3(nh), dim3(64), 0, stream, pass, st, hist);
+      hipLaunchKernelGGL(hsa::gfill_pick_kernel, dim3(nh), dim3(hsa::kSelThreads), 0, stream, pass, st,
+                         hist);
     }
     HSA_KPL_DISPATCH(nb, hsa::thresh_emit_kernel, grid, dim3(hsa::kSelThreads), S, nh, nb, row_thr,
                      st, kv_idx, kv_cnt, max_kv);
