@@ -42,6 +42,16 @@
 namespace hsa {
 
 
+// tok[i] = max(lane i of this lane's 16-lane row of v, 0) for i < N (DPP
+// row broadcast; the control must be a constant, hence the recursion).
+template <int N, int I = 0>
+__device__ __forceinline__ void row_bcast_clamped(int v, int (&tok)[N]) {
+  if constexpr (I < N) {
+    tok[I] = max(__builtin_amdgcn_update_dpp(0, v, 0x150 + I, 0xF, 0xF, false), 0);
+    row_bcast_clamped<N, I + 1>(v, tok);
+  }
+}
+
 // (head, query block) of workgroup b. Without an order, neighbouring blocks
 // of one head go to one XCD (shared L2). With one, the b-th workgroup takes
 // list row order[b] (longest lists first); shared lists order blocks, and
@@ -153,22 +163,33 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     entry(t / NS, J, L);
     return min(max(L - (t % NS) * ST, 0), ST);
   };
-  // Gathered K/V: the token rows this lane's loads of stage t read (raw map
-  // entries; clamped to >= 0 before use). Uniform base, unsigned lane offset.
+  // Gathered K/V: the token rows this lane's loads of stage t read. With
+  // D = 128 a 16-lane row of the wave fills one tile row per load, so each
+  // lane fetches the map entry of load (lane mod NI) of its row and load i
+  // takes lane i of the row by a DPP row broadcast: one lookup per stage.
+  // Otherwise every load's entry is fetched. Raw entries are clamped to >= 0
+  // when expanded (pad keys read token 0 and are masked).
   using TL = TileLoads<D, ST, NW>;
-  uint32_t prow[TL::NI];
+  constexpr bool kRowBcast = TL::CPR == 16 && 16 % TL::NI == 0;
+  constexpr int RAW = kRowBcast ? 1 : TL::NI;
+  uint32_t prow[RAW];
 #pragma unroll
-  for (int i = 0; i < TL::NI; ++i) prow[i] = static_cast<uint32_t>(TL::row(w, i, lane));
-  auto stage_rows = [&](int t, int (&tok)[TL::NI]) {
+  for (int r = 0; r < RAW; ++r)
+    prow[r] = static_cast<uint32_t>(kRowBcast ? TL::row(w, lane % TL::NI, lane) : TL::row(w, r, lane));
+  auto stage_rows = [&](int t, int (&raw)[RAW]) {
     int J, L;
     entry(t / NS, J, L);
     const int32_t *pr = perm + (J * BK + (t % NS) * ST);
 #pragma unroll
-    for (int i = 0; i < TL::NI; ++i) tok[i] = pr[prow[i]];
+    for (int r = 0; r < RAW; ++r) raw[r] = pr[prow[r]];
   };
-  auto clamp_rows = [&](int (&tok)[TL::NI]) {
+  auto expand_rows = [&](const int (&raw)[RAW], int (&tok)[TL::NI]) {
+    if constexpr (kRowBcast) {
+      row_bcast_clamped<TL::NI>(raw[0], tok);
+    } else {
 #pragma unroll
-    for (int i = 0; i < TL::NI; ++i) tok[i] = max(tok[i], 0);
+      for (int i = 0; i < TL::NI; ++i) tok[i] = max(raw[i], 0);
+    }
   };
   // keep entries (c + 1) / NS .. (c + 2) / NS inside the window
   auto slide = [&](int c) {
@@ -337,24 +358,42 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     }
   };
 
-  // Gathered K/V: source rows of the V stage issued next (rv), of the K
-  // stage issued next (rk) and of the stage after it (rn, in flight).
-  int rv[TL::NI], rk[TL::NI], rn[TL::NI];
+  // Gathered K/V: byte offsets of this lane's loads for the V stage issued
+  // next (ov) and the K stage issued next (ok), the source rows of that K
+  // stage (rk, which the V stage after it reuses), and the raw entries of
+  // the stage after it (rn, in flight). Offsets are formed at the end of
+  // the previous iteration, so the loads issue without waiting on
+  // arithmetic.
+  int rk[TL::NI], rn[RAW], r0[RAW], r1[RAW];
+  uint32_t ok[TL::NI], ov[TL::NI];
 #pragma unroll
-  for (int i = 0; i < TL::NI; ++i) rv[i] = rk[i] = rn[i] = 0;
+  for (int i = 0; i < TL::NI; ++i) {
+    rk[i] = 0;
+    ok[i] = ov[i] = 0;
+  }
+  auto offsets = [&](const int (&tok)[TL::NI], const uint32_t (&coff)[4], uint32_t (&off)[TL::NI]) {
+#pragma unroll
+    for (int i = 0; i < TL::NI; ++i) off[i] = __umul24(static_cast<uint32_t>(tok[i]), kv_row_bytes) + coff[i & 3];
+  };
+#pragma unroll
+  for (int r = 0; r < RAW; ++r) rn[r] = r0[r] = r1[r] = 0;
 
   // Prologue: K(0), V(0) and K(1) in flight, S(0) once all three landed.
   f32x16 sA[MT][QT], sB[MT][QT];
   if (nst > 0) {
     if constexpr (GKV) {
-      stage_rows(0, rv);
-      if (nst > 1) stage_rows(1, rk);
+      stage_rows(0, r0);
+      if (nst > 1) stage_rows(1, r1);
       wait_vmcnt<0>();
-      clamp_rows(rv);
-      clamp_rows(rk);
-      issue_tile_rows<D, ST, NW>(kbase, kv_row_bytes, ldsK, w, koff, rv);
-      issue_tile_rows<D, ST, NW>(vbase, kv_row_bytes, ldsV, w, voff, rv);
-      if (nst > 1) issue_tile_rows<D, ST, NW>(kbase, kv_row_bytes, ldsK + TILE * 2, w, koff, rk);
+      int t0[TL::NI];
+      expand_rows(r0, t0);
+      expand_rows(r1, rk);
+      offsets(t0, koff, ok);
+      issue_tile_offs<D, ST, NW>(kbase, ldsK, w, ok);
+      offsets(t0, voff, ov);
+      issue_tile_offs<D, ST, NW>(vbase, ldsV, w, ov);
+      offsets(rk, koff, ok);
+      if (nst > 1) issue_tile_offs<D, ST, NW>(kbase, ldsK + TILE * 2, w, ok);
       if (nst > 2) stage_rows(2, rn);
     } else {
       issue_tile<D, ST, NW>(kbase + stage_ofs(0), ldsK, w, koff);
@@ -364,11 +403,9 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     // iteration 0 reads K(1) as well, so all three stages must have landed
     wait_vmcnt<0>();
     if constexpr (GKV) {
-#pragma unroll
-      for (int i = 0; i < TL::NI; ++i) {
-        rv[i] = rk[i];            // V(1)
-        rk[i] = max(rn[i], 0);    // K(2)
-      }
+      offsets(rk, voff, ov);  // V(1)
+      expand_rows(rn, rk);    // K(2)
+      offsets(rk, koff, ok);
     }
     __syncthreads();
     compute_s(sA, 0);
@@ -382,8 +419,8 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     slide(c);
     if constexpr (GKV) {
       if (c + 3 < nst) stage_rows(c + 3, rn);
-      if (has2) issue_tile_rows<D, ST, NW>(kbase, kv_row_bytes, ldsK + (c & 1) * TILE * 2, w, koff, rk);
-      if (has1) issue_tile_rows<D, ST, NW>(vbase, kv_row_bytes, ldsV + ((c + 1) & 1) * TILE * 2, w, voff, rv);
+      if (has2) issue_tile_offs<D, ST, NW>(kbase, ldsK + (c & 1) * TILE * 2, w, ok);
+      if (has1) issue_tile_offs<D, ST, NW>(vbase, ldsV + ((c + 1) & 1) * TILE * 2, w, ov);
     } else {
       if (has2) issue_tile<D, ST, NW>(kbase + stage_ofs(c + 2), ldsK + (c & 1) * TILE * 2, w, koff);
       if (has1) issue_tile<D, ST, NW>(vbase + stage_ofs(c + 1), ldsV + ((c + 1) & 1) * TILE * 2, w, voff);
@@ -399,11 +436,9 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     mask_and_rescale(nxt, has1 ? stage_valid(c + 1) : 0);
     wait_vmcnt<0>();
     if constexpr (GKV) {
-#pragma unroll
-      for (int i = 0; i < TL::NI; ++i) {
-        rv[i] = rk[i];            // V(c+2) reads K(c+2)'s rows
-        rk[i] = max(rn[i], 0);    // K(c+3)
-      }
+      offsets(rk, voff, ov);  // V(c+2) reads K(c+2)'s rows
+      expand_rows(rn, rk);    // K(c+3)
+      offsets(rk, koff, ok);
     }
   };
   for (int c = 0; c < nst; c += 2) {

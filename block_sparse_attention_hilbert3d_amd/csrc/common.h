@@ -130,19 +130,16 @@ struct TileLoads {
 };
 
 // Issue the direct loads of one BKxD bf16 tile whose rows are gathered:
-// this lane's load i reads gbase + tok[i] * row_bytes + coff[i & 3], where
-// tok[i] >= 0 is the source row of the tile row it fills. Offsets are 32-bit
-// (24-bit multiply: tok and row_bytes below 2^24, product below 2^32).
+// this lane's load i reads gbase + off[i] (32-bit byte offsets) into the
+// slot the swizzled layout assigns it.
 template <int D, int BK, int NW>
-__device__ __forceinline__ void issue_tile_rows(const uint16_t *gbase, uint32_t row_bytes, uint32_t lds_tile,
-                                                int w, const uint32_t (&coff)[4],
-                                                const int (&tok)[TileLoads<D, BK, NW>::NI]) {
+__device__ __forceinline__ void issue_tile_offs(const uint16_t *gbase, uint32_t lds_tile, int w,
+                                                const uint32_t (&off)[TileLoads<D, BK, NW>::NI]) {
   constexpr int NI = TileLoads<D, BK, NW>::NI;
   static_assert(D / 8 == 8 || NI % 4 == 0, "the swizzle key must not depend on the wave");
   const uint32_t lbase = lds_tile + w * NI * 1024;
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
-    load_lds16(gbase, __umul24(static_cast<uint32_t>(tok[i]), row_bytes) + coff[i & 3], lbase + i * 1024);
+  for (int i = 0; i < NI; ++i) load_lds16(gbase, off[i], lbase + i * 1024);
 }
 
 // Issue the direct loads of one BKxD bf16 tile (row-major in HBM) into a
