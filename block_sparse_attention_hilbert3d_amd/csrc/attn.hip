@@ -530,7 +530,34 @@ attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
       }
     }
     __syncthreads();
-    for (int key = 0; key < kvalid; ++key) {
+    // four keys at a time: four independent dot-product chains, one max
+    // update and one pass over O per group; then the ragged tail one by one
+    int key = 0;
+    for (; key + 4 <= kvalid; key += 4) {
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        s0 = fmaf(q[d], sK[key * D + d], s0);
+        s1 = fmaf(q[d], sK[(key + 1) * D + d], s1);
+        s2 = fmaf(q[d], sK[(key + 2) * D + d], s2);
+        s3 = fmaf(q[d], sK[(key + 3) * D + d], s3);
+      }
+      const float mx = fmaxf(fmaxf(s0, s1), fmaxf(s2, s3));
+      if (mx > m) {
+        const float a = exp2f(m - mx);
+        l *= a;
+#pragma unroll
+        for (int d = 0; d < D; ++d) o[d] *= a;
+        m = mx;
+      }
+      const float p0 = exp2f(s0 - m), p1 = exp2f(s1 - m), p2 = exp2f(s2 - m), p3 = exp2f(s3 - m);
+      l += (p0 + p1) + (p2 + p3);
+#pragma unroll
+      for (int d = 0; d < D; ++d)
+        o[d] = fmaf(p3, sV[(key + 3) * D + d],
+                    fmaf(p2, sV[(key + 2) * D + d], fmaf(p1, sV[(key + 1) * D + d], fmaf(p0, sV[key * D + d], o[d]))));
+    }
+    for (; key < kvalid; ++key) {
       float s = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) s = fmaf(q[d], sK[key * D + d], s);
