@@ -52,26 +52,6 @@ __device__ __forceinline__ void row_bcast_clamped(int v, int (&tok)[N]) {
   }
 }
 
-// (head, query block) of workgroup b. Without an order, neighbouring blocks
-// of one head go to one XCD (shared L2). With one, the b-th workgroup takes
-// list row order[b] (longest lists first); shared lists order blocks, and
-// the nh heads of a block are consecutive workgroups.
-__device__ __forceinline__ void block_of(int b, const int32_t *order, int kv_shared, int nh, int nb,
-                                         int &h, int &I) {
-  if (order == nullptr) {
-    const int bid = xcd_remap(b, nh * nb);
-    h = bid / nb;
-    I = bid - h * nb;
-  } else if (kv_shared) {
-    h = b % nh;
-    I = min(max(order[b / nh], 0), nb - 1);
-  } else {
-    const int e = min(max(order[b], 0), nh * nb - 1);
-    h = e / nb;
-    I = e - h * nb;
-  }
-}
-
 // Software-pipelined variant. Each listed key block is processed in stages
 // of ST keys (ST = 64 splits a 128-key block in two). K and V stages are
 // double-buffered in LDS so that S(c+1) = K(c+1) Q^T is computed in the same

@@ -8,14 +8,16 @@
 //   dV_j = sum_i P_ij dO_i,   dS_ij = P_ij (dO_i . V_j - D_i),
 //   dQ_i = scale sum_j dS_ij K_j,   dK_j = scale sum_i dS_ij Q_i.
 // P is rebuilt from the forward's log-sum-exp, so nothing quadratic is
-// stored. Two kernels keep every sum in a fixed order (bit-reproducible):
+// stored. Three kernels keep every sum in a fixed order (bit-reproducible):
 //  - dQ: one workgroup per (head, query block), over its list (as the
 //    forward), S^T = K Q^T and dP^T = V dO^T with one query per lane
 //    column, dQ^T += K^T dS^T with K^T read by ds_read_b64_tr_b16;
-//  - dK/dV: one workgroup per (head, key block), over the query blocks whose
-//    list holds it (a transposed list built first), S = Q K^T and
-//    dP = dO V^T with one key per lane column so P and dS feed
-//    dV^T += dO^T P and dK^T += Q^T dS straight from the accumulators.
+//  - dV and dK: one workgroup per (head, key block), over the query blocks
+//    whose list holds it (a transposed list built first), S = Q K^T (and
+//    dP = dO V^T) with one key per lane column so P (dS) feeds
+//    dV^T += dO^T P (dK^T += Q^T dS) straight from the accumulators.
+// Each is software-pipelined and sized for two waves per SIMD; workgroups
+// take their rows longest list first.
 // bf16 runs on 32x32x16 matrix cores with float accumulation; P and dS are
 // rounded to bf16 for the products, as the forward rounds P. Float inputs use
 // plain one-thread-per-row loops. Pad query rows and pad keys get zero
@@ -146,27 +148,33 @@ __device__ __forceinline__ void store_rows(uint16_t *row, const f32x16 (&acc)[D 
     }
 }
 
-// Stages of ST = 64 rows (half a 128-row block) are double-buffered in LDS:
-// the direct loads of stage t + 1 are issued before stage t is computed.
-constexpr int kBwdStage = 64;
+// dQ, software-pipelined like the forward: stage c's dS and dQ products
+// run in the same scheduling region as the next stage's S and dP products.
+// K and V stages in row layout (b128 reads) are consumed an iteration
+// before the transposed K copy, so iteration c issues K, V for stage c + 2
+// and the transposed K for stage c + 1, each into the buffer freed by the
+// barrier that opens the iteration.
+constexpr int kDqStage = 32;
 
 template <int D, int BK>
-__global__ void __launch_bounds__(BK * 2, 1)
+__global__ void __launch_bounds__(BK * 2, 2)
 attn_bwd_dq_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
                    const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
                    const float *__restrict__ lse, const float *__restrict__ delta,
                    const int32_t *__restrict__ blk_len, const int32_t *__restrict__ kv_idx,
-                   const int32_t *__restrict__ kv_cnt, int max_kv, int kv_shared, int nh, int nb,
-                   float scale_log2, float scale, uint16_t *__restrict__ dqp) {
-  constexpr int ST = kBwdStage, NS = BK / ST;
+                   const int32_t *__restrict__ kv_cnt, const int32_t *__restrict__ order, int max_kv,
+                   int kv_shared, int nh, int nb, float scale_log2, float scale,
+                   uint16_t *__restrict__ dqp) {
+  // 32-key stages keep registers under 256 and LDS at 48 KB, so two
+  // workgroups (two waves per SIMD) share a CU
+  constexpr int ST = kDqStage, NS = BK / ST;
   constexpr int NW = BK / 32, CPR = D / 8, DK = D / 16, DM = D / 32, MT = ST / 32, TILE = ST * D;
-  constexpr int LOADS = 3 * (ST * CPR / (64 * NW));  // direct loads per wave per stage
+  constexpr int NI = ST * CPR / (64 * NW);  // direct loads per wave per tile
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2 * TILE];   // b128 rows (K swizzle)
   __shared__ __attribute__((aligned(1024))) uint16_t sKt[2 * TILE];  // transposed reads (V swizzle)
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2 * TILE];   // b128 rows (K swizzle)
-  const int total = nh * nb;
-  const int bid = xcd_remap(blockIdx.x, total);
-  const int h = bid / nb, I = bid - h * nb;
+  int h, I;  // longest lists first
+  block_of(blockIdx.x, order, kv_shared, nh, nb, h, I);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ln = lane & 31;
@@ -174,11 +182,13 @@ attn_bwd_dq_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__
   const int64_t head_off = static_cast<int64_t>(h) * n_pad * D;
   const int qslot = I * BK + w * 32 + ln;
   const FragOffsets<D> fo(lane);
-  uint32_t koff[4], voff[4];
+  // lane offsets of this wave's NI direct loads (slice w*NI + i of the tile;
+  // the swizzle key depends on the absolute slice)
+  uint32_t koff[NI], voff[NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    koff[i] = tile_lane_offset<D, false>(i, lane);
-    voff[i] = tile_lane_offset<D, true>(i, lane);
+  for (int i = 0; i < NI; ++i) {
+    koff[i] = tile_lane_offset<D, false>(w * NI + i, lane);
+    voff[i] = tile_lane_offset<D, true>(w * NI + i, lane);
   }
   const uint32_t ldsK = lds_addr(sK), ldsKt = lds_addr(sKt), ldsV = lds_addr(sV);
   lds_char_t *const ktl = to_lds(sKt);
@@ -201,47 +211,58 @@ attn_bwd_dq_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__
   const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
   const int nst = kv_cnt[lrow] * NS;
   const int32_t *list = kv_idx + lrow * max_kv;
-  auto issue = [&](int t) {
-    const int64_t off = head_off + (static_cast<int64_t>(list[t / NS]) * BK + (t % NS) * ST) * D;
-    const uint32_t b = static_cast<uint32_t>((t & 1) * TILE * 2);
-    issue_tile<D, ST, NW>(kp + off, ldsK + b, w, koff);
-    issue_tile<D, ST, NW>(kp + off, ldsKt + b, w, voff);
-    issue_tile<D, ST, NW>(vp + off, ldsV + b, w, koff);
+  auto stage_off = [&](int t) {
+    return head_off + (static_cast<int64_t>(list[t / NS]) * BK + (t % NS) * ST) * D;
   };
-  if (nst > 0) issue(0);
-  for (int t = 0; t < nst; ++t) {
-    const int buf = t & 1;
-    const int kvalid = min(max(blk_len[list[t / NS]] - (t % NS) * ST, 0), ST);
-    if (t + 1 < nst) {
-      issue(t + 1);  // its buffer was released by the barrier closing iteration t - 1
-      wait_vmcnt<LOADS>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __syncthreads();  // stage t is in LDS for every wave
+  auto stage_valid = [&](int t) { return min(max(blk_len[list[t / NS]] - (t % NS) * ST, 0), ST); };
+  auto issue = [&](const uint16_t *src, uint32_t lds_tile, const uint32_t (&off)[NI]) {
+    const char *gb = reinterpret_cast<const char *>(src) + w * NI * 1024;
+    const uint32_t lb = lds_tile + w * NI * 1024;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) load_lds16(gb + i * 1024, off[i] - static_cast<uint32_t>(0), lb + i * 1024);
+  };
+  auto issue_rows = [&](int t) {  // K and V in row layout, buffer t & 1
+    const int64_t off = stage_off(t);
+    const uint32_t b = static_cast<uint32_t>((t & 1) * TILE * 2);
+    issue(kp + off, ldsK + b, koff);
+    issue(vp + off, ldsV + b, koff);
+  };
+  auto issue_tr = [&](int t) {  // transposed K, buffer t & 1
+    issue(kp + stage_off(t), ldsKt + static_cast<uint32_t>((t & 1) * TILE * 2), voff);
+  };
+  // S^T = K Q^T and dP^T = V dO^T of one stage (one query per lane column)
+  auto compute_sdp = [&](f32x16 (&s)[MT], f32x16 (&dp)[MT], int buf) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s[i] = 0.f;
-        dp[i] = 0.f;
+        s[mt][i] = 0.f;
+        dp[mt][i] = 0.f;
       }
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(&sK[buf * TILE + (mt * 32 * CPR + fo.row[ks]) * 8]);
         const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(&sV[buf * TILE + (mt * 32 * CPR + fo.row[ks]) * 8]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[ks], dp, 0, 0, 0);
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mt], 0, 0, 0);
+        dp[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, dof[ks], dp[mt], 0, 0, 0);
       }
+    }
+  };
+  // dS = P (dP - D) from the stage's S, dP; dQ^T += K^T dS^T
+  auto ds_dq = [&](const f32x16 (&s)[MT], const f32x16 (&dp)[MT], int buf, int kvalid) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
       // element i is key mt*32 + 8(i/4) + 4g + i%4 of the stage, query = lane column
       const int lim = kvalid - mt * 32 - g * 4;
       float ds[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const bool real_key = (i >> 2) * 8 + (i & 3) < lim;
-        const float p = real_key ? __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -lq2)) : 0.f;
-        ds[i] = p * (dp[i] - dq_i);
+        // pad keys: exponent -inf, so p = 0 (computed, then selected)
+        float arg = fmaf(s[mt][i], scale_log2, -lq2);
+        arg = real_key ? arg : -INFINITY;
+        const float p = __builtin_amdgcn_exp2f(arg);
+        ds[i] = p * (dp[mt][i] - dq_i);
       }
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
@@ -254,34 +275,75 @@ attn_bwd_dq_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__
               tr_frag<D>(ktl + buf * TILE * 2, fo.tr[md], mt * 2 + ks2), dsf, acc[md], 0, 0, 0);
       }
     }
-    __syncthreads();  // every wave is done with buffer t & 1
+  };
+
+  f32x16 sA[MT], dA[MT], sB[MT], dB[MT];
+  if (nst > 0) {
+    issue_rows(0);
+    issue_tr(0);
+    if (nst > 1) issue_rows(1);
+    wait_vmcnt<0>();
+    __syncthreads();
+    compute_sdp(sA, dA, 0);
+  }
+  // iteration c: issue K, V (c + 2) and K^T (c + 1); S, dP (c + 1) beside dS, dQ (c)
+  auto body = [&](int c, f32x16 (&sc)[MT], f32x16 (&dc)[MT], f32x16 (&sn)[MT], f32x16 (&dn)[MT]) {
+    __syncthreads();  // row buffer c & 1 and transposed buffer (c + 1) & 1 are free
+    if (c + 2 < nst) issue_rows(c + 2);
+    if (c + 1 < nst) issue_tr(c + 1);
+    const int kvalid = stage_valid(c);
+    // unconditional so it shares a scheduling region with ds_dq; on the last
+    // stage it reads an idle buffer and the result is unused
+    compute_sdp(sn, dn, (c + 1) & 1);
+    ds_dq(sc, dc, c & 1, kvalid);
+    __builtin_amdgcn_iglp_opt(3);
+    wait_vmcnt<0>();
+  };
+  for (int c = 0; c < nst; c += 2) {
+    body(c, sA, dA, sB, dB);
+    if (c + 1 < nst) body(c + 1, sB, dB, sA, dA);
   }
   const bool real = (w * 32 + ln) < blk_len[I];
   store_rows<D>(dqp + head_off + static_cast<int64_t>(qslot) * D, acc, real ? scale : 0.f, g);
 }
 
-template <int D, int BK>
-__global__ void __launch_bounds__(BK * 2, 1)
-attn_bwd_dkdv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
-                     const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
-                     const float *__restrict__ lse, const float *__restrict__ delta,
-                     const int32_t *__restrict__ blk_len, const int32_t *__restrict__ t_idx,
-                     const int32_t *__restrict__ t_cnt, int kv_shared, int nh, int nb, float scale_log2,
-                     float scale, uint16_t *__restrict__ dkp, uint16_t *__restrict__ dvp) {
-  constexpr int ST = kBwdStage, NS = BK / ST;
-  constexpr int NW = BK / 32, CPR = D / 8, DK = D / 16, DM = D / 32, QT = ST / 32, TILE = ST * D;
-  // four tiles per stage, plus the stage's lse and D rows (one load each)
-  constexpr int LOADS = 4 * (ST * CPR / (64 * NW)) + 2;
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ[2 * TILE];    // b128 rows
-  __shared__ __attribute__((aligned(1024))) uint16_t sQt[2 * TILE];   // transposed reads
-  __shared__ __attribute__((aligned(1024))) uint16_t sdO[2 * TILE];   // b128 rows
-  __shared__ __attribute__((aligned(1024))) uint16_t sdOt[2 * TILE];  // transposed reads
-  // per wave and buffer: 64 lse values then 64 D values (each 1 KB load
-  // fills 256 B of data; the other lanes repeat it)
+// dK and dV in two kernels over the transposed lists (one workgroup per
+// (head, key block), one key per lane column): the dV kernel forms S and P
+// and accumulates dV^T += dO^T P; the dK kernel forms S, dP and dS and
+// accumulates dK^T += Q^T dS. Splitting recomputes S once more (5 products
+// instead of 4) but halves the accumulators, so each kernel fits two waves
+// per SIMD with 32-query stages and is software-pipelined like the forward:
+// the next stage's S (and dP) products share a scheduling region with this
+// stage's exponentials and accumulation. Tiles read in row layout (Q, dO)
+// are consumed an iteration before the transposed ones (dO^T, Q^T) and the
+// stage's lse / D rows.
+// 64-query stages for dV (fewer barriers per product; registers allow it),
+// 32 for dK (more live accumulators).
+template <bool DK>
+constexpr int dkv_stage() { return DK ? 32 : 64; }
+
+template <int D, int BK, bool DK>
+__global__ void __launch_bounds__(BK * 2, 2)
+attn_bwd_dkv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
+                    const uint16_t *__restrict__ vp, const uint16_t *__restrict__ dop,
+                    const float *__restrict__ lse, const float *__restrict__ delta,
+                    const int32_t *__restrict__ blk_len, const int32_t *__restrict__ t_idx,
+                    const int32_t *__restrict__ t_cnt, const int32_t *__restrict__ order, int kv_shared,
+                    int nh, int nb, float scale_log2, float scale, uint16_t *__restrict__ outp) {
+  constexpr int ST = dkv_stage<DK>(), NS = BK / ST, QT = ST / 32;
+  constexpr int NW = BK / 32, CPR = D / 8, DKS = D / 16, DM = D / 32, TILE = ST * D;
+  constexpr int NI = ST * CPR / (64 * NW);  // direct loads per wave per tile
+  // row-layout tiles: Q (and dO for dK); transposed: dO^T for dV, Q^T for dK
+  __shared__ __attribute__((aligned(1024))) uint16_t sA[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB[DK ? 2 * TILE : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t sT[2 * TILE];
+  // per wave and buffer: the stage's lse (and D) rows; each 1 KB load
+  // fills ST * 4 bytes of data, the other lanes repeat it
   __shared__ __attribute__((aligned(1024))) float sLD[NW][2][2][256];
-  const int total = nh * nb;
-  const int bid = xcd_remap(blockIdx.x, total);
-  const int h = bid / nb, J = bid - h * nb;
+  // key blocks with the longest transposed lists first (uneven lists would
+  // otherwise leave a tail of long workgroups)
+  int h, J;
+  block_of(blockIdx.x, order, kv_shared, nh, nb, h, J);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ln = lane & 31;
@@ -289,116 +351,146 @@ attn_bwd_dkdv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict
   const int64_t head_off = static_cast<int64_t>(h) * n_pad * D;
   const int kslot = J * BK + w * 32 + ln;
   const FragOffsets<D> fo(lane);
-  uint32_t koff[4], voff[4];
+  uint32_t koff[NI], voff[NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    koff[i] = tile_lane_offset<D, false>(i, lane);
-    voff[i] = tile_lane_offset<D, true>(i, lane);
+  for (int i = 0; i < NI; ++i) {
+    koff[i] = tile_lane_offset<D, false>(w * NI + i, lane);
+    voff[i] = tile_lane_offset<D, true>(w * NI + i, lane);
   }
-  const uint32_t ldsQ = lds_addr(sQ), ldsQt = lds_addr(sQt), ldsO = lds_addr(sdO), ldsOt = lds_addr(sdOt);
+  const uint32_t ldsA = lds_addr(sA), ldsB = lds_addr(sB), ldsT = lds_addr(sT);
   const uint32_t ldsLD = __builtin_amdgcn_readfirstlane(lds_addr(&sLD[w][0][0][0]));
-  lds_char_t *const qtl = to_lds(sQt);
-  lds_char_t *const otl = to_lds(sdOt);
+  lds_char_t *const ttl = to_lds(sT);
 
-  bf16x8 kf[DK], vf[DK];
+  bf16x8 kf[DKS], vf[DKS];
   load_row_frags<D>(kp + head_off + static_cast<int64_t>(kslot) * D, g, kf);
-  load_row_frags<D>(vp + head_off + static_cast<int64_t>(kslot) * D, g, vf);
+  if constexpr (DK) load_row_frags<D>(vp + head_off + static_cast<int64_t>(kslot) * D, g, vf);
 #pragma unroll
-  for (int ks = 0; ks < DK; ++ks) asm volatile("" ::"v"(kf[ks]), "v"(vf[ks]));
+  for (int ks = 0; ks < DKS; ++ks) {
+    asm volatile("" ::"v"(kf[ks]));
+    if constexpr (DK) asm volatile("" ::"v"(vf[ks]));
+  }
 
-  f32x16 dk[DM], dv[DM];
+  f32x16 acc[DM];
 #pragma unroll
   for (int md = 0; md < DM; ++md)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dk[md][i] = 0.f;
-      dv[md][i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) acc[md][i] = 0.f;
 
   const int64_t lrow = kv_shared ? static_cast<int64_t>(J) : static_cast<int64_t>(h) * nb + J;
   const int nst = t_cnt[lrow] * NS;
   const int32_t *tl = t_idx + lrow * nb;
-  const uint32_t ld_off = static_cast<uint32_t>((lane & 15) * 16);  // 16 lanes x 16 B = 64 floats
-  auto issue = [&](int t) {
-    const int64_t row0 = static_cast<int64_t>(tl[t / NS]) * BK + (t % NS) * ST;
-    const int64_t off = head_off + row0 * D;
+  const uint32_t ld_off = static_cast<uint32_t>((lane & (ST / 4 - 1)) * 16);  // ST floats
+  auto stage_row0 = [&](int t) { return static_cast<int64_t>(tl[t / NS]) * BK + (t % NS) * ST; };
+  auto stage_valid = [&](int t) { return min(max(blk_len[tl[t / NS]] - (t % NS) * ST, 0), ST); };
+  auto issue = [&](const uint16_t *src, uint32_t lds_tile, const uint32_t (&off)[NI]) {
+    const char *gb = reinterpret_cast<const char *>(src) + w * NI * 1024;
+    const uint32_t lb = lds_tile + w * NI * 1024;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) load_lds16(gb + i * 1024, off[i], lb + i * 1024);
+  };
+  auto issue_rows = [&](int t) {  // Q (and dO) in row layout, buffer t & 1
+    const int64_t off = head_off + stage_row0(t) * D;
     const uint32_t b = static_cast<uint32_t>((t & 1) * TILE * 2);
-    issue_tile<D, ST, NW>(qp + off, ldsQ + b, w, koff);
-    issue_tile<D, ST, NW>(qp + off, ldsQt + b, w, voff);
-    issue_tile<D, ST, NW>(dop + off, ldsO + b, w, koff);
-    issue_tile<D, ST, NW>(dop + off, ldsOt + b, w, voff);
+    issue(qp + off, ldsA + b, koff);
+    if constexpr (DK) issue(dop + off, ldsB + b, koff);
+  };
+  auto issue_tr = [&](int t) {  // dO^T (dV) or Q^T (dK), and the lse / D rows, buffer t & 1
+    const int64_t row0 = stage_row0(t);
+    issue((DK ? qp : dop) + head_off + row0 * D, ldsT + static_cast<uint32_t>((t & 1) * TILE * 2), voff);
     const int64_t r = static_cast<int64_t>(h) * n_pad + row0;
     const uint32_t lb = ldsLD + static_cast<uint32_t>((t & 1) * 2 * 256 * 4);
     load_lds16(lse + r, ld_off, lb);
-    load_lds16(delta + r, ld_off, lb + 256 * 4);
+    if constexpr (DK) load_lds16(delta + r, ld_off, lb + 256 * 4);
   };
-  if (nst > 0) issue(0);
-  for (int t = 0; t < nst; ++t) {
-    const int buf = t & 1;
-    const int qvalid = min(max(blk_len[tl[t / NS]] - (t % NS) * ST, 0), ST);
-    if (t + 1 < nst) {
-      issue(t + 1);
-      wait_vmcnt<LOADS>();
-    } else {
-      wait_vmcnt<0>();
+  // S = Q K^T (and dP = dO V^T): element i of tile qt is query
+  // qt*32 + 8(i/4) + 4g + i%4 of the stage, key = lane column
+  auto compute_s = [&](f32x16 (&s)[QT], f32x16 (&dp)[QT], int buf) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[qt][i] = 0.f;
+        dp[qt][i] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < DKS; ++ks) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(&sA[buf * TILE + (qt * 32 * CPR + fo.row[ks]) * 8]);
+        s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s[qt], 0, 0, 0);
+        if constexpr (DK) {
+          const bf16x8 oa = *reinterpret_cast<const bf16x8 *>(&sB[buf * TILE + (qt * 32 * CPR + fo.row[ks]) * 8]);
+          dp[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp[qt], 0, 0, 0);
+        }
+      }
     }
-    __syncthreads();
+  };
+  // P (and dS) of a stage, then dV^T += dO^T P or dK^T += Q^T dS
+  auto accumulate = [&](const f32x16 (&s)[QT], const f32x16 (&dp)[QT], int buf, int qvalid) {
     const float *sL = &sLD[w][buf][0][0];
     const float *sD = &sLD[w][buf][1][0];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      f32x16 s, dp;
+    float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] = 0.f;
-        dp[i] = 0.f;
-      }
-#pragma unroll
-      for (int ks = 0; ks < DK; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(&sQ[buf * TILE + (qt * 32 * CPR + fo.row[ks]) * 8]);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8 *>(&sdO[buf * TILE + (qt * 32 * CPR + fo.row[ks]) * 8]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ks], dp, 0, 0, 0);
-      }
-      // element i is query qt*32 + 8(i/4) + 4g + i%4 of the stage, key = lane column
-      float p[16], ds[16];
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int q0 = qt * 32 + i4 * 8 + g * 4;
-        const float4 l4 = *reinterpret_cast<const float4 *>(&sL[q0]);
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int q0 = qt * 32 + i4 * 8 + g * 4;
+      const float4 l4 = *reinterpret_cast<const float4 *>(&sL[q0]);
+      const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+      float dv4[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (DK) {
         const float4 d4 = *reinterpret_cast<const float4 *>(&sD[q0]);
-        const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = i4 * 4 + r;
-          const float pv = (q0 + r < qvalid) ? __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -lv[r])) : 0.f;
-          p[i] = pv;
-          ds[i] = pv * (dp[i] - dv4[r]);
-        }
+        dv4[0] = d4.x; dv4[1] = d4.y; dv4[2] = d4.z; dv4[3] = d4.w;
       }
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        bf16x8 pf, dsf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pf[j] = static_cast<__bf16>(p[ks2 * 8 + j]);
-          dsf[j] = static_cast<__bf16>(ds[ks2 * 8 + j]);
-        }
-#pragma unroll
-        for (int md = 0; md < DM; ++md) {
-          dv[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_frag<D>(otl + buf * TILE * 2, fo.tr[md], qt * 2 + ks2), pf, dv[md], 0, 0, 0);
-          dk[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_frag<D>(qtl + buf * TILE * 2, fo.tr[md], qt * 2 + ks2), dsf, dk[md], 0, 0, 0);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int i = i4 * 4 + r;
+        // pad query rows: exponent -inf, so p = 0 (computed unconditionally,
+        // then selected, so no branch splits the scheduling region)
+        float arg = fmaf(s[qt][i], scale_log2, -lv[r]);
+        arg = (q0 + r < qvalid) ? arg : -INFINITY;
+        const float pv = __builtin_amdgcn_exp2f(arg);
+        x[i] = DK ? pv * (dp[qt][i] - dv4[r]) : pv;
       }
     }
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      bf16x8 xf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xf[j] = static_cast<__bf16>(x[ks2 * 8 + j]);
+#pragma unroll
+      for (int md = 0; md < DM; ++md)
+        acc[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_frag<D>(ttl + buf * TILE * 2, fo.tr[md], qt * 2 + ks2), xf, acc[md], 0, 0, 0);
+    }
+    }
+  };
+
+  f32x16 s0[QT], d0[QT], s1[QT], d1[QT];
+  if (nst > 0) {
+    issue_rows(0);
+    issue_tr(0);
+    if (nst > 1) issue_rows(1);
+    wait_vmcnt<0>();
     __syncthreads();
+    compute_s(s0, d0, 0);
+  }
+  // iteration c: row tiles of stage c + 2, transposed tile and lse / D of
+  // stage c + 1; S (dP) of stage c + 1 beside the accumulation of stage c
+  auto body = [&](int c, f32x16 (&sc)[QT], f32x16 (&dc)[QT], f32x16 (&sn)[QT], f32x16 (&dn)[QT]) {
+    __syncthreads();  // row buffer c & 1 and transposed buffer (c + 1) & 1 are free
+    if (c + 2 < nst) issue_rows(c + 2);
+    if (c + 1 < nst) issue_tr(c + 1);
+    const int qvalid = stage_valid(c);
+    compute_s(sn, dn, (c + 1) & 1);  // on the last stage: an idle buffer, result unused
+    accumulate(sc, dc, c & 1, qvalid);
+    __builtin_amdgcn_iglp_opt(3);
+    wait_vmcnt<0>();
+  };
+  for (int c = 0; c < nst; c += 2) {
+    body(c, s0, d0, s1, d1);
+    if (c + 1 < nst) body(c + 1, s1, d1, s0, d0);
   }
   const bool real = (w * 32 + ln) < blk_len[J];
-  store_rows<D>(dkp + head_off + static_cast<int64_t>(kslot) * D, dk, real ? scale : 0.f, g);
-  store_rows<D>(dvp + head_off + static_cast<int64_t>(kslot) * D, dv, real ? 1.f : 0.f, g);
+  store_rows<D>(outp + head_off + static_cast<int64_t>(kslot) * D, acc, real ? (DK ? scale : 1.f) : 0.f, g);
 }
 
 // Float inputs: one thread per query row (dQ) / per key row (dK, dV), tiles
@@ -526,10 +618,13 @@ namespace hsa_host {
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
+hsa_status_t launch_attn_order(const int32_t *kv_cnt, int G, int nb, int max_kv, int32_t *order,
+                               hipStream_t stream);
+
 size_t attn_bwd_ws_bytes(int nh, int nb, int B, int G) {
   return align256(static_cast<size_t>(nh) * nb * B * sizeof(float)) +
          align256(static_cast<size_t>(G) * nb * nb * sizeof(int32_t)) +
-         align256(static_cast<size_t>(G) * nb * sizeof(int32_t));
+         3 * align256(static_cast<size_t>(G) * nb * sizeof(int32_t));
 }
 
 hsa_status_t launch_attn_bwd(const void *qp, const void *kp, const void *vp, const void *op, const void *dop,
@@ -544,6 +639,10 @@ hsa_status_t launch_attn_bwd(const void *qp, const void *kp, const void *vp, con
   int32_t *t_idx = reinterpret_cast<int32_t *>(base);
   base += align256(static_cast<size_t>(G) * nb * nb * sizeof(int32_t));
   int32_t *t_cnt = reinterpret_cast<int32_t *>(base);
+  base += align256(static_cast<size_t>(G) * nb * sizeof(int32_t));
+  int32_t *t_order = reinterpret_cast<int32_t *>(base);
+  base += align256(static_cast<size_t>(G) * nb * sizeof(int32_t));
+  int32_t *q_order = reinterpret_cast<int32_t *>(base);
   const int n_pad = nb * B;
   const int64_t total = static_cast<int64_t>(nh) * n_pad;
   const dim3 dgrid(static_cast<unsigned>((total + 255) / 256));
@@ -556,6 +655,17 @@ hsa_status_t launch_attn_bwd(const void *qp, const void *kp, const void *vp, con
 #undef HSA_DELTA
   hipLaunchKernelGGL(hsa::bwd_transpose_kernel, dim3(G * nb), dim3(64), 0, stream, kv_idx, kv_cnt, nb,
                      max_kv, t_idx, t_cnt);
+  // longest transposed lists first for the dK / dV kernels (the counting
+  // sort takes lengths up to 4095; beyond that the natural order is kept)
+  const int32_t *korder = nullptr, *qorder = nullptr;
+  if (nb <= 4095) {
+    launch_attn_order(t_cnt, G, nb, nb, t_order, stream);
+    korder = t_order;
+  }
+  if (max_kv <= 4095) {  // and the query blocks' own lists for dQ
+    launch_attn_order(kv_cnt, G, nb, max_kv, q_order, stream);
+    qorder = q_order;
+  }
   const dim3 grid(nh * nb);
   const float sl2 = scale * hsa::kLog2e;
   if (bf) {
@@ -565,9 +675,11 @@ hsa_status_t launch_attn_bwd(const void *qp, const void *kp, const void *vp, con
 #define HSA_BWD(DD, BB)                                                                                 \
   do {                                                                                                  \
     hipLaunchKernelGGL((hsa::attn_bwd_dq_kernel<DD, BB>), grid, dim3(BB * 2), 0, stream, q, k, v, dO, lse, \
-                       delta, blk_len, kv_idx, kv_cnt, max_kv, kv_shared, nh, nb, sl2, scale, dq);        \
-    hipLaunchKernelGGL((hsa::attn_bwd_dkdv_kernel<DD, BB>), grid, dim3(BB * 2), 0, stream, q, k, v, dO,    \
-                       lse, delta, blk_len, t_idx, t_cnt, kv_shared, nh, nb, sl2, scale, dk, dv);         \
+                       delta, blk_len, kv_idx, kv_cnt, qorder, max_kv, kv_shared, nh, nb, sl2, scale, dq); \
+    hipLaunchKernelGGL((hsa::attn_bwd_dkv_kernel<DD, BB, false>), grid, dim3(BB * 2), 0, stream, q, k, v, dO, \
+                       lse, delta, blk_len, t_idx, t_cnt, korder, kv_shared, nh, nb, sl2, scale, dv);     \
+    hipLaunchKernelGGL((hsa::attn_bwd_dkv_kernel<DD, BB, true>), grid, dim3(BB * 2), 0, stream, q, k, v, dO, \
+                       lse, delta, blk_len, t_idx, t_cnt, korder, kv_shared, nh, nb, sl2, scale, dk);     \
   } while (0)
     if (D == 128 && B == 128) HSA_BWD(128, 128);
     else if (D == 64 && B == 128) HSA_BWD(64, 128);

@@ -57,6 +57,27 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return (b % 8) * per + b / 8;
 }
 
+// (head, list row) of workgroup b for kernels with one workgroup per (head,
+// block). Without an order, neighbouring blocks of one head go to one XCD
+// (shared L2). With one, the b-th workgroup takes row order[b] (longest
+// lists first); shared lists order blocks, and the nh heads of a block are
+// consecutive workgroups.
+__device__ __forceinline__ void block_of(int b, const int32_t *order, int kv_shared, int nh, int nb,
+                                         int &h, int &I) {
+  if (order == nullptr) {
+    const int bid = xcd_remap(b, nh * nb);
+    h = bid / nb;
+    I = bid - h * nb;
+  } else if (kv_shared) {
+    h = b % nh;
+    I = min(max(order[b / nh], 0), nb - 1);
+  } else {
+    const int e = min(max(order[b], 0), nh * nb - 1);
+    h = e / nb;
+    I = e - h * nb;
+  }
+}
+
 // One 16-byte-per-lane direct global->LDS load: lane l's 16 bytes come from
 // sbase + voff (sbase wave-uniform) and land at lds_base + 16*l. Issued from
 // asm so the compiler does not add blanket vmcnt(0) waits in front of
