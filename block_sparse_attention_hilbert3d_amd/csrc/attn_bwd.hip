@@ -216,10 +216,7 @@ attn_bwd_dq_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__
   };
   auto stage_valid = [&](int t) { return min(max(blk_len[list[t / NS]] - (t % NS) * ST, 0), ST); };
   auto issue = [&](const uint16_t *src, uint32_t lds_tile, const uint32_t (&off)[NI]) {
-    const char *gb = reinterpret_cast<const char *>(src) + w * NI * 1024;
-    const uint32_t lb = lds_tile + w * NI * 1024;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) load_lds16(gb + i * 1024, off[i] - static_cast<uint32_t>(0), lb + i * 1024);
+    issue_tile_slices<NI>(src, lds_tile, w, off);
   };
   auto issue_rows = [&](int t) {  // K and V in row layout, buffer t & 1
     const int64_t off = stage_off(t);
@@ -383,10 +380,7 @@ attn_bwd_dkv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict_
   auto stage_row0 = [&](int t) { return static_cast<int64_t>(tl[t / NS]) * BK + (t % NS) * ST; };
   auto stage_valid = [&](int t) { return min(max(blk_len[tl[t / NS]] - (t % NS) * ST, 0), ST); };
   auto issue = [&](const uint16_t *src, uint32_t lds_tile, const uint32_t (&off)[NI]) {
-    const char *gb = reinterpret_cast<const char *>(src) + w * NI * 1024;
-    const uint32_t lb = lds_tile + w * NI * 1024;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) load_lds16(gb + i * 1024, off[i], lb + i * 1024);
+    issue_tile_slices<NI>(src, lds_tile, w, off);
   };
   auto issue_rows = [&](int t) {  // Q (and dO) in row layout, buffer t & 1
     const int64_t off = head_off + stage_row0(t) * D;

@@ -163,6 +163,19 @@ __device__ __forceinline__ void issue_tile_offs(const uint16_t *gbase, uint32_t 
   for (int i = 0; i < NI; ++i) load_lds16(gbase, off[i], lbase + i * 1024);
 }
 
+// Issue wave w's NI consecutive 1 KB slices of a row-major tile (slices
+// w*NI .. w*NI + NI - 1) with one lane offset per load, for tiles whose
+// swizzle key changes from wave to wave (off[i] from tile_lane_offset of
+// slice w*NI + i).
+template <int NI>
+__device__ __forceinline__ void issue_tile_slices(const uint16_t *gtile, uint32_t lds_tile, int w,
+                                                  const uint32_t (&off)[NI]) {
+  const char *gb = reinterpret_cast<const char *>(gtile) + w * NI * 1024;
+  const uint32_t lb = lds_tile + w * NI * 1024;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) load_lds16(gb + i * 1024, off[i], lb + i * 1024);
+}
+
 // Issue the direct loads of one BKxD bf16 tile (row-major in HBM) into a
 // swizzled LDS tile; each wave moves NI consecutive 1 KB slices.
 template <int D, int BK, int NW>

@@ -439,6 +439,15 @@ def test_full_keep_is_dense_attention(hsa, B, D, dtype):
     err = np.abs(to_np(o) - ref).max()
     _say(f"  max err vs dense = {err:.3e}")
     assert err <= TOL[dtype]
+    # the token-order entry point, with K/V reordered and with K/V gathered,
+    # gives the same bits and the same lse on real slots
+    qd, kd, vd = (x.to(dev()) for x in (q, k, v))
+    real = perm >= 0
+    for kk, vv in ((kp, vp), (kd, vd)):
+        ot, lset = hsa.hsa_attn_tokens(qd, kk, vv, perm, blk_len, kv_idx, kv_cnt, B)
+        torch.cuda.synchronize()
+        assert torch.equal(ot, o)
+        assert torch.equal(lset[:, real], lse[:, real])
 
 
 def test_lists_with_single_and_repeated_blocks(hsa):
@@ -650,6 +659,10 @@ def test_empty_lists_forward_backward(hsa):
             empty = np.broadcast_to(empty, (nh, nb * B)) if G == 1 else empty
             assert np.all(to_np(op)[empty] == 0) and np.all(to_np(lse)[empty] == 0)
             assert np.all(to_np(dq)[empty] == 0)
+            # token-order entry point: the same output rows, written in token order
+            ot, _ = hsa.hsa_attn_tokens(q.to(dev()), kp, vp, perm, blk_len, kv_idx, kv_cnt, B, order=o)
+            torch.cuda.synchronize()
+            assert torch.equal(ot, hsa.hsa_unperm(op, perm, T * H * W))
             ref = oracle.attn_blocks_bwd(*(oracle.gather(x, p) for x in (q, k, v, do)), p, B, idx, cnt)
             for a, r in zip((dq, dk, dv), ref):
                 assert np.abs(to_np(a) - r).max() <= BWD_TOL["bf16"] * max(float(np.abs(r).max()), 1e-6)
