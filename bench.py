@@ -159,8 +159,8 @@ def main():
                          "traffic, to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build's path runs on a single MI355X; "
-              "run it with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the attention path here runs on a single MI355X "
+              "(multi-GPU sharding is designed, not built); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -2,7 +2,7 @@
 
 DFSAttn (Problem, Methodology designs 1-2) argues that a global 3D Hilbert
 order keeps semantically related tokens in the same block and that sub-block
-scoring estimates block importance better than coarse pooling. This driver
+scoring estimates block importance better than coarse pooling. This script
 measures both claims on the synthetic smoothed-field inputs: for each token
 order and sub-block size it builds the layer, selects the top-k key blocks
 (the workload's keep ratio), and reports the share of the exact attention
