@@ -3,11 +3,12 @@
  * tokens, MI355X (gfx950) HIP library, plain C ABI.
  *
  * The path has five steps, each one entry point (plus a once-per-shape plan):
- *   hsa_plan    token order for a latent grid (Hilbert / row-major / frame)
+ *   hsa_plan    token order for a latent grid (3D Hilbert, row-major, frame
+ *               tiles, per-frame 2D Hilbert, VMoBA 2D tiles / 3D cubes)
  *   hsa_perm    gather Q, K, V into the reordered, padded, head-major layout
  *   hsa_score   sub-block pooled block-to-block importance scores
  *   hsa_select  per-query-block lists of key blocks (top-k, threshold +
- *               global budget, or the LVSA frame mask)
+ *               global budget, the LVSA frame mask, DynamicRad radial masks)
  *   hsa_attn    block-sparse flash attention over the listed key blocks
  *   hsa_unperm  scatter the output back to the original token order
  *   (hsa_attn_tokens fuses the gathers and this scatter into attention)
