@@ -17,6 +17,16 @@
 
 namespace hsa {
 
+// Streaming 16-byte load with the nontemporal hint: the token-major inputs
+// are read once here, and the hint measured ~3-5 % faster for the gather
+// (a nontemporal store of the reordered rows was slower: attention reads them
+// right after).
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const void *p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 constexpr int kPermThreads = 256;
 constexpr int kPermMaxPos = 4;  // chunk positions per thread: P <= 1024
 
@@ -79,8 +89,7 @@ perm_gather_kernel(PermArgs a, const int32_t *__restrict__ perm, int n_pad, int 
       for (int k = 0; k < NP; ++k) {
         v[u][k] = make_uint4(0, 0, 0, 0);
         if (tok[u] >= 0 && pos[k] < P)
-          v[u][k] = *reinterpret_cast<const uint4 *>(src + tok[u] * tok_stride_bytes +
-                                                     static_cast<int64_t>(pos[k]) * 16);
+          v[u][k] = load_stream16(src + tok[u] * tok_stride_bytes + static_cast<int64_t>(pos[k]) * 16);
       }
     }
 #pragma unroll
@@ -143,8 +152,7 @@ perm_scatter_kernel(const char *__restrict__ src, char *__restrict__ dst,
     if (tok < 0) continue;
     const int h = rem >> row_shift;
     const int c = rem & (cpr - 1);
-    const uint4 val = *reinterpret_cast<const uint4 *>(
-        src + h * head_stride_bytes + (static_cast<int64_t>(slot) * cpr + c) * 16);
+    const uint4 val = load_stream16(src + h * head_stride_bytes + (static_cast<int64_t>(slot) * cpr + c) * 16);
     *reinterpret_cast<uint4 *>(dst + tok * tok_stride_bytes + static_cast<int64_t>(rem) * 16) = val;
   }
 }
