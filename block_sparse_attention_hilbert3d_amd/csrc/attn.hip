@@ -105,7 +105,8 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     voff[i] = GKV ? tile_lane_chunk<D, true>(i, lane) : tile_lane_offset<D, true>(i, lane);
   }
   const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
-  const int cnt = kv_cnt[lrow];
+  // caller lists: lengths clamped to [0, max_kv], entries to [0, nb)
+  const int cnt = min(max(kv_cnt[lrow], 0), max_kv);
   const int32_t *list = kv_idx + lrow * max_kv;
   const uint16_t *kbase = GKV ? kp + h * D : kp + head_off;
   const uint16_t *vbase = GKV ? vp + h * D : vp + head_off;
@@ -119,7 +120,7 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   int mbase = 0, lo_J, lo_L, hi_J, hi_L;
   auto fetch = [&](int b0, int &mJ, int &mL) {
     const int i = b0 + lane;
-    mJ = i < cnt ? list[i] : 0;
+    mJ = i < cnt ? min(max(list[i], 0), nb - 1) : 0;
     mL = i < cnt ? blk_len[mJ] : 0;
   };
   fetch(0, lo_J, lo_L);
@@ -489,10 +490,10 @@ attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
   }
   float m = -1e30f, l = 0.f;
   const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
-  const int cnt = kv_cnt[lrow];
+  const int cnt = min(max(kv_cnt[lrow], 0), max_kv);
   const int32_t *list = kv_idx + lrow * max_kv;
   for (int c = 0; c < cnt; ++c) {
-    const int J = list[c];
+    const int J = min(max(list[c], 0), nb - 1);
     const int kvalid = blk_len[J];
     if (perm && kv_stride > 0) {  // K/V rows gathered from the token-major tensors
       for (int i = tid; i < BK * D / 4; i += BK) {

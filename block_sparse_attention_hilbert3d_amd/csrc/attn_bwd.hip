@@ -76,7 +76,7 @@ bwd_transpose_kernel(const int32_t *__restrict__ kv_idx, const int32_t *__restri
     bool found = false;
     if (I < nb) {
       const int32_t *list = kv_idx + (static_cast<int64_t>(g) * nb + I) * max_kv;
-      int lo = 0, hi = kv_cnt[static_cast<int64_t>(g) * nb + I];
+      int lo = 0, hi = min(max(kv_cnt[static_cast<int64_t>(g) * nb + I], 0), max_kv);
       const int cnt = hi;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
@@ -209,12 +209,14 @@ attn_bwd_dq_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__
     for (int i = 0; i < 16; ++i) acc[md][i] = 0.f;
 
   const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
-  const int nst = kv_cnt[lrow] * NS;
+  // caller lists: lengths clamped to [0, max_kv], entries to [0, nb)
+  const int nst = min(max(kv_cnt[lrow], 0), max_kv) * NS;
   const int32_t *list = kv_idx + lrow * max_kv;
+  auto entry = [&](int t) { return min(max(list[t / NS], 0), nb - 1); };
   auto stage_off = [&](int t) {
-    return head_off + (static_cast<int64_t>(list[t / NS]) * BK + (t % NS) * ST) * D;
+    return head_off + (static_cast<int64_t>(entry(t)) * BK + (t % NS) * ST) * D;
   };
-  auto stage_valid = [&](int t) { return min(max(blk_len[list[t / NS]] - (t % NS) * ST, 0), ST); };
+  auto stage_valid = [&](int t) { return min(max(blk_len[entry(t)] - (t % NS) * ST, 0), ST); };
   auto issue = [&](const uint16_t *src, uint32_t lds_tile, const uint32_t (&off)[NI]) {
     issue_tile_slices<NI>(src, lds_tile, w, off);
   };
@@ -513,10 +515,10 @@ attn_bwd_dq_f32_kernel(const float *__restrict__ qp, const float *__restrict__ k
   const float L = lse[static_cast<int64_t>(h) * n_pad + qslot];
   const float Di = delta[static_cast<int64_t>(h) * n_pad + qslot];
   const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
-  const int cnt = kv_cnt[lrow];
+  const int cnt = min(max(kv_cnt[lrow], 0), max_kv);
   const int32_t *list = kv_idx + lrow * max_kv;
   for (int c = 0; c < cnt; ++c) {
-    const int J = list[c];
+    const int J = min(max(list[c], 0), nb - 1);
     const int kvalid = blk_len[J];
     const float4 *ks = reinterpret_cast<const float4 *>(kp + head_off + static_cast<int64_t>(J) * BK * D);
     const float4 *vs = reinterpret_cast<const float4 *>(vp + head_off + static_cast<int64_t>(J) * BK * D);

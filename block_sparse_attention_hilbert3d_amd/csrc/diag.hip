@@ -77,7 +77,7 @@ block_mass_kernel(const T *__restrict__ qp, const T *__restrict__ kp, const int3
   }
   const int I = r / B;
   const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
-  const int cnt = (recall != nullptr) ? kv_cnt[lrow] : 0;
+  const int cnt = (recall != nullptr) ? min(max(kv_cnt[lrow], 0), max_kv) : 0;
   const int32_t *list = (recall != nullptr) ? kv_idx + lrow * max_kv : nullptr;
   int p = 0;
   float rec = 0.f;

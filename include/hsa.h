@@ -37,6 +37,11 @@
  *      scores        float [nh][nb][nb];
  *      lists         kv_idx int32 [G][nb][max_kv] ascending, -1 after
  *                    kv_cnt int32 [G][nb] entries; G = nh, or 1 when shared.
+ *                    Kernels that read caller lists clamp each length to
+ *                    [0, max_kv] and each entry to [0, nb), so a malformed
+ *                    list gives wrong rows, never an access outside the
+ *                    buffers; the backward pass and the block-mass
+ *                    diagnostic search the lists and need them ascending.
  *  - Token n is grid cell (t, y, x) with n = (t*H + y)*W + x.
  */
 #ifndef HSA_H

@@ -450,6 +450,38 @@ def test_full_keep_is_dense_attention(hsa, B, D, dtype):
         assert torch.equal(lset[:, real], lse[:, real])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_malformed_lists_are_clamped(hsa, dtype):
+    """List lengths outside [0, max_kv] and entries outside [0, nb) are
+    clamped inside the kernels (no read outside the buffers): the rows equal
+    those computed from the clamped lists, bit for bit."""
+    _say(f"malformed lists {dtype}")
+    T, H, W, nh, B, D = 4, 16, 16, 2, 64, 64
+    g = torch.Generator().manual_seed(17)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q, k, v = (torch.randn((1, T * H * W, nh, D), generator=g).to(tdt) for _ in range(3))
+    perm, blk_len = hsa.hsa_plan(T, H, W, "hilbert", B, device=dev())
+    nb = perm.numel() // B
+    max_kv = 6
+    rng = np.random.default_rng(18)
+    cnt = rng.integers(-3, max_kv + 6, size=(nh, nb)).astype(np.int32)
+    idx = rng.integers(-2 * nb, 3 * nb, size=(nh, nb, max_kv)).astype(np.int32)
+    cnt[-1, -1] = max_kv + 50            # the last row would read past the buffer
+    bad = [torch.from_numpy(x).to(dev()) for x in (idx, cnt)]
+    ok = [torch.from_numpy(x).to(dev()) for x in (np.clip(idx, 0, nb - 1), np.clip(cnt, 0, max_kv))]
+    qd, kd, vd = (x.to(dev()) for x in (q, k, v))
+    qp, kp, vp = hsa.hsa_perm([qd, kd, vd], perm, perm.numel())
+    op_b, lse_b = hsa.hsa_attn(qp, kp, vp, blk_len, *bad, B)
+    op_o, lse_o = hsa.hsa_attn(qp, kp, vp, blk_len, *ok, B)
+    torch.cuda.synchronize()
+    assert torch.equal(op_b, op_o) and torch.equal(lse_b, lse_o)
+    for kk, vv in ((kp, vp), (kd, vd)):
+        ot_b, _ = hsa.hsa_attn_tokens(qd, kk, vv, perm, blk_len, *bad, B)
+        ot_o, _ = hsa.hsa_attn_tokens(qd, kk, vv, perm, blk_len, *ok, B)
+        torch.cuda.synchronize()
+        assert torch.equal(ot_b, ot_o)
+
+
 def test_lists_with_single_and_repeated_blocks(hsa):
     """Uneven list lengths (1 .. nb) across heads and query blocks."""
     _say("uneven lists")
