@@ -11,9 +11,10 @@
 //  THRESH_GLOBAL VMoBA abstract: threshold selection by cumulative
 //                similarity, then global selection over the head, under a
 //                budget that shrinks across steps (DFSAttn design 3).
-//                Per row: MSB-first radix search (8-bit digits, exact 2^-62
-//                fixed-point mass histograms in LDS) for the boundary key of
-//                the shortest prefix reaching tau. Per head: an MSB-first
+//                Per row: MSB-first radix search (digits of up to 8 bits
+//                below the row's common key prefix, exact 2^-62 fixed-point
+//                mass histograms in LDS) for the boundary key of the
+//                shortest prefix reaching tau. Per head: an MSB-first
 //                radix select (11-bit digits, count histograms) of the
 //                remaining budget among pairs outside the row prefixes, a
 //                small pick kernel choosing each digit; the search stops as
@@ -123,7 +124,7 @@ template <int KPL>
 __global__ void __launch_bounds__(kSelThreads)
 thresh_row_kernel(const float *__restrict__ S, int rows, int nb, uint64_t target,
                   uint64_t *__restrict__ row_thr, int32_t *__restrict__ row_cnt) {
-  __shared__ uint64_t row_hist[kSelThreads / 64][256];
+  __shared__ uint64_t row_hist[kSelThreads / 64][2][256];
   const int row = blockIdx.x * (kSelThreads / 64) + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int lane = lane_id();
@@ -160,29 +161,50 @@ thresh_row_kernel(const float *__restrict__ S, int rows, int nb, uint64_t target
   } else {
     // Largest order key thr whose tail sum F(thr) = sum_{key >= thr} fx
     // still reaches the target: the boundary value of the shortest prefix.
-    // Radix search from the top byte: with the higher bytes fixed to P and
-    // A = mass of the keys above P, the next byte is the highest digit d
-    // with A + (mass of digits >= d under P) >= target.
-    uint64_t *mh = row_hist[threadIdx.x >> 6];
-    uint32_t thr = 0;
+    // Radix search from the highest bit in which the row's keys differ (the
+    // bits above it are common to every key), in digits of up to 8 bits:
+    // with the higher bits fixed to P and A = mass of the keys above P, the
+    // next digit is the highest d with A + (mass of digits >= d under P) >=
+    // target. Each half-wave has its own histogram (half the atomic
+    // contention); the search ends early once one key is left under P.
+    uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int r = 0; r < KPL; ++r)
+      if (lane + 64 * r < nb) {
+        kmax = max(kmax, key[r]);
+        kmin = min(kmin, key[r]);
+      }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), off, 64)));
+      kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), off, 64)));
+    }
+    uint64_t(*mh)[256] = row_hist[threadIdx.x >> 6];
+    uint64_t *mine = mh[lane >> 5];
+    int top = 31 - static_cast<int>(__builtin_clz((kmax ^ kmin) | 1u));  // highest differing bit
+    if (kmax == kmin) top = -1;                                        // one distinct key
+    uint32_t thr = top >= 31 ? 0u : (kmax & ~((2u << top) - 1u));       // the common bits
+    if (top < 0) thr = kmax;
     uint64_t A = 0;
 #pragma unroll 1
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      const uint32_t pmask = shift == 24 ? 0u : (~0u << (shift + 8));
+    while (top >= 0) {
+      const int width = min(8, top + 1);
+      const int lo = top - width + 1;
+      const uint32_t pmask = top >= 31 ? 0u : ~((2u << top) - 1u);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mh[lane * 4 + j] = 0;
+      for (int j = 0; j < 4; ++j) mh[0][lane * 4 + j] = mh[1][lane * 4 + j] = 0;
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int r = 0; r < KPL; ++r)
         if (lane + 64 * r < nb && (key[r] & pmask) == thr)
-          atomicAdd(reinterpret_cast<unsigned long long *>(&mh[(key[r] >> shift) & 255]),
+          atomicAdd(reinterpret_cast<unsigned long long *>(&mine[(key[r] >> lo) & ((1u << width) - 1u)]),
                     static_cast<unsigned long long>(fx[r]));
       __builtin_amdgcn_wave_barrier();
       // lane l holds digits 255 - 4l - j (j = 0..3): lanes run from the top
       uint64_t v[4], loc = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v[j] = mh[255 - 4 * lane - j];
+        v[j] = mh[0][255 - 4 * lane - j] + mh[1][255 - 4 * lane - j];
         loc += v[j];
       }
       uint64_t incl = loc;  // inclusive prefix over lanes (higher digits first)
@@ -206,9 +228,28 @@ thresh_row_kernel(const float *__restrict__ S, int rows, int nb, uint64_t target
         if (j < jhit) above_d += v[j];
       above_d = __shfl(above_d, src, 64);
       const uint32_t d = 255u - 4u * static_cast<uint32_t>(src) - static_cast<uint32_t>(jsel);
-      thr |= d << shift;
+      thr |= d << lo;
       A = above_d;
+      top = lo - 1;
       __builtin_amdgcn_wave_barrier();
+      if (top >= 0) {
+        // keys left under the new prefix; the boundary key is one of them
+        const uint32_t qmask = ~((2u << top) - 1u);
+        int left = 0;
+        uint32_t only = 0;
+#pragma unroll
+        for (int r = 0; r < KPL; ++r) {
+          const bool in = lane + 64 * r < nb && (key[r] & qmask) == thr;
+          left += popc64(__ballot(in));
+          if (in) only = key[r];
+        }
+        if (left == 1) {
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) only = max(only, static_cast<uint32_t>(__shfl_xor(static_cast<int>(only), off, 64)));
+          thr = only;
+          top = -1;
+        }
+      }
     }
     uint64_t above = 0;
     int n_above = 0;
