@@ -57,11 +57,23 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return (b % 8) * per + b / 8;
 }
 
+// Ordered launches: give each XCD runs of kRun consecutive order positions
+// (rows next to each other in the order share key blocks in that XCD's L2)
+// while the runs still go to the XCDs in turn, so the longest rows, which
+// come first, stay spread over all of them.
+__device__ __forceinline__ int xcd_runs(int b, int total) {
+  constexpr int kRun = 4;
+  const int full = total / (8 * kRun) * (8 * kRun);
+  if (b >= full) return b;
+  const int x = b & 7, q = b >> 3;
+  return ((q / kRun) * 8 + x) * kRun + q % kRun;
+}
+
 // (head, list row) of workgroup b for kernels with one workgroup per (head,
 // block). Without an order, neighbouring blocks of one head go to one XCD
-// (shared L2). With one, the b-th workgroup takes row order[b] (longest
-// lists first); shared lists order blocks, and the nh heads of a block are
-// consecutive workgroups.
+// (shared L2). With one, the b-th workgroup takes row order[xcd_runs(b)]
+// (longest lists first); shared lists order blocks, and the nh heads of a
+// block are consecutive workgroups.
 __device__ __forceinline__ void block_of(int b, const int32_t *order, int kv_shared, int nh, int nb,
                                          int &h, int &I) {
   if (order == nullptr) {
@@ -72,7 +84,7 @@ __device__ __forceinline__ void block_of(int b, const int32_t *order, int kv_sha
     h = b % nh;
     I = min(max(order[b / nh], 0), nb - 1);
   } else {
-    const int e = min(max(order[b], 0), nh * nb - 1);
+    const int e = min(max(order[xcd_runs(b, nh * nb)], 0), nh * nb - 1);
     h = e / nb;
     I = e - h * nb;
   }
