@@ -482,6 +482,44 @@ def test_malformed_lists_are_clamped(hsa, dtype):
         assert torch.equal(ot_b, ot_o)
 
 
+@pytest.mark.parametrize("B,D", [(64, 64), (128, 128)])
+def test_long_lists_with_growing_logits(hsa, B, D):
+    """Lists of 64+ blocks (the deferred-value pipeline) on keys whose scale
+    grows block by block, with one block 30x larger: the running reference
+    goes stale again and again and once by far; the result must still be
+    dense softmax attention (full keep), and the same in token order."""
+    _say(f"long lists, growing logits B={B} D={D}")
+    T, H, W, nh = 8, 32, 32, 2                      # 8192 tokens
+    g = torch.Generator().manual_seed(B + 3 * D)
+    q = torch.randn((1, T * H * W, nh, D), generator=g)
+    k = torch.randn((1, T * H * W, nh, D), generator=g)
+    v = torch.randn((1, T * H * W, nh, D), generator=g)
+    perm, blk_len = hsa.hsa_plan(T, H, W, "hilbert", B, device=dev())
+    nb = perm.numel() // B
+    p = perm.cpu().numpy()
+    grow = torch.ones(T * H * W)
+    for i in range(nb):                              # scale by the key's block in the plan
+        toks = p[i * B:(i + 1) * B]
+        toks = toks[toks >= 0]
+        grow[torch.from_numpy(toks.astype(np.int64))] = 0.2 + 0.05 * i + (30.0 if i == nb // 2 else 0.0)
+    k = (k * grow[None, :, None, None]).to(torch.bfloat16)
+    q, v = q.to(torch.bfloat16), v.to(torch.bfloat16)
+    assert nb >= 64
+    qd, kd, vd = (x.to(dev()) for x in (q, k, v))
+    qp, kp, vp = hsa.hsa_perm([qd, kd, vd], perm, perm.numel())
+    kv_idx = torch.arange(nb, dtype=torch.int32, device=dev()).repeat(nh, nb, 1).contiguous()
+    kv_cnt = torch.full((nh, nb), nb, dtype=torch.int32, device=dev())
+    op, lse = hsa.hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B)
+    o = hsa.hsa_unperm(op, perm, T * H * W)
+    ot, _ = hsa.hsa_attn_tokens(qd, kd, vd, perm, blk_len, kv_idx, kv_cnt, B)
+    torch.cuda.synchronize()
+    ref = oracle.attn_dense(*(x.double().numpy() for x in (q, k, v)))
+    err = np.abs(to_np(o) - ref).max()
+    _say(f"  max err vs dense = {err:.3e}, max |o| = {np.abs(ref).max():.2f}")
+    assert err <= TOL["bf16"]
+    assert torch.equal(ot, o)
+
+
 def test_lists_with_single_and_repeated_blocks(hsa):
     """Uneven list lengths (1 .. nb) across heads and query blocks."""
     _say("uneven lists")
