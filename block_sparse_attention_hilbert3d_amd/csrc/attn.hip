@@ -41,8 +41,9 @@
 // K/V the direct LDS loads also fetch key/value rows from the token-major
 // tensors (each lane's source rows for a stage are looked up in the map one
 // iteration ahead), so no reordered copy of Q, K or V is made at all.
-// f32 kernel: a plain one-thread-per-query online-softmax loop with K/V tiles
-// in LDS, for float inputs (small shapes).
+// f32 kernel: a plain online-softmax loop with K/V tiles in LDS, for float
+// inputs (small shapes); on small tiles four threads share each query, each
+// over a quarter of the keys, merged at the end.
 #include <type_traits>
 
 #include "common.h"
@@ -669,21 +670,34 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   }
 }
 
+// Float kernel: one thread per (query, key split); KS splits share each key
+// tile (split j takes keys j, j + KS, ...) with their own running max, sum
+// and output row, merged through LDS at the end. KS = 4 for small tiles
+// (short serial chains for the latency-bound small shapes), 1 otherwise.
 template <int D, int BK>
-__global__ void __launch_bounds__(BK)
+struct F32Split {
+  static constexpr int KS = (BK * D <= 64 * 64) ? 4 : 1;
+};
+
+template <int D, int BK>
+__global__ void __launch_bounds__((BK * F32Split<D, BK>::KS))
 attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
                 const float *__restrict__ vp, float *__restrict__ op, float *__restrict__ lse,
                 const int32_t *__restrict__ blk_len, const int32_t *__restrict__ kv_idx,
                 const int32_t *__restrict__ kv_cnt, const int32_t *__restrict__ order, int max_kv,
                 int kv_shared, int nh, int nb, float scale_log2, const int32_t *__restrict__ perm,
                 int64_t q_stride, int64_t kv_stride, int64_t o_stride) {
+  constexpr int KS = F32Split<D, BK>::KS;
+  constexpr int NT = BK * KS;
   __shared__ __attribute__((aligned(16))) float sK[BK * D];
   __shared__ __attribute__((aligned(16))) float sV[BK * D];
+  __shared__ float mrg[KS > 1 ? (KS - 1) * BK * (D + 2) : 1];  // [KS-1][BK][D + 2]
   int h, I;
   block_of(blockIdx.x, order, kv_shared, nh, nb, h, I);
   const int tid = threadIdx.x;
+  const int row = tid % BK, split = tid / BK;
   const int64_t head_off = static_cast<int64_t>(h) * nb * BK * D;
-  const int qslot = I * BK + tid;
+  const int qslot = I * BK + row;
   // token-layout I/O when perm is given (pad slots: zero query, no store)
   const int tok = perm ? perm[qslot] : 0;
   const int64_t qofs = perm ? static_cast<int64_t>(max(tok, 0)) * q_stride + h * D
@@ -704,7 +718,7 @@ attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
     const int J = min(max(list[c], 0), nb - 1);
     const int kvalid = blk_len[J];
     if (perm && kv_stride > 0) {  // K/V rows gathered from the token-major tensors
-      for (int i = tid; i < BK * D / 4; i += BK) {
+      for (int i = tid; i < BK * D / 4; i += NT) {
         const int r = i / (D / 4), c4 = i - r * (D / 4);
         const int64_t src = static_cast<int64_t>(max(perm[J * BK + r], 0)) * kv_stride + h * D + c4 * 4;
         reinterpret_cast<float4 *>(sK)[i] = *reinterpret_cast<const float4 *>(kp + src);
@@ -713,25 +727,24 @@ attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
     } else {
       const float4 *ks = reinterpret_cast<const float4 *>(kp + head_off + static_cast<int64_t>(J) * BK * D);
       const float4 *vs = reinterpret_cast<const float4 *>(vp + head_off + static_cast<int64_t>(J) * BK * D);
-      for (int i = tid; i < BK * D / 4; i += BK) {
+      for (int i = tid; i < BK * D / 4; i += NT) {
         reinterpret_cast<float4 *>(sK)[i] = ks[i];
         reinterpret_cast<float4 *>(sV)[i] = vs[i];
       }
     }
     __syncthreads();
-    // four keys at a time: four independent dot-product chains, one max
-    // update and one pass over O per group; then the ragged tail one by one
-    int key = 0;
-    for (; key + 4 <= kvalid; key += 4) {
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    // this split's keys split, split + KS, ...: two at a time (two dot
+    // chains, one max update and one pass over O per pair), then the tail
+    int key = split;
+    for (; key + KS < kvalid; key += 2 * KS) {
+      const int k1 = key + KS;
+      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         s0 = fmaf(q[d], sK[key * D + d], s0);
-        s1 = fmaf(q[d], sK[(key + 1) * D + d], s1);
-        s2 = fmaf(q[d], sK[(key + 2) * D + d], s2);
-        s3 = fmaf(q[d], sK[(key + 3) * D + d], s3);
+        s1 = fmaf(q[d], sK[k1 * D + d], s1);
       }
-      const float mx = fmaxf(fmaxf(s0, s1), fmaxf(s2, s3));
+      const float mx = fmaxf(s0, s1);
       if (mx > m) {
         const float a = exp2f(m - mx);
         l *= a;
@@ -739,14 +752,12 @@ attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
         for (int d = 0; d < D; ++d) o[d] *= a;
         m = mx;
       }
-      const float p0 = exp2f(s0 - m), p1 = exp2f(s1 - m), p2 = exp2f(s2 - m), p3 = exp2f(s3 - m);
-      l += (p0 + p1) + (p2 + p3);
+      const float p0 = exp2f(s0 - m), p1 = exp2f(s1 - m);
+      l += p0 + p1;
 #pragma unroll
-      for (int d = 0; d < D; ++d)
-        o[d] = fmaf(p3, sV[(key + 3) * D + d],
-                    fmaf(p2, sV[(key + 2) * D + d], fmaf(p1, sV[(key + 1) * D + d], fmaf(p0, sV[key * D + d], o[d]))));
+      for (int d = 0; d < D; ++d) o[d] = fmaf(p1, sV[k1 * D + d], fmaf(p0, sV[key * D + d], o[d]));
     }
-    for (; key < kvalid; ++key) {
+    for (; key < kvalid; key += KS) {
       float s = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) s = fmaf(q[d], sK[key * D + d], s);
@@ -764,7 +775,35 @@ attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
     }
     __syncthreads();
   }
-  const bool real = tid < blk_len[I];
+  if constexpr (KS > 1) {
+    // splits 1.. hand (m, l, o) to split 0
+    if (split > 0) {
+      float *dst = mrg + (static_cast<int64_t>(split - 1) * BK + row) * (D + 2);
+      dst[0] = m;
+      dst[1] = l;
+#pragma unroll
+      for (int d = 0; d < D; ++d) dst[2 + d] = o[d];
+    }
+    __syncthreads();
+    if (split > 0) return;
+    float mt = m;
+#pragma unroll
+    for (int j = 0; j < KS - 1; ++j) mt = fmaxf(mt, mrg[(static_cast<int64_t>(j) * BK + row) * (D + 2)]);
+    const float a0 = exp2f(m - mt);
+    l *= a0;
+#pragma unroll
+    for (int d = 0; d < D; ++d) o[d] *= a0;
+#pragma unroll
+    for (int j = 0; j < KS - 1; ++j) {
+      const float *src = mrg + (static_cast<int64_t>(j) * BK + row) * (D + 2);
+      const float a = exp2f(src[0] - mt);
+      l = fmaf(src[1], a, l);
+#pragma unroll
+      for (int d = 0; d < D; ++d) o[d] = fmaf(src[2 + d], a, o[d]);
+    }
+    m = mt;
+  }
+  const bool real = row < blk_len[I];
   const float inv = (real && l > 0.f) ? 1.f / l : 0.f;
   if (!perm || (real && tok >= 0)) {
 #pragma unroll
@@ -881,7 +920,7 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
     const float *q = static_cast<const float *>(qp), *k = static_cast<const float *>(kp),
                 *v = static_cast<const float *>(vp);
     float *o = static_cast<float *>(op);
-    const dim3 block(B);
+    const dim3 block(B * ((D * B <= 64 * 64) ? 4 : 1));  // F32Split<D, B>::KS threads per query
     if (D == 128 && B == 128) launch_k(hsa::attn_f32_kernel<128, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
     else if (D == 64 && B == 128) launch_k(hsa::attn_f32_kernel<64, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
     else if (D == 128 && B == 64) launch_k(hsa::attn_f32_kernel<128, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
