@@ -28,11 +28,14 @@ namespace hsa {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// D_i = dO_i . O_i in float; zero for pad slots.
+// D_i = dO_i . O_i in float, zero for pad slots; and the log-sum-exp in
+// log2 units, +inf for pad slots (their weights then come out as 0 with no
+// per-element select in the dK / dV kernels).
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 bwd_delta_kernel(const T *__restrict__ op, const T *__restrict__ dop, const int32_t *__restrict__ blk_len,
-                 int n_pad, int B, int64_t total, float *__restrict__ delta) {
+                 int n_pad, int B, int64_t total, const float *__restrict__ lse, float *__restrict__ delta,
+                 float *__restrict__ lse2) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= total) return;
   const int slot = static_cast<int>(idx % n_pad);
@@ -59,6 +62,7 @@ bwd_delta_kernel(const T *__restrict__ op, const T *__restrict__ dop, const int3
     }
   }
   delta[idx] = s;
+  lse2[idx] = real ? lse[idx] * kLog2e : INFINITY;
 }
 
 // Transposed lists: for list set g and key block J, the query blocks I whose
@@ -380,7 +384,6 @@ attn_bwd_dkv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict_
   const int32_t *tl = t_idx + lrow * nb;
   const uint32_t ld_off = static_cast<uint32_t>((lane & (ST / 4 - 1)) * 16);  // ST floats
   auto stage_row0 = [&](int t) { return static_cast<int64_t>(tl[t / NS]) * BK + (t % NS) * ST; };
-  auto stage_valid = [&](int t) { return min(max(blk_len[tl[t / NS]] - (t % NS) * ST, 0), ST); };
   auto issue = [&](const uint16_t *src, uint32_t lds_tile, const uint32_t (&off)[NI]) {
     issue_tile_slices<NI>(src, lds_tile, w, off);
   };
@@ -420,7 +423,7 @@ attn_bwd_dkv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict_
     }
   };
   // P (and dS) of a stage, then dV^T += dO^T P or dK^T += Q^T dS
-  auto accumulate = [&](const f32x16 (&s)[QT], const f32x16 (&dp)[QT], int buf, int qvalid) {
+  auto accumulate = [&](const f32x16 (&s)[QT], const f32x16 (&dp)[QT], int buf) {
     const float *sL = &sLD[w][buf][0][0];
     const float *sD = &sLD[w][buf][1][0];
 #pragma unroll
@@ -430,7 +433,7 @@ attn_bwd_dkv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict_
     for (int i4 = 0; i4 < 4; ++i4) {
       const int q0 = qt * 32 + i4 * 8 + g * 4;
       const float4 l4 = *reinterpret_cast<const float4 *>(&sL[q0]);
-      const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};  // log2 units, +inf on pad rows
       float dv4[4] = {0.f, 0.f, 0.f, 0.f};
       if constexpr (DK) {
         const float4 d4 = *reinterpret_cast<const float4 *>(&sD[q0]);
@@ -439,11 +442,8 @@ attn_bwd_dkv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict_
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i4 * 4 + r;
-        // pad query rows: exponent -inf, so p = 0 (computed unconditionally,
-        // then selected, so no branch splits the scheduling region)
-        float arg = fmaf(s[qt][i], scale_log2, -lv[r]);
-        arg = (q0 + r < qvalid) ? arg : -INFINITY;
-        const float pv = __builtin_amdgcn_exp2f(arg);
+        // pad query rows: lse is +inf there, so the exponent is -inf and p = 0
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[qt][i], scale_log2, -lv[r]));
         x[i] = DK ? pv * (dp[qt][i] - dv4[r]) : pv;
       }
     }
@@ -475,9 +475,8 @@ attn_bwd_dkv_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict_
     __syncthreads();  // row buffer c & 1 and transposed buffer (c + 1) & 1 are free
     if (c + 2 < nst) issue_rows(c + 2);
     if (c + 1 < nst) issue_tr(c + 1);
-    const int qvalid = stage_valid(c);
     compute_s(sn, dn, (c + 1) & 1);  // on the last stage: an idle buffer, result unused
-    accumulate(sc, dc, c & 1, qvalid);
+    accumulate(sc, dc, c & 1);
     __builtin_amdgcn_iglp_opt(3);
     wait_vmcnt<0>();
   };
@@ -618,7 +617,7 @@ hsa_status_t launch_attn_order(const int32_t *kv_cnt, int G, int nb, int max_kv,
                                hipStream_t stream);
 
 size_t attn_bwd_ws_bytes(int nh, int nb, int B, int G) {
-  return align256(static_cast<size_t>(nh) * nb * B * sizeof(float)) +
+  return 2 * align256(static_cast<size_t>(nh) * nb * B * sizeof(float)) +
          align256(static_cast<size_t>(G) * nb * nb * sizeof(int32_t)) +
          3 * align256(static_cast<size_t>(G) * nb * sizeof(int32_t));
 }
@@ -631,6 +630,8 @@ hsa_status_t launch_attn_bwd(const void *qp, const void *kp, const void *vp, con
   const int G = kv_shared ? 1 : nh;
   char *base = static_cast<char *>(ws);
   float *delta = reinterpret_cast<float *>(base);
+  base += align256(static_cast<size_t>(nh) * nb * B * sizeof(float));
+  float *lse2 = reinterpret_cast<float *>(base);  // log-sum-exp in log2 units, +inf on pads
   base += align256(static_cast<size_t>(nh) * nb * B * sizeof(float));
   int32_t *t_idx = reinterpret_cast<int32_t *>(base);
   base += align256(static_cast<size_t>(G) * nb * nb * sizeof(int32_t));
@@ -645,7 +646,8 @@ hsa_status_t launch_attn_bwd(const void *qp, const void *kp, const void *vp, con
   const bool bf = dtype == HSA_BF16;
 #define HSA_DELTA(TT, DD)                                                                          \
   hipLaunchKernelGGL((hsa::bwd_delta_kernel<TT, DD>), dgrid, dim3(256), 0, stream,                 \
-                     static_cast<const TT *>(op), static_cast<const TT *>(dop), blk_len, n_pad, B, total, delta)
+                     static_cast<const TT *>(op), static_cast<const TT *>(dop), blk_len, n_pad, B, total, lse, \
+                     delta, lse2)
   if (bf) { if (D == 128) HSA_DELTA(uint16_t, 128); else HSA_DELTA(uint16_t, 64); }
   else { if (D == 128) HSA_DELTA(float, 128); else HSA_DELTA(float, 64); }
 #undef HSA_DELTA
@@ -673,9 +675,9 @@ hsa_status_t launch_attn_bwd(const void *qp, const void *kp, const void *vp, con
     hipLaunchKernelGGL((hsa::attn_bwd_dq_kernel<DD, BB>), grid, dim3(BB * 2), 0, stream, q, k, v, dO, lse, \
                        delta, blk_len, kv_idx, kv_cnt, qorder, max_kv, kv_shared, nh, nb, sl2, scale, dq); \
     hipLaunchKernelGGL((hsa::attn_bwd_dkv_kernel<DD, BB, false>), grid, dim3(BB * 2), 0, stream, q, k, v, dO, \
-                       lse, delta, blk_len, t_idx, t_cnt, korder, kv_shared, nh, nb, sl2, scale, dv);     \
+                       lse2, delta, blk_len, t_idx, t_cnt, korder, kv_shared, nh, nb, sl2, scale, dv);    \
     hipLaunchKernelGGL((hsa::attn_bwd_dkv_kernel<DD, BB, true>), grid, dim3(BB * 2), 0, stream, q, k, v, dO, \
-                       lse, delta, blk_len, t_idx, t_cnt, korder, kv_shared, nh, nb, sl2, scale, dk);     \
+                       lse2, delta, blk_len, t_idx, t_cnt, korder, kv_shared, nh, nb, sl2, scale, dk);     \
   } while (0)
     if (D == 128 && B == 128) HSA_BWD(128, 128);
     else if (D == 64 && B == 128) HSA_BWD(64, 128);

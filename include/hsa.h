@@ -323,8 +323,9 @@ hsa_status_t hsa_attn_order(const int32_t *kv_cnt, int32_t G, int32_t nb, int32_
  *   the products; F32 in float. Results are bit-reproducible (fixed sum
  *   order, no atomics).
  * ws: device workspace of hsa_attn_bwd_ws_size bytes (row deltas, the
- *   transposed lists -- for each key block, the query blocks that list it --
- *   and longest-first processing orders for both list directions).
+ *   log-sum-exp in log2 units with pad rows at +inf, the transposed lists --
+ *   for each key block, the query blocks that list it -- and longest-first
+ *   processing orders for both list directions).
  */
 size_t hsa_attn_bwd_ws_size(int32_t nh, int32_t nb, int32_t B, int32_t kv_shared);
 hsa_status_t hsa_attn_bwd(const void *qp, const void *kp, const void *vp, const void *op,
