@@ -19,7 +19,7 @@
 //  - online softmax in the log2 domain (scale folded into one FMA), keys
 //    beyond a ragged block's real length masked to -inf, and a lazy rescale
 //    that only touches O when a row max grows by more than 2^8;
-//  - lists of 64 or more key blocks use a deferred-value variant: a stage's
+//  - lists of 16 or more key blocks use a deferred-value variant: a stage's
 //    exponentials are taken against the running reference without the
 //    stage's own row max, the rounded row sums (every weight is at most its
 //    row's sum) show when the reference is stale, and only then is the max
@@ -358,14 +358,16 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     }
   };
 
-  // Deferred-value pipeline (long lists): the exponentials of stage c are
-  // taken against the current reference max without looking at the stage's
-  // own max first; their rounded row sums decide afterwards whether the
-  // reference is stale (a sum above 2^8, which bounds every weight, or not
-  // finite), and only then is the max taken, O rescaled and the stage
-  // recomputed. P.V of stage c runs one iteration later, beside the next
-  // stage's exponentials.
-  constexpr float kSumCap = 256.f;
+  // Deferred-value pipeline: the exponentials of stage c are taken against
+  // the current reference max without looking at the stage's own max first;
+  // their rounded row sums decide afterwards whether the reference is stale
+  // (a sum above 2^20, which bounds every weight, or not finite), and only
+  // then is the max taken, O rescaled and the stage recomputed. Weights up
+  // to 2^20 lose nothing in bf16 or in the float sums, and the high bound
+  // makes the recomputation rare (with 2^8 it ran often enough to cost ~3
+  // stages per workgroup). P.V of stage c runs one iteration later, beside
+  // the next stage's exponentials.
+  constexpr float kSumCap = 1048576.f;
   auto mask_tail = [&](f32x16 (&sacc)[MT][QT], int kvalid) {
     if (kvalid < ST) {
       const int lim = kvalid - g * 4;
@@ -906,9 +908,10 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
   } while (0)
     const int io = perm == nullptr ? 0 : (kv_stride > 0 ? 2 : 1);
     const bool L = lse != nullptr;
-    // Lists of 64 or more blocks take the deferred-value pipeline (no row
-    // max per stage; ~2 % faster there, ~2 % slower on short lists).
-    const bool defer = max_kv >= 64;
+    // Lists of 16 or more blocks take the deferred-value pipeline (no row
+    // max per stage; 0.5-2 % faster); very short lists keep the eager one,
+    // whose prologue and epilogue are shorter.
+    const bool defer = max_kv >= 16;
     if (D == 128 && B == 128) HSA_ATTN_BF16_IO(128, 128);
     else if (D == 64 && B == 128) HSA_ATTN_BF16_IO(64, 128);
     else if (D == 128 && B == 64) HSA_ATTN_BF16_IO(128, 64);

@@ -484,7 +484,7 @@ def test_malformed_lists_are_clamped(hsa, dtype):
 
 @pytest.mark.parametrize("B,D", [(64, 64), (128, 128)])
 def test_long_lists_with_growing_logits(hsa, B, D):
-    """Lists of 64+ blocks (the deferred-value pipeline) on keys whose scale
+    """Long lists (the deferred-value pipeline) on keys whose scale
     grows block by block, with one block 30x larger: the running reference
     goes stale again and again and once by far; the result must still be
     dense softmax attention (full keep), and the same in token order."""
