@@ -515,22 +515,25 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   }
   // Iteration c: issue K(c+2) and V(c+1); S(c+1) alongside softmax + PV(c);
   // then wait for this iteration's loads.
-  auto body = [&](int c, f32x16 (&cur)[MT][QT], f32x16 (&nxt)[MT][QT]) {
+  // (par: c & 1 as a compile-time constant, so LDS buffer offsets are
+  // immediates rather than per-stage address arithmetic)
+  auto body = [&](auto par, int c, f32x16 (&cur)[MT][QT], f32x16 (&nxt)[MT][QT]) {
+    constexpr int P = decltype(par)::value;
     const bool has1 = c + 1 < nst, has2 = c + 2 < nst;
     __syncthreads();  // K(c) and V(c-1) buffers are free, K(c+1) and V(c) visible
     slide(c);
     if constexpr (GKV) {
       if (c + 3 < nst) stage_rows(c + 3, rn);
-      if (has2) issue_tile_offs<D, ST, NW>(kbase, ldsK + (c & 1) * TILE * 2, w, ok);
-      if (has1) issue_tile_offs<D, ST, NW>(vbase, ldsV + ((c + 1) & 1) * TILE * 2, w, ov);
+      if (has2) issue_tile_offs<D, ST, NW>(kbase, ldsK + P * TILE * 2, w, ok);
+      if (has1) issue_tile_offs<D, ST, NW>(vbase, ldsV + (P ^ 1) * TILE * 2, w, ov);
     } else {
-      if (has2) issue_tile<D, ST, NW>(kbase + stage_ofs(c + 2), ldsK + (c & 1) * TILE * 2, w, koff);
-      if (has1) issue_tile<D, ST, NW>(vbase + stage_ofs(c + 1), ldsV + ((c + 1) & 1) * TILE * 2, w, voff);
+      if (has2) issue_tile<D, ST, NW>(kbase + stage_ofs(c + 2), ldsK + P * TILE * 2, w, koff);
+      if (has1) issue_tile<D, ST, NW>(vbase + stage_ofs(c + 1), ldsV + (P ^ 1) * TILE * 2, w, voff);
     }
     // Unconditional so it shares a scheduling region with exp_pv; on the
     // last stage it reads an idle buffer (no load in flight) and is unused.
-    compute_s(nxt, (c + 1) & 1);
-    exp_pv(cur, c & 1);
+    compute_s(nxt, P ^ 1);
+    exp_pv(cur, P);
     // LLVM's interleave strategy for matrix and exponential instructions
     // (measured ~2 % faster than the default schedule here)
     __builtin_amdgcn_iglp_opt(3);
@@ -544,8 +547,8 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     }
   };
   for (int c = 0; c < nst; c += 2) {
-    body(c, sA, sB);
-    if (c + 1 < nst) body(c + 1, sB, sA);
+    body(std::integral_constant<int, 0>{}, c, sA, sB);
+    if (c + 1 < nst) body(std::integral_constant<int, 1>{}, c + 1, sB, sA);
   }
   } else {
   // Prologue: K(0) and K(1) in flight, S(0) once both landed. Gathered
@@ -597,23 +600,24 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   }
   // Iteration c: issue K(c+2) and V(c); S(c+1), the exponentials of stage c
   // and P.V of stage c-1 in one region; then settle stage c.
-  auto body2 = [&](auto with_pv, int c, f32x16 (&cur)[MT][QT], f32x16 (&nxt)[MT][QT],
+  auto body2 = [&](auto with_pv, auto par, int c, f32x16 (&cur)[MT][QT], f32x16 (&nxt)[MT][QT],
                    bf16x8 (&pprev)[QT][PK], bf16x8 (&pcur)[QT][PK]) {
+    constexpr int P = decltype(par)::value;  // c & 1
     const bool has1 = c + 1 < nst, has2 = c + 2 < nst;
     __syncthreads();  // K(c) and V(c-2) buffers are free, K(c+1) and V(c-1) visible
     slide_low(c);
     if constexpr (GKV) {
       if (c + 3 < nst) stage_rows(c + 3, rn);
-      if (has2) issue_tile_offs<D, ST, NW>(kbase, ldsK + (c & 1) * TILE * 2, w, ok);
-      issue_tile_offs<D, ST, NW>(vbase, ldsV + (c & 1) * TILE * 2, w, ov);
+      if (has2) issue_tile_offs<D, ST, NW>(kbase, ldsK + P * TILE * 2, w, ok);
+      issue_tile_offs<D, ST, NW>(vbase, ldsV + P * TILE * 2, w, ov);
     } else {
-      if (has2) issue_tile<D, ST, NW>(kbase + stage_ofs(c + 2), ldsK + (c & 1) * TILE * 2, w, koff);
-      issue_tile<D, ST, NW>(vbase + stage_ofs(c), ldsV + (c & 1) * TILE * 2, w, voff);
+      if (has2) issue_tile<D, ST, NW>(kbase + stage_ofs(c + 2), ldsK + P * TILE * 2, w, koff);
+      issue_tile<D, ST, NW>(vbase + stage_ofs(c), ldsV + P * TILE * 2, w, voff);
     }
-    compute_s(nxt, (c + 1) & 1);
+    compute_s(nxt, P ^ 1);
     float rs[QT], es[QT];
     exps(cur, pcur, rs, es);
-    if constexpr (decltype(with_pv)::value) pv_only(pprev, (c - 1) & 1);
+    if constexpr (decltype(with_pv)::value) pv_only(pprev, P ^ 1);
     __builtin_amdgcn_iglp_opt(3);
     settle(cur, pcur, rs, es);
     mask_tail(nxt, has1 ? stage_valid(c + 1) : 0);
@@ -626,10 +630,10 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
       offsets(rk, koff, ok);
     }
   };
-  if (nst > 0) body2(std::false_type{}, 0, sA, sB, pY, pX);
+  if (nst > 0) body2(std::false_type{}, std::integral_constant<int, 0>{}, 0, sA, sB, pY, pX);
   for (int c = 1; c < nst; c += 2) {
-    body2(std::true_type{}, c, sB, sA, pX, pY);
-    if (c + 1 < nst) body2(std::true_type{}, c + 1, sA, sB, pY, pX);
+    body2(std::true_type{}, std::integral_constant<int, 1>{}, c, sB, sA, pX, pY);
+    if (c + 1 < nst) body2(std::true_type{}, std::integral_constant<int, 0>{}, c + 1, sA, sB, pY, pX);
   }
   if (nst > 0) {
     __syncthreads();  // V(nst-1) visible
