@@ -520,6 +520,38 @@ def test_long_lists_with_growing_logits(hsa, B, D):
     assert torch.equal(ot, o)
 
 
+def test_eager_and_deferred_pipelines_agree(hsa):
+    """The same lists with a capacity of 15 (eager pipeline) and 16 (deferred
+    pipeline): both within tolerance of the oracle, and within a few output
+    roundings of each other."""
+    _say("eager vs deferred attention pipelines")
+    T, H, W, nh, B, D = 4, 32, 32, 2, 128, 128      # 4096 tokens, 32 blocks
+    g = torch.Generator().manual_seed(23)
+    q, k, v = (torch.randn((1, T * H * W, nh, D), generator=g).to(torch.bfloat16) for _ in range(3))
+    perm, blk_len = hsa.hsa_plan(T, H, W, "hilbert", B, device=dev())
+    nb = perm.numel() // B
+    rng = np.random.default_rng(24)
+    cnt = rng.integers(1, 16, size=(nh, nb)).astype(np.int32)
+    idx = np.full((nh, nb, 16), -1, dtype=np.int32)
+    for h in range(nh):
+        for i in range(nb):
+            idx[h, i, :cnt[h, i]] = np.sort(rng.choice(nb, cnt[h, i], replace=False))
+    qp, kp, vp = hsa.hsa_perm([x.to(dev()) for x in (q, k, v)], perm, perm.numel())
+    cnt_d = torch.from_numpy(cnt).to(dev())
+    o15, l15 = hsa.hsa_attn(qp, kp, vp, blk_len, torch.from_numpy(idx[:, :, :15].copy()).to(dev()), cnt_d, B)
+    o16, l16 = hsa.hsa_attn(qp, kp, vp, blk_len, torch.from_numpy(idx).to(dev()), cnt_d, B)
+    torch.cuda.synchronize()
+    p = perm.cpu().numpy().astype(np.int64)
+    ref, _ = oracle.attn_blocks(*(oracle.gather(x, p) for x in (q, k, v)), p, B, idx, cnt)
+    e15, e16 = np.abs(to_np(o15) - ref).max(), np.abs(to_np(o16) - ref).max()
+    d = (o15.float() - o16.float()).abs().max().item()
+    _say(f"  eager err {e15:.3e}, deferred err {e16:.3e}, between {d:.3e}")
+    assert e15 <= TOL["bf16"] and e16 <= TOL["bf16"]
+    assert d <= 4 * 2.0 ** -7 * max(1.0, float(np.abs(ref).max()))
+    real = perm >= 0
+    assert torch.allclose(l15[:, real], l16[:, real], rtol=0, atol=1e-3)
+
+
 def test_lists_with_single_and_repeated_blocks(hsa):
     """Uneven list lengths (1 .. nb) across heads and query blocks."""
     _say("uneven lists")
