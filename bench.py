@@ -150,10 +150,11 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="also time the attention backward (hsa_attn_bwd) on the layer's lists")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--io", choices=["reordered", "tokens_qo", "tokens"], default="tokens_qo",
+    ap.add_argument("--io", choices=["auto", "reordered", "tokens_qo", "tokens"], default="tokens_qo",
                     help="where the reorders happen: five separate passes (reordered), the "
                          "attention kernel reading Q / writing O in token order (tokens_qo), "
-                         "or also gathering K/V rows itself (tokens)")
+                         "or also gathering K/V rows itself (tokens); auto picks tokens for "
+                         "short top-k lists and tokens_qo otherwise")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one device-to-device copy of this many MiB (a kernel of known "
                          "traffic, to scale hardware byte counters)")

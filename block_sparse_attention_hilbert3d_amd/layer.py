@@ -6,7 +6,8 @@ grid shape (hsa_plan). Buffers and workspaces are allocated once per layer
 so a step enqueues kernels only.
 
 ``io`` chooses where the reorders happen; the output is bit-identical in
-all three forms:
+all three forms ("auto" picks "tokens" for top-k lists of at most 6144 keys
+per query block and "tokens_qo" otherwise):
   "reordered"  the five passes above;
   "tokens_qo"  (default) the attention kernel reads Q and writes the output
                in token order (hsa_attn_tokens); hsa_perm reorders K and V
@@ -14,8 +15,11 @@ all three forms:
   "tokens"     the attention kernel also gathers K and V rows from the
                token-major tensors; hsa_perm runs on refresh steps only, to
                pool the Q/K sub-blocks that scoring needs. The per-stage row
-               lookups cost the attention kernel ~4 %, so this pays only
-               when lists are short (the reorder pass is then a larger share).
+               lookups cost the attention kernel ~4-5 %, so this pays only
+               when lists are short (the reorder pass is then a larger
+               share): at the Wan 480p shape with top-38 lists it equals
+               "tokens_qo" on refresh steps and is ~2.5 % faster on cached
+               ones; on the long LVSA / threshold lists it loses ~2 %.
 
 Mask caching (DFSAttn, Methodology, design 3): ``step(..., reuse_mask=True)``
 skips scoring and selection and attends with the lists kept from the last
@@ -30,6 +34,7 @@ import torch
 from . import binding as B_
 
 IO_FORMS = ("reordered", "tokens_qo", "tokens")
+AUTO_TOKENS_MAX_KEYS = 6144   # top-k lists up to this many keys per query block gather K/V
 
 
 class SparseAttentionLayer:
@@ -45,8 +50,10 @@ class SparseAttentionLayer:
         if select == "radial_dyn":
             self.agg = "max"   # the dynamic threshold reads pre-softmax logits
         self.dtype, self.device = dtype, device
+        if io == "auto":
+            io = "tokens" if (select == "topk" and k * B <= AUTO_TOKENS_MAX_KEYS) else "tokens_qo"
         if io not in IO_FORMS:
-            raise ValueError(f"io must be one of {IO_FORMS}")
+            raise ValueError(f"io must be 'auto' or one of {IO_FORMS}")
         self.io = io
         self._qkv = None
         self.scale = 1.0 / math.sqrt(D)

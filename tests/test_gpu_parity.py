@@ -552,6 +552,14 @@ def test_eager_and_deferred_pipelines_agree(hsa):
     assert torch.allclose(l15[:, real], l16[:, real], rtol=0, atol=1e-3)
 
 
+def test_io_auto_rule(hsa):
+    """io="auto": short top-k lists gather K/V inside attention, long or
+    structured lists keep the K/V reorder."""
+    for idx, want in ((2, "tokens"), (3, "tokens"), (4, "tokens_qo"), (5, "tokens_qo"), (6, "tokens_qo")):
+        L = hsa.layer_for_workload(wl.get(idx), device=dev(), want_lse=False, io="auto")
+        assert L.io == want, (idx, L.io)
+
+
 def test_lists_with_single_and_repeated_blocks(hsa):
     """Uneven list lengths (1 .. nb) across heads and query blocks."""
     _say("uneven lists")
