@@ -619,8 +619,11 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     exps(cur, pcur, rs, es);
     if constexpr (decltype(with_pv)::value) pv_only(pprev, P ^ 1);
     // LLVM's interleave strategy 1 here (strategy 3, kept for the eager
-    // pipeline, measured 0.8-1.6 % slower on this instruction mix)
-    __builtin_amdgcn_iglp_opt(1);
+    // pipeline, measured 0.8-1.6 % slower on this instruction mix); with
+    // the log-sum-exp sums the register budget is tighter and strategy 1
+    // spills into the loop, so that variant keeps strategy 3
+    if constexpr (LSE) __builtin_amdgcn_iglp_opt(3);
+    else __builtin_amdgcn_iglp_opt(1);
     settle(cur, pcur, rs, es);
     mask_tail(nxt, has1 ? stage_valid(c + 1) : 0);
     wait_vmcnt<0>();
