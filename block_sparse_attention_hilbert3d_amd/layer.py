@@ -21,6 +21,12 @@ per query block and "tokens_qo" otherwise):
                "tokens_qo" on refresh steps and is ~2.5 % faster on cached
                ones; on the long LVSA / threshold lists it loses ~2 %.
 
+``want_lse`` (off by default) also keeps the log-sum-exp of every row, which
+the backward (hsa_attn_bwd) needs; inference does not, and the kernel that
+produces it carries more registers (~7 % slower at the Wan 480p shape; with
+gathered K/V it spills and runs ~25 % slower, so prefer "tokens_qo" when
+the log-sum-exp is wanted).
+
 Mask caching (DFSAttn, Methodology, design 3): ``step(..., reuse_mask=True)``
 skips scoring and selection and attends with the lists kept from the last
 refresh, on the new step's Q/K/V.
@@ -41,7 +47,7 @@ class SparseAttentionLayer:
     def __init__(self, T: int, H: int, W: int, heads: int, D: int, *, order: str, B: int,
                  select: str, s: int = 0, agg: str = "mass", k: int = 0, tau: float = 0.0,
                  C: int = 0, T_per: int = 1, lam: float = 0.0, delta: float = 0.0,
-                 dtype=torch.bfloat16, device="cuda", want_lse: bool = True,
+                 dtype=torch.bfloat16, device="cuda", want_lse: bool = False,
                  io: str = "tokens_qo"):
         self.T, self.H, self.W, self.heads, self.D = T, H, W, heads, D
         self.N = T * H * W
@@ -186,7 +192,7 @@ def vmoba_order(layer_index: int) -> str:
     return VMOBA_CYCLE[layer_index % 3]
 
 
-def layer_for_workload(w, device="cuda", want_lse=True, io="tokens_qo") -> SparseAttentionLayer:
+def layer_for_workload(w, device="cuda", want_lse=False, io="tokens_qo") -> SparseAttentionLayer:
     """Layer configured for one of the synthetic workloads (workloads.Workload)."""
     dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
     nb = B_.hsa_plan_size(w.T, w.H, w.W, w.order, w.B)[1]

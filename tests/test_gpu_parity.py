@@ -226,7 +226,7 @@ def test_select_ties_and_edges(hsa):
 def _layer(hsa, w, step, mask=None, io="tokens_qo"):
     _say(f"  generating inputs for workload {w.idx} step {step}")
     q, k, v = (x.to(dev()) for x in wl.make_qkv(w, step))
-    L = hsa.layer_for_workload(w, device=dev(), io=io)
+    L = hsa.layer_for_workload(w, device=dev(), want_lse=True, io=io)
     if mask is not None:
         L.reorder(q, k, v)
         L.kv_idx.copy_(mask[0])
@@ -364,7 +364,7 @@ def test_cached_mask_step(hsa):
     w = wl.get(3)
     _say("cached mask step (workload 3, step 0 -> 2)")
     q0, k0, v0 = (x.to(dev()) for x in wl.make_qkv(w, 0))
-    L = hsa.layer_for_workload(w, device=dev())
+    L = hsa.layer_for_workload(w, device=dev(), want_lse=True)
     L.step(q0, k0, v0, step=0)
     mask0 = (L.kv_idx.clone(), L.kv_cnt.clone())
     q2, k2, v2 = (x.to(dev()) for x in wl.make_qkv(w, 2))
@@ -705,7 +705,7 @@ def test_attn_bwd_wan_shape_sampled(hsa):
     do = torch.randn(q.shape, generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
     from dataclasses import replace
     w2 = replace(w, heads=2)
-    L = hsa.layer_for_workload(w2, device=dev(), io="reordered")
+    L = hsa.layer_for_workload(w2, device=dev(), want_lse=True, io="reordered")
     L.step(q.to(dev()), k.to(dev()), v.to(dev()))
     dop = hsa.hsa_perm([do.to(dev())], L.perm, L.n_pad)[0]
     dq, dk, dv = hsa.hsa_attn_bwd(*L.xp, L.op, dop, L.lse, L.blk_len, L.kv_idx, L.kv_cnt, w.B)
@@ -817,7 +817,7 @@ def test_layer_step_in_a_hip_graph(hsa, idx):
     eagerly and synchronisations between replays, equals the eager step."""
     w = wl.get(idx)
     _say(f"layer step in a HIP graph (workload {idx})")
-    L = hsa.layer_for_workload(w, device=dev())
+    L = hsa.layer_for_workload(w, device=dev(), want_lse=True)
     inputs = [tuple(x.to(dev()) for x in wl.make_qkv(w, s)) for s in range(3)]
     static = tuple(torch.empty_like(x) for x in inputs[0])
     for x, y in zip(static, inputs[0]):
