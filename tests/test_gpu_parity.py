@@ -734,12 +734,14 @@ def test_attn_bwd_wan_shape_sampled(hsa):
 
 # ---------------------------------------------------------------- edge cases
 
-def test_empty_lists_forward_backward(hsa):
+@pytest.mark.parametrize("cap", [4, 16])
+def test_empty_lists_forward_backward(hsa, cap):
     """Query blocks with an empty list (kv_cnt = 0) attend to nothing: their
     output rows and log-sum-exp are zero, and they pass no gradient; the
     other rows match the oracle (per-head and shared lists, with and without
-    a processing order)."""
-    _say("empty lists")
+    a processing order; list capacity 4 takes the eager attention pipeline,
+    16 the deferred one)."""
+    _say(f"empty lists, capacity {cap}")
     T, H, W, nh, B, D = 4, 16, 16, 2, 64, 64
     g = torch.Generator().manual_seed(41)
     q, k, v, do = (torch.randn((1, T * H * W, nh, D), generator=g).to(torch.bfloat16) for _ in range(4))
@@ -752,12 +754,12 @@ def test_empty_lists_forward_backward(hsa):
     for G in (nh, 1):
         cnt = rng.integers(0, 4, size=(G, nb)).astype(np.int32)
         cnt[:, :3] = 0
-        idx = np.full((G, nb, 4), -1, dtype=np.int32)
+        idx = np.full((G, nb, cap), -1, dtype=np.int32)
         for h in range(G):
             for i in range(nb):
                 idx[h, i, :cnt[h, i]] = np.sort(rng.choice(nb, cnt[h, i], replace=False))
         kv_idx, kv_cnt = torch.from_numpy(idx).to(dev()), torch.from_numpy(cnt).to(dev())
-        order = hsa.hsa_attn_order(kv_cnt, 4)
+        order = hsa.hsa_attn_order(kv_cnt, cap)
         for o in (None, order):
             op, lse = hsa.hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B, order=o)
             dq, dk, dv = hsa.hsa_attn_bwd(qp, kp, vp, op, dop, lse, blk_len, kv_idx, kv_cnt, B)
