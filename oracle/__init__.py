@@ -25,8 +25,8 @@ values. Each function cites the page and section it follows:
   static-ratio and dynamic-threshold modes over a logarithmic radial window
   with a long-range factor.
 
-Readings of points the pages leave open are listed in the repository's
-design notes and repeated at each function. Parity-unpinned items: the MASS
+Readings of points the pages leave open are stated at each function that
+takes them. Parity-unpinned items: the MASS
 aggregation choice, the way threshold and global budget combine, the window
 tie order and the synthetic-field recipe are readings that only invariants
 pin, not values printed on the pages.
