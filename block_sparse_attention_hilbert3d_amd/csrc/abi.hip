@@ -295,7 +295,8 @@ hsa_status_t hsa_select(const float *S, int32_t nh, int32_t nb, const hsa_select
     case HSA_SELECT_THRESH_GLOBAL: {
       if (!S) return fail(HSA_ERR_NULL_PTR, "hsa_select: scores required");
       if (nb > 1024) return fail(HSA_ERR_UNSUPPORTED, "hsa_select: nb %d > 1024", nb);
-      if (!(p->tau >= 0.0) || !(p->tau <= 4.0)) return fail(HSA_ERR_BAD_ARG, "hsa_select: tau %g not in [0, 4]", p->tau);
+      // tau * 2^62 must fit the unsigned 64-bit fixed-point target
+      if (!(p->tau >= 0.0) || !(p->tau < 4.0)) return fail(HSA_ERR_BAD_ARG, "hsa_select: tau %g not in [0, 4)", p->tau);
       if (!(p->budget_ratio >= 0.0) || !(p->budget_ratio <= 1.0)) return fail(HSA_ERR_BAD_ARG, "hsa_select: budget_ratio %g not in [0, 1]", p->budget_ratio);
       if (max_kv != nb) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: THRESH_GLOBAL needs max_kv == nb");
       const size_t need = select_ws_bytes(nh, nb, p->mode);
@@ -377,6 +378,9 @@ hsa_status_t hsa_attn_tokens(const void *q, const void *k, const void *v, void *
   // gathered rows are addressed with 32-bit byte offsets from the tensor start
   if (kv_stride > 0 && static_cast<int64_t>(N) * kv_stride * es > (1ll << 32) - 1)
     return fail(HSA_ERR_UNSUPPORTED, "hsa_attn_tokens: token-major K/V span more than 4 GiB; reorder them with hsa_perm");
+  // ... formed as token index x row bytes with 24-bit multiplies
+  if (kv_stride > 0 && (N > (1 << 24) || kv_stride * es >= (1ll << 24)))
+    return fail(HSA_ERR_UNSUPPORTED, "hsa_attn_tokens: gathered K/V need N <= 2^24 tokens and rows under 16 MiB; reorder them with hsa_perm");
   if (kv_shared != 0 && kv_shared != 1) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: kv_shared must be 0 or 1");
   if (!(scale > 0.f) || !isfinite(scale)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: scale must be finite and positive");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: tensors must be 16-byte aligned");

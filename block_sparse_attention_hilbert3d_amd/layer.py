@@ -97,13 +97,10 @@ class SparseAttentionLayer:
         self.select_ws = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
     def _lvsa_width(self) -> int:
-        worst = 0
-        for step in range(self.T_per):
-            rot = step % self.T_per
-            anchors = (self.T - 1 - rot) // self.T_per + 1 if rot < self.T else 0
-            nw = min(max(self.C - anchors, 1), self.T - anchors)
-            worst = max(worst, anchors + nw)
-        return worst * self.tiles_per_frame
+        """List capacity that holds the LVSA lists of every step: the widest
+        of the T_per anchor rotations, as the library reports them."""
+        return max(B_.hsa_select_list_width(self.heads, self.nb, self.params(step, 0.0))
+                   for step in range(self.T_per))
 
     def params(self, step: int, budget_ratio: float) -> B_.SelectParams:
         return B_.make_params(self.select, k=self.k, tau=self.tau, budget_ratio=budget_ratio,

@@ -91,7 +91,7 @@ typedef void *hsa_stream_t; /* a hipStream_t */
 typedef struct hsa_select_params {
   int32_t mode;            /* hsa_select_mode_t */
   int32_t k;               /* TOPK: key blocks kept per query block, 1..nb */
-  double tau;              /* THRESH_GLOBAL: cumulative score per query block, >= 0 */
+  double tau;              /* THRESH_GLOBAL: cumulative score per query block, 0 <= tau < 4 */
   double budget_ratio;     /* THRESH_GLOBAL: head budget floor(ratio*nb*nb + 0.5) pairs */
   int32_t frames;          /* LVSA, RADIAL*: number of frames T (nb = frames*tiles_per_frame) */
   int32_t tiles_per_frame; /* LVSA, RADIAL*: tiles (blocks) per frame */
@@ -109,7 +109,10 @@ const char *hsa_status_str(hsa_status_t status);
 const char *hsa_last_error(void);
 
 /*
- * hsa_plan_size -- host-only: padded length and block count of a plan.
+ * hsa_plan_size -- host-only: padded length and block count of a plan (the
+ * blocks DFSAttn, Methodology, design 1, cuts the reordered sequence into;
+ * LVSA section 2's per-frame tiles; VMoBA abstract's 2D and 3D partitions).
+ * Closed forms, no device work; n_pad and nb are host outputs.
  * ROW / HILBERT3D / HILBERT2D: n_pad = ceil(N/B)*B. FRAME: n_pad = T*ceil(H*W/B)*B.
  * TILE2D / CUBE3D with tiles tT x tH x tW: one block per tile,
  * nb = ceil(T/tT)*ceil(H/tH)*ceil(W/tW). Grid sides 1..1024, n_pad < 2^31.
@@ -281,7 +284,8 @@ hsa_status_t hsa_attn(const void *qp, const void *kp, const void *vp, void *op, 
  *   elements between tokens; every real token's row is written once and
  *   nothing else in o is touched.
  * k, v: kv_stride > 0: token-major like q with that token stride (the byte
- *   span N*kv_stride*element size must stay below 4 GiB); kv_stride = 0:
+ *   span N*kv_stride*element size must stay below 4 GiB, N <= 2^24 and a
+ *   token row below 16 MiB; otherwise HSA_ERR_UNSUPPORTED); kv_stride = 0:
  *   reordered [nh][nb*B][D] from hsa_perm.
  * Strides are >= nh*D elements and multiples of 16 bytes.
  * perm: the plan's int32 [nb*B] slot -> token map; entries are -1 or < N,
@@ -342,7 +346,13 @@ hsa_status_t hsa_attn_bwd(const void *qp, const void *kp, const void *vp, const 
 
 /*
  * hsa_unperm -- scatter back to token order: o[perm[i]][h][:] = op[h][i][:]
- * for every real slot i (pad slots are dropped). Layouts as hsa_perm.
+ * for every real slot i (pad slots are dropped). DFSAttn (Methodology,
+ * design 1): attention runs on the reordered sequence and its outputs go
+ * back to the original token order (the inverse of hsa_perm's gather).
+ * op: reordered [nh][n_pad][D]; o: token-major [N][nh][D] with tok_stride
+ * elements between tokens (>= nh*D, a multiple of 16 bytes); perm: the
+ * plan's slot -> token map. Rows of o that no real slot maps to are not
+ * touched. Errors as hsa_perm (checked before any launch).
  */
 hsa_status_t hsa_unperm(const void *op, void *o, const int32_t *perm, int32_t N, int32_t n_pad,
                         int32_t nh, int32_t D, int64_t tok_stride, int32_t dtype,

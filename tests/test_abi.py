@@ -139,6 +139,11 @@ def test_select_validation(B):
     assert L.hsa_select(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 4, FAKE, n - 1, NULL) == 5
     p = B.make_params("thresh_global", tau=0.25, budget_ratio=1.5)
     assert L.hsa_select(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 4, FAKE, n, NULL) == 6
+    # tau * 2^62 must fit 64 bits: 4 is refused, the largest double below it is not
+    p = B.make_params("thresh_global", tau=4.0, budget_ratio=0.3)
+    assert L.hsa_select(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 4, FAKE, n, NULL) == 6
+    p = B.make_params("thresh_global", tau=float.fromhex("0x1.fffffffffffffp+1"), budget_ratio=0.3)
+    assert L.hsa_select(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 3, FAKE, n, NULL) == 2     # passes tau
     p = B.make_params("lvsa", frames=61, tiles_per_frame=13, C=21, T_per=8, step=0)
     assert L.hsa_select(NULL, 12, 793, ctypes.byref(p), FAKE, FAKE, 21 * 13 - 1, NULL, 0, NULL) == 2
     p = B.make_params("lvsa", frames=61, tiles_per_frame=13, C=21, T_per=8, step=0)
@@ -197,6 +202,12 @@ def test_attn_and_unperm_validation(B):
     # gathered K/V rows use 32-bit byte offsets: a 4 GiB token-major span is refused
     assert L.hsa_attn_tokens(FAKE, FAKE, FAKE, FAKE, 1 << 14, 1 << 14, 1 << 14, NULL, FAKE, 1 << 17,
                              FAKE, FAKE, FAKE, NULL, 4, 0, 128, 1024, 128, 128, 1, 0.125, NULL) == 4
+    # ... and their offsets use 24-bit factors: more than 2^24 tokens, or rows of 16 MiB, are refused
+    assert L.hsa_attn_tokens(FAKE, FAKE, FAKE, FAKE, 128, 128, 128, NULL, FAKE, (1 << 24) + 64,
+                             FAKE, FAKE, FAKE, NULL, 4, 0, 2, (1 << 18) + 1, 64, 64, 1, 0.125, NULL) == 4
+    assert L.hsa_attn_tokens(FAKE, FAKE, FAKE, FAKE, 128, 1 << 23, 128, NULL, FAKE, 200,
+                             FAKE, FAKE, FAKE, NULL, 4, 0, 2, 4, 64, 64, 1, 0.125, NULL) == 4
+    assert b"2^24" in L.hsa_last_error()
     assert L.hsa_unperm(FAKE, FAKE, FAKE, 10, 8, 2, 64, 128, 1, NULL) == 2
     assert L.hsa_unperm(FAKE, NULL, FAKE, 10, 16, 2, 64, 128, 1, NULL) == 1
 

@@ -264,3 +264,55 @@ def test_radial_dynamic_union_and_threshold():
                     assert len(sets[h][i]) == nb
         prev = sets
     assert 5 in set(oracle.select_radial_dynamic(S, T, P, 0.0, 0.0)[0][0, 3])
+
+
+def test_radial_dynamic_hand_derived(golden_dir):
+    """The dynamic-threshold reading (best logit minus delta, at or above
+    kept) on a hand-derived 2-frame case (tests/golden/radial_dyn_T2_P2.txt):
+    a block exactly on the threshold is kept, one just below is dropped, and
+    a block a mean-relative rule would keep is dropped."""
+    S = np.zeros((1, 4, 4), dtype=np.float32)
+    want = {}
+    with open(os.path.join(golden_dir, "radial_dyn_T2_P2.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            head, vals = line.split(":")
+            head = head.split()
+            if head[0] == "S":
+                S[0, int(head[1])] = [float(x) for x in vals.split()]
+            else:
+                want[(float(head[0]), int(head[1]))] = [int(x) for x in vals.split()]
+    assert len(want) == 8
+    for (delta, i), ids in want.items():
+        kv_idx, kv_cnt = oracle.select_radial_dynamic(S, 2, 2, 0.0, delta)
+        assert list(kv_idx[0, i, :kv_cnt[0, i]]) == ids, (delta, i)
+
+
+def test_thresh_difference_explanations():
+    """The helper that explains threshold-selection differences between
+    float32 and float64 scores: lists from slightly perturbed scores are all
+    explained; a planted low-score pair is not."""
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from _gpu_common import thresh_differences
+    rng = np.random.default_rng(5)
+    nh, nb = 2, 40
+    S = rng.random((nh, nb, nb)) ** 6
+    S /= S.sum(axis=2, keepdims=True)
+    S32 = np.clip(S + rng.uniform(-1e-3, 1e-3, S.shape), 0, None)   # large enough to move pairs
+    tau, ratio = 0.3, 0.12
+    idx, cnt = oracle.select_thresh_global(S32, tau, ratio)
+    diff, explained = thresh_differences(S, S32, idx, cnt, tau, ratio)
+    assert diff > 0 and explained == diff
+    # plant the lowest-scoring pair of a row into its list
+    i = 3
+    j = int(np.argmin(S[0, i]))
+    assert j not in set(idx[0, i, :cnt[0, i]])
+    row = np.sort(np.append(idx[0, i, :cnt[0, i]], j))
+    idx2, cnt2 = idx.copy(), cnt.copy()
+    cnt2[0, i] = row.size
+    idx2[0, i, :row.size] = row
+    diff2, explained2 = thresh_differences(S, S32, idx2, cnt2, tau, ratio)
+    assert diff2 == diff + 1 and explained2 == explained
