@@ -47,6 +47,7 @@ _SIGS = {
     "hsa_select_ws_size": (_c_sz, [_c_i32, _c_i32, ctypes.POINTER(SelectParams)]),
     "hsa_select_list_width": (_c_i32, [_c_i32, _c_i32, ctypes.POINTER(SelectParams)]),
     "hsa_select": (ctypes.c_int, [_p, _c_i32, _c_i32, ctypes.POINTER(SelectParams), _p, _p, _c_i32, _p, _c_sz, _p]),
+    "hsa_select_noalloc": (ctypes.c_int, [_p, _c_i32, _c_i32, ctypes.POINTER(SelectParams), _p, _p, _c_i32, _p]),
     "hsa_attn": (ctypes.c_int, [_p] * 9 + [_c_i32] * 7 + [_c_f32, _p]),
     "hsa_attn_tokens": (ctypes.c_int, [_p] * 4 + [_c_i64] * 3 + [_p, _p, _c_i32, _p, _p, _p, _p]
                         + [_c_i32] * 7 + [_c_f32, _p]),
@@ -211,6 +212,16 @@ def hsa_select(S, nh: int, nb: int, params: SelectParams, max_kv: int, device="c
         ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=device)
     _check(lib().hsa_select(_ptr(S), nh, nb, ctypes.byref(params), _ptr(kv_idx), _ptr(kv_cnt),
                             max_kv, _ptr(ws), ws.numel(), _stream()), "hsa_select")
+    return kv_idx, kv_cnt
+
+
+def hsa_select_noalloc(S, nh: int, nb: int, params: SelectParams, max_kv: int, outs):
+    """hsa_select with the library's static workspace (no workspace argument;
+    the caller passes the output lists `outs` = (kv_idx, kv_cnt))."""
+    kv_idx, kv_cnt = outs
+    _need_device(S, kv_idx, kv_cnt)
+    _check(lib().hsa_select_noalloc(_ptr(S), nh, nb, ctypes.byref(params), _ptr(kv_idx), _ptr(kv_cnt),
+                                    max_kv, _stream()), "hsa_select_noalloc")
     return kv_idx, kv_cnt
 
 

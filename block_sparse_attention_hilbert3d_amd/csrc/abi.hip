@@ -3,6 +3,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -278,60 +279,132 @@ size_t hsa_select_ws_size(int32_t nh, int32_t nb, const hsa_select_params_t *p) 
   return select_ws_bytes(nh, nb, p->mode);
 }
 
-hsa_status_t hsa_select(const float *S, int32_t nh, int32_t nb, const hsa_select_params_t *p,
-                        int32_t *kv_idx, int32_t *kv_cnt, int32_t max_kv, void *ws,
-                        size_t ws_bytes, hsa_stream_t stream) {
-  g_last_error.clear();
-  if (!p || !kv_idx || !kv_cnt) return fail(HSA_ERR_NULL_PTR, "hsa_select: params and lists are required");
-  if (nh < 1 || nb < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: nh=%d nb=%d", nh, nb);
-  if (max_kv < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: max_kv=%d", max_kv);
+}  // extern "C"
+
+namespace hsa_host {
+
+// Argument checks shared by hsa_select and hsa_select_noalloc (everything
+// but the workspace); `who` names the entry point in the message.
+static hsa_status_t check_select_args(const char *who, const float *S, int32_t nh, int32_t nb,
+                                      const hsa_select_params_t *p, const int32_t *kv_idx,
+                                      const int32_t *kv_cnt, int32_t max_kv) {
+  if (!p || !kv_idx || !kv_cnt) return fail(HSA_ERR_NULL_PTR, "%s: params and lists are required", who);
+  if (nh < 1 || nb < 1) return fail(HSA_ERR_BAD_SHAPE, "%s: nh=%d nb=%d", who, nh, nb);
+  if (max_kv < 1) return fail(HSA_ERR_BAD_SHAPE, "%s: max_kv=%d", who, max_kv);
   switch (p->mode) {
     case HSA_SELECT_TOPK:
-      if (!S) return fail(HSA_ERR_NULL_PTR, "hsa_select: scores required");
-      if (nb > 1024) return fail(HSA_ERR_UNSUPPORTED, "hsa_select: nb %d > 1024", nb);
-      if (p->k < 1 || p->k > nb) return fail(HSA_ERR_BAD_ARG, "hsa_select: k=%d not in 1..%d", p->k, nb);
-      if (max_kv < p->k) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: max_kv %d < k %d", max_kv, p->k);
+      if (!S) return fail(HSA_ERR_NULL_PTR, "%s: scores required", who);
+      if (nb > 1024) return fail(HSA_ERR_UNSUPPORTED, "%s: nb %d > 1024", who, nb);
+      if (p->k < 1 || p->k > nb) return fail(HSA_ERR_BAD_ARG, "%s: k=%d not in 1..%d", who, p->k, nb);
+      if (max_kv < p->k) return fail(HSA_ERR_BAD_SHAPE, "%s: max_kv %d < k %d", who, max_kv, p->k);
       break;
     case HSA_SELECT_THRESH_GLOBAL: {
-      if (!S) return fail(HSA_ERR_NULL_PTR, "hsa_select: scores required");
-      if (nb > 1024) return fail(HSA_ERR_UNSUPPORTED, "hsa_select: nb %d > 1024", nb);
+      if (!S) return fail(HSA_ERR_NULL_PTR, "%s: scores required", who);
+      if (nb > 1024) return fail(HSA_ERR_UNSUPPORTED, "%s: nb %d > 1024", who, nb);
       // tau * 2^62 must fit the unsigned 64-bit fixed-point target
-      if (!(p->tau >= 0.0) || !(p->tau < 4.0)) return fail(HSA_ERR_BAD_ARG, "hsa_select: tau %g not in [0, 4)", p->tau);
-      if (!(p->budget_ratio >= 0.0) || !(p->budget_ratio <= 1.0)) return fail(HSA_ERR_BAD_ARG, "hsa_select: budget_ratio %g not in [0, 1]", p->budget_ratio);
-      if (max_kv != nb) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: THRESH_GLOBAL needs max_kv == nb");
-      const size_t need = select_ws_bytes(nh, nb, p->mode);
-      if (!ws || ws_bytes < need) return fail(HSA_ERR_WORKSPACE, "hsa_select: workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
-      if (!aligned16(ws)) return fail(HSA_ERR_BAD_ARG, "hsa_select: workspace must be 16-byte aligned");
+      if (!(p->tau >= 0.0) || !(p->tau < 4.0)) return fail(HSA_ERR_BAD_ARG, "%s: tau %g not in [0, 4)", who, p->tau);
+      if (!(p->budget_ratio >= 0.0) || !(p->budget_ratio <= 1.0)) return fail(HSA_ERR_BAD_ARG, "%s: budget_ratio %g not in [0, 1]", who, p->budget_ratio);
+      if (max_kv != nb) return fail(HSA_ERR_BAD_SHAPE, "%s: THRESH_GLOBAL needs max_kv == nb", who);
       break;
     }
     case HSA_SELECT_LVSA: {
-      if (p->frames < 1 || p->frames > 1024 || p->tiles_per_frame < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: frames=%d tiles_per_frame=%d", p->frames, p->tiles_per_frame);
-      if (static_cast<int64_t>(p->frames) * p->tiles_per_frame != nb) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: frames*tiles_per_frame != nb");
-      if (p->C < 1 || p->T_per < 1 || p->step < 0) return fail(HSA_ERR_BAD_ARG, "hsa_select: C=%d T_per=%d step=%d", p->C, p->T_per, p->step);
+      if (p->frames < 1 || p->frames > 1024 || p->tiles_per_frame < 1) return fail(HSA_ERR_BAD_SHAPE, "%s: frames=%d tiles_per_frame=%d", who, p->frames, p->tiles_per_frame);
+      if (static_cast<int64_t>(p->frames) * p->tiles_per_frame != nb) return fail(HSA_ERR_BAD_SHAPE, "%s: frames*tiles_per_frame != nb", who);
+      if (p->C < 1 || p->T_per < 1 || p->step < 0) return fail(HSA_ERR_BAD_ARG, "%s: C=%d T_per=%d step=%d", who, p->C, p->T_per, p->step);
       // largest |A(t)|: all anchors plus max(C - anchors, 1) window frames
       const int64_t need = lvsa_list_width(p);
-      if (max_kv < need) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: max_kv %d < %lld tiles per list", max_kv, static_cast<long long>(need));
+      if (max_kv < need) return fail(HSA_ERR_BAD_SHAPE, "%s: max_kv %d < %lld tiles per list", who, max_kv, static_cast<long long>(need));
       break;
     }
     case HSA_SELECT_RADIAL:
     case HSA_SELECT_RADIAL_DYN: {
-      if (p->frames < 1 || p->frames > 1024 || p->tiles_per_frame < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: frames=%d tiles_per_frame=%d", p->frames, p->tiles_per_frame);
-      if (static_cast<int64_t>(p->frames) * p->tiles_per_frame != nb) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: frames*tiles_per_frame != nb");
-      if (!(p->lam >= 0.0) || !(p->lam <= 1.0)) return fail(HSA_ERR_BAD_ARG, "hsa_select: lam %g not in [0, 1]", p->lam);
+      if (p->frames < 1 || p->frames > 1024 || p->tiles_per_frame < 1) return fail(HSA_ERR_BAD_SHAPE, "%s: frames=%d tiles_per_frame=%d", who, p->frames, p->tiles_per_frame);
+      if (static_cast<int64_t>(p->frames) * p->tiles_per_frame != nb) return fail(HSA_ERR_BAD_SHAPE, "%s: frames*tiles_per_frame != nb", who);
+      if (!(p->lam >= 0.0) || !(p->lam <= 1.0)) return fail(HSA_ERR_BAD_ARG, "%s: lam %g not in [0, 1]", who, p->lam);
       if (p->mode == HSA_SELECT_RADIAL) {
         const int need = radial_list_width(p->frames, p->tiles_per_frame, p->lam);
-        if (max_kv < need) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: max_kv %d < %d tiles per list", max_kv, need);
+        if (max_kv < need) return fail(HSA_ERR_BAD_SHAPE, "%s: max_kv %d < %d tiles per list", who, max_kv, need);
       } else {
-        if (!S) return fail(HSA_ERR_NULL_PTR, "hsa_select: scores required");
-        if (!(p->delta >= 0.0) || !isfinite(p->delta)) return fail(HSA_ERR_BAD_ARG, "hsa_select: delta %g must be finite and >= 0", p->delta);
-        if (max_kv != nb) return fail(HSA_ERR_BAD_SHAPE, "hsa_select: RADIAL_DYN needs max_kv == nb");
-        if (nb > 4096) return fail(HSA_ERR_UNSUPPORTED, "hsa_select: nb %d > 4096", nb);
+        if (!S) return fail(HSA_ERR_NULL_PTR, "%s: scores required", who);
+        if (!(p->delta >= 0.0) || !isfinite(p->delta)) return fail(HSA_ERR_BAD_ARG, "%s: delta %g must be finite and >= 0", who, p->delta);
+        if (max_kv != nb) return fail(HSA_ERR_BAD_SHAPE, "%s: RADIAL_DYN needs max_kv == nb", who);
+        if (nb > 4096) return fail(HSA_ERR_UNSUPPORTED, "%s: nb %d > 4096", who, nb);
       }
       break;
     }
     default:
-      return fail(HSA_ERR_BAD_ARG, "hsa_select: unknown mode %d", p->mode);
+      return fail(HSA_ERR_BAD_ARG, "%s: unknown mode %d", who, p->mode);
   }
+  return HSA_OK;
+}
+
+}  // namespace hsa_host
+
+extern "C" {
+
+hsa_status_t hsa_select(const float *S, int32_t nh, int32_t nb, const hsa_select_params_t *p,
+                        int32_t *kv_idx, int32_t *kv_cnt, int32_t max_kv, void *ws,
+                        size_t ws_bytes, hsa_stream_t stream) {
+  g_last_error.clear();
+  hsa_status_t st = check_select_args("hsa_select", S, nh, nb, p, kv_idx, kv_cnt, max_kv);
+  if (st != HSA_OK) return st;
+  const size_t need = select_ws_bytes(nh, nb, p->mode);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return fail(HSA_ERR_WORKSPACE, "hsa_select: workspace needs %zu bytes, got %zu", need, ws ? ws_bytes : 0);
+    if (!aligned16(ws)) return fail(HSA_ERR_BAD_ARG, "hsa_select: workspace must be 16-byte aligned");
+  }
+  return launch_select(S, nh, nb, p, kv_idx, kv_cnt, max_kv, ws, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace hsa_host {
+
+// Workspace of hsa_select_noalloc: one array per GPU, part of the loaded
+// code object (nothing is allocated at run time). In host code the name is a
+// host-side stand-in, never a device address: kernels get the address that
+// hipGetSymbolAddress reports for the current device.
+constexpr size_t kSelectScratchBytes = HSA_SELECT_NOALLOC_MAX_WS;
+static __device__ __align__(256) unsigned char scratch[kSelectScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_dev[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+static hsa_status_t scratch_on_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HSA_ERR_HIP, "hsa_select_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(HSA_ERR_UNSUPPORTED, "hsa_select_noalloc: device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(HSA_ERR_HIP, "hsa_select_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return HSA_OK;
+}
+
+}  // namespace hsa_host
+
+extern "C" {
+
+hsa_status_t hsa_select_noalloc(const float *S, int32_t nh, int32_t nb, const hsa_select_params_t *p,
+                                int32_t *kv_idx, int32_t *kv_cnt, int32_t max_kv, hsa_stream_t stream) {
+  g_last_error.clear();
+  hsa_status_t st = check_select_args("hsa_select_noalloc", S, nh, nb, p, kv_idx, kv_cnt, max_kv);
+  if (st != HSA_OK) return st;
+  const size_t need = select_ws_bytes(nh, nb, p->mode);
+  if (need > kSelectScratchBytes)
+    return fail(HSA_ERR_UNSUPPORTED, "hsa_select_noalloc: nh=%d nb=%d need %zu bytes of workspace, more than the "
+                "%zu-byte static scratch; use hsa_select with a caller workspace", nh, nb, need, kSelectScratchBytes);
+  void *ws = nullptr;
+  if (need > 0 && (st = scratch_on_current_device(&ws)) != HSA_OK) return st;
   return launch_select(S, nh, nb, p, kv_idx, kv_cnt, max_kv, ws, static_cast<hipStream_t>(stream));
 }
 

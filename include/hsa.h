@@ -243,6 +243,25 @@ hsa_status_t hsa_select(const float *S, int32_t nh, int32_t nb, const hsa_select
                         size_t ws_bytes, hsa_stream_t stream);
 
 /*
+ * hsa_select_noalloc -- hsa_select without a caller workspace, for callers
+ *   that cannot allocate device memory (code under HIP graph capture, tight
+ *   serving loops, harnesses that forbid allocation). Same arguments, lists,
+ *   results and errors as hsa_select minus ws/ws_bytes; the workspace is a
+ *   static array of HSA_SELECT_NOALLOC_MAX_WS bytes that the library holds on
+ *   every GPU it runs on until the process ends. Parameters whose workspace
+ *   (hsa_select_ws_size) exceeds that size fail with HSA_ERR_UNSUPPORTED
+ *   before anything is enqueued (THRESH_GLOBAL fits up to nh = 64 heads at
+ *   nb = 1024; the other modes need no workspace). The call allocates nothing
+ *   and clears what it needs itself; its first call on a device looks up
+ *   that device's copy of the array (the device current at the call).
+ *   Calls that overlap on one GPU (several streams or threads at once) share
+ *   that GPU's array and race: serialise them.
+ */
+#define HSA_SELECT_NOALLOC_MAX_WS ((size_t)4 << 20)
+hsa_status_t hsa_select_noalloc(const float *S, int32_t nh, int32_t nb, const hsa_select_params_t *p,
+                                int32_t *kv_idx, int32_t *kv_cnt, int32_t max_kv, hsa_stream_t stream);
+
+/*
  * hsa_attn -- block-sparse attention: for every query slot i of block I,
  *   o_i = sum_j softmax_j(scale * q_i . k_j) v_j over the real key slots j of
  *   the blocks listed for I (DFSAttn Significance: block-wise execution over

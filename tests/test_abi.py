@@ -154,6 +154,21 @@ def test_select_validation(B):
     assert L.hsa_select(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 4, NULL, 0, NULL) == 6
 
 
+def test_select_noalloc_validation(B):
+    """The allocation-free selection checks its arguments like hsa_select and
+    refuses, before any launch, a problem whose workspace exceeds its static
+    array."""
+    L = B.lib()
+    p = B.make_params("thresh_global", tau=0.25, budget_ratio=0.3)
+    assert L.hsa_select_noalloc(FAKE, 512, 1024, ctypes.byref(p), FAKE, FAKE, 1024, NULL) == 4
+    assert b"static scratch" in L.hsa_last_error()
+    assert L.hsa_select_noalloc(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 3, NULL) == 2     # max_kv != nb
+    assert L.hsa_select_noalloc(NULL, 2, 4, ctypes.byref(p), FAKE, FAKE, 4, NULL) == 1
+    p = B.make_params("thresh_global", tau=4.0, budget_ratio=0.3)
+    assert L.hsa_select_noalloc(FAKE, 2, 4, ctypes.byref(p), FAKE, FAKE, 4, NULL) == 6
+    assert b"hsa_select_noalloc" in L.hsa_last_error()
+
+
 def test_radial_select_validation_and_width(B):
     L = B.lib()
     p = B.make_params("radial", frames=61, tiles_per_frame=13, lam=0.125)
