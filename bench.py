@@ -12,7 +12,12 @@ taken from HIP events recorded on the stream the library launches on;
 `stages` gives every step's time and its fraction of HBM or MFMA peak;
 `cpu_baseline` times the CPU oracle on a bounded sample of the same layer.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 3] [--no-cpu]
+Beside the headline workload the line carries `workloads`: the LVSA
+long-video frame mask (61x30x52) and the HunyuanVideo-like 720p threshold
+selection (33x45x80), each over every step of its schedule, with its own
+per-stage times, roofline fractions and a smaller oracle sample.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 3] [--no-cpu] [--no-extra]
 """
 from __future__ import annotations
 
@@ -53,7 +58,23 @@ def _traffic(w_idx):
     return c.get("hbm_bytes_per_launch")
 
 
-def _cpu_baseline(w, q, k, v, blocks_per_head=32):
+def _oracle_select(w, S, nb, step):
+    """The oracle's lists for a workload's selection rule at a step."""
+    import oracle
+    import workloads as wl
+    if w.select == "topk":
+        return oracle.select_topk(S, wl.topk_of(w, nb))
+    if w.select == "thresh_global":
+        return oracle.select_thresh_global(S, w.tau, wl.budget_ratio(w, step))
+    tiles = nb // w.T
+    if w.select == "lvsa":
+        return oracle.select_lvsa(w.T, tiles, w.C, w.T_per, step)
+    if w.select == "radial":
+        return oracle.select_radial(w.T, tiles, w.lam)
+    return oracle.select_radial_dynamic(S.astype("float32"), w.T, tiles, w.lam, w.delta)
+
+
+def _cpu_baseline(w, q, k, v, step=0, blocks_per_head=32):
     """Time the CPU oracle on a bounded sample of the same layer: plan,
     gather, scoring and selection on the whole problem, attention on every
     row of `blocks_per_head` seeded query blocks per head, extrapolated
@@ -66,10 +87,9 @@ def _cpu_baseline(w, q, k, v, blocks_per_head=32):
     perm, blk_len = oracle.plan(w.T, w.H, w.W, w.order, w.B)
     qp, kp, vp = (oracle.gather(x, perm) for x in (q, k, v))
     t1 = time.perf_counter()
-    S = oracle.score(qp, kp, perm, w.B, w.s)
     nb = perm.size // w.B
-    kk = w.k if w.k > 0 else max(1, int(math.floor(w.keep_ratio * nb + 0.5)))
-    kv_idx, kv_cnt = oracle.select_topk(S, kk)
+    S = oracle.score(qp, kp, perm, w.B, w.s, agg=w.agg) if w.s > 0 else None
+    kv_idx, kv_cnt = _oracle_select(w, S, nb, step)
     t2 = time.perf_counter()
     nblk = min(blocks_per_head, nb)
     rows = []
@@ -89,6 +109,19 @@ def _cpu_baseline(w, q, k, v, blocks_per_head=32):
                 attn_sample_s=t3 - t2, attn_extrapolated_s=full_attn, wall_s=t3 - t0,
                 cores=max(1, min(len(os.sched_getaffinity(0)), blas)), blocks_per_head=nblk,
                 nb=nb)
+
+
+def _cpu_record(cb, flop_dense):
+    return {
+        "value": flop_dense / cb["layer_s"] / 1e12, "unit": "TFLOP/s (dense-equivalent)",
+        "cores": cb["cores"], "kind": "oracle",
+        "sample": (f"float64 numpy oracle on this host: plan+gather {cb['plan_gather_s']:.2f}s and "
+                   f"score+select {cb['score_select_s']:.2f}s on the whole layer, attention on "
+                   f"{cb['blocks_per_head']} seeded query blocks/head ({cb['attn_sample_s']:.2f}s) "
+                   f"extrapolated linearly to all {cb['nb']} blocks; layer {cb['layer_s']:.1f}s; "
+                   f"cores = BLAS threads"),
+        "ms_per_layer": cb["layer_s"] * 1e3,
+    }
 
 
 def _time_backward(hsa, L, qkv, K, stream, flop_fwd):
@@ -139,57 +172,47 @@ def _keep_text(w, L, nb, tiles_steps, nh):
             f"query block (mean over {len(tiles_steps)} steps)")
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3)
-    ap.add_argument("--order", choices=["row", "hilbert", "frame", "tile2d", "cube3d"], default=None,
-                    help="token order instead of the workload's own (e.g. the VMoBA 2D/3D partitions)")
-    ap.add_argument("--backward", action="store_true",
-                    help="also time the attention backward (hsa_attn_bwd) on the layer's lists")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--io", choices=["auto", "reordered", "tokens_qo", "tokens"], default="tokens_qo",
-                    help="where the reorders happen: five separate passes (reordered), the "
-                         "attention kernel reading Q / writing O in token order (tokens_qo), "
-                         "or also gathering K/V rows itself (tokens); auto picks tokens for "
-                         "short top-k lists and tokens_qo otherwise")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="first run one device-to-device copy of this many MiB (a kernel of known "
-                         "traffic, to scale hardware byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the attention path here runs on a single MI355X "
-              "(multi-GPU sharding is designed, not built); run it with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def _copy_rate(torch, dev, stream):
+    """Measured device-to-device copy bandwidth (context for the HBM
+    fractions: the practical ceiling of plain streaming on this part)."""
+    ca = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    cb = torch.empty_like(ca)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    copy_us = []
+    for r in range(4):
+        flush.fill_(r)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cb.copy_(ca)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_us.append(e0.elapsed_time(e1) * 1e3)
+    return 2 * ca.numel() * 4 / min(copy_us[1:]) / 1e3
 
+
+def _measure(hsa, wl, w, io, K, W, n_sets, detailed):
+    """Time K layer steps of workload w (after W warm-up steps) on input sets
+    rotated step by step; per-stage times from HIP events on the launch
+    stream. Returns (record, layer, host input sets)."""
     import numpy as np
     import torch
 
-    import block_sparse_attention_hilbert3d_amd as hsa
-    import workloads as wl
-
-    w = wl.get(args.workload)
-    if args.order is not None:
-        from dataclasses import replace
-        w = replace(w, order=args.order)
     dev = torch.device("cuda:0")
-    sets_cpu = [wl.make_qkv(w, s) for s in range(2)]
-    sets = [tuple(x.to(dev) for x in s) for s in sets_cpu]
-    L = hsa.layer_for_workload(w, device=dev, want_lse=False, io=args.io)
+    stream = torch.cuda.current_stream()
+    sets_cpu = [wl.make_qkv(w, s) for s in range(n_sets)]
+    sets = [tuple(x.to(dev) for x in st) for st in sets_cpu]
+    L = hsa.layer_for_workload(w, device=dev, want_lse=False, io=io)
     nb, B, D, nh, N = L.nb, w.B, w.D, w.heads, w.N
     esz = 2 if w.dtype == "bf16" else 4
-    stream = torch.cuda.current_stream()
-
     scored = L.S is not None
+
     # the diffusion step a timed step stands for: its budget (threshold mode)
     # or its anchor rotation (LVSA); top-k steps refresh the same way each time
     def step_of(i):
         return i % max(w.steps, 1)
 
     def one_step(i, ev=None):
-        q, k, v = sets[i % 2]
+        q, k, v = sets[i % n_sets]
         st = step_of(i)
         if ev is not None:
             ev[0].record(stream)
@@ -214,37 +237,9 @@ def main():
         if ev is not None:
             ev[5].record(stream)
 
-    # measured device-to-device copy bandwidth (context for the HBM fractions:
-    # the practical ceiling of plain streaming on this part)
-    ca = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)
-    cb = torch.empty_like(ca)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    copy_us = []
-    for r in range(4):
-        flush.fill_(r)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        cb.copy_(ca)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        copy_us.append(e0.elapsed_time(e1) * 1e3)
-    copy_gbs = 2 * ca.numel() * 4 / min(copy_us[1:]) / 1e3
-    del ca, cb, flush
-
-    if args.copy_calibration > 0:
-        n = args.copy_calibration * (1 << 20) // 4
-        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
-
-    for i in range(args.warmup):
+    for i in range(W):
         one_step(i)
     torch.cuda.synchronize()
-
-    K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -257,64 +252,31 @@ def main():
     names = ["perm", "score", "select", "attn", "unperm"]
     stage_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
     per_step = np.array([e[0].elapsed_time(e[5]) for e in evs])
-    # computed tile pairs of every timed step (lists change with the step in
-    # threshold and LVSA modes); attention time is the mean over those steps
-    tiles_steps = []
+
+    # the lists of every timed step (they change with the step in threshold
+    # and LVSA modes): computed tile pairs, useful (query, key) pairs over
+    # real tokens, and list entries written
+    G = L.kv_idx.shape[0]
+    blk_len = L.blk_len.to(torch.int64)
+    tiles_steps, useful_steps, entries_steps = [], [], []
     for i in range(K):
         one_step(i)
-        tiles_steps.append(int(L.kv_cnt.sum().item()) * (nh if L.kv_idx.shape[0] == 1 else 1))
+        cnt = L.kv_cnt.to(torch.int64)
+        valid = torch.arange(L.max_kv, device=dev)[None, None, :] < cnt[..., None]
+        keys = torch.where(valid, blk_len[L.kv_idx.clamp(0, nb - 1).to(torch.int64)], 0).sum(-1)
+        tiles_steps.append(int(cnt.sum().item()) * (nh // G))
+        useful_steps.append(int((keys * blk_len[None, :]).sum().item()) * (nh // G))
+        entries_steps.append(int(cnt.sum().item()))
     torch.cuda.synchronize()
-
-    # cached-mask steps (mask reused: reorder, attention, restore)
-    cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for i in range(K):
-        q, k, v = sets[(i + 1) % 2]
-        cevs[i][0].record(stream)
-        L.step(q, k, v, reuse_mask=True)
-        cevs[i][1].record(stream)
-    torch.cuda.synchronize()
-    ms_cached = float(np.mean([a.elapsed_time(b) for a, b in cevs]))
 
     flop_tiles = 4.0 * B * B * D * float(np.mean(tiles_steps))
-    # useful pairs of the last timed step's lists, scaled to the mean tile count
-    # the same refresh step captured once in a HIP graph and replayed (no
-    # per-kernel launch cost); one graph per input set
-    graphs = []
-    for i in range(2):
-        L.step(*sets[i], step=0, budget_ratio=wl.budget_ratio(w, 0))
-        torch.cuda.synchronize()
-        gph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gph):
-            L.step(*sets[i], step=0, budget_ratio=wl.budget_ratio(w, 0))
-        graphs.append(gph)
-    torch.cuda.synchronize()
-    for gph in graphs:
-        gph.replay()
-    torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g0.record(stream)
-    for i in range(K):
-        graphs[i % 2].replay()
-    g1.record(stream)
-    torch.cuda.synchronize()
-    ms_graph = g0.elapsed_time(g1) / K
-    del graphs
-
-    kv_cnt = L.kv_cnt.cpu().numpy()
-    blk_len = L.blk_len.cpu().numpy().astype(np.int64)
-    kv_idx = L.kv_idx.cpu().numpy()
-    G = kv_idx.shape[0]
-    kept_keys = sum(int((blk_len[kv_idx[h, i, :kv_cnt[h, i]]].sum()) * blk_len[i])
-                    for h in range(G) for i in range(nb)) * (nh // G)
-    flop_useful = 4.0 * D * kept_keys * float(np.mean(tiles_steps)) / max(tiles_steps[-1], 1)
+    flop_useful = 4.0 * D * float(np.mean(useful_steps))
     flop_dense = 4.0 * N * N * D * nh
     t_attn = stage_ms["attn"] * 1e-3
     achieved = flop_tiles / t_attn / 1e12
     row = N * nh * D * esz
     U = L.n_pad // w.s if scored else 0
     pooled_bytes = 2 * nh * U * D * 4
-    G = L.kv_idx.shape[0]
-    io = L.io
     stage_bytes = {
         # reordered: Q, K, V read and written once, plus the Q/K sub-block
         # means. tokens_qo: only K and V are reordered (Q is read for its
@@ -322,23 +284,24 @@ def main():
         # read for their means on refresh steps only.
         "perm": {"reordered": 3 * 2 * row + pooled_bytes,
                  "tokens_qo": 4 * row + ((row + pooled_bytes) if scored else 0),
-                 "tokens": (2 * row + pooled_bytes) if scored else 0}[io],
+                 "tokens": (2 * row + pooled_bytes) if scored else 0}[L.io],
         "score": pooled_bytes + nh * nb * nb * 4,
-        # S read (scored modes) and the lists written
-        "select": (nh * nb * nb * 4 if scored else 0) + G * nb * (L.max_kv + 1) * 4,
+        # S read once (scored modes), the list entries and counts written
+        "select": (nh * nb * nb * 4 if scored else 0) + (float(np.mean(entries_steps)) + G * nb) * 4,
         "unperm": 2 * row,
     }
     score_flop = 2.0 * U * U * D * nh
     stages = {}
     for n in names:
         t = stage_ms[n] * 1e-3
-        if ((n == "score" and not scored) or (n == "unperm" and io != "reordered")
+        if ((n == "score" and not scored) or (n == "unperm" and L.io != "reordered")
                 or (n == "perm" and stage_bytes["perm"] == 0)):
             continue
         if n == "attn":
             stages[n] = {"ms": stage_ms[n], "tflops_computed_tiles": achieved,
                          "tflops_useful": flop_useful / t / 1e12,
-                         "frac_mfma_peak": achieved / BF16_PEAK_TFLOPS}
+                         "frac_mfma_peak": achieved / BF16_PEAK_TFLOPS,
+                         "frac_mfma_peak_useful": flop_useful / t / 1e12 / BF16_PEAK_TFLOPS}
         elif n == "score":
             # pooling happens inside perm; what remains is the fp32 contraction
             stages[n] = {"ms": stage_ms[n], "bytes": stage_bytes[n], "flop": score_flop,
@@ -350,17 +313,124 @@ def main():
             gbs = stage_bytes[n] / t / 1e9
             stages[n] = {"ms": stage_ms[n], "bytes": stage_bytes[n], "GB/s": gbs,
                          "frac_hbm_peak": gbs / HBM_PEAK_GBS}
-    dense_tflops = flop_dense / (ms_step * 1e-3) / 1e12
     peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
-    cycle_ms = (ms_step + (w.refresh - 1) * ms_cached) / w.refresh if w.refresh > 1 else ms_step
+    rec = {
+        "workload": w.name, "tokens": N, "heads": nh, "head_dim": D, "block": B,
+        "sub_block": w.s, "order": w.order, "dtype": w.dtype,
+        "keep": _keep_text(w, L, nb, tiles_steps, nh),
+        "steps": K, "warmup": W,
+        "ms_per_layer": ms_step,
+        "ms_per_layer_p10_p50_p90": [float(np.percentile(per_step, p)) for p in (10, 50, 90)],
+        "tflops_dense_equivalent": flop_dense / (ms_step * 1e-3) / 1e12,
+        "stages": stages,
+        "flop": {"dense": flop_dense, "computed_tiles": flop_tiles, "useful": flop_useful},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "frac_useful": flop_useful / t_attn / 1e12 / peak,
+                     "kernel": "attn_bf16_pipe_kernel" if w.dtype == "bf16" else "attn_f32_kernel"},
+    }
+    if detailed:
+        # cached-mask steps (mask reused: reorder, attention, restore)
+        cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for i in range(K):
+            q, k, v = sets[(i + 1) % n_sets]
+            cevs[i][0].record(stream)
+            L.step(q, k, v, reuse_mask=True)
+            cevs[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms_cached = float(np.mean([a.elapsed_time(b) for a, b in cevs]))
+        # the same refresh step captured once in a HIP graph and replayed (no
+        # per-kernel launch cost); one graph per input set
+        graphs = []
+        for i in range(n_sets):
+            L.step(*sets[i], step=0, budget_ratio=wl.budget_ratio(w, 0))
+            torch.cuda.synchronize()
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                L.step(*sets[i], step=0, budget_ratio=wl.budget_ratio(w, 0))
+            graphs.append(gph)
+        torch.cuda.synchronize()
+        for gph in graphs:
+            gph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for i in range(K):
+            graphs[i % n_sets].replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        rec["ms_per_layer_cached_mask"] = ms_cached
+        rec["ms_per_step_hip_graph"] = g0.elapsed_time(g1) / K
+        rec["ms_per_layer_refresh_cycle"] = ((ms_step + (w.refresh - 1) * ms_cached) / w.refresh
+                                             if w.refresh > 1 else ms_step)
+        rec["refresh_interval"] = w.refresh
+        del graphs
+    return rec, L, sets_cpu
+
+
+# extra workloads reported beside the headline one: the LVSA long-video frame
+# mask and the HunyuanVideo-like 720p threshold selection (one input set each,
+# every step of their schedules, a smaller oracle sample)
+EXTRA = {4: "lvsa_61x30x52", 5: "hunyuan720p_33x45x80"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--order", choices=["row", "hilbert", "frame", "tile2d", "cube3d"], default=None,
+                    help="token order instead of the workload's own (e.g. the VMoBA 2D/3D partitions)")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the attention backward (hsa_attn_bwd) on the layer's lists")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the LVSA and 720p threshold workloads reported beside the default one")
+    ap.add_argument("--io", choices=["auto", "reordered", "tokens_qo", "tokens"], default="tokens_qo",
+                    help="where the reorders happen: five separate passes (reordered), the "
+                         "attention kernel reading Q / writing O in token order (tokens_qo), "
+                         "or also gathering K/V rows itself (tokens); auto picks tokens for "
+                         "short top-k lists and tokens_qo otherwise")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one device-to-device copy of this many MiB (a kernel of known "
+                         "traffic, to scale hardware byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the attention path here runs on a single MI355X "
+              "(multi-GPU sharding is designed, not built); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_attention_hilbert3d_amd as hsa
+    import workloads as wl
+
+    w = wl.get(args.workload)
+    if args.order is not None:
+        from dataclasses import replace
+        w = replace(w, order=args.order)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    copy_gbs = _copy_rate(torch, dev, stream)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    rec, L, sets_cpu = _measure(hsa, wl, w, args.io, args.steps, args.warmup, 2, detailed=True)
+    K = args.steps
     out = {
         "metric": METRIC,
-        "value": dense_tflops,
+        "value": rec["tflops_dense_equivalent"],
         "unit": "TFLOP/s (dense-equivalent)",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": rec["ms_per_layer"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -368,39 +438,44 @@ def main():
         "data": "synthetic (seeded smoothed-field Q/K, i.i.d. V; no model weights)",
         "config": {"workload": f"Wan-2.1-1.3B-like 480p 81-frame latent {w.T}x{w.H}x{w.W}"
                                if w.idx == 3 else w.name,
-                   "tokens": N, "heads": nh, "head_dim": D, "block": B, "sub_block": w.s,
-                   "order": w.order, "keep": _keep_text(w, L, nb, tiles_steps, nh),
+                   "tokens": rec["tokens"], "heads": rec["heads"], "head_dim": rec["head_dim"],
+                   "block": rec["block"], "sub_block": w.s, "order": w.order, "keep": rec["keep"],
                    "io": {"reordered": "five passes (reorder Q/K/V, attention, unperm)",
                           "tokens_qo": "K/V reordered; attention reads Q and writes O in token order",
                           "tokens": "attention gathers Q/K/V rows and writes O in token order; "
-                                    "the reorder pass only pools Q/K on refresh steps"}[io],
+                                    "the reorder pass only pools Q/K on refresh steps"}[L.io],
                    "batch": 1},
-        "ms_per_step_p10_p50_p90": [float(np.percentile(per_step, p)) for p in (10, 50, 90)],
-        "ms_per_layer_cached_mask": ms_cached,
-        "ms_per_step_hip_graph": ms_graph,
-        "ms_per_layer_refresh_cycle": cycle_ms,
-        "refresh_interval": w.refresh,
-        "stages": stages,
+        "ms_per_step_p10_p50_p90": rec["ms_per_layer_p10_p50_p90"],
+        "ms_per_layer_cached_mask": rec["ms_per_layer_cached_mask"],
+        "ms_per_step_hip_graph": rec["ms_per_step_hip_graph"],
+        "ms_per_layer_refresh_cycle": rec["ms_per_layer_refresh_cycle"],
+        "refresh_interval": rec["refresh_interval"],
+        "stages": rec["stages"],
         "measured_copy_GB/s": copy_gbs,
-        "flop": {"dense": flop_dense, "computed_tiles": flop_tiles, "useful": flop_useful},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": _traffic(w.idx),
-                     "kernel": "attn_bf16_pipe_kernel" if w.dtype == "bf16" else "attn_f32_kernel"},
+        "flop": rec["flop"],
+        "roofline": dict(rec["roofline"], traffic=_traffic(w.idx)),
     }
     if args.backward:
-        out["backward"] = _time_backward(hsa, L, sets[0], K, stream, flop_tiles)
-    if not args.no_cpu and w.select == "topk":
-        cb = _cpu_baseline(w, *sets_cpu[0])
-        out["cpu_baseline"] = {
-            "value": flop_dense / cb["layer_s"] / 1e12, "unit": "TFLOP/s (dense-equivalent)",
-            "cores": cb["cores"], "kind": "oracle",
-            "sample": (f"float64 numpy oracle on this host: plan+gather {cb['plan_gather_s']:.2f}s and "
-                       f"score+select {cb['score_select_s']:.2f}s on the whole layer, attention on "
-                       f"{cb['blocks_per_head']} seeded query blocks/head ({cb['attn_sample_s']:.2f}s) "
-                       f"extrapolated linearly to all {cb['nb']} blocks; layer {cb['layer_s']:.1f}s; "
-                       f"cores = BLAS threads"),
-            "ms_per_layer": cb["layer_s"] * 1e3,
-        }
+        out["backward"] = _time_backward(hsa, L, tuple(x.to(dev) for x in sets_cpu[0]), K, stream,
+                                         rec["flop"]["computed_tiles"])
+    del L
+    torch.cuda.empty_cache()
+    if not args.no_cpu:
+        out["cpu_baseline"] = _cpu_record(_cpu_baseline(w, *sets_cpu[0]), rec["flop"]["dense"])
+    del sets_cpu
+    if args.workload == 3 and args.order is None and not args.no_extra:
+        extra = {}
+        for idx, key in EXTRA.items():
+            we = wl.get(idx)
+            r, Le, sc = _measure(hsa, wl, we, "tokens_qo", we.steps, 2, 1, detailed=False)
+            del Le
+            torch.cuda.empty_cache()
+            if not args.no_cpu:
+                r["cpu_baseline"] = _cpu_record(_cpu_baseline(we, *sc[0], step=0, blocks_per_head=8),
+                                                r["flop"]["dense"])
+            del sc
+            extra[key] = r
+        out["workloads"] = extra
     print(json.dumps(out), flush=True)
 
 

@@ -209,7 +209,7 @@ hsa_status_t hsa_score(const void *qp, const void *kp, const float *pooled,
   if (s != 16 && s != 32 && s != 64 && s != 128) return fail(HSA_ERR_UNSUPPORTED, "hsa_score: sub-block %d not in {16,32,64,128}", s);
   if (B % s) return fail(HSA_ERR_BAD_SHAPE, "hsa_score: sub-block %d does not divide block %d", s, B);
   if (nh < 1 || nb < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_score: nh=%d nb=%d", nh, nb);
-  if (static_cast<int64_t>(nb) * (B / s) > 2048) return fail(HSA_ERR_UNSUPPORTED, "hsa_score: %lld sub-blocks > 2048", static_cast<long long>(nb) * (B / s));
+  if (static_cast<int64_t>(nb) * (B / s) > (1 << 20)) return fail(HSA_ERR_UNSUPPORTED, "hsa_score: %lld sub-blocks > 2^20", static_cast<long long>(nb) * (B / s));
   if (agg != HSA_AGG_MASS && agg != HSA_AGG_MAX) return fail(HSA_ERR_BAD_ARG, "hsa_score: unknown aggregation %d", agg);
   if (!(scale > 0.f) || !isfinite(scale)) return fail(HSA_ERR_BAD_ARG, "hsa_score: scale must be finite and positive");
   if (!aligned16(S)) return fail(HSA_ERR_BAD_ARG, "hsa_score: S must be 16-byte aligned");

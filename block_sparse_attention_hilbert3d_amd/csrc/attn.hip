@@ -121,38 +121,45 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   const uint16_t *vbase = GKV ? vp + h * D : vp + head_off;
   const uint32_t kv_row_bytes = static_cast<uint32_t>(kv_stride * 2);
   // Stage t covers keys (t % NS)*ST .. +ST of listed block t / NS. The
-  // listed blocks and their real lengths sit in lanes (lane i of the lo/hi
-  // pair holds entry mbase + i / mbase + 64 + i), so a stage's address and
-  // length cost two lane reads instead of dependent scalar loads. The window
-  // slides by 64 entries when the list is longer than 128.
+  // listed blocks and their real lengths sit in lanes, packed as
+  // (J << 8) | L (lane i of the lo/hi pair holds entry mbase + i / mbase +
+  // 64 + i), so a stage's address and length cost two lane reads instead of
+  // dependent scalar loads. The window slides by 64 entries when the list is
+  // longer than 128. (J < 2^24 and L <= BK <= 128 are checked on the host /
+  // clamped here.)
   const int nst = cnt * NS;
-  int mbase = 0, lo_J, lo_L, hi_J, hi_L;
-  auto fetch = [&](int b0, int &mJ, int &mL) {
+  int mbase = 0, lo_E, hi_E;
+  auto fetch = [&](int b0, int &mE) {
     const int i = b0 + lane;
-    mJ = i < cnt ? min(max(list[i], 0), nb - 1) : 0;
-    mL = i < cnt ? blk_len[mJ] : 0;
+    const int J = i < cnt ? min(max(list[i], 0), nb - 1) : 0;
+    const int L = i < cnt ? min(max(blk_len[J], 0), BK) : 0;
+    mE = static_cast<int>((static_cast<uint32_t>(J) << 8) | static_cast<uint32_t>(L));
   };
-  fetch(0, lo_J, lo_L);
-  fetch(64, hi_J, hi_L);
+  fetch(0, lo_E);
+  fetch(64, hi_E);
   wait_vmcnt<0>();
-  auto entry = [&](int b, int &J, int &L) {  // b in [mbase, mbase + 128), wave-uniform
+  auto entry_packed = [&](int b) {  // b in [mbase, mbase + 128), wave-uniform
     const int r = b - mbase;
     const int rl = r & 63;
-    const int jl = __builtin_amdgcn_readlane(lo_J, rl), jh = __builtin_amdgcn_readlane(hi_J, rl);
-    const int ll = __builtin_amdgcn_readlane(lo_L, rl), lh = __builtin_amdgcn_readlane(hi_L, rl);
-    J = r < 64 ? jl : jh;
-    L = r < 64 ? ll : lh;
+    const int el = __builtin_amdgcn_readlane(lo_E, rl), eh = __builtin_amdgcn_readlane(hi_E, rl);
+    return r < 64 ? el : eh;
   };
-  auto stage_ofs = [&](int t) {
-    int J, L;
-    entry(t / NS, J, L);
-    return static_cast<int64_t>(J) * BK * D + static_cast<int64_t>(t % NS) * ST * D;
+  auto entry = [&](int b, int &J, int &L) {
+    const uint32_t e = static_cast<uint32_t>(entry_packed(b));
+    J = static_cast<int>(e >> 8);
+    L = static_cast<int>(e & 255u);
   };
-  auto stage_valid = [&](int t) {
-    int J, L;
-    entry(t / NS, J, L);
-    return min(max(L - (t % NS) * ST, 0), ST);
+  auto ofs_of = [&](int e, int half) {  // element offset of half `half` of packed entry e
+    return static_cast<int64_t>(static_cast<uint32_t>(e) >> 8) * BK * D + static_cast<int64_t>(half) * ST * D;
   };
+  auto valid_of = [&](int e, int half) { return min(max(static_cast<int>(e & 255) - half * ST, 0), ST); };
+  auto stage_ofs = [&](int t) { return ofs_of(entry_packed(t / NS), t % NS); };
+  auto stage_valid = [&](int t) { return valid_of(entry_packed(t / NS), t % NS); };
+  // With two stages per block and contiguous tiles, iteration c only needs
+  // the entries of blocks c/2 and c/2 + 1 (ea, eb): read once per block, at
+  // even iterations, instead of once per use.
+  constexpr bool kPair = NS == 2 && !GKV;
+  int ea = 0, eb = 0;
   // Gathered K/V: the token rows this lane's loads of stage t read. With
   // D = 128 a 16-lane row of the wave fills one tile row per load, so each
   // lane fetches the map entry of load (lane mod NI) of its row and load i
@@ -185,9 +192,8 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   auto slide = [&](int c) {
     if ((c + 1) / NS - mbase >= 64) {
       mbase += 64;
-      lo_J = hi_J;
-      lo_L = hi_L;
-      fetch(mbase + 64, hi_J, hi_L);
+      lo_E = hi_E;
+      fetch(mbase + 64, hi_E);
       wait_vmcnt<0>();  // settle the window here, not at its first lane read
     }
   };
@@ -195,9 +201,8 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   auto slide_low = [&](int c) {
     if (c / NS - mbase >= 64) {
       mbase += 64;
-      lo_J = hi_J;
-      lo_L = hi_L;
-      fetch(mbase + 64, hi_J, hi_L);
+      lo_E = hi_E;
+      fetch(mbase + 64, hi_E);
       wait_vmcnt<0>();  // settle the window here, not at its first lane read
     }
   };
@@ -249,13 +254,31 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     for (int md = 0; md < DM; ++md)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[qt][md][i] = 0.f;
+  // Softmax reference m_ref (log2 units): the score buffers hold raw q.k
+  // and each weight is exp2(s * scale_log2 - m_ref). noref: no stage with a
+  // real key seen yet (then the first real max becomes the reference).
   float m_ref[QT], l_run[QT], e_run[QT];
+  bool noref = true;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    m_ref[qt] = -1e30f;
+    m_ref[qt] = 0.f;
     l_run[qt] = 0.f;
     e_run[qt] = 0.f;
   }
+  // a score as a log2 weight relative to the reference
+  auto rel = [&](float x, int qt) { return fmaf(x, scale_log2, -m_ref[qt]); };
+  // row max of a buffer relative to the reference (the two half-waves' runs
+  // of the same query combined by a lane swap)
+  auto rel_max = [&](const f32x16 (&sacc)[MT][QT], int qt) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][qt][i]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    return mx * scale_log2 - m_ref[qt];
+  };
 
   auto compute_s = [&](f32x16 (&sacc)[MT][QT], int buf) {
 #pragma unroll
@@ -275,8 +298,8 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
           sacc[mt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qt][ks], sacc[mt][qt], 0, 0, 0);
     }
   };
-  // Mask the ragged tail, then rescale O if this tile's max outgrows the
-  // reference by more than 2^8 (lazy rescale).
+  // Mask the ragged tail, then move the reference (rescaling O) if this
+  // tile's max outgrows it by more than 2^8 (lazy rescale).
   auto mask_and_rescale = [&](f32x16 (&sacc)[MT][QT], int kvalid) {
     if (kvalid < ST) {
       const int lim = kvalid - g * 4;
@@ -288,19 +311,15 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
           for (int i = 0; i < 16; ++i)
             if (mt * 32 + (i >> 2) * 8 + (i & 3) >= lim) sacc[mt][qt][i] = -INFINITY;
     }
+    bool found = false;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][qt][i]);
-      // other half-wave's max via a lane swap (no LDS round trip)
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
-      if (__any(mx > m_ref[qt] + kLazy)) {
-        const float m_new = fmaxf(m_ref[qt], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
+      const float mx = rel_max(sacc, qt);
+      if (__any(mx > kLazy) || noref) {
+        const float tm = m_ref[qt] + mx;
+        const bool fin = tm > -INFINITY;
+        const float m_new = noref ? (fin ? tm : m_ref[qt]) : fmaxf(m_ref[qt], tm);
+        const float alpha = noref ? 1.f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
         l_run[qt] *= alpha;
         e_run[qt] *= alpha;
 #pragma unroll
@@ -308,8 +327,10 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[qt][md][i] *= alpha;
         m_ref[qt] = m_new;
+        found |= fin;
       }
     }
+    if (noref && __any(found)) noref = false;
   };
   auto exp_pv = [&](const f32x16 (&sacc)[MT][QT], int buf) {
     float rs[QT], es[QT];
@@ -335,8 +356,7 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
         bf16x8 pf;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float p = __builtin_amdgcn_exp2f(
-              fmaf(sacc[ks2 >> 1][qt][(ks2 & 1) * 8 + j], scale_log2, -m_ref[qt]));
+          const float p = __builtin_amdgcn_exp2f(rel(sacc[ks2 >> 1][qt][(ks2 & 1) * 8 + j], qt));
           if constexpr (LSE) es[qt] += p;
           pf[j] = static_cast<__bf16>(p);
         }
@@ -389,8 +409,7 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
       for (int ks2 = 0; ks2 < PK; ++ks2) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float p = __builtin_amdgcn_exp2f(
-              fmaf(sacc[ks2 >> 1][qt][(ks2 & 1) * 8 + j], scale_log2, -m_ref[qt]));
+          const float p = __builtin_amdgcn_exp2f(rel(sacc[ks2 >> 1][qt][(ks2 & 1) * 8 + j], qt));
           if constexpr (LSE) es[qt] += p;
           pf[qt][ks2][j] = static_cast<__bf16>(p);
         }
@@ -427,21 +446,17 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   // After the exponentials of a stage: rescale if any row's weights outgrew
   // the cap, then fold the stage's sums into the running ones.
   auto settle = [&](const f32x16 (&sacc)[MT][QT], bf16x8 (&pf)[QT][PK], float (&rs)[QT], float (&es)[QT]) {
-    bool stale = false;
+    bool stale = noref;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) stale |= !(rs[qt] <= kSumCap);
     if (__any(stale)) {
+      bool found = false;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mt][qt][i]);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
-        const float m_new = fmaxf(m_ref[qt], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
+        const float tm = m_ref[qt] + rel_max(sacc, qt);
+        const bool fin = tm > -INFINITY;
+        const float m_new = noref ? (fin ? tm : m_ref[qt]) : fmaxf(m_ref[qt], tm);
+        const float alpha = noref ? 1.f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
         l_run[qt] *= alpha;
         e_run[qt] *= alpha;
 #pragma unroll
@@ -449,7 +464,9 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[qt][md][i] *= alpha;
         m_ref[qt] = m_new;
+        found |= fin;
       }
+      if (__any(found)) noref = false;
       exps(sacc, pf, rs, es);
     }
 #pragma unroll
@@ -498,6 +515,7 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
       if (nst > 1) issue_tile_offs<D, ST, NW>(kbase, ldsK + TILE * 2, w, ok);
       if (nst > 2) stage_rows(2, rn);
     } else {
+      if constexpr (kPair) eb = entry_packed(0);  // the first even iteration shifts it to ea
       issue_tile<D, ST, NW>(kbase + stage_ofs(0), ldsK, w, koff);
       issue_tile<D, ST, NW>(vbase + stage_ofs(0), ldsV, w, voff);
       if (nst > 1) issue_tile<D, ST, NW>(kbase + stage_ofs(1), ldsK + TILE * 2, w, koff);
@@ -522,10 +540,19 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     const bool has1 = c + 1 < nst, has2 = c + 2 < nst;
     __syncthreads();  // K(c) and V(c-1) buffers are free, K(c+1) and V(c) visible
     slide(c);
+    // (kPair) K(c+2) is half P of block c/2 + 1; V(c+1) and the length of
+    // stage c+1 are half 1 of block c/2 (P = 0) or half 0 of block c/2 + 1
+    if constexpr (kPair && P == 0) {
+      ea = eb;
+      eb = entry_packed((c >> 1) + 1);
+    }
     if constexpr (GKV) {
       if (c + 3 < nst) stage_rows(c + 3, rn);
       if (has2) issue_tile_offs<D, ST, NW>(kbase, ldsK + P * TILE * 2, w, ok);
       if (has1) issue_tile_offs<D, ST, NW>(vbase, ldsV + (P ^ 1) * TILE * 2, w, ov);
+    } else if constexpr (kPair) {
+      if (has2) issue_tile<D, ST, NW>(kbase + ofs_of(eb, P), ldsK + P * TILE * 2, w, koff);
+      if (has1) issue_tile<D, ST, NW>(vbase + ofs_of(P == 0 ? ea : eb, P ^ 1), ldsV + (P ^ 1) * TILE * 2, w, voff);
     } else {
       if (has2) issue_tile<D, ST, NW>(kbase + stage_ofs(c + 2), ldsK + P * TILE * 2, w, koff);
       if (has1) issue_tile<D, ST, NW>(vbase + stage_ofs(c + 1), ldsV + (P ^ 1) * TILE * 2, w, voff);
@@ -538,7 +565,10 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     // (measured ~2 % faster than the default schedule here)
     __builtin_amdgcn_iglp_opt(3);
     // an empty mask on the last stage leaves the running max untouched
-    mask_and_rescale(nxt, has1 ? stage_valid(c + 1) : 0);
+    int v1 = 0;
+    if constexpr (kPair) v1 = valid_of(P == 0 ? ea : eb, P ^ 1);
+    else if (has1) v1 = stage_valid(c + 1);
+    mask_and_rescale(nxt, has1 ? v1 : 0);
     wait_vmcnt<0>();
     if constexpr (GKV) {
       offsets(rk, voff, ov);  // V(c+2) reads K(c+2)'s rows
@@ -575,6 +605,7 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
       offsets(t0, voff, ov);  // V(0)
       if (nst > 2) stage_rows(2, rn);
     } else {
+      if constexpr (kPair) eb = entry_packed(0);  // the first even iteration shifts it to ea
       issue_tile<D, ST, NW>(kbase + stage_ofs(0), ldsK, w, koff);
       if (nst > 1) issue_tile<D, ST, NW>(kbase + stage_ofs(1), ldsK + TILE * 2, w, koff);
     }
@@ -586,17 +617,18 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     __syncthreads();
     compute_s(sA, 0);
     mask_tail(sA, stage_valid(0));
-    // the first stage's own row max as the reference (no recomputation)
+    // the first stage's own row max as the reference (no recomputation);
+    // a stage without a real key leaves noref set
+    bool found = false;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sA[mt][qt][i]);
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      m_ref[qt] = fmaxf(m_ref[qt], fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2);
+      const float tm = rel_max(sA, qt);  // m_ref = 0 so far
+      if (tm > -INFINITY) {
+        m_ref[qt] = tm;
+        found = true;
+      }
     }
+    if (__any(found)) noref = false;
   }
   // Iteration c: issue K(c+2) and V(c); S(c+1), the exponentials of stage c
   // and P.V of stage c-1 in one region; then settle stage c.
@@ -606,10 +638,20 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     const bool has1 = c + 1 < nst, has2 = c + 2 < nst;
     __syncthreads();  // K(c) and V(c-2) buffers are free, K(c+1) and V(c-1) visible
     slide_low(c);
+    // (kPair) K(c+2) is half P of block c/2 + 1, V(c) half P of block c/2;
+    // the length of stage c+1 is half 1 of block c/2 (P = 0) or half 0 of
+    // block c/2 + 1 (P = 1)
+    if constexpr (kPair && P == 0) {
+      ea = eb;
+      eb = entry_packed((c >> 1) + 1);
+    }
     if constexpr (GKV) {
       if (c + 3 < nst) stage_rows(c + 3, rn);
       if (has2) issue_tile_offs<D, ST, NW>(kbase, ldsK + P * TILE * 2, w, ok);
       issue_tile_offs<D, ST, NW>(vbase, ldsV + P * TILE * 2, w, ov);
+    } else if constexpr (kPair) {
+      if (has2) issue_tile<D, ST, NW>(kbase + ofs_of(eb, P), ldsK + P * TILE * 2, w, koff);
+      issue_tile<D, ST, NW>(vbase + ofs_of(ea, P), ldsV + P * TILE * 2, w, voff);
     } else {
       if (has2) issue_tile<D, ST, NW>(kbase + stage_ofs(c + 2), ldsK + P * TILE * 2, w, koff);
       issue_tile<D, ST, NW>(vbase + stage_ofs(c), ldsV + P * TILE * 2, w, voff);
@@ -625,7 +667,10 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     if constexpr (LSE) __builtin_amdgcn_iglp_opt(3);
     else __builtin_amdgcn_iglp_opt(1);
     settle(cur, pcur, rs, es);
-    mask_tail(nxt, has1 ? stage_valid(c + 1) : 0);
+    int v1 = 0;
+    if constexpr (kPair) v1 = valid_of(P == 0 ? ea : eb, P ^ 1);
+    else if (has1) v1 = stage_valid(c + 1);
+    mask_tail(nxt, has1 ? v1 : 0);
     wait_vmcnt<0>();
     if constexpr (GKV) {
       offsets(rk1, voff, ov);  // V(c+1) reads K(c+1)'s rows
@@ -893,6 +938,8 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                          const int32_t *order, int max_kv, int kv_shared, int nh, int nb, int B,
                          int D, int dtype, float scale, const int32_t *perm, int64_t q_stride,
                          int64_t kv_stride, int64_t o_stride, hipStream_t stream) {
+  // list entries are packed as (block << 8) | length in the bf16 kernel
+  if (nb > (1 << 24)) return fail(HSA_ERR_UNSUPPORTED, "hsa_attn: nb %d > 2^24 blocks", nb);
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid(nh * nb);
   if (dtype == HSA_BF16) {

@@ -12,6 +12,9 @@
 //     logits kept in registers; the MASS softmax (count-weighted, max
 //     subtracted) and the per-block sums are reduced with lane shuffles and
 //     a small LDS exchange between the four waves; MAX takes maxima instead.
+//     Beyond 2048 sub-blocks per head the logits do not fit in registers and
+//     a streaming variant passes over the key tiles twice (online maximum
+//     and sum, then the normalised aggregation).
 #include "common.h"
 
 namespace hsa {
@@ -295,6 +298,165 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
   }
 }
 
+
+// Any number of sub-blocks: the key tiles are streamed twice instead of
+// being held in registers. Pass 1 keeps, per query sub-block, an online
+// maximum and count-weighted exponential sum (combined across the lane
+// groups and the waves at the end); pass 2 recomputes each tile's logits
+// and aggregates the normalised mass (or, for MAX, the largest logit) per
+// key block. Each wave streams its own contiguous range of key tiles.
+template <int D, int NWV, bool MAXAGG>
+__global__ void __launch_bounds__(NWV * 64)
+contract_stream_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
+                       const int32_t *__restrict__ blk_len, int s, int U, int R, int nb, float scale,
+                       float *__restrict__ S) {
+  constexpr int DQ = D / 4;
+  constexpr int CPR = D / 4;
+  constexpr int NI = 16 * D * 4 / 1024;
+  __shared__ float redm[NWV][16], redd[NWV][16];
+  __shared__ __attribute__((aligned(1024))) float kt[NWV][16 * D];
+  const float zscale = MAXAGG ? scale : scale * 1.4426950408889634f;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ul = lane & 15;
+  const int g = lane >> 4;
+  const int h = blockIdx.y;
+  const int u0 = blockIdx.x * 16;
+  const int u = u0 + ul;
+  const int tiles = (U + 15) / 16;
+  const int VT = (tiles + NWV - 1) / NWV;
+  const int t0 = w * VT, t1 = min(tiles, t0 + VT);  // this wave's tiles
+  const float *qb = qbar + static_cast<int64_t>(h) * U * D;
+  const float *kb = kbar + static_cast<int64_t>(h) * U * D;
+  const uint32_t slot = __builtin_amdgcn_readfirstlane(lds_addr(&kt[w][0]));
+  const float *kslot = &kt[w][0];
+  auto issue = [&](int t) {
+    const int v0 = t * 16;
+    const float *base = kb + static_cast<int64_t>(v0) * D;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int P = i * 64 + lane;
+      const int row = P / CPR, c = (P % CPR) ^ (row & 15);
+      const int rowc = min(v0 + row, U - 1) - v0;
+      load_lds16(base, static_cast<uint32_t>(rowc * D * 4 + c * 16), slot + i * 1024);
+    }
+  };
+  float qreg[DQ];
+  if (u < U) {
+#pragma unroll
+    for (int m = 0; m < DQ / 4; ++m) {
+      const float4 t = *reinterpret_cast<const float4 *>(qb + static_cast<int64_t>(u) * D + 16 * m + 4 * g);
+      qreg[4 * m] = t.x; qreg[4 * m + 1] = t.y; qreg[4 * m + 2] = t.z; qreg[4 * m + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < DQ; ++j) qreg[j] = 0.f;
+  }
+  const int cu = (u < U) ? sub_count(blk_len, u, R, s) : 0;
+  // logits of tile t (already in the slot): z[r] for key sub-block
+  // 16t + 4g + r, -inf for an empty one; the next tile's loads are issued
+  // once this one's operands are read
+  auto tile_logits = [&](int t, int tnext, float (&z)[4], float (&cv)[4]) {
+    wait_vmcnt<0>();
+    float kreg[DQ];
+#pragma unroll
+    for (int m = 0; m < DQ / 4; ++m) {
+      const float4 k4 = *reinterpret_cast<const float4 *>(kslot + ul * D + (((g + 4 * m) ^ ul) * 4));
+      kreg[4 * m] = k4.x; kreg[4 * m + 1] = k4.y; kreg[4 * m + 2] = k4.z; kreg[4 * m + 3] = k4.w;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the slot may be refilled
+    if (tnext >= 0) issue(tnext);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < DQ; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kreg[j], qreg[j], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int v = t * 16 + 4 * g + r;
+      cv[r] = (v < U) ? static_cast<float>(sub_count(blk_len, v, R, s)) : 0.f;
+      z[r] = (cv[r] > 0.f && cu > 0) ? acc[r] * zscale : -INFINITY;
+    }
+  };
+  const int I = u / R;
+  const bool leader = (ul % R) == 0 && u < U;
+  float M = -INFINITY, wu = 0.f, inv_c = 0.f;
+  if constexpr (!MAXAGG) {
+    // pass 1: online max and count-weighted exponential sum
+    float m = -INFINITY, den = 0.f;
+    if (t0 < t1) issue(t0);
+    for (int t = t0; t < t1; ++t) {
+      float z[4], cv[4];
+      tile_logits(t, t + 1 < t1 ? t + 1 : -1, z, cv);
+      const float tm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      if (tm > m) {
+        den *= __builtin_amdgcn_exp2f(m - tm);
+        m = tm;
+      }
+      if (m > -INFINITY) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) den += cv[r] * __builtin_amdgcn_exp2f(z[r] - m);
+      }
+    }
+    // combine the four lane groups of the query, then the waves
+    auto combine = [](float &ma, float &da, float mb, float db) {
+      const float mm = fmaxf(ma, mb);
+      da = (mm > -INFINITY) ? da * __builtin_amdgcn_exp2f(ma - mm) + db * __builtin_amdgcn_exp2f(mb - mm) : 0.f;
+      ma = mm;
+    };
+    combine(m, den, __shfl_xor(m, 16, 64), __shfl_xor(den, 16, 64));
+    combine(m, den, __shfl_xor(m, 32, 64), __shfl_xor(den, 32, 64));
+    if (g == 0) {
+      redm[w][ul] = m;
+      redd[w][ul] = den;
+    }
+    __syncthreads();
+    M = redm[0][ul];
+    float DEN = redd[0][ul];
+#pragma unroll
+    for (int i = 1; i < NWV; ++i) combine(M, DEN, redm[i][ul], redd[i][ul]);
+    wu = (DEN > 0.f) ? static_cast<float>(cu) / DEN : 0.f;
+    const float cblk = reduce_block_lanes(static_cast<float>(cu), R, false);
+    inv_c = cblk > 0.f ? 1.f / cblk : 0.f;
+  }
+  // pass 2 (the only pass for MAX): per key block of each tile
+  if (t0 < t1) issue(t0);
+  for (int t = t0; t < t1; ++t) {
+    float z[4], cv[4];
+    tile_logits(t, t + 1 < t1 ? t + 1 : -1, z, cv);
+    float o[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (MAXAGG) o[r] = z[r];
+      else o[r] = (z[r] > -INFINITY) ? cv[r] * __builtin_amdgcn_exp2f(z[r] - M) * wu : 0.f;
+    }
+    const int v0 = t * 16;
+    if (R == 1) {
+      const int J0 = v0 + 4 * g;
+      if (leader) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (J0 + r < nb) S[(static_cast<int64_t>(h) * nb + I) * nb + J0 + r] = MAXAGG ? o[r] : o[r] * inv_c;
+      }
+    } else if (R == 2) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        float val = MAXAGG ? fmaxf(o[2 * p], o[2 * p + 1]) : o[2 * p] + o[2 * p + 1];
+        val = reduce_block_lanes(val, R, MAXAGG);
+        const int J = (v0 + 4 * g + 2 * p) / 2;
+        if (leader && J < nb) S[(static_cast<int64_t>(h) * nb + I) * nb + J] = MAXAGG ? val : val * inv_c;
+      }
+    } else {
+      // R = 4 or 8 (s >= 16 and B <= 128): a block's key sub-blocks are one
+      // lane group (R = 4) or two neighbouring ones (R = 8)
+      float val = MAXAGG ? fmaxf(fmaxf(o[0], o[1]), fmaxf(o[2], o[3])) : (o[0] + o[1]) + (o[2] + o[3]);
+      if (R == 8) val = MAXAGG ? fmaxf(val, __shfl_xor(val, 16, 64)) : val + __shfl_xor(val, 16, 64);
+      val = reduce_block_lanes(val, R, MAXAGG);
+      const int J = (v0 + 4 * g) / R;
+      const bool writer = leader && (R == 4 || (g & 1) == 0);
+      if (writer && J < nb) S[(static_cast<int64_t>(h) * nb + I) * nb + J] = MAXAGG ? val : val * inv_c;
+    }
+  }
+}
+
 }  // namespace hsa
 
 namespace hsa_host {
@@ -350,6 +512,16 @@ hsa_status_t launch_score(const void *qp, const void *kp, const float *pooled,
   const float *qb = means;
   const float *kb = means + static_cast<size_t>(nh) * U * D;
   const dim3 cgrid((U + 15) / 16, nh);
+  if (U > hsa::kMaxSub) {  // logits do not fit in registers: stream the key tiles twice
+    if (D == 128) {
+      if (agg == HSA_AGG_MAX) hipLaunchKernelGGL((hsa::contract_stream_kernel<128, 4, true>), cgrid, dim3(256), 0, stream, qb, kb, blk_len, s, U, R, nb, scale, S);
+      else hipLaunchKernelGGL((hsa::contract_stream_kernel<128, 4, false>), cgrid, dim3(256), 0, stream, qb, kb, blk_len, s, U, R, nb, scale, S);
+    } else {
+      if (agg == HSA_AGG_MAX) hipLaunchKernelGGL((hsa::contract_stream_kernel<64, 4, true>), cgrid, dim3(256), 0, stream, qb, kb, blk_len, s, U, R, nb, scale, S);
+      else hipLaunchKernelGGL((hsa::contract_stream_kernel<64, 4, false>), cgrid, dim3(256), 0, stream, qb, kb, blk_len, s, U, R, nb, scale, S);
+    }
+    return check_launch("hsa_score");
+  }
   if (D == 128) {
     if (agg == HSA_AGG_MAX) launch_contract<128, true>(U, cgrid, qb, kb, blk_len, s, R, nb, scale, S, stream);
     else launch_contract<128, false>(U, cgrid, qb, kb, blk_len, s, R, nb, scale, S, stream);

@@ -35,8 +35,10 @@
  *      blk_len       int32 [nb]: real tokens in block I (they are the first
  *                    blk_len[I] slots of the block; pads follow);
  *      scores        float [nh][nb][nb];
- *      lists         kv_idx int32 [G][nb][max_kv] ascending, -1 after
- *                    kv_cnt int32 [G][nb] entries; G = nh, or 1 when shared.
+ *      lists         kv_idx int32 [G][nb][max_kv]: the first kv_cnt entries of
+ *                    each row, ascending, are the list (hsa_select writes
+ *                    only those; the rest of a row is not written and never
+ *                    read); kv_cnt int32 [G][nb]; G = nh, or 1 when shared.
  *                    Kernels that read caller lists clamp each length to
  *                    [0, max_kv] and each entry to [0, nb), so a malformed
  *                    list gives wrong rows, never an access outside the
@@ -188,7 +190,8 @@ size_t hsa_score_ws_size(int32_t nh, int32_t n_pad, int32_t s, int32_t D);
  * pooled (optional): the means hsa_perm wrote with pool_s = s; when given,
  * qp, kp and ws are not used (may be NULL) and no pooling pass runs.
  * Otherwise ws must hold hsa_score_ws_size bytes.
- * Limits: nb*B/s <= 2048 sub-blocks. Computed in float32 (matrix cores).
+ * Limits: nb*B/s <= 2^20 sub-blocks per head. Computed in float32 (matrix
+ * cores); beyond 2048 sub-blocks the key sub-blocks are streamed twice.
  */
 hsa_status_t hsa_score(const void *qp, const void *kp, const float *pooled,
                        const int32_t *blk_len, int32_t nh, int32_t nb, int32_t B, int32_t s,
@@ -216,7 +219,7 @@ int32_t hsa_select_list_width(int32_t nh, int32_t nb, const hsa_select_params_t 
  *   reaches tau (sums exact in 2^-62 fixed point; at least one block); then
  *   per head the best-ranked remaining pairs are added until the head holds
  *   floor(budget_ratio*nb*nb + 0.5) pairs. Scores must be finite and >= 0
- *   (MASS). Lists [nh][nb][max_kv]; max_kv must be nb.
+ *   (MASS). Lists [nh][nb][max_kv]; max_kv must be nb; nb <= 1024.
  * LVSA (LVSA section 2, A(t) = G_s u W(t)): frame t attends to the anchor
  *   frames f = step (mod T_per) and to the C - |G_s| nearest non-anchor
  *   frames (ties to the earlier frame; at least one); every tile of frame t
@@ -278,7 +281,8 @@ hsa_status_t hsa_select_noalloc(const float *S, int32_t nh, int32_t nb, const hs
  *   twice and leaves others unwritten.
  * BF16 runs on bf16 matrix cores with float accumulation and softmax; the
  * probabilities are rounded to bf16 for the value product and the output is
- * rounded to bf16 (nearest even). F32 computes in float throughout.
+ * rounded to bf16 (nearest even); the output bits do not depend on whether
+ * lse is requested. F32 computes in float throughout.
  * Two bf16 pipelines: max_kv >= 16 takes the deferred-value one (a stage's
  * weights are formed against the running max and checked afterwards),
  * shorter list capacities the eager one (row max first); both compute the

@@ -39,8 +39,17 @@ def oracle_select(w, S, nb, step, max_kv=None):
 
 
 def lists_equal(a_idx, a_cnt, b_idx, b_cnt):
-    return np.array_equal(np.asarray(a_cnt), np.asarray(b_cnt)) and np.array_equal(
-        np.asarray(a_idx), np.asarray(b_idx))
+    """Same counts and the same first kv_cnt entries in every row (entries
+    past a row's count are not part of the lists: the library leaves them
+    unwritten, the oracle fills -1)."""
+    a_idx, a_cnt, b_idx, b_cnt = (np.asarray(x) for x in (a_idx, a_cnt, b_idx, b_cnt))
+    if not np.array_equal(a_cnt, b_cnt):
+        return False
+    w = min(a_idx.shape[-1], b_idx.shape[-1])
+    if a_cnt.size and int(a_cnt.max()) > w:
+        return False
+    valid = np.arange(w)[None, None, :] < a_cnt[..., None]
+    return bool(np.all((a_idx[..., :w] == b_idx[..., :w]) | ~valid))
 
 
 def attn_rows(w, step, perm):

@@ -118,7 +118,7 @@ def test_score_validation(B):
     assert call(args(scale=-1.0)) == 6
     assert call(args(wsn=ws_n - 1)) == 5
     assert call(args(ws=NULL)) == 5
-    assert call(args(nb=300, Bs=128, s=16)) == 4        # 2400 sub-blocks > 2048
+    assert call(args(nb=140000, Bs=128, s=16)) == 4     # more than 2^20 sub-blocks per head
     assert L.hsa_score(NULL, FAKE, NULL, FAKE, 2, 4, 64, 16, 64, 1, 0, 0.125, FAKE, FAKE, ws_n, NULL) == 1
     # with pooled means the workspace is not needed, but S must still be valid
     assert L.hsa_score(NULL, NULL, FAKE, FAKE, 2, 4, 64, 16, 64, 1, 0, 0.125, NULL, NULL, 0, NULL) == 1

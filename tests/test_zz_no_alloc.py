@@ -43,7 +43,10 @@ def test_noalloc_select_equals_workspace_select(mode):
                torch.full((nh, nb), 7, dtype=torch.int32, device="cuda"))
         hsa.hsa_select_noalloc(S, nh, nb, p, cap, outs=got)
         torch.cuda.synchronize()
-        assert torch.equal(got[0], want[0]) and torch.equal(got[1], want[1])
+        assert torch.equal(got[1], want[1])
+        # each row's first kv_cnt entries (the rest of a row is not written)
+        valid = torch.arange(cap, device="cuda")[None, None, :] < want[1][..., None]
+        assert torch.equal(torch.where(valid, got[0], -1), torch.where(valid, want[0], -1))
 
 
 def test_noalloc_select_rejects_oversize():
