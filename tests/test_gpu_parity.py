@@ -269,11 +269,56 @@ def test_thresh_tied_heads(hsa):
     S /= S.sum(axis=2, keepdims=True)
     S = S.astype(np.float32)
     St = torch.from_numpy(S).to(dev())
-    for tau, ratio in ((0.25, 0.5), (0.25, 0.2), (0.1, 0.9), (0.6, 0.3), (0.05, 0.05)):
+    for tau, ratio in ((0.25, 0.5), (0.25, 0.2), (0.1, 0.9), (0.6, 0.3), (0.05, 0.05), (0.0, 0.3)):
         p = hsa.make_params("thresh_global", tau=tau, budget_ratio=ratio)
         kv_idx, kv_cnt = hsa.hsa_select(St, nh, nb, p, nb)
         ref = oracle.select_thresh_global(S.astype(np.float64), tau, ratio)
         assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), *ref), (tau, ratio)
+
+
+def _thresh_rows(kind, nb, rng):
+    """Score rows (float32, row sums below 1) whose prefix boundary lies where
+    `kind` says: in a 12-bit key bin of n columns ("bin<n>": 5 scores of 0.08,
+    n scores in [1.024e-3, 1.075e-3) with every fourth one repeated, the rest
+    in [1e-7, 1e-6)), or about 40 binades below the row's largest score
+    ("far": one 0.5, the rest near 1e-13). Returns (S [nb, nb], tau)."""
+    S = np.empty((nb, nb))
+    if kind == "far":
+        for I in range(nb):
+            row = 1e-13 * (1.0 + rng.random(nb))
+            row[rng.integers(nb)] = 0.5
+            S[I] = row
+        return S.astype(np.float32), 0.5 + 0.4 * (nb - 1) * 1.5e-13
+    n = int(kind[3:])
+    for I in range(nb):
+        row = rng.uniform(1e-7, 1e-6, nb)
+        cols = rng.choice(nb, n + 5, replace=False)
+        row[cols[:5]] = 0.08
+        mid = 1e-3 * (1.024 + 0.05 * rng.random(n))
+        mid[1::4] = mid[0::4][: len(mid[1::4])]
+        row[cols[5:]] = mid
+        S[I] = row
+    return S.astype(np.float32), 0.4 + 0.5 * n * 1.05e-3
+
+
+@pytest.mark.parametrize("kind,nb", [("bin12", 60), ("bin24", 200), ("bin48", 200), ("bin100", 200),
+                                     ("far", 200), ("bin40", 1000)])
+def test_thresh_row_search_paths(hsa, kind, nb):
+    """Threshold selection on rows built to take each way of finding a row
+    prefix's boundary: a boundary key bin of up to 16, 32 or 64 columns (the
+    register sorts of one, two and four 16-lane rows, with equal scores in the
+    bin), more than 64 (the full-key search), a boundary about 40 binades
+    below the row's largest score (below the histogram window); equal to the
+    oracle with no fill, with a fill and with nearly everything filled."""
+    _say(f"threshold selection, row search path {kind}, nb {nb}")
+    rng = np.random.default_rng(40 + nb + len(kind))
+    S, tau = _thresh_rows(kind, nb, rng)
+    St = torch.from_numpy(S[None]).to(dev())
+    for ratio in (0.0, 0.3, 0.9):
+        p = hsa.make_params("thresh_global", tau=tau, budget_ratio=ratio)
+        kv_idx, kv_cnt = hsa.hsa_select(St, 1, nb, p, nb)
+        ref = oracle.select_thresh_global(S[None].astype(np.float64), tau, ratio)
+        assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), *ref), (kind, nb, ratio)
 
 
 # ---------------------------------------------------------------- attention / layer
