@@ -41,9 +41,11 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 
 __device__ __forceinline__ int popc64(uint64_t x) { return __popcll(x); }
 
-// Order-preserving map of a float to uint32 (larger float -> larger key).
+// Order-preserving map of a float to uint32 (larger float -> larger key);
+// -0 takes the key of +0, since the two compare equal (and so tie).
 __device__ __forceinline__ uint32_t float_order_key(float f) {
-  const uint32_t u = __float_as_uint(f);
+  uint32_t u = __float_as_uint(f);
+  u = (u == 0x80000000u) ? 0u : u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

@@ -44,8 +44,6 @@ def study(widx: int = 3, orders=("row", "hilbert2d", "hilbert", "tile2d", "cube3
             w = replace(base, order=order, s=s, select="topk", k=0,
                         keep_ratio=base.keep_ratio if base.keep_ratio else 0.15)
             L = layer_for_workload(w, device=dev, want_lse=False)
-            if L.n_pad // s > 2048:
-                continue
             L.reorder(q, k, v)
             L.make_mask(step)
             perm = L.perm.cpu().numpy()
@@ -69,8 +67,11 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--rows", type=int, default=4096)
     ap.add_argument("--step", type=int, default=0)
+    ap.add_argument("--orders", default="row,hilbert2d,hilbert,tile2d,cube3d")
+    ap.add_argument("--subs", default="16,32,64,128")
     args = ap.parse_args()
-    res = study(args.workload, rows_per_head=args.rows, step=args.step)
+    res = study(args.workload, orders=tuple(args.orders.split(",")),
+                subs=tuple(int(x) for x in args.subs.split(",")), rows_per_head=args.rows, step=args.step)
     print("| order | s | blocks | k (kept) | mean recall | p10 recall |")
     print("|---|---:|---:|---:|---:|---:|")
     for r in res:

@@ -301,6 +301,30 @@ def _thresh_rows(kind, nb, rng):
     return S.astype(np.float32), 0.4 + 0.5 * n * 1.05e-3
 
 
+def test_select_signed_zero_ties(hsa):
+    """Scores of +0.0 and -0.0 compare equal, so they tie and rank by the
+    lower index, for top-k (boundary among the zeros) and for threshold
+    selection (the global fill reaching the zeros); equal to the oracle."""
+    _say("selection with signed-zero ties")
+    nh, nb = 2, 80
+    rng = np.random.default_rng(77)
+    S = rng.random((nh, nb, nb))
+    S[rng.random((nh, nb, nb)) < 0.4] = 0.0
+    S /= S.sum(axis=2, keepdims=True)
+    S = S.astype(np.float32)
+    S[(S == 0) & (rng.random((nh, nb, nb)) < 0.5)] = -0.0
+    assert np.signbit(S[S == 0]).any() and (~np.signbit(S[S == 0])).any()
+    St = torch.from_numpy(S).to(dev())
+    p = hsa.make_params("topk", k=60)
+    kv_idx, kv_cnt = hsa.hsa_select(St, nh, nb, p, 60)
+    ref = oracle.select_topk(S.astype(np.float64), 60)
+    assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), *ref)
+    p = hsa.make_params("thresh_global", tau=0.5, budget_ratio=0.9)
+    kv_idx, kv_cnt = hsa.hsa_select(St, nh, nb, p, nb)
+    ref = oracle.select_thresh_global(S.astype(np.float64), 0.5, 0.9)
+    assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), *ref)
+
+
 @pytest.mark.parametrize("kind,nb", [("bin12", 60), ("bin24", 200), ("bin48", 200), ("bin100", 200),
                                      ("far", 200), ("bin40", 1000)])
 def test_thresh_row_search_paths(hsa, kind, nb):
