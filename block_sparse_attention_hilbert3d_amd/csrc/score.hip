@@ -76,10 +76,31 @@ pool_kernel(const T *__restrict__ qp, const T *__restrict__ kp, const int32_t *_
 }
 
 // Sum (or max) across the R lanes of a query block: lanes u0..u0+15 hold
-// consecutive sub-blocks; R divides 16.
+// consecutive sub-blocks; R divides 16. The partners (lane ^ 1, 2, 4, 8) sit
+// in the same 16-lane row, so DPP moves reach them: quad permutations for 1
+// and 2, row rotations by 4 or 12 (chosen by bit 2) for 4, by 8 for 8.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float reduce_block_lanes(float v, int R, bool take_max) {
-  for (int off = 1; off < R; off <<= 1) {
-    const float o = __shfl_xor(v, off, 64);
+  const bool b2 = (lane_id() & 4) != 0;
+  float o;
+  if (R > 1) {
+    o = dpp_f<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
+    v = take_max ? fmaxf(v, o) : v + o;
+  }
+  if (R > 2) {
+    o = dpp_f<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
+    v = take_max ? fmaxf(v, o) : v + o;
+  }
+  if (R > 4) {
+    const float a = dpp_f<0x124>(v), c = dpp_f<0x12C>(v);  // row rotations by 4 and 12: lane ^ 4
+    o = b2 ? a : c;
+    v = take_max ? fmaxf(v, o) : v + o;
+  }
+  if (R > 8) {
+    o = dpp_f<0x128>(v);  // row rotation by 8: lane ^ 8
     v = take_max ? fmaxf(v, o) : v + o;
   }
   return v;
@@ -105,11 +126,12 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
   constexpr int CPR = D / 4;         // 16-byte chunks per fp32 row
   constexpr int NI = 16 * D * 4 / 1024;  // direct loads per 16-row tile
   __shared__ float red[NWV][16];
-  __shared__ float cnt_s[kMaxSub];   // real tokens of every key sub-block
+  __shared__ float cnt_s[kMaxSub + 16];  // real tokens of every key sub-block (0 past U, to whole tiles)
   // One key tile per wave, chunk c of row r at slot c ^ (r mod 16): the 16
   // rows read by one MFMA operand load hit distinct banks.
   __shared__ __attribute__((aligned(1024))) float kt[NWV][16 * D];
-  for (int v = threadIdx.x; v < U; v += NWV * 64) cnt_s[v] = static_cast<float>(sub_count(blk_len, v, R, s));
+  for (int v = threadIdx.x; v < (U + 15) / 16 * 16; v += NWV * 64)
+    cnt_s[v] = v < U ? static_cast<float>(sub_count(blk_len, v, R, s)) : 0.f;
   // MASS works in the log2 domain: logits carry scale * log2(e).
   const float zscale = MAXAGG ? scale : scale * 1.4426950408889634f;
   const int lane = threadIdx.x & 63;
@@ -128,16 +150,29 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
   const float *kslot = &kt[w][0];
 
   // Direct loads of tile t into this wave's slot; rows past U repeat row
-  // U - 1 (their logits are discarded).
+  // U - 1 (their logits are discarded). A lane's byte offsets inside a whole
+  // tile are the same for every tile: formed once.
+  uint32_t loff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int P = i * 64 + lane;
+    const int row = P / CPR, c = (P % CPR) ^ (row & 15);
+    loff[i] = static_cast<uint32_t>(row * D * 4 + c * 16);
+  }
   auto issue = [&](int t) {
     const int v0 = (w * VT + t) * 16;
     const float *base = kb + static_cast<int64_t>(v0) * D;
+    if (v0 + 16 <= U) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int P = i * 64 + lane;
-      const int row = P / CPR, c = (P % CPR) ^ (row & 15);
-      const int rowc = min(v0 + row, U - 1) - v0;
-      load_lds16(base, static_cast<uint32_t>(rowc * D * 4 + c * 16), slot + i * 1024);
+      for (int i = 0; i < NI; ++i) load_lds16(base, loff[i], slot + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int P = i * 64 + lane;
+        const int row = P / CPR, c = (P % CPR) ^ (row & 15);
+        const int rowc = min(v0 + row, U - 1) - v0;
+        load_lds16(base, static_cast<uint32_t>(rowc * D * 4 + c * 16), slot + i * 1024);
+      }
     }
   };
   if (nt > 0) issue(0);
@@ -177,12 +212,11 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
 #pragma unroll
       for (int j = 0; j < DQ; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kreg[j], qreg[j], acc, 0, 0, 0);
       const int v0 = (w * VT + t) * 16;
+      const float4 c4 = *reinterpret_cast<const float4 *>(&cnt_s[v0 + 4 * g]);  // 0 past U
+      const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int v = v0 + 4 * g + r;
-        const float c = (v < U) ? cnt_s[v] : 0.f;
-        if (c > 0.f && cu > 0) z[t][r] = acc[r] * zscale;
-      }
+      for (int r = 0; r < 4; ++r)
+        if (cv[r] > 0.f && cu > 0) z[t][r] = acc[r] * zscale;
     }
   }
 
@@ -205,11 +239,14 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
     float den = 0.f;
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) {
-      const int v0 = (w * VT + t) * 16 + 4 * g;
+      float cv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (t < nt) {
+        const float4 c4 = *reinterpret_cast<const float4 *>(&cnt_s[(w * VT + t) * 16 + 4 * g]);
+        cv[0] = c4.x; cv[1] = c4.y; cv[2] = c4.z; cv[3] = c4.w;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float e = 0.f;
-        if (t < VT && z[t][r] != -INFINITY) e = cnt_s[v0 + r] * __builtin_amdgcn_exp2f(z[t][r] - m);
+        const float e = z[t][r] != -INFINITY ? cv[r] * __builtin_amdgcn_exp2f(z[t][r] - m) : 0.f;
         z[t][r] = e;
         den += e;
       }
