@@ -301,6 +301,31 @@ def _thresh_rows(kind, nb, rng):
     return S.astype(np.float32), 0.4 + 0.5 * n * 1.05e-3
 
 
+@pytest.mark.parametrize("nb", [1, 2, 63, 64, 65, 128, 129, 1024])
+def test_select_sizes(hsa, nb):
+    """Threshold and top-k selection at the edges of the per-lane register
+    layout (one block; a full and a just-spilled 64-lane row; the largest
+    grid, 1024 blocks, every register full), random rows normalised to sum
+    1; equal to the oracle."""
+    _say(f"selection sizes nb = {nb}")
+    nh = 2
+    rng = np.random.default_rng(500 + nb)
+    S = rng.random((nh, nb, nb)) ** 3
+    S /= S.sum(axis=2, keepdims=True)
+    S = S.astype(np.float32)
+    St = torch.from_numpy(S).to(dev())
+    for tau, ratio in ((0.5, 0.3), (0.9, 0.05), (0.2, 0.8)):
+        p = hsa.make_params("thresh_global", tau=tau, budget_ratio=ratio)
+        kv_idx, kv_cnt = hsa.hsa_select(St, nh, nb, p, nb)
+        ref = oracle.select_thresh_global(S.astype(np.float64), tau, ratio)
+        assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), *ref), (nb, tau, ratio)
+    k = max(1, nb // 7)
+    p = hsa.make_params("topk", k=k)
+    kv_idx, kv_cnt = hsa.hsa_select(St, nh, nb, p, k)
+    ref = oracle.select_topk(S.astype(np.float64), k)
+    assert lists_equal(kv_idx.cpu().numpy(), kv_cnt.cpu().numpy(), *ref), nb
+
+
 def test_select_signed_zero_ties(hsa):
     """Scores of +0.0 and -0.0 compare equal, so they tie and rank by the
     lower index, for top-k (boundary among the zeros) and for threshold
