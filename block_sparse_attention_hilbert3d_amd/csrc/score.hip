@@ -9,9 +9,11 @@
 //     caller passes the means hsa_perm computed while reordering.
 //  2. contract + aggregate: per head, a strip of 16 query sub-blocks against
 //     all key sub-blocks on float32 matrix cores (v_mfma_f32_16x16x4_f32),
-//     logits kept in registers; the MASS softmax (count-weighted, max
-//     subtracted) and the per-block sums are reduced with lane shuffles and
-//     a small LDS exchange between the four waves; MAX takes maxima instead.
+//     logits kept in registers; the MASS softmax (count-weighted: the log2
+//     of each key sub-block's count is added to its logit, so a weight is
+//     one exp2; max subtracted) and the per-block sums are reduced with lane
+//     shuffles and a small LDS exchange between the four waves; MAX takes
+//     maxima instead.
 //     Beyond 2048 sub-blocks per head the logits do not fit in registers and
 //     a streaming variant passes over the key tiles twice (online maximum
 //     and sum, then the normalised aggregation).
@@ -114,11 +116,64 @@ __device__ __forceinline__ int sub_count(const int32_t *blk_len, int v, int R, i
 
 constexpr int kMaxSub = 2048;  // sub-blocks per head (validated at the boundary)
 
+// Block scores of one strip from per-lane values z[t][r] (query sub-block
+// u, key sub-block 16 (w VT + t) + 4g + r): MASS sums the R x R sub-block
+// pairs of each block pair, each query sub-block's weights scaled by wu,
+// the total by inv_c; MAX takes the largest. RR = R (sub-blocks per block,
+// a power of two <= 8), so block indices are shifts.
+template <int RR, int MAXT, bool MAXAGG>
+__device__ __forceinline__ void store_block_scores(const float (&z)[MAXT][4], float wu, float inv_c, int w, int VT,
+                                                   int U, int nb, int h, int u, int g, float *__restrict__ S) {
+  const int ul = u & 15;
+  const int I = u / RR;
+  const bool leader = (ul % RR) == 0 && u < U;
+  float *Srow = S + (static_cast<int64_t>(h) * nb + I) * nb;
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    if (t < VT) {
+      const int v0 = (w * VT + t) * 16;  // a multiple of 16: block of v0 + 4g + r is v0 / RR + (4g + r) / RR
+      if (v0 < U) {
+        if constexpr (RR == 1) {
+          const int J0 = v0 + 4 * g;
+          if (leader) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float o = MAXAGG ? z[t][r] : z[t][r] * wu * inv_c;
+              if (J0 + r < nb) Srow[J0 + r] = o;
+            }
+          }
+        } else if constexpr (RR == 2) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            float val = MAXAGG ? fmaxf(z[t][2 * p], z[t][2 * p + 1]) : (z[t][2 * p] + z[t][2 * p + 1]) * wu;
+            val = reduce_block_lanes(val, RR, MAXAGG);
+            if constexpr (!MAXAGG) val *= inv_c;
+            const int J = v0 / 2 + 2 * g + p;
+            if (leader && J < nb) Srow[J] = val;
+          }
+        } else {
+          float val = MAXAGG ? fmaxf(fmaxf(z[t][0], z[t][1]), fmaxf(z[t][2], z[t][3]))
+                             : ((z[t][0] + z[t][1]) + (z[t][2] + z[t][3])) * wu;
+          if constexpr (RR == 8) {
+            const float o = __shfl_xor(val, 16, 64);
+            val = MAXAGG ? fmaxf(val, o) : val + o;
+          }
+          val = reduce_block_lanes(val, RR, MAXAGG);
+          if constexpr (!MAXAGG) val *= inv_c;
+          const int J = v0 / RR + (4 * g) / RR;
+          const bool writer = leader && (RR == 4 || (g & 1) == 0);
+          if (writer && J < nb) Srow[J] = val;
+        }
+      }
+    }
+  }
+}
+
 // Each lane group g of an MFMA chain owns columns 16m + 4g .. +3 (m = 0 ..
 // D/16 - 1) of its row, so a row's four lane groups read 64 contiguous bytes
 // per load and the k-slots of Q and K line up.
 template <int D, int NWV, int MAXT, bool MAXAGG>
-__global__ void __launch_bounds__(NWV * 64)
+__global__ void __launch_bounds__(NWV * 64, 3)
 contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
                 const int32_t *__restrict__ blk_len, int s, int U, int R, int nb, float scale,
                 float *__restrict__ S) {
@@ -126,12 +181,15 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
   constexpr int CPR = D / 4;         // 16-byte chunks per fp32 row
   constexpr int NI = 16 * D * 4 / 1024;  // direct loads per 16-row tile
   __shared__ float red[NWV][16];
-  __shared__ float cnt_s[kMaxSub + 16];  // real tokens of every key sub-block (0 past U, to whole tiles)
+  // Per key sub-block: MASS the log2 of its real tokens (-inf when empty),
+  // so a count-weighted exponential is one exp2 of logit + log2 count; MAX
+  // the count itself. Past U: -inf (MASS) or 0, over every tile a wave may
+  // index (NWV MAXT tiles).
+  __shared__ float kv_s[kMaxSub + 16];
+  __shared__ int cq[16];  // real tokens of the strip's query sub-blocks
   // One key tile per wave, chunk c of row r at slot c ^ (r mod 16): the 16
   // rows read by one MFMA operand load hit distinct banks.
   __shared__ __attribute__((aligned(1024))) float kt[NWV][16 * D];
-  for (int v = threadIdx.x; v < (U + 15) / 16 * 16; v += NWV * 64)
-    cnt_s[v] = v < U ? static_cast<float>(sub_count(blk_len, v, R, s)) : 0.f;
   // MASS works in the log2 domain: logits carry scale * log2(e).
   const float zscale = MAXAGG ? scale : scale * 1.4426950408889634f;
   const int lane = threadIdx.x & 63;
@@ -150,21 +208,19 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
   const float *kslot = &kt[w][0];
 
   // Direct loads of tile t into this wave's slot; rows past U repeat row
-  // U - 1 (their logits are discarded). A lane's byte offsets inside a whole
-  // tile are the same for every tile: formed once.
-  uint32_t loff[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int P = i * 64 + lane;
-    const int row = P / CPR, c = (P % CPR) ^ (row & 15);
-    loff[i] = static_cast<uint32_t>(row * D * 4 + c * 16);
-  }
+  // U - 1 (their logits are discarded). (A lane's offsets are formed per
+  // tile: kept across tiles they would cost the registers of a third
+  // resident wave.)
   auto issue = [&](int t) {
     const int v0 = (w * VT + t) * 16;
     const float *base = kb + static_cast<int64_t>(v0) * D;
     if (v0 + 16 <= U) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) load_lds16(base, loff[i], slot + i * 1024);
+      for (int i = 0; i < NI; ++i) {
+        const int P = i * 64 + lane;
+        const int row = P / CPR, c = (P % CPR) ^ (row & 15);
+        load_lds16(base, static_cast<uint32_t>(row * D * 4 + c * 16), slot + i * 1024);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
@@ -188,8 +244,33 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
 #pragma unroll
     for (int j = 0; j < DQ; ++j) qreg[j] = 0.f;
   }
-  __syncthreads();  // cnt_s
-  const int cu = (u < U) ? static_cast<int>(cnt_s[u]) : 0;
+  // Key sub-block entries: one length load per block (U = nb R), a
+  // thread's loads issued after the first key tile's and the Q rows', so
+  // that one round trip covers them all; then the R sub-block entries of
+  // each block, and the counts of the strip's own query sub-blocks.
+  {
+    constexpr int kPer = kMaxSub / (NWV * 64);
+    int len[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int I = threadIdx.x + k * NWV * 64;
+      len[k] = I < nb ? blk_len[I] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int I = threadIdx.x + k * NWV * 64;
+      if (I < nb)
+        for (int r = 0; r < R; ++r) {
+          const int c = min(max(len[k] - r * s, 0), s);
+          kv_s[I * R + r] = MAXAGG ? static_cast<float>(c) : (c > 0 ? __builtin_amdgcn_logf(static_cast<float>(c)) : -INFINITY);
+          const int q = I * R + r - u0;
+          if (q >= 0 && q < 16) cq[q] = c;
+        }
+    }
+    for (int v = U + static_cast<int>(threadIdx.x); v < NWV * MAXT * 16; v += NWV * 64) kv_s[v] = MAXAGG ? 0.f : -INFINITY;
+  }
+  __syncthreads();  // kv_s, cq
+  const int cu = (u < U) ? cq[ul] : 0;  // real tokens of query sub-block u
 
   // Logits z[t][r]: query sub-block u, key sub-block v = v0 + 4g + r.
   float z[MAXT][4];  // -inf marks an empty key sub-block
@@ -199,6 +280,11 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
     for (int r = 0; r < 4; ++r) z[t][r] = -INFINITY;
     if (t < nt) {
       wait_vmcnt<0>();  // tile t is in the slot (and the Q loads are in)
+      if (!MAXAGG && t == 0 && cu == 0) {
+        // an empty query sub-block gets weight wu = 0; zero means keep its logits finite
+#pragma unroll
+        for (int j = 0; j < DQ; ++j) qreg[j] = 0.f;
+      }
       float kreg[DQ];
 #pragma unroll
       for (int m = 0; m < DQ / 4; ++m) {
@@ -212,11 +298,16 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
 #pragma unroll
       for (int j = 0; j < DQ; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kreg[j], qreg[j], acc, 0, 0, 0);
       const int v0 = (w * VT + t) * 16;
-      const float4 c4 = *reinterpret_cast<const float4 *>(&cnt_s[v0 + 4 * g]);  // 0 past U
-      const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+      const float4 c4 = *reinterpret_cast<const float4 *>(&kv_s[v0 + 4 * g]);
+      const float kv[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (cv[r] > 0.f && cu > 0) z[t][r] = acc[r] * zscale;
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (MAXAGG) {
+          if (kv[r] > 0.f && cu > 0) z[t][r] = acc[r] * zscale;
+        } else {
+          z[t][r] = fmaf(acc[r], zscale, kv[r]);  // log2(count) + logit, -inf for an empty key sub-block
+        }
+      }
     }
   }
 
@@ -235,22 +326,20 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
 #pragma unroll
     for (int i = 1; i < NWV; ++i) m = fmaxf(m, red[i][ul]);
     __syncthreads();
-    // Count-weighted exponentials and their row sum.
+    // Count-weighted exponentials c_v 2^(z - m) = 2^(z + log2 c_v - m) and
+    // their row sum; m is the largest count-weighted term's exponent (the
+    // shift cancels in the normalisation). A row without real keys (m =
+    // -inf) takes m = 0, so every weight is exactly zero.
+    m = (m == -INFINITY) ? 0.f : m;
     float den = 0.f;
 #pragma unroll
-    for (int t = 0; t < MAXT; ++t) {
-      float cv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (t < nt) {
-        const float4 c4 = *reinterpret_cast<const float4 *>(&cnt_s[(w * VT + t) * 16 + 4 * g]);
-        cv[0] = c4.x; cv[1] = c4.y; cv[2] = c4.z; cv[3] = c4.w;
-      }
+    for (int t = 0; t < MAXT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = z[t][r] != -INFINITY ? cv[r] * __builtin_amdgcn_exp2f(z[t][r] - m) : 0.f;
+        const float e = __builtin_amdgcn_exp2f(z[t][r] - m);
         z[t][r] = e;
         den += e;
       }
-    }
     den += __shfl_xor(den, 16, 64);
     den += __shfl_xor(den, 32, 64);
     if (g == 0) red[w][ul] = den;
@@ -261,76 +350,19 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
     const float wu = (den > 0.f) ? static_cast<float>(cu) / den : 0.f;
     const float cblk = reduce_block_lanes(static_cast<float>(cu), R, false);
     const float inv_c = cblk > 0.f ? 1.f / cblk : 0.f;
-    const int I = u / R;
-    const bool leader = (ul % R) == 0 && u < U;
-#pragma unroll
-    for (int t = 0; t < MAXT; ++t) {
-      if (t < VT) {
-        const int v0 = (w * VT + t) * 16;
-        if (v0 < U) {
-          if (R == 1) {
-            float o[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = z[t][r] * wu * inv_c;
-            const int J0 = v0 + 4 * g;
-            if (leader) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (J0 + r < nb) S[(static_cast<int64_t>(h) * nb + I) * nb + J0 + r] = o[r];
-            }
-          } else if (R == 2) {
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-              float val = (z[t][2 * p] + z[t][2 * p + 1]) * wu;
-              val = reduce_block_lanes(val, R, false) * inv_c;
-              const int J = (v0 + 4 * g + 2 * p) / 2;
-              if (leader && J < nb) S[(static_cast<int64_t>(h) * nb + I) * nb + J] = val;
-            }
-          } else {
-            float val = ((z[t][0] + z[t][1]) + (z[t][2] + z[t][3])) * wu;
-            if (R == 8) val += __shfl_xor(val, 16, 64);
-            val = reduce_block_lanes(val, R < 16 ? R : 16, false) * inv_c;
-            const int J = (v0 + 4 * g) / R;
-            const bool writer = leader && (R == 4 || (g & 1) == 0);
-            if (writer && J < nb) S[(static_cast<int64_t>(h) * nb + I) * nb + J] = val;
-          }
-        }
-      }
+    switch (R) {
+      case 1: store_block_scores<1, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, u, g, S); break;
+      case 2: store_block_scores<2, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, u, g, S); break;
+      case 4: store_block_scores<4, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, u, g, S); break;
+      default: store_block_scores<8, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, u, g, S); break;
     }
   } else {
     // MAX: largest sub-block logit between the two blocks.
-    const int I = u / R;
-    const bool leader = (ul % R) == 0 && u < U;
-#pragma unroll
-    for (int t = 0; t < MAXT; ++t) {
-      if (t < VT) {
-        const int v0 = (w * VT + t) * 16;
-        if (v0 < U) {
-          if (R == 1) {
-            const int J0 = v0 + 4 * g;
-            if (leader) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (J0 + r < nb) S[(static_cast<int64_t>(h) * nb + I) * nb + J0 + r] = z[t][r];
-            }
-          } else if (R == 2) {
-#pragma unroll
-            for (int p = 0; p < 2; ++p) {
-              float val = fmaxf(z[t][2 * p], z[t][2 * p + 1]);
-              val = reduce_block_lanes(val, R, true);
-              const int J = (v0 + 4 * g + 2 * p) / 2;
-              if (leader && J < nb) S[(static_cast<int64_t>(h) * nb + I) * nb + J] = val;
-            }
-          } else {
-            float val = fmaxf(fmaxf(z[t][0], z[t][1]), fmaxf(z[t][2], z[t][3]));
-            if (R == 8) val = fmaxf(val, __shfl_xor(val, 16, 64));
-            val = reduce_block_lanes(val, R, true);
-            const int J = (v0 + 4 * g) / R;
-            const bool writer = leader && (R == 4 || (g & 1) == 0);
-            if (writer && J < nb) S[(static_cast<int64_t>(h) * nb + I) * nb + J] = val;
-          }
-        }
-      }
+    switch (R) {
+      case 1: store_block_scores<1, MAXT, true>(z, 1.f, 1.f, w, VT, U, nb, h, u, g, S); break;
+      case 2: store_block_scores<2, MAXT, true>(z, 1.f, 1.f, w, VT, U, nb, h, u, g, S); break;
+      case 4: store_block_scores<4, MAXT, true>(z, 1.f, 1.f, w, VT, U, nb, h, u, g, S); break;
+      default: store_block_scores<8, MAXT, true>(z, 1.f, 1.f, w, VT, U, nb, h, u, g, S); break;
     }
   }
 }
@@ -508,9 +540,11 @@ static void launch_contract(int U, dim3 grid, const float *qb, const float *kb,
                             const int32_t *blk_len, int s, int R, int nb, float scale, float *S,
                             hipStream_t stream) {
   // Each wave owns up to MAXT 16-wide key tiles of the strip. Sixteen tiles
-  // per wave keep a wave's logits in ~160 registers, so three waves share a
-  // SIMD and several workgroups a CU: one's softmax phase overlaps another's
-  // matrix work (measured 5-6 % faster than eight tiles per wave).
+  // per wave keep a wave's logits in registers within the 168 that let three
+  // waves share a SIMD (the kernel's launch bounds ask for three): three
+  // workgroups per CU, so a 1024-sub-block head's 64 strips x 12 heads run
+  // in one round on 256 CUs (at two per CU the last third ran as a second,
+  // half-empty round: 52 -> 39 us).
   const int tiles = (U + 15) / 16;
   if (tiles <= 16)
     hipLaunchKernelGGL((hsa::contract_kernel<D, 4, 4, MAXAGG>), grid, dim3(256), 0, stream, qb, kb, blk_len, s, U, R, nb, scale, S);
