@@ -429,10 +429,23 @@ __device__ __forceinline__ void load_row_bits(const float *__restrict__ row, int
 // instruction then spread over the most banks); then the boundary bin's
 // columns for the register sort.
 struct RowWin {
-  unsigned long long mass[kWin + 1];
-  uint32_t cnt[kWin + 1];
+  unsigned long long pk[kWin + 1];
   uint32_t cand[kSortMax];
 };
+
+// Every key of a digit-0 bin shares its exponent e and the top 3 significand
+// bits m3, so the bin's exact 2^-62 mass is fixed by its count and the sum
+// of its keys' low 20 significand bits: for e >= 88 (p >= 2^-39, where the
+// fixed-point value p 2^62 is an integer) it is the significand sum
+// (count (8 + m3) 2^20 + low-bit sum) times 2^(e - 88). A window slot packs
+// both sums in one 64-bit LDS word, count above bit 32 (a row's low-bit sum
+// stays below 2^30), so one atomic per column builds it.
+constexpr uint32_t kBinE88 = (1u << 11) | (88u << 3);  // digit 0 of the smallest key with e = 88
+__device__ __forceinline__ uint64_t bin_mass(uint64_t pk, uint32_t bin) {
+  const uint32_t cnt = static_cast<uint32_t>(pk >> 32);
+  const uint64_t sig = static_cast<uint64_t>(cnt) * ((8u + (bin & 7u)) << 20) + static_cast<uint32_t>(pk);
+  return sig << (((bin >> 3) & 0xFFu) - 88u);
+}
 
 // Exact boundary key of the shortest prefix by an MSB-first radix search
 // (digits of up to 8 bits, 2^-62 fixed-point mass histograms in `mh`), for
@@ -510,9 +523,10 @@ __device__ uint32_t radix_boundary(const uint32_t (&key)[KPL], int nb, int lane,
 // Row prefixes. One wave per row at a time, each wave walking `rpw`
 // consecutive rows of one head (few registers, so that many waves hide the
 // loads of each other's rows): the threshold key K_I such that T_I is exactly the
-// columns with key64 >= K_I. One pass of LDS atomics builds, over a window of
-// kWin digit-0 bins below the row's largest key, the exact 2^-62 fixed-point
-// mass and the count of each bin; the scan from the top finds the bin where
+// columns with key64 >= K_I. One pass of LDS atomics (one per column)
+// builds, over a window of up to kWin digit-0 bins below the row's largest
+// key (bins of keys p >= 2^-39), the count and the exact 2^-62 fixed-point
+// mass of each bin (see bin_mass); the scan from the top finds the bin where
 // the cumulative mass reaches tau, whose columns (at most kSortMax) are then
 // sorted in registers by key64 and scanned, which fixes the boundary column.
 // The bins' counts (the boundary bin's part outside the prefix) feed global
@@ -549,21 +563,18 @@ thresh_row_kernel(const float *__restrict__ S, int nb, int rpw, uint64_t target,
     const uint32_t ktop = kmax | 0xFFFFFu;  // (ktop - key) >> 20: bins below the top bin
     const int bmax = static_cast<int>(kmax >> 20);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      R.mass[4 * lane + q] = 0;
-      R.cnt[4 * lane + q] = 0;
-    }
-    if (lane == 0) {
-      R.mass[kWin] = 0;
-      R.cnt[kWin] = 0;
-    }
+    for (int q = 0; q < 4; ++q) R.pk[4 * lane + q] = 0;
+    if (lane == 0) R.pk[kWin] = 0;
+    // window slots 0 .. qlim - 1 (bins of keys with e >= 88); every lower
+    // key goes to slot kWin
+    const int qlim = min(max(bmax - static_cast<int>(kBinE88) + 1, 0), kWin);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int r = 0; r < KPL; ++r)
       if (col_live<KPL>(r, lane, nb)) {  // (columns past the end would all hit one address)
-        const uint32_t q = min((ktop - key[r]) >> 20, static_cast<uint32_t>(kWin));
-        atomicAdd(&R.cnt[q], 1u);
-        atomicAdd(&R.mass[q], static_cast<unsigned long long>(fixed62(key[r])));
+        const uint32_t raw = (ktop - key[r]) >> 20;
+        const uint32_t q = raw < static_cast<uint32_t>(qlim) ? raw : static_cast<uint32_t>(kWin);
+        atomicAdd(&R.pk[q], (1ull << 32) | (key[r] & 0xFFFFFu));
       }
     __builtin_amdgcn_wave_barrier();
     // lane l holds window slots 4l + q (q = 0..3): lanes run from the top
@@ -571,14 +582,16 @@ thresh_row_kernel(const float *__restrict__ S, int nb, int rpw, uint64_t target,
     uint32_t cv[4], cloc = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      mv[q] = R.mass[4 * lane + q];
-      cv[q] = R.cnt[4 * lane + q];
+      const int sl = 4 * lane + q;
+      const uint64_t pk = R.pk[sl];
+      cv[q] = static_cast<uint32_t>(pk >> 32);
+      mv[q] = sl < qlim ? bin_mass(pk, static_cast<uint32_t>(bmax - sl)) : 0ull;
       mloc += mv[q];
       cloc += cv[q];
     }
-    const uint32_t under_cnt = R.cnt[kWin];
+    const uint32_t under_cnt = static_cast<uint32_t>(R.pk[kWin] >> 32);
     const uint64_t mincl = wave_scan_u64(mloc);
-    const uint64_t total = readlane_u64(mincl, 63) + R.mass[kWin];
+    const uint64_t wtotal = readlane_u64(mincl, 63);  // (the mass below the window is not formed)
     uint64_t K = 0;
     int cnt = 0;
     int sc = kWin + 1;  // window slot holding the prefix boundary (kWin + 1: none)
@@ -597,9 +610,13 @@ thresh_row_kernel(const float *__restrict__ S, int nb, int rpw, uint64_t target,
       cnt = 1;
       sc = 0;
       sub = 1;
-    } else if (total < target) {
-      K = 0;  // the whole row
-      cnt = nb;
+    } else if (wtotal < target) {
+      if (under_cnt == 0) {
+        K = 0;  // the whole row
+        cnt = nb;
+      } else {
+        fix = true;  // the boundary (or the row's end) lies below the window
+      }
     } else {
       // first window slot (from the top) where the cumulative mass reaches the target
       const uint32_t cincl = wave_scan_u32(cloc);
@@ -663,7 +680,7 @@ thresh_row_kernel(const float *__restrict__ S, int nb, int rpw, uint64_t target,
         if (o != 0) atomicAdd(&h0[(bmax - sl) & (kHBins / 2 - 1)], o);
       }
       if (under_cnt != 0 && K != 0) {
-        const uint32_t wlo = static_cast<uint32_t>(bmax - (kWin - 1)) << 20;  // lowest key of the window
+        const uint32_t wlo = static_cast<uint32_t>(bmax - qlim + 1) << 20;  // lowest key of the window
 #pragma unroll
         for (int r = 0; r < KPL; ++r)
           if (col_live<KPL>(r, lane, nb) && key[r] < wlo) atomicAdd(&h0[(key[r] >> 20) & (kHBins / 2 - 1)], 1u);
@@ -688,9 +705,10 @@ thresh_row_kernel(const float *__restrict__ S, int nb, int rpw, uint64_t target,
   }
 }
 
-// Rows the row pass listed (boundary below the window or in a crowded bin):
-// the full-key radix search, then digit 0 of their columns outside the
-// prefix. The head's last workgroup then picks the boundary digit of the
+// Rows the row pass listed (boundary below the window or in a crowded bin,
+// or a row whose mass inside the window falls short of tau with columns
+// below it): the whole row when its total mass falls short, else the
+// full-key radix search; then digit 0 of their columns outside the prefix. The head's last workgroup then picks the boundary digit of the
 // fill from the complete digit-0 histogram and the prefix total.
 template <int KPL>
 __global__ void __launch_bounds__(kSelThreads)
@@ -716,8 +734,17 @@ thresh_fix_kernel(const float *__restrict__ S, int nb, uint64_t target, int64_t 
       const int I = fix_rows[hrow + i];
       uint32_t key[KPL];
       load_row_bits<KPL>(S + (hrow + I) * nb, nb, key, lane);
+      uint64_t tot = 0;
 #pragma unroll
-      for (int r = 0; r < KPL; ++r) key[r] = mass_key(key[r]);
+      for (int r = 0; r < KPL; ++r) {
+        key[r] = mass_key(key[r]);
+        tot += col_live<KPL>(r, lane, nb) ? fixed62(key[r]) : 0ull;
+      }
+      if (wave_total_u64(tot) < target) {  // the whole row is its prefix
+        if (lane == 0) row_thr[hrow + I] = 0;
+        cnt_w += nb;
+        continue;
+      }
       const uint32_t thr = radix_boundary<KPL>(key, nb, lane, target, mh[w]);
       uint64_t above = 0;
       int n_above = 0, n_tie = 0;

@@ -281,8 +281,27 @@ def _thresh_rows(kind, nb, rng):
     `kind` says: in a 12-bit key bin of n columns ("bin<n>": 5 scores of 0.08,
     n scores in [1.024e-3, 1.075e-3) with every fourth one repeated, the rest
     in [1e-7, 1e-6)), or about 40 binades below the row's largest score
-    ("far": one 0.5, the rest near 1e-13). Returns (S [nb, nb], tau)."""
+    ("far": one 0.5, the rest near 1e-13), or among the smallest scores the
+    histogram window holds exactly ("e88": one 0.5, 40 scores in [2^-39,
+    2^-37), the rest in [2^-41, 2^-39)), or nowhere: rows whose whole mass
+    falls short of tau, half of them with scores below 2^-39 as well
+    ("short"). Returns (S [nb, nb], tau)."""
     S = np.empty((nb, nb))
+    if kind == "e88":
+        for I in range(nb):
+            row = 2.0 ** rng.uniform(-41, -39, nb)
+            cols = rng.choice(nb, 41, replace=False)
+            row[cols[0]] = 0.5
+            row[cols[1:]] = 2.0 ** rng.uniform(-39, -37, 40)
+            S[I] = row
+        return S.astype(np.float32), 0.5 + 20 * 2.0 ** -38
+    if kind == "short":
+        for I in range(nb):
+            row = rng.uniform(1e-4, 2e-4, nb)
+            if I % 2:
+                row[rng.choice(nb, 20, replace=False)] = 1e-13
+            S[I] = row
+        return S.astype(np.float32), 0.5
     if kind == "far":
         for I in range(nb):
             row = 1e-13 * (1.0 + rng.random(nb))
@@ -351,14 +370,17 @@ def test_select_signed_zero_ties(hsa):
 
 
 @pytest.mark.parametrize("kind,nb", [("bin12", 60), ("bin24", 200), ("bin48", 200), ("bin100", 200),
-                                     ("far", 200), ("bin40", 1000)])
+                                     ("far", 200), ("e88", 200), ("short", 200), ("bin40", 1000)])
 def test_thresh_row_search_paths(hsa, kind, nb):
     """Threshold selection on rows built to take each way of finding a row
     prefix's boundary: a boundary key bin of up to 16, 32 or 64 columns (the
     register sorts of one, two and four 16-lane rows, with equal scores in the
     bin), more than 64 (the full-key search), a boundary about 40 binades
-    below the row's largest score (below the histogram window); equal to the
-    oracle with no fill, with a fill and with nearly everything filled."""
+    below the row's largest score (below the histogram window), a boundary
+    in the window's lowest bins (scores just above 2^-39, with smaller ones
+    below the window), rows whose whole mass falls short of tau (with and
+    without scores below the window); equal to the oracle with no fill, with
+    a fill and with nearly everything filled."""
     _say(f"threshold selection, row search path {kind}, nb {nb}")
     rng = np.random.default_rng(40 + nb + len(kind))
     S, tau = _thresh_rows(kind, nb, rng)
