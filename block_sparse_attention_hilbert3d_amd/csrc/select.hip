@@ -222,7 +222,7 @@ struct ThreshState {
 // Per-head counters, cleared by thresh_init_kernel.
 struct ThreshCounters {
   unsigned long long prefix_total;  // sum of |T_I| over the head's rows
-  int32_t done_fix, done_emit;      // finished workgroups of the passes that end in a pick
+  int32_t done_emit, pad;          // finished workgroups of the emitting pass (which ends in a pick)
   int32_t cand;                     // collected boundary pairs
   int32_t nfix;                     // rows listed for thresh_fix_kernel
 };
@@ -332,20 +332,26 @@ __device__ __forceinline__ uint64_t row_fill_key(uint64_t t, int I, int nb) {
 // multiple of kSelThreads), digits scanned from the top: the digit whose
 // cumulative count (from the top) first reaches `want` (>= 1). Returns the
 // digit, the count above it and its own count (all threads). If the
-// histogram holds fewer than `want` keys, digit = -1.
+// histogram holds fewer than `want` keys, digit = -1. wg_load_desc reads the
+// bins (thread t holds bins NB - 1 - t PER - j), wg_pick_vals picks from
+// them.
 template <int NB, bool COHERENT>
-__device__ void wg_pick(const uint32_t *hist, int64_t want, int &digit, int64_t &above, int64_t &count,
-                        int64_t (&part)[kSelThreads / 64], int64_t (&res)[3]) {
+__device__ __forceinline__ void wg_load_desc(const uint32_t *hist, uint32_t (&v)[NB / kSelThreads]) {
   constexpr int PER = NB / kSelThreads;
-  const int t = threadIdx.x, lane = lane_id(), w = t >> 6;
-  uint32_t v[PER];
-  uint64_t loc = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int d = NB - 1 - (t * PER + j);
+    const int d = NB - 1 - (static_cast<int>(threadIdx.x) * PER + j);
     v[j] = COHERENT ? coherent_load_u32(&hist[d]) : hist[d];
-    loc += v[j];
   }
+}
+template <int NB>
+__device__ void wg_pick_vals(const uint32_t (&v)[NB / kSelThreads], int64_t want, int &digit, int64_t &above,
+                             int64_t &count, int64_t (&part)[kSelThreads / 64], int64_t (&res)[3]) {
+  constexpr int PER = NB / kSelThreads;
+  const int t = threadIdx.x, lane = lane_id(), w = t >> 6;
+  uint64_t loc = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) loc += v[j];
   const uint64_t incl = wave_scan_u64(loc);
   if (lane == 63) part[w] = static_cast<int64_t>(incl);
   if (t == 0) res[0] = -1;
@@ -368,6 +374,82 @@ __device__ void wg_pick(const uint32_t *hist, int64_t want, int &digit, int64_t 
   digit = static_cast<int>(res[0]);
   above = res[1];
   count = res[2];
+  __syncthreads();  // part and res may be reused at once
+}
+template <int NB, bool COHERENT>
+__device__ void wg_pick(const uint32_t *hist, int64_t want, int &digit, int64_t &above, int64_t &count,
+                        int64_t (&part)[kSelThreads / 64], int64_t (&res)[3]) {
+  uint32_t v[NB / kSelThreads];
+  wg_load_desc<NB, COHERENT>(hist, v);
+  wg_pick_vals<NB>(v, want, digit, above, count, part, res);
+}
+
+// The head's fill after digit 0, from its prefix total and its complete
+// digit-0 histogram (bins as wg_load_desc reads them); the same in every
+// thread, so every workgroup that needs it forms it.
+__device__ ThreshState fill_state0(const uint32_t (&v0)[kHBins / kSelThreads], int64_t pref, int64_t budget,
+                                   int64_t (&part)[kSelThreads / 64], int64_t (&res)[3]) {
+  ThreshState ns{};
+  const int64_t need = budget - pref;
+  if (need <= 0) {
+    ns.mode = kFillNone;
+    return ns;
+  }
+  int d;
+  int64_t above, count;
+  wg_pick_vals<kHBins>(v0, need, d, above, count, part, res);
+  if (d < 0) {  // fewer pairs outside the prefixes than the budget asks: all of them
+    ns.mode = kFillThr;
+    ns.thr = 0;
+  } else {
+    ns.b0 = d;
+    ns.rem = need - above;
+    if (count == ns.rem) {
+      ns.mode = kFillThr;
+      ns.thr = static_cast<uint64_t>(d) << 40;
+    } else {
+      ns.mode = kFillDigit0;
+    }
+  }
+  return ns;
+}
+
+// A state formed in every thread, moved to scalar registers (the compiler
+// cannot tell that values read back from LDS are the same in every lane).
+__device__ __forceinline__ ThreshState uniform_state(const ThreshState &s) {
+  ThreshState u;
+  u.thr = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(s.thr >> 32))))
+           << 32) |
+          static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(s.thr))));
+  u.rem = static_cast<int64_t>(
+      (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint64_t>(s.rem) >> 32))))
+       << 32) |
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(s.rem)))));
+  u.mode = __builtin_amdgcn_readfirstlane(s.mode);
+  u.b0 = __builtin_amdgcn_readfirstlane(s.b0);
+  u.b1 = __builtin_amdgcn_readfirstlane(s.b1);
+  u.pad = 0;
+  return u;
+}
+
+// ... and after digit 1 (heads whose digit 0 is open), from the digit-1
+// histogram of the pairs in b0 outside the prefixes.
+__device__ ThreshState fill_state1(const ThreshState &s, const uint32_t (&v1)[kHBins / kSelThreads],
+                                   int64_t (&part)[kSelThreads / 64], int64_t (&res)[3]) {
+  if (s.mode != kFillDigit0) return s;
+  int d;
+  int64_t above, count;
+  wg_pick_vals<kHBins>(v1, s.rem, d, above, count, part, res);
+  ThreshState ns = s;
+  ns.b1 = d;  // the rem pairs lie in digit 0's histogram, so d >= 0
+  ns.rem = s.rem - above;
+  if (count == ns.rem) {
+    ns.mode = kFillThr;
+    ns.thr = (static_cast<uint64_t>(s.b0) << 40) | (static_cast<uint64_t>(d) << 28);
+  } else {
+    ns.mode = kFillDigit1;
+  }
+  return ns;
 }
 
 // Per-head counters and histograms to zero before a selection; workgroup 0
@@ -379,7 +461,7 @@ thresh_init_kernel(uint32_t *__restrict__ hist, ThreshCounters *__restrict__ ctr
   for (int i = threadIdx.x; i < 2 * kHBins; i += 256) hh[i] = 0;
   if (threadIdx.x == 0) {
     ctr[h].prefix_total = 0;
-    ctr[h].done_fix = ctr[h].done_emit = 0;
+    ctr[h].done_emit = 0;
     ctr[h].cand = 0;
     ctr[h].nfix = 0;
     if (h == 0) *n_def = 0;
@@ -708,19 +790,16 @@ thresh_row_kernel(const float *__restrict__ S, int nb, int rpw, uint64_t target,
 // Rows the row pass listed (boundary below the window or in a crowded bin,
 // or a row whose mass inside the window falls short of tau with columns
 // below it): the whole row when its total mass falls short, else the
-// full-key radix search; then digit 0 of their columns outside the prefix. The head's last workgroup then picks the boundary digit of the
-// fill from the complete digit-0 histogram and the prefix total.
+// full-key radix search; then digit 0 of their columns outside the prefix.
+// (The passes after it pick the fill's boundary digits themselves.)
 template <int KPL>
 __global__ void __launch_bounds__(kSelThreads)
-thresh_fix_kernel(const float *__restrict__ S, int nb, uint64_t target, int64_t budget,
-                  uint64_t *__restrict__ row_thr, uint32_t *__restrict__ hist,
-                  ThreshCounters *__restrict__ ctr, const int32_t *__restrict__ fix_rows,
-                  ThreshState *__restrict__ st) {
+thresh_fix_kernel(const float *__restrict__ S, int nb, uint64_t target, uint64_t *__restrict__ row_thr,
+                  uint32_t *__restrict__ hist, ThreshCounters *__restrict__ ctr,
+                  const int32_t *__restrict__ fix_rows) {
   __shared__ uint64_t mh[kSelThreads / 64][256];
   __shared__ uint32_t h0[kHBins / 2];
   __shared__ int s_cnt[kSelThreads / 64];
-  __shared__ int s_last;
-  __shared__ int64_t s_part[kSelThreads / 64], s_res[3];
   const int h = blockIdx.y;
   const int w = threadIdx.x >> 6, lane = lane_id();
   const int64_t hrow = static_cast<int64_t>(h) * nb;
@@ -794,35 +873,6 @@ thresh_fix_kernel(const float *__restrict__ S, int nb, uint64_t target, int64_t 
       if (sum) atomicAdd(&ctr[h].prefix_total, static_cast<unsigned long long>(sum));
     }
   }
-  // the head's last workgroup picks the boundary digit of the fill
-  last_arrival_wait();
-  if (threadIdx.x == 0) s_last = atomicAdd(&ctr[h].done_fix, 1) == static_cast<int>(gridDim.x) - 1;
-  __syncthreads();
-  if (!s_last) return;
-  const int64_t pref = static_cast<int64_t>(__hip_atomic_load(&ctr[h].prefix_total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  const int64_t need = budget - pref;
-  ThreshState ns{};
-  if (need <= 0) {
-    ns.mode = kFillNone;
-  } else {
-    int d;
-    int64_t above, count;
-    wg_pick<kHBins, true>(gh, need, d, above, count, s_part, s_res);
-    if (d < 0) {  // fewer pairs outside the prefixes than the budget asks: all of them
-      ns.mode = kFillThr;
-      ns.thr = 0;
-    } else {
-      ns.b0 = d;
-      ns.rem = need - above;
-      if (count == ns.rem) {
-        ns.mode = kFillThr;
-        ns.thr = static_cast<uint64_t>(d) << 40;
-      } else {
-        ns.mode = kFillDigit0;
-      }
-    }
-  }
-  if (threadIdx.x == 0) st[h] = ns;
 }
 
 // Rows of a wave's walk in pairs: both rows' scores are loaded into fresh
@@ -848,17 +898,27 @@ __device__ __forceinline__ void walk_row_pairs(const float *__restrict__ Sh, int
   }
 }
 
-// Second pass (heads whose boundary digit 0 is open): count digit 1 of the
-// pairs outside the prefixes in the boundary digit 0. Rows whose prefix
-// boundary lies in a lower digit 0 than b0 hold every pair of b0 inside
-// their prefix and are not read. thresh_pick1_kernel then picks the digit.
+// Second pass: each workgroup picks the fill's digit 0 from the complete
+// digit-0 histogram (the head's first one stores it for the emitting pass);
+// heads whose boundary digit 0 is open then count digit 1
+// of the pairs outside the prefixes in the boundary digit 0. Rows whose
+// prefix boundary lies in a lower digit 0 than b0 hold every pair of b0
+// inside their prefix and are not read.
 template <int KPL>
 __global__ void __launch_bounds__(kSelThreads)
-thresh_hist1_kernel(const float *__restrict__ S, int nb, int rpw, const uint64_t *__restrict__ row_thr,
-                    uint32_t *__restrict__ hist, const ThreshState *__restrict__ st) {
+thresh_hist1_kernel(const float *__restrict__ S, int nb, int rpw, int64_t budget,
+                    const uint64_t *__restrict__ row_thr, uint32_t *__restrict__ hist,
+                    const ThreshCounters *__restrict__ ctr, ThreshState *__restrict__ st) {
   __shared__ uint32_t h1[kHBins];
+  __shared__ int64_t s_part[kSelThreads / 64], s_res[3];
   const int h = blockIdx.y;
-  const ThreshState s = st[h];
+  ThreshState s;
+  {
+    uint32_t v0[kHBins / kSelThreads];
+    wg_load_desc<kHBins, false>(hist + static_cast<int64_t>(h) * 2 * kHBins, v0);
+    s = uniform_state(fill_state0(v0, static_cast<int64_t>(ctr[h].prefix_total), budget, s_part, s_res));
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) st[h] = s;  // for the emitting pass
   if (s.mode != kFillDigit0) return;
   const int w = threadIdx.x >> 6, lane = lane_id();
   for (int i = threadIdx.x; i < kHBins; i += kSelThreads) h1[i] = 0;
@@ -899,28 +959,6 @@ thresh_hist1_kernel(const float *__restrict__ S, int nb, int rpw, const uint64_t
   }
 }
 
-// The boundary digit 1 of heads whose digit 0 is open: one workgroup per head.
-__global__ void __launch_bounds__(kSelThreads)
-thresh_pick1_kernel(const uint32_t *__restrict__ hist, ThreshState *__restrict__ st) {
-  __shared__ int64_t s_part[kSelThreads / 64], s_res[3];
-  const int h = blockIdx.x;
-  const ThreshState s = st[h];
-  if (s.mode != kFillDigit0) return;
-  int d;
-  int64_t above, count;
-  wg_pick<kHBins, false>(hist + (static_cast<int64_t>(h) * 2 + 1) * kHBins, s.rem, d, above, count, s_part, s_res);
-  ThreshState ns = s;
-  ns.b1 = d;  // the rem pairs lie in digit 0's histogram, so d >= 0
-  ns.rem = s.rem - above;
-  if (count == ns.rem) {
-    ns.mode = kFillThr;
-    ns.thr = (static_cast<uint64_t>(s.b0) << 40) | (static_cast<uint64_t>(d) << 28);
-  } else {
-    ns.mode = kFillDigit1;
-  }
-  if (threadIdx.x == 0) st[h] = ns;
-}
-
 // Writes the row's list: the columns with key64 >= E, ascending; returns the
 // count. Entries past the count are not written.
 template <int KPL>
@@ -946,6 +984,7 @@ __device__ __forceinline__ int emit_row(const uint32_t (&key)[KPL], int nb, uint
 template <int KPL>
 __global__ void __launch_bounds__(kSelThreads)
 thresh_emit_kernel(const float *__restrict__ S, int nb, int rpw, const uint64_t *__restrict__ row_thr,
+                   const uint32_t *__restrict__ hist,
                    ThreshState *__restrict__ st, ThreshCounters *__restrict__ ctr,
                    uint64_t *__restrict__ cand, int32_t *__restrict__ def_rows, int32_t *__restrict__ n_def,
                    int32_t *__restrict__ kv_idx, int32_t *__restrict__ kv_cnt, int max_kv) {
@@ -953,7 +992,13 @@ thresh_emit_kernel(const float *__restrict__ S, int nb, int rpw, const uint64_t 
   __shared__ int s_last;
   __shared__ int64_t s_part[kSelThreads / 64], s_res[3];
   const int h = blockIdx.y;
-  const ThreshState s = st[h];
+  // the fill's state after digit 0 (from the digit-1 pass), then digit 1
+  ThreshState s = st[h];
+  if (s.mode == kFillDigit0) {
+    uint32_t v1[kHBins / kSelThreads];
+    wg_load_desc<kHBins, false>(hist + (static_cast<int64_t>(h) * 2 + 1) * kHBins, v1);
+    s = uniform_state(fill_state1(s, v1, s_part, s_res));
+  }
   const int w = threadIdx.x >> 6;
   const uint64_t hi01 = (static_cast<uint64_t>(s.b0) << 12) | static_cast<uint64_t>(s.b1);  // gkey >> 28 of the open digits
   const int I0 = (blockIdx.x * (kSelThreads / 64) + w) * rpw;
@@ -1291,12 +1336,11 @@ hsa_status_t launch_select(const float *S, int nh, int nb, const hsa_select_para
     HSA_KPL_DISPATCH(nb, hsa::thresh_row_kernel, rgrid, dim3(hsa::kSelThreads), S, nb, rpw_row, target,
                      row_thr, hist, ctr, fix_rows);
     HSA_KPL_DISPATCH(nb, hsa::thresh_fix_kernel, dim3(std::min(8, (nb + rows_per_wg - 1) / rows_per_wg), nh),
-                     dim3(hsa::kSelThreads), S, nb, target, budget, row_thr, hist, ctr, fix_rows, st);
-    HSA_KPL_DISPATCH(nb, hsa::thresh_hist1_kernel, hgrid, dim3(hsa::kSelThreads), S, nb, rpw_h1, row_thr, hist,
-                     st);
-    hipLaunchKernelGGL(hsa::thresh_pick1_kernel, dim3(nh), dim3(hsa::kSelThreads), 0, stream, hist, st);
-    HSA_KPL_DISPATCH(nb, hsa::thresh_emit_kernel, egrid, dim3(hsa::kSelThreads), S, nb, rpw_emit, row_thr, st, ctr,
-                     cand, def_rows, n_def, kv_idx, kv_cnt, max_kv);
+                     dim3(hsa::kSelThreads), S, nb, target, row_thr, hist, ctr, fix_rows);
+    HSA_KPL_DISPATCH(nb, hsa::thresh_hist1_kernel, hgrid, dim3(hsa::kSelThreads), S, nb, rpw_h1, budget, row_thr,
+                     hist, ctr, st);
+    HSA_KPL_DISPATCH(nb, hsa::thresh_emit_kernel, egrid, dim3(hsa::kSelThreads), S, nb, rpw_emit, row_thr, hist, st,
+                     ctr, cand, def_rows, n_def, kv_idx, kv_cnt, max_kv);
     const dim3 dgrid(std::min(256, (rows + rows_per_wg - 1) / rows_per_wg));
     HSA_KPL_DISPATCH(nb, hsa::thresh_emit_deferred_kernel, dgrid, dim3(hsa::kSelThreads), S, nb, row_thr, st,
                      def_rows, n_def, kv_idx, kv_cnt, max_kv);
