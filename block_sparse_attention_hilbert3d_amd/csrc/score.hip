@@ -286,10 +286,17 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
         for (int j = 0; j < DQ; ++j) qreg[j] = 0.f;
       }
       float kreg[DQ];
+      {
+        // this lane's fragment addresses, formed per tile (kept across the
+        // loop they would cost the registers of a third resident wave)
+        int lt = lane;
+        asm volatile("" : "+v"(lt));
+        const int ult = lt & 15, gt = lt >> 4;
 #pragma unroll
-      for (int m = 0; m < DQ / 4; ++m) {
-        const float4 k4 = *reinterpret_cast<const float4 *>(kslot + ul * D + (((g + 4 * m) ^ ul) * 4));
-        kreg[4 * m] = k4.x; kreg[4 * m + 1] = k4.y; kreg[4 * m + 2] = k4.z; kreg[4 * m + 3] = k4.w;
+        for (int m = 0; m < DQ / 4; ++m) {
+          const float4 k4 = *reinterpret_cast<const float4 *>(kslot + ult * D + (((gt + 4 * m) ^ ult) * 4));
+          kreg[4 * m] = k4.x; kreg[4 * m + 1] = k4.y; kreg[4 * m + 2] = k4.z; kreg[4 * m + 3] = k4.w;
+        }
       }
       // the slot is reused by the next tile's loads: its reads must be done
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
@@ -312,10 +319,12 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
   }
 
   if constexpr (!MAXAGG) {
-    // Row maximum over every key sub-block of query sub-block u.
+    // Row maximum over every key sub-block of query sub-block u (the last
+    // tiles first: a value held through the loop in scratch is then read
+    // last).
     float m = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < MAXT; ++t)
+    for (int t = MAXT - 1; t >= 0; --t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) m = fmaxf(m, z[t][r]);
     m = fmaxf(m, __shfl_xor(m, 16, 64));
@@ -347,14 +356,19 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
     den = 0.f;
 #pragma unroll
     for (int i = 0; i < NWV; ++i) den += red[i][ul];
-    const float wu = (den > 0.f) ? static_cast<float>(cu) / den : 0.f;
-    const float cblk = reduce_block_lanes(static_cast<float>(cu), R, false);
+    // The query count and index are taken again here rather than kept across
+    // the tile loop (where holding them spills at three waves per SIMD).
+    int ue = u;
+    asm volatile("" : "+v"(ue));
+    const int cue = (ue < U) ? *static_cast<volatile int *>(&cq[ue & 15]) : 0;
+    const float wu = (den > 0.f) ? static_cast<float>(cue) / den : 0.f;
+    const float cblk = reduce_block_lanes(static_cast<float>(cue), R, false);
     const float inv_c = cblk > 0.f ? 1.f / cblk : 0.f;
     switch (R) {
-      case 1: store_block_scores<1, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, u, g, S); break;
-      case 2: store_block_scores<2, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, u, g, S); break;
-      case 4: store_block_scores<4, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, u, g, S); break;
-      default: store_block_scores<8, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, u, g, S); break;
+      case 1: store_block_scores<1, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, ue, g, S); break;
+      case 2: store_block_scores<2, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, ue, g, S); break;
+      case 4: store_block_scores<4, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, ue, g, S); break;
+      default: store_block_scores<8, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, ue, g, S); break;
     }
   } else {
     // MAX: largest sub-block logit between the two blocks.
