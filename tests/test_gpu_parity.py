@@ -157,7 +157,7 @@ def test_score_matches_oracle(hsa, idx, agg):
     assert err <= SCORE_TOL[agg]
 
 
-@pytest.mark.parametrize("idx,step", [(1, 0), (2, 0), (3, 0), (5, 0), (5, 9)])
+@pytest.mark.parametrize("idx,step", [(1, 0), (2, 0), (3, 0), (5, 0), (5, 4), (5, 9)])
 def test_select_bit_exact_on_gpu_scores(hsa, idx, step):
     """Reading S26: (ii) the GPU selection on the GPU's float32 scores equals
     the oracle's selection on those same scores, bit for bit; (iii) against
@@ -477,7 +477,7 @@ def test_layer_all_rows(hsa, idx):
     _check_layer(hsa, w, 0, *_layer(hsa, w, 0))
 
 
-@pytest.mark.parametrize("idx,step", [(3, 0), (4, 0), (4, 5), (5, 0), (5, 9), (6, 0), (7, 0)])
+@pytest.mark.parametrize("idx,step", [(3, 0), (4, 0), (4, 5), (5, 0), (5, 4), (5, 9), (6, 0), (7, 0)])
 def test_layer_sampled_rows(hsa, idx, step):
     w = wl.get(idx)
     _say(f"layer workload {idx} step {step} (sampled rows)")
