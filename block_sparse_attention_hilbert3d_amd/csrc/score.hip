@@ -120,52 +120,109 @@ constexpr int kMaxSub = 2048;  // sub-blocks per head (validated at the boundary
 // u, key sub-block 16 (w VT + t) + 4g + r): MASS sums the R x R sub-block
 // pairs of each block pair, each query sub-block's weights scaled by wu,
 // the total by inv_c; MAX takes the largest. RR = R (sub-blocks per block,
-// a power of two <= 8), so block indices are shifts.
+// 2, 4 or 8), so block indices are shifts. A tile gives 16/RR rows x 16/RR
+// columns of block scores; they are gathered in the wave's (now idle)
+// key-tile slot and leave as runs of up to 64 consecutive columns of a row
+// (stored tile by tile they would touch 16/RR rows per store).
 template <int RR, int MAXT, bool MAXAGG>
 __device__ __forceinline__ void store_block_scores(const float (&z)[MAXT][4], float wu, float inv_c, int w, int VT,
-                                                   int U, int nb, int h, int u, int g, float *__restrict__ S) {
-  const int ul = u & 15;
-  const int I = u / RR;
+                                                   int U, int nb, int h, int u, int g, float *__restrict__ S,
+                                                   float *slot) {
+  static_assert(RR == 2 || RR == 4 || RR == 8, "sub-blocks per block");
+  constexpr int BPT = 16 / RR;       // block rows (and columns) per tile
+  constexpr int WC = MAXT * BPT;     // slot row length: the wave's block columns
+  const int ul = u & 15, u0 = u - ul;
   const bool leader = (ul % RR) == 0 && u < U;
-  float *Srow = S + (static_cast<int64_t>(h) * nb + I) * nb;
+  const int ri = ul / RR;            // this lane's block row within the strip
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) {
     if (t < VT) {
-      const int v0 = (w * VT + t) * 16;  // a multiple of 16: block of v0 + 4g + r is v0 / RR + (4g + r) / RR
-      if (v0 < U) {
-        if constexpr (RR == 1) {
-          const int J0 = v0 + 4 * g;
-          if (leader) {
+      if constexpr (RR == 2) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float o = MAXAGG ? z[t][r] : z[t][r] * wu * inv_c;
-              if (J0 + r < nb) Srow[J0 + r] = o;
-            }
-          }
-        } else if constexpr (RR == 2) {
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            float val = MAXAGG ? fmaxf(z[t][2 * p], z[t][2 * p + 1]) : (z[t][2 * p] + z[t][2 * p + 1]) * wu;
-            val = reduce_block_lanes(val, RR, MAXAGG);
-            if constexpr (!MAXAGG) val *= inv_c;
-            const int J = v0 / 2 + 2 * g + p;
-            if (leader && J < nb) Srow[J] = val;
-          }
-        } else {
-          float val = MAXAGG ? fmaxf(fmaxf(z[t][0], z[t][1]), fmaxf(z[t][2], z[t][3]))
-                             : ((z[t][0] + z[t][1]) + (z[t][2] + z[t][3])) * wu;
-          if constexpr (RR == 8) {
-            const float o = __shfl_xor(val, 16, 64);
-            val = MAXAGG ? fmaxf(val, o) : val + o;
-          }
+        for (int p = 0; p < 2; ++p) {
+          float val = MAXAGG ? fmaxf(z[t][2 * p], z[t][2 * p + 1]) : (z[t][2 * p] + z[t][2 * p + 1]) * wu;
           val = reduce_block_lanes(val, RR, MAXAGG);
           if constexpr (!MAXAGG) val *= inv_c;
-          const int J = v0 / RR + (4 * g) / RR;
-          const bool writer = leader && (RR == 4 || (g & 1) == 0);
-          if (writer && J < nb) Srow[J] = val;
+          if (leader) slot[ri * WC + t * BPT + 2 * g + p] = val;
+        }
+      } else {
+        float val = MAXAGG ? fmaxf(fmaxf(z[t][0], z[t][1]), fmaxf(z[t][2], z[t][3]))
+                           : ((z[t][0] + z[t][1]) + (z[t][2] + z[t][3])) * wu;
+        if constexpr (RR == 8) {
+          const float o = __shfl_xor(val, 16, 64);
+          val = MAXAGG ? fmaxf(val, o) : val + o;
+        }
+        val = reduce_block_lanes(val, RR, MAXAGG);
+        if constexpr (!MAXAGG) val *= inv_c;
+        const bool writer = leader && (RR == 4 || (g & 1) == 0);
+        if (writer) slot[ri * WC + t * BPT + (4 * g) / RR] = val;
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int lane = lane_id();
+  const int J0 = w * VT * BPT;                   // the wave's first block column
+  const int ncol = min(VT * BPT, nb - J0);       // its block columns that exist
+#pragma unroll
+  for (int rho = 0; rho < BPT; ++rho) {
+    if (u0 + rho * RR < U) {
+      float *Srow = S + (static_cast<int64_t>(h) * nb + u0 / RR + rho) * nb + J0;
+#pragma unroll
+      for (int c = 0; c < WC; c += 64)
+        if (c + lane < ncol) Srow[c + lane] = slot[rho * WC + c + lane];
+    }
+  }
+}
+
+// R = 1 (a sub-block per block): every score is a block score, 16 rows x
+// 16 columns per tile, held one row per lane (columns 4g .. 4g + 3). Written
+// as they are, each store would touch 16 rows; instead the wave's scores go
+// through its (now idle) key-tile slot, TC tiles at a time, and leave as
+// runs of 64 consecutive columns of one row.
+template <int D, int MAXT, bool MAXAGG>
+__device__ __forceinline__ void store_rows_r1(const float (&z)[MAXT][4], float wu, float inv_c, int w, int VT, int U,
+                                              int nb, int h, int u, int g, float *__restrict__ S, float *slot) {
+  constexpr int TC = D / 16;  // tiles per pass: 16 rows x 16 TC columns fill the 16 x D slot
+  constexpr int W = TC * 16;  // columns per pass
+  const int ul = u & 15, u0 = u - ul;
+  const int lane = lane_id();
+#pragma unroll
+  for (int t0 = 0; t0 < MAXT; t0 += TC) {
+    if (t0 >= VT) break;
+#pragma unroll
+    for (int tt = 0; tt < TC; ++tt) {
+      const int t = t0 + tt;
+      if (t < MAXT && t < VT) {
+        float4 o;
+        o.x = MAXAGG ? z[t][0] : z[t][0] * wu * inv_c;
+        o.y = MAXAGG ? z[t][1] : z[t][1] * wu * inv_c;
+        o.z = MAXAGG ? z[t][2] : z[t][2] * wu * inv_c;
+        o.w = MAXAGG ? z[t][3] : z[t][3] * wu * inv_c;
+        *reinterpret_cast<float4 *>(slot + ul * W + tt * 16 + 4 * g) = o;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int c0 = (w * VT + t0) * 16;                 // first column of the pass
+    const int cend = min(min((w * VT + VT) * 16, c0 + W), nb);  // this wave's columns end there
+#pragma unroll
+    for (int rho = 0; rho < 16; ++rho) {
+      const int row = u0 + rho;
+      if (row < U) {
+        float *Srow = S + (static_cast<int64_t>(h) * nb + row) * nb;
+#pragma unroll
+        for (int c = 0; c < W; c += 64) {
+          const int col = c0 + c + lane;
+          if (col < cend) Srow[col] = slot[rho * W + c + lane];
         }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -365,18 +422,18 @@ contract_kernel(const float *__restrict__ qbar, const float *__restrict__ kbar,
     const float cblk = reduce_block_lanes(static_cast<float>(cue), R, false);
     const float inv_c = cblk > 0.f ? 1.f / cblk : 0.f;
     switch (R) {
-      case 1: store_block_scores<1, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, ue, g, S); break;
-      case 2: store_block_scores<2, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, ue, g, S); break;
-      case 4: store_block_scores<4, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, ue, g, S); break;
-      default: store_block_scores<8, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, ue, g, S); break;
+      case 1: store_rows_r1<D, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, ue, g, S, &kt[w][0]); break;
+      case 2: store_block_scores<2, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, ue, g, S, &kt[w][0]); break;
+      case 4: store_block_scores<4, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, ue, g, S, &kt[w][0]); break;
+      default: store_block_scores<8, MAXT, false>(z, wu, inv_c, w, VT, U, nb, h, ue, g, S, &kt[w][0]); break;
     }
   } else {
     // MAX: largest sub-block logit between the two blocks.
     switch (R) {
-      case 1: store_block_scores<1, MAXT, true>(z, 1.f, 1.f, w, VT, U, nb, h, u, g, S); break;
-      case 2: store_block_scores<2, MAXT, true>(z, 1.f, 1.f, w, VT, U, nb, h, u, g, S); break;
-      case 4: store_block_scores<4, MAXT, true>(z, 1.f, 1.f, w, VT, U, nb, h, u, g, S); break;
-      default: store_block_scores<8, MAXT, true>(z, 1.f, 1.f, w, VT, U, nb, h, u, g, S); break;
+      case 1: store_rows_r1<D, MAXT, true>(z, 1.f, 1.f, w, VT, U, nb, h, u, g, S, &kt[w][0]); break;
+      case 2: store_block_scores<2, MAXT, true>(z, 1.f, 1.f, w, VT, U, nb, h, u, g, S, &kt[w][0]); break;
+      case 4: store_block_scores<4, MAXT, true>(z, 1.f, 1.f, w, VT, U, nb, h, u, g, S, &kt[w][0]); break;
+      default: store_block_scores<8, MAXT, true>(z, 1.f, 1.f, w, VT, U, nb, h, u, g, S, &kt[w][0]); break;
     }
   }
 }
