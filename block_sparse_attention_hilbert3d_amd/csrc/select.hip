@@ -11,20 +11,24 @@
 //  THRESH_GLOBAL VMoBA abstract: threshold selection by cumulative
 //                similarity, then global selection over the head, under a
 //                budget that shrinks across steps (DFSAttn design 3).
-//                Per row: MSB-first radix search (digits of up to 8 bits
-//                below the row's common key prefix, exact 2^-62 fixed-point
-//                mass histograms in LDS) for the boundary key of the
-//                shortest prefix reaching tau. Per head: an MSB-first radix
-//                select of the remaining budget among the pairs outside the
-//                row prefixes over 52-bit pair keys (score order key, then
-//                the lower linear index): digit 0 counted while the row
-//                prefixes are found, digit 1 in a second pass over the
-//                scores, the last 28 bits resolved among the few pairs left
-//                in the boundary digits, which the emitting pass collects;
-//                each pass's last workgroup of a head picks that head's
-//                digit, so there is no pass per digit and no pick launch.
-//                Lists are written in the emitting pass (rows holding
-//                boundary pairs right after the resolve).
+//                Per row: the count and exact 2^-62 fixed-point mass of
+//                each 12-bit key bin in a window below the row's largest
+//                key (one packed LDS atomic per column), a scan to the bin
+//                where the mass reaches tau, and a register sort of that
+//                bin's columns give the boundary key of the shortest prefix
+//                reaching tau; rows whose boundary bin is crowded or below
+//                the window take an MSB-first radix search (digits of up to
+//                8 bits) in a pass of their own. Per head: an MSB-first
+//                radix select of the remaining budget among the pairs
+//                outside the row prefixes over 52-bit pair keys (score
+//                order key, then the lower linear index): digit 0 counted
+//                while the row prefixes are found, digit 1 in a second pass
+//                over the scores (whose workgroups first pick digit 0), the
+//                last 28 bits resolved among the few pairs left in the
+//                boundary digits, which the emitting pass collects (its
+//                workgroups first pick digit 1; a head's last one resolves
+//                the rest). Lists are written in the emitting pass (rows
+//                holding boundary pairs by a small pass after the resolve).
 //  Every mode writes kv_cnt and the first kv_cnt entries of each list;
 //  entries past the count are not written.
 //  LVSA          LVSA section 2, A(t) = G_s u W(t): rotating anchors plus the
