@@ -12,8 +12,9 @@
 //     logits kept in registers; the MASS softmax (count-weighted: the log2
 //     of each key sub-block's count is added to its logit, so a weight is
 //     one exp2; max subtracted) and the per-block sums are reduced with lane
-//     shuffles and a small LDS exchange between the four waves; MAX takes
-//     maxima instead.
+//     shuffles and a small LDS exchange between the waves; MAX takes maxima
+//     instead. The block scores leave through each wave's idle key-tile
+//     slot as runs of consecutive columns of a row.
 //     Beyond 2048 sub-blocks per head the logits do not fit in registers and
 //     a streaming variant passes over the key tiles twice (online maximum
 //     and sum, then the normalised aggregation).
