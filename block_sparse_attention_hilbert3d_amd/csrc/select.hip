@@ -537,13 +537,15 @@ __device__ __forceinline__ uint64_t bin_mass(uint64_t pk, uint32_t bin) {
 // (digits of up to 8 bits, 2^-62 fixed-point mass histograms in `mh`), for
 // rows whose boundary bin holds more columns than the register sort takes or
 // lies below the window; ends once one key is left under the fixed digits.
-// Returns the boundary key value.
+// The search starts below key bit top0 with the bits above it fixed to those
+// of thr0 and A0 the mass of the keys above that prefix (thr0 = 0, top0 =
+// 31, A0 = 0: from the top). Returns the boundary key value.
 template <int KPL>
 __device__ uint32_t radix_boundary(const uint32_t (&key)[KPL], int nb, int lane, uint64_t target,
-                                   uint64_t *mh) {
-  uint32_t thr = 0;
-  uint64_t A = 0;
-  int top = 31;
+                                   uint64_t *mh, uint32_t thr0, int top0, uint64_t A0) {
+  uint32_t thr = thr0;
+  uint64_t A = A0;
+  int top = top0;
 #pragma unroll 1
   while (top >= 0) {
     const int width = min(8, top + 1);
@@ -683,6 +685,7 @@ thresh_row_kernel(const float *__restrict__ S, int nb, int rpw, uint64_t target,
     int sc = kWin + 1;  // window slot holding the prefix boundary (kWin + 1: none)
     int sub = 0;        // that slot's columns inside the prefix
     bool fix = false;
+    int fix_bin = -1;   // a crowded boundary bin handed to the fix pass
     if (target == 0) {
       // An empty prefix already reaches the threshold; keep the best block
       // (the lowest column among equal best scores).
@@ -724,7 +727,8 @@ thresh_row_kernel(const float *__restrict__ S, int nb, int rpw, uint64_t target,
       const int srcl = hitm ? __builtin_ctzll(hitm) : 0;
       const int c_d = __builtin_amdgcn_readlane(static_cast<int>(cd), srcl);
       if (hitm == 0 || c_d > kSortMax) {
-        fix = true;  // below the window, or a crowded boundary bin
+        fix = true;  // below the window, or a crowded boundary bin (whose digit 0 the fix pass takes as known)
+        if (hitm != 0) fix_bin = bmax - (4 * srcl + __builtin_amdgcn_readlane(qhit, srcl));
       } else {
         sc = 4 * srcl + __builtin_amdgcn_readlane(qhit, srcl);
         const uint32_t d = static_cast<uint32_t>(bmax - sc);
@@ -753,7 +757,8 @@ thresh_row_kernel(const float *__restrict__ S, int nb, int rpw, uint64_t target,
       }
     }
     if (fix) {
-      if (lane == 0) fix_rows[hrow + atomicAdd(&ctr[h].nfix, 1)] = I;
+      // (row, crowded boundary bin + 1 or 0) packed as I | bin' << 11 (I < 1024)
+      if (lane == 0) fix_rows[hrow + atomicAdd(&ctr[h].nfix, 1)] = I | ((fix_bin + 1) << 11);
     } else {
       // global digit 0 of the columns outside the prefix: whole window bins
       // below the boundary bin, the boundary bin's columns after the
@@ -814,21 +819,24 @@ thresh_fix_kernel(const float *__restrict__ S, int nb, uint64_t target, uint64_t
     __syncthreads();
     int cnt_w = 0;
     for (int i = blockIdx.x * (kSelThreads / 64) + w; i < n_fix; i += gridDim.x * (kSelThreads / 64)) {
-      const int I = fix_rows[hrow + i];
+      const int e = fix_rows[hrow + i];
+      const int I = e & 2047, fb = (e >> 11) - 1;  // fb: the crowded boundary bin, or -1
       uint32_t key[KPL];
       load_row_bits<KPL>(S + (hrow + I) * nb, nb, key, lane);
-      uint64_t tot = 0;
+      uint64_t tot = 0;  // all of the row (fb < 0), or the mass above bin fb
 #pragma unroll
       for (int r = 0; r < KPL; ++r) {
         key[r] = mass_key(key[r]);
-        tot += col_live<KPL>(r, lane, nb) ? fixed62(key[r]) : 0ull;
+        tot += (col_live<KPL>(r, lane, nb) && static_cast<int>(key[r] >> 20) > fb) ? fixed62(key[r]) : 0ull;
       }
-      if (wave_total_u64(tot) < target) {  // the whole row is its prefix
+      tot = wave_total_u64(tot);
+      if (fb < 0 && tot < target) {  // the whole row is its prefix
         if (lane == 0) row_thr[hrow + I] = 0;
         cnt_w += nb;
         continue;
       }
-      const uint32_t thr = radix_boundary<KPL>(key, nb, lane, target, mh[w]);
+      const uint32_t thr = radix_boundary<KPL>(key, nb, lane, target, mh[w], fb < 0 ? 0u : static_cast<uint32_t>(fb) << 20,
+                                               fb < 0 ? 31 : 19, fb < 0 ? 0ull : tot);
       uint64_t above = 0;
       int n_above = 0, n_tie = 0;
 #pragma unroll
