@@ -1060,6 +1060,31 @@ def test_score_beyond_the_register_path(hsa, idx, s, agg):
     assert err <= SCORE_TOL[agg]
 
 
+@pytest.mark.parametrize("B,s", [(64, 16), (64, 32), (64, 64),
+                                 (128, 16), (128, 32), (128, 64), (128, 128)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_score_every_subblock_ratio(hsa, B, s, D):
+    """Every block/sub-block ratio B/s in {1, 2, 4, 8} at both head dims, on a
+    ragged 7x13x19 Hilbert grid (1729 tokens: a partial last block and empty
+    sub-blocks in it), MASS and MAX, against the oracle."""
+    from dataclasses import replace
+    w = replace(wl.get(2), T=7, H=13, W=19, heads=3, D=D, B=B, s=s)
+    _say(f"score ratio B/s = {B}/{s}, D = {D}")
+    q, k, _ = wl.make_qkv(w, 0)
+    perm, blk_len = hsa.hsa_plan(w.T, w.H, w.W, w.order, B, device=dev())
+    qp, kp = hsa.hsa_perm([q.to(dev()), k.to(dev())], perm, perm.numel())
+    p = perm.cpu().numpy().astype(np.int64)
+    assert (p < 0).any(), "the grid should leave padded slots"
+    qo, ko = oracle.gather(q, p), oracle.gather(k, p)
+    for agg in ("mass", "max"):
+        S = hsa.hsa_score(qp, kp, blk_len, B, s, agg)
+        torch.cuda.synchronize()
+        ref = oracle.score(qo, ko, p, B, s, agg=agg)
+        err = float(np.abs(S.cpu().numpy() - ref).max())
+        _say(f"  {agg}: max err {err:.2e}")
+        assert err <= SCORE_TOL[agg]
+
+
 @pytest.mark.parametrize("idx", [2, 5])
 def test_layer_step_in_a_hip_graph(hsa, idx):
     """A whole layer step (reorder, score, select, order, attend, restore) is
