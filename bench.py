@@ -141,10 +141,17 @@ def _time_backward(hsa, L, qkv, K, stream, flop_fwd):
     ws = torch.empty(max(hsa.lib().hsa_attn_bwd_ws_size(L.heads, L.nb, L.B, int(L.kv_idx.shape[0] == 1)), 16),
                      dtype=torch.uint8, device=L.op.device)
     args = (*L.xp, L.op, dop, L.lse, L.blk_len, L.kv_idx, L.kv_cnt, L.B)
-    for _ in range(2):
-        hsa.hsa_attn_bwd(*args, outs=outs, ws=ws)
-    torch.cuda.synchronize()
+    # warm-up: at least two passes and 50 ms of GPU time (clock settle)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    n, t = 0, 0.0
+    while n < 2 or (t < 50.0 and n < 1000):
+        hsa.hsa_attn_bwd(*args, outs=outs, ws=ws)
+        n += 1
+        e1.record(stream)
+        e1.synchronize()
+        t = e0.elapsed_time(e1)
+    torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(K):
         hsa.hsa_attn_bwd(*args, outs=outs, ws=ws)
@@ -243,15 +250,19 @@ def _measure(hsa, wl, w, io, K, W, n_sets, detailed):
     # layers of a model run back to back, so the steps are repeated for at
     # least 50 ms of GPU time before the W warm-up steps (reported as
     # `settle`).
-    settle_steps, settle_ms = 0, 0.0
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
-    while settle_ms < 50.0 and settle_steps < 1000:
-        one_step(settle_steps)
-        settle_steps += 1
-        s1.record(stream)
-        s1.synchronize()
-        settle_ms = s0.elapsed_time(s1)
+    def settle(min_ms=50.0):
+        n, t = 0, 0.0
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        while t < min_ms and n < 1000:
+            one_step(n)
+            n += 1
+            s1.record(stream)
+            s1.synchronize()
+            t = s0.elapsed_time(s1)
+        return n, t
+
+    settle_steps, settle_ms = settle()
     for i in range(W):
         one_step(i)
     torch.cuda.synchronize()
@@ -356,7 +367,10 @@ def _measure(hsa, wl, w, io, K, W, n_sets, detailed):
                      "kernel": "attn_bf16_pipe_kernel" if w.dtype == "bf16" else "attn_f32_kernel"},
     }
     if detailed:
-        # cached-mask steps (mask reused: reorder, attention, restore)
+        # cached-mask steps (mask reused: reorder, attention, restore), after
+        # the clock is settled again (the list bookkeeping above syncs every
+        # step and leaves the GPU idle in between)
+        settle()
         cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
         for i in range(K):
             q, k, v = sets[(i + 1) % n_sets]
@@ -376,6 +390,7 @@ def _measure(hsa, wl, w, io, K, W, n_sets, detailed):
                 L.step(*sets[i], step=0, budget_ratio=wl.budget_ratio(w, 0))
             graphs.append(gph)
         torch.cuda.synchronize()
+        settle()
         for gph in graphs:
             gph.replay()
         torch.cuda.synchronize()
