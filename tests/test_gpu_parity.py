@@ -693,7 +693,7 @@ def test_malformed_lists_are_clamped(hsa, dtype):
         assert torch.equal(tb[0], to[0]) and torch.equal(tb.o_lse, to.o_lse)
 
 
-@pytest.mark.parametrize("B,D", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("B,D", [(64, 64), (128, 128), (64, 128), (128, 64)])
 def test_long_lists_with_growing_logits(hsa, B, D):
     """Long lists (the deferred-value pipeline) on keys whose scale
     grows block by block, with one block 30x larger: the running reference
