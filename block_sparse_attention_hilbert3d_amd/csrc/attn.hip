@@ -17,14 +17,13 @@
 //    next stage's S is computed in the same scheduling region as the current
 //    stage's softmax and value product, so matrix and vector work overlap;
 //  - online softmax in the log2 domain (scale folded into one FMA), keys
-//    beyond a ragged block's real length masked to -inf, and a lazy rescale
-//    that only touches O when a row max grows by more than 2^8;
-//  - lists of 16 or more key blocks use a deferred-value variant: a stage's
-//    exponentials are taken against the running reference without the
-//    stage's own row max, the rounded row sums (every weight is at most its
-//    row's sum) show when the reference is stale, and only then is the max
-//    taken and the stage redone; P.V of a stage runs beside the next
-//    stage's exponentials (fewer vector instructions per stage);
+//    beyond a ragged block's real length masked to -inf;
+//  - deferred values: a stage's exponentials are taken against the running
+//    reference without the stage's own row max, the rounded row sums (every
+//    weight is at most its row's sum) show when the reference is stale, and
+//    only then is the max taken, O rescaled and the stage redone; P.V of a
+//    stage runs beside the next stage's exponentials (fewer vector
+//    instructions per stage than taking each stage's max first);
 //  - P is rounded to bf16 straight from the accumulator layout and used as
 //    the B operand of O^T += V^T P^T; V^T comes from the row-major V tile via
 //    ds_read_b64_tr_b16 (no transpose pass) in the accumulator's key order;
@@ -74,7 +73,7 @@ __device__ __forceinline__ void row_bcast_clamped(int v, int (&tok)[N]) {
 // overlap of matrix and vector work comes from the pipelining alone. With
 // QT = 1 two workgroups of four waves share a CU, two waves per SIMD.
 // IO: 0 reordered Q/K/V/O; 1 token-major Q and O; 2 token-major Q, K, V, O.
-template <int D, int BK, int ST, int QT, bool LSE, int IO, bool DEFER>
+template <int D, int BK, int ST, int QT, bool LSE, int IO>
 __global__ void __launch_bounds__(BK * 2 / QT, QT == 1 ? 2 : 1)
 attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
                       const uint16_t *__restrict__ vp, uint16_t *__restrict__ op,
@@ -94,7 +93,6 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   constexpr int TILE = ST * D;  // elements per stage buffer
   static_assert(BK % ST == 0 && ST % 32 == 0, "stage size");
   static_assert(NW >= 1 && BK % (32 * QT) == 0, "query tiles per wave");
-  constexpr float kLazy = 8.f;
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2 * TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2 * TILE];
 
@@ -188,17 +186,8 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
       for (int i = 0; i < TL::NI; ++i) tok[i] = max(raw[i], 0);
     }
   };
-  // keep entries (c + 1) / NS .. (c + 2) / NS inside the window
+  // keep entries c / NS .. (c + 2) / NS inside the window
   auto slide = [&](int c) {
-    if ((c + 1) / NS - mbase >= 64) {
-      mbase += 64;
-      lo_E = hi_E;
-      fetch(mbase + 64, hi_E);
-      wait_vmcnt<0>();  // settle the window here, not at its first lane read
-    }
-  };
-  // the deferred-value pipeline reads entries c / NS .. (c + 2) / NS
-  auto slide_low = [&](int c) {
     if (c / NS - mbase >= 64) {
       mbase += 64;
       lo_E = hi_E;
@@ -298,86 +287,6 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
           sacc[mt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[qt][ks], sacc[mt][qt], 0, 0, 0);
     }
   };
-  // Mask the ragged tail, then move the reference (rescaling O) if this
-  // tile's max outgrows it by more than 2^8 (lazy rescale).
-  auto mask_and_rescale = [&](f32x16 (&sacc)[MT][QT], int kvalid) {
-    if (kvalid < ST) {
-      const int lim = kvalid - g * 4;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (mt * 32 + (i >> 2) * 8 + (i & 3) >= lim) sacc[mt][qt][i] = -INFINITY;
-    }
-    bool found = false;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float mx = rel_max(sacc, qt);
-      if (__any(mx > kLazy) || noref) {
-        const float tm = m_ref[qt] + mx;
-        const bool fin = tm > -INFINITY;
-        const float m_new = noref ? (fin ? tm : m_ref[qt]) : fmaxf(m_ref[qt], tm);
-        const float alpha = noref ? 1.f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
-        l_run[qt] *= alpha;
-        e_run[qt] *= alpha;
-#pragma unroll
-        for (int md = 0; md < DM; ++md)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[qt][md][i] *= alpha;
-        m_ref[qt] = m_new;
-        found |= fin;
-      }
-    }
-    if (noref && __any(found)) noref = false;
-  };
-  auto exp_pv = [&](const f32x16 (&sacc)[MT][QT], int buf) {
-    float rs[QT], es[QT];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      rs[qt] = 0.f;
-      es[qt] = 0.f;
-    }
-#pragma unroll
-    for (int ks2 = 0; ks2 < PK; ++ks2) {
-      bf16x8 va[DM];
-#pragma unroll
-      for (int md = 0; md < DM; ++md) {
-        lds_i16x4_t *a0 = (lds_i16x4_t *)(vl + buf * TILE * 2 + vofs[md] + ks2 * 16 * CPR * 16);
-        lds_i16x4_t *a1 = (lds_i16x4_t *)(vl + buf * TILE * 2 + vofs[md] + (ks2 * 16 + 8) * CPR * 16);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1);
-        const i16x8_t both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        va[md] = __builtin_bit_cast(bf16x8, both);
-      }
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        bf16x8 pf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = __builtin_amdgcn_exp2f(rel(sacc[ks2 >> 1][qt][(ks2 & 1) * 8 + j], qt));
-          if constexpr (LSE) es[qt] += p;
-          pf[j] = static_cast<__bf16>(p);
-        }
-        const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-        const bf16x2 p01 = {pf[0], pf[1]}, p23 = {pf[2], pf[3]}, p45 = {pf[4], pf[5]}, p67 = {pf[6], pf[7]};
-        rs[qt] = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, rs[qt], false);
-        rs[qt] = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, rs[qt], false);
-        rs[qt] = __builtin_amdgcn_fdot2_f32_bf16(p45, ones, rs[qt], false);
-        rs[qt] = __builtin_amdgcn_fdot2_f32_bf16(p67, ones, rs[qt], false);
-#pragma unroll
-        for (int md = 0; md < DM; ++md)
-          oacc[qt][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[md], pf, oacc[qt][md], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      l_run[qt] += rs[qt];
-      if constexpr (LSE) e_run[qt] += es[qt];
-    }
-  };
-
   // Deferred-value pipeline: the exponentials of stage c are taken against
   // the current reference max without looking at the stage's own max first;
   // their rounded row sums decide afterwards whether the reference is stale
@@ -496,91 +405,6 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
 #pragma unroll
   for (int r = 0; r < RAW; ++r) rn[r] = r0[r] = r1[r] = 0;
 
-  if constexpr (!DEFER) {
-  // Prologue: K(0), V(0) and K(1) in flight, S(0) once all three landed.
-  f32x16 sA[MT][QT], sB[MT][QT];
-  if (nst > 0) {
-    if constexpr (GKV) {
-      stage_rows(0, r0);
-      if (nst > 1) stage_rows(1, r1);
-      wait_vmcnt<0>();
-      int t0[TL::NI];
-      expand_rows(r0, t0);
-      expand_rows(r1, rk);
-      offsets(t0, koff, ok);
-      issue_tile_offs<D, ST, NW>(kbase, ldsK, w, ok);
-      offsets(t0, voff, ov);
-      issue_tile_offs<D, ST, NW>(vbase, ldsV, w, ov);
-      offsets(rk, koff, ok);
-      if (nst > 1) issue_tile_offs<D, ST, NW>(kbase, ldsK + TILE * 2, w, ok);
-      if (nst > 2) stage_rows(2, rn);
-    } else {
-      if constexpr (kPair) eb = entry_packed(0);  // the first even iteration shifts it to ea
-      issue_tile<D, ST, NW>(kbase + stage_ofs(0), ldsK, w, koff);
-      issue_tile<D, ST, NW>(vbase + stage_ofs(0), ldsV, w, voff);
-      if (nst > 1) issue_tile<D, ST, NW>(kbase + stage_ofs(1), ldsK + TILE * 2, w, koff);
-    }
-    // iteration 0 reads K(1) as well, so all three stages must have landed
-    wait_vmcnt<0>();
-    if constexpr (GKV) {
-      offsets(rk, voff, ov);  // V(1)
-      expand_rows(rn, rk);    // K(2)
-      offsets(rk, koff, ok);
-    }
-    __syncthreads();
-    compute_s(sA, 0);
-    mask_and_rescale(sA, stage_valid(0));
-  }
-  // Iteration c: issue K(c+2) and V(c+1); S(c+1) alongside softmax + PV(c);
-  // then wait for this iteration's loads.
-  // (par: c & 1 as a compile-time constant, so LDS buffer offsets are
-  // immediates rather than per-stage address arithmetic)
-  auto body = [&](auto par, int c, f32x16 (&cur)[MT][QT], f32x16 (&nxt)[MT][QT]) {
-    constexpr int P = decltype(par)::value;
-    const bool has1 = c + 1 < nst, has2 = c + 2 < nst;
-    __syncthreads();  // K(c) and V(c-1) buffers are free, K(c+1) and V(c) visible
-    slide(c);
-    // (kPair) K(c+2) is half P of block c/2 + 1; V(c+1) and the length of
-    // stage c+1 are half 1 of block c/2 (P = 0) or half 0 of block c/2 + 1
-    if constexpr (kPair && P == 0) {
-      ea = eb;
-      eb = entry_packed((c >> 1) + 1);
-    }
-    if constexpr (GKV) {
-      if (c + 3 < nst) stage_rows(c + 3, rn);
-      if (has2) issue_tile_offs<D, ST, NW>(kbase, ldsK + P * TILE * 2, w, ok);
-      if (has1) issue_tile_offs<D, ST, NW>(vbase, ldsV + (P ^ 1) * TILE * 2, w, ov);
-    } else if constexpr (kPair) {
-      if (has2) issue_tile<D, ST, NW>(kbase + ofs_of(eb, P), ldsK + P * TILE * 2, w, koff);
-      if (has1) issue_tile<D, ST, NW>(vbase + ofs_of(P == 0 ? ea : eb, P ^ 1), ldsV + (P ^ 1) * TILE * 2, w, voff);
-    } else {
-      if (has2) issue_tile<D, ST, NW>(kbase + stage_ofs(c + 2), ldsK + P * TILE * 2, w, koff);
-      if (has1) issue_tile<D, ST, NW>(vbase + stage_ofs(c + 1), ldsV + (P ^ 1) * TILE * 2, w, voff);
-    }
-    // Unconditional so it shares a scheduling region with exp_pv; on the
-    // last stage it reads an idle buffer (no load in flight) and is unused.
-    compute_s(nxt, P ^ 1);
-    exp_pv(cur, P);
-    // LLVM's interleave strategy for matrix and exponential instructions
-    // (measured ~2 % faster than the default schedule here)
-    __builtin_amdgcn_iglp_opt(3);
-    // an empty mask on the last stage leaves the running max untouched
-    int v1 = 0;
-    if constexpr (kPair) v1 = valid_of(P == 0 ? ea : eb, P ^ 1);
-    else if (has1) v1 = stage_valid(c + 1);
-    mask_and_rescale(nxt, has1 ? v1 : 0);
-    wait_vmcnt<0>();
-    if constexpr (GKV) {
-      offsets(rk, voff, ov);  // V(c+2) reads K(c+2)'s rows
-      expand_rows(rn, rk);    // K(c+3)
-      offsets(rk, koff, ok);
-    }
-  };
-  for (int c = 0; c < nst; c += 2) {
-    body(std::integral_constant<int, 0>{}, c, sA, sB);
-    if (c + 1 < nst) body(std::integral_constant<int, 1>{}, c + 1, sB, sA);
-  }
-  } else {
   // Prologue: K(0) and K(1) in flight, S(0) once both landed. Gathered
   // K/V: at the start of iteration c, ok holds K(c+2)'s offsets and rk its
   // rows, rk1 the rows of K(c+1) (which V(c+1) reuses), ov V(c)'s offsets
@@ -637,7 +461,7 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     constexpr int P = decltype(par)::value;  // c & 1
     const bool has1 = c + 1 < nst, has2 = c + 2 < nst;
     __syncthreads();  // K(c) and V(c-2) buffers are free, K(c+1) and V(c-1) visible
-    slide_low(c);
+    slide(c);
     // (kPair) K(c+2) is half P of block c/2 + 1, V(c) half P of block c/2;
     // the length of stage c+1 is half 1 of block c/2 (P = 0) or half 0 of
     // block c/2 + 1 (P = 1)
@@ -660,10 +484,10 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     float rs[QT], es[QT];
     exps(cur, pcur, rs, es);
     if constexpr (decltype(with_pv)::value) pv_only(pprev, P ^ 1);
-    // LLVM's interleave strategy 1 here (strategy 3, kept for the eager
-    // pipeline, measured 0.8-1.6 % slower on this instruction mix); with
-    // the log-sum-exp sums the register budget is tighter and strategy 1
-    // spills into the loop, so that variant keeps strategy 3
+    // LLVM's interleave strategy 1 here (strategy 3 measured 0.8-1.6 %
+    // slower on this instruction mix); with the log-sum-exp sums the
+    // register budget is tighter and strategy 1 spills into the loop, so
+    // that variant keeps strategy 3
     if constexpr (LSE) __builtin_amdgcn_iglp_opt(3);
     else __builtin_amdgcn_iglp_opt(1);
     settle(cur, pcur, rs, es);
@@ -689,7 +513,6 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     __syncthreads();  // V(nst-1) visible
     if ((nst - 1) & 1) pv_only(pY, (nst - 1) & 1);
     else pv_only(pX, (nst - 1) & 1);
-  }
   }
 
 #pragma unroll
@@ -947,15 +770,10 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                    *v = static_cast<const uint16_t *>(vp);
     uint16_t *o = static_cast<uint16_t *>(op);
     const dim3 block(B * 2);
-#define HSA_ATTN_BF16_D(DD, BB, QQ, L, IO, DF)                                                \
-  launch_k(hsa::attn_bf16_pipe_kernel<DD, BB, (QQ == 2 ? 32 : 64), QQ, L, IO, DF>, grid, dim3(BB * 2 / QQ), stream, \
+#define HSA_ATTN_BF16(DD, BB, QQ, L, IO)                                                        \
+  launch_k(hsa::attn_bf16_pipe_kernel<DD, BB, (QQ == 2 ? 32 : 64), QQ, L, IO>, grid, dim3(BB * 2 / QQ), stream, \
            q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, \
            kv_stride, o_stride)
-#define HSA_ATTN_BF16(DD, BB, QQ, L, IO)                                   \
-  do {                                                                     \
-    if (defer) HSA_ATTN_BF16_D(DD, BB, QQ, L, IO, true);                   \
-    else HSA_ATTN_BF16_D(DD, BB, QQ, L, IO, false);                        \
-  } while (0)
 #define HSA_ATTN_BF16_IO(DD, BB)                                      \
   do {                                                                \
     if (io == 2) { if (L) HSA_ATTN_BF16(DD, BB, 1, true, 2); else HSA_ATTN_BF16(DD, BB, 1, false, 2); }      \
@@ -964,17 +782,12 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
   } while (0)
     const int io = perm == nullptr ? 0 : (kv_stride > 0 ? 2 : 1);
     const bool L = lse != nullptr;
-    // Lists of 16 or more blocks take the deferred-value pipeline (no row
-    // max per stage; 0.5-2 % faster); very short lists keep the eager one,
-    // whose prologue and epilogue are shorter.
-    const bool defer = max_kv >= 16;
     if (D == 128 && B == 128) HSA_ATTN_BF16_IO(128, 128);
     else if (D == 64 && B == 128) HSA_ATTN_BF16_IO(64, 128);
     else if (D == 128 && B == 64) HSA_ATTN_BF16_IO(128, 64);
     else HSA_ATTN_BF16_IO(64, 64);
 #undef HSA_ATTN_BF16_IO
 #undef HSA_ATTN_BF16
-#undef HSA_ATTN_BF16_D
   } else {
     const float *q = static_cast<const float *>(qp), *k = static_cast<const float *>(kp),
                 *v = static_cast<const float *>(vp);

@@ -283,11 +283,8 @@ hsa_status_t hsa_select_noalloc(const float *S, int32_t nh, int32_t nb, const hs
  * probabilities are rounded to bf16 for the value product and the output is
  * rounded to bf16 (nearest even); the output bits do not depend on whether
  * lse is requested. F32 computes in float throughout.
- * Two bf16 pipelines: max_kv >= 16 takes the deferred-value one (a stage's
- * weights are formed against the running max and checked afterwards),
- * shorter list capacities the eager one (row max first); both compute the
- * same softmax and may differ in the last bit of a rounded output. Results
- * are deterministic for a given max_kv.
+ * Results are deterministic, and the same lists give the same bits in
+ * buffers of any capacity max_kv.
  */
 hsa_status_t hsa_attn(const void *qp, const void *kp, const void *vp, void *op, float *lse,
                       const int32_t *blk_len, const int32_t *kv_idx, const int32_t *kv_cnt,
