@@ -40,9 +40,8 @@
 // K/V the direct LDS loads also fetch key/value rows from the token-major
 // tensors (each lane's source rows for a stage are looked up in the map one
 // iteration ahead), so no reordered copy of Q, K or V is made at all.
-// f32 kernel: a plain online-softmax loop with K/V tiles in LDS, for float
-// inputs (small shapes); on small tiles four threads share each query, each
-// over a quarter of the keys, merged at the end.
+// f32 kernel: the same block-sparse online softmax on the float32 matrix
+// cores (16x16x4 products, a wave per 16 queries), for float inputs.
 #include <type_traits>
 
 #include "common.h"
@@ -549,146 +548,140 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   }
 }
 
-// Float kernel: one thread per (query, key split); KS splits share each key
-// tile (split j takes keys j, j + KS, ...) with their own running max, sum
-// and output row, merged through LDS at the end. KS = 4 for small tiles
-// (short serial chains for the latency-bound small shapes), 1 otherwise.
+// Float kernel on the float32 matrix cores (v_mfma_f32_16x16x4_f32). A wave
+// owns 16 queries; K and V of each listed block pass through LDS in chunks of
+// KC keys (K row-major with its 16-byte chunks XOR-swizzled by row, V stored
+// transposed with padded rows, so both operand reads are conflict-free).
+// Per 16-key tile: S^T = K Q^T (Q pre-scaled to log2 units and held in
+// registers, lane group g owning dimensions 16m + 4g .. + 3), each lane then
+// holds keys 4g .. 4g + 3 of its query; online softmax in the log2 domain
+// with O rescaled only when a query's max grows by more than 2^8; O^T +=
+// V^T P^T in four steps whose keys are 4g + r (r = the step), so every lane
+// feeds its own weights. Chunks past a block's real keys are skipped.
 template <int D, int BK>
-struct F32Split {
-  static constexpr int KS = (BK * D <= 64 * 64) ? 4 : 1;
-};
-
-template <int D, int BK>
-__global__ void __launch_bounds__((BK * F32Split<D, BK>::KS))
+__global__ void __launch_bounds__(BK * 4)
 attn_f32_kernel(const float *__restrict__ qp, const float *__restrict__ kp,
                 const float *__restrict__ vp, float *__restrict__ op, float *__restrict__ lse,
                 const int32_t *__restrict__ blk_len, const int32_t *__restrict__ kv_idx,
                 const int32_t *__restrict__ kv_cnt, const int32_t *__restrict__ order, int max_kv,
                 int kv_shared, int nh, int nb, float scale_log2, const int32_t *__restrict__ perm,
                 int64_t q_stride, int64_t kv_stride, int64_t o_stride) {
-  constexpr int KS = F32Split<D, BK>::KS;
-  constexpr int NT = BK * KS;
-  __shared__ __attribute__((aligned(16))) float sK[BK * D];
-  __shared__ __attribute__((aligned(16))) float sV[BK * D];
-  __shared__ float mrg[KS > 1 ? (KS - 1) * BK * (D + 2) : 1];  // [KS-1][BK][D + 2]
+  constexpr int NT = BK * 4;    // BK / 16 waves
+  constexpr int KC = 32;        // keys per LDS chunk
+  constexpr int DQ = D / 4;     // MFMA k-steps of S
+  constexpr int DT = D / 16;    // 16-wide d tiles of O
+  constexpr int VS = KC + 4;    // V^T row stride (floats): rows 144 B apart hit distinct banks
+  constexpr float kLazy = 8.f;
+  static_assert(BK % KC == 0 && D % 16 == 0, "tile shapes");
+  __shared__ __attribute__((aligned(16))) float sK[KC * D];
+  __shared__ __attribute__((aligned(16))) float sVt[D * VS];
   int h, I;
   block_of(blockIdx.x, order, kv_shared, nh, nb, h, I);
-  const int tid = threadIdx.x;
-  const int row = tid % BK, split = tid / BK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ul = lane & 15, g = lane >> 4;
   const int64_t head_off = static_cast<int64_t>(h) * nb * BK * D;
-  const int qslot = I * BK + row;
+  const int qrow = w * 16 + ul;
+  const int qslot = I * BK + qrow;
   // token-layout I/O when perm is given (pad slots: zero query, no store)
   const int tok = perm ? perm[qslot] : 0;
   const int64_t qofs = perm ? static_cast<int64_t>(max(tok, 0)) * q_stride + h * D
                             : head_off + static_cast<int64_t>(qslot) * D;
   const int64_t oofs = perm ? static_cast<int64_t>(max(tok, 0)) * o_stride + h * D
                             : head_off + static_cast<int64_t>(qslot) * D;
-  float q[D], o[D];
+  float qreg[DQ];
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    q[d] = (perm && tok < 0) ? 0.f : qp[qofs + d] * scale_log2;
-    o[d] = 0.f;
+  for (int m = 0; m < D / 16; ++m) {
+    const float4 t = *reinterpret_cast<const float4 *>(qp + qofs + 16 * m + 4 * g);
+    const float z = (perm && tok < 0) ? 0.f : scale_log2;
+    qreg[4 * m] = t.x * z; qreg[4 * m + 1] = t.y * z; qreg[4 * m + 2] = t.z * z; qreg[4 * m + 3] = t.w * z;
   }
-  float m = -1e30f, l = 0.f;
+  f32x4 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;  // this lane's query; l over this lane's keys
   const int64_t lrow = kv_shared ? static_cast<int64_t>(I) : static_cast<int64_t>(h) * nb + I;
   const int cnt = min(max(kv_cnt[lrow], 0), max_kv);
   const int32_t *list = kv_idx + lrow * max_kv;
   for (int c = 0; c < cnt; ++c) {
     const int J = min(max(list[c], 0), nb - 1);
-    const int kvalid = blk_len[J];
-    if (perm && kv_stride > 0) {  // K/V rows gathered from the token-major tensors
-      for (int i = tid; i < BK * D / 4; i += NT) {
+    const int kvalid = min(max(blk_len[J], 0), BK);
+    for (int k0 = 0; k0 < kvalid; k0 += KC) {
+      __syncthreads();  // the previous chunk's reads are done
+      for (int i = tid; i < KC * D / 4; i += NT) {
         const int r = i / (D / 4), c4 = i - r * (D / 4);
-        const int64_t src = static_cast<int64_t>(max(perm[J * BK + r], 0)) * kv_stride + h * D + c4 * 4;
-        reinterpret_cast<float4 *>(sK)[i] = *reinterpret_cast<const float4 *>(kp + src);
-        reinterpret_cast<float4 *>(sV)[i] = *reinterpret_cast<const float4 *>(vp + src);
+        int64_t src;
+        if (perm && kv_stride > 0)  // K/V rows gathered from the token-major tensors
+          src = static_cast<int64_t>(max(perm[J * BK + k0 + r], 0)) * kv_stride + h * D + c4 * 4;
+        else
+          src = head_off + static_cast<int64_t>(J * BK + k0 + r) * D + c4 * 4;
+        const float4 kv4 = *reinterpret_cast<const float4 *>(kp + src);
+        const float4 vv4 = *reinterpret_cast<const float4 *>(vp + src);
+        *reinterpret_cast<float4 *>(&sK[r * D + ((c4 ^ (r & 15)) * 4)]) = kv4;
+        sVt[(4 * c4 + 0) * VS + r] = vv4.x;
+        sVt[(4 * c4 + 1) * VS + r] = vv4.y;
+        sVt[(4 * c4 + 2) * VS + r] = vv4.z;
+        sVt[(4 * c4 + 3) * VS + r] = vv4.w;
       }
-    } else {
-      const float4 *ks = reinterpret_cast<const float4 *>(kp + head_off + static_cast<int64_t>(J) * BK * D);
-      const float4 *vs = reinterpret_cast<const float4 *>(vp + head_off + static_cast<int64_t>(J) * BK * D);
-      for (int i = tid; i < BK * D / 4; i += NT) {
-        reinterpret_cast<float4 *>(sK)[i] = ks[i];
-        reinterpret_cast<float4 *>(sV)[i] = vs[i];
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < KC / 16; ++t) {
+        const int kt0 = k0 + 16 * t;
+        if (kt0 >= kvalid) break;
+        float kreg[DQ];
+#pragma unroll
+        for (int m = 0; m < D / 16; ++m) {
+          const float4 k4 = *reinterpret_cast<const float4 *>(&sK[(16 * t + ul) * D + (((4 * m + g) ^ ul) * 4)]);
+          kreg[4 * m] = k4.x; kreg[4 * m + 1] = k4.y; kreg[4 * m + 2] = k4.z; kreg[4 * m + 3] = k4.w;
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < DQ; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kreg[j], qreg[j], acc, 0, 0, 0);
+        float sv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[r] = (kt0 + 4 * g + r < kvalid) ? acc[r] : -INFINITY;
+        // the tile's max for this query (its keys sit in the four lane groups)
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (mx > m_run + kLazy) {  // (always on the first tile: m_run = -inf)
+          const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+          m_run = mx;
+        }
+        float pv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pv[r] = __builtin_amdgcn_exp2f(sv[r] - m_run);
+          l_run += pv[r];
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const float4 vf = *reinterpret_cast<const float4 *>(&sVt[(16 * dt + ul) * VS + 16 * t + 4 * g]);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf.x, pv[0], oacc[dt], 0, 0, 0);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf.y, pv[1], oacc[dt], 0, 0, 0);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf.z, pv[2], oacc[dt], 0, 0, 0);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf.w, pv[3], oacc[dt], 0, 0, 0);
+        }
       }
     }
-    __syncthreads();
-    // this split's keys split, split + KS, ...: two at a time (two dot
-    // chains, one max update and one pass over O per pair), then the tail
-    int key = split;
-    for (; key + KS < kvalid; key += 2 * KS) {
-      const int k1 = key + KS;
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        s0 = fmaf(q[d], sK[key * D + d], s0);
-        s1 = fmaf(q[d], sK[k1 * D + d], s1);
-      }
-      const float mx = fmaxf(s0, s1);
-      if (mx > m) {
-        const float a = exp2f(m - mx);
-        l *= a;
-#pragma unroll
-        for (int d = 0; d < D; ++d) o[d] *= a;
-        m = mx;
-      }
-      const float p0 = exp2f(s0 - m), p1 = exp2f(s1 - m);
-      l += p0 + p1;
-#pragma unroll
-      for (int d = 0; d < D; ++d) o[d] = fmaf(p1, sV[k1 * D + d], fmaf(p0, sV[key * D + d], o[d]));
-    }
-    for (; key < kvalid; key += KS) {
-      float s = 0.f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) s = fmaf(q[d], sK[key * D + d], s);
-      if (s > m) {
-        const float a = exp2f(m - s);
-        l *= a;
-#pragma unroll
-        for (int d = 0; d < D; ++d) o[d] *= a;
-        m = s;
-      }
-      const float p = exp2f(s - m);
-      l += p;
-#pragma unroll
-      for (int d = 0; d < D; ++d) o[d] = fmaf(p, sV[key * D + d], o[d]);
-    }
-    __syncthreads();
   }
-  if constexpr (KS > 1) {
-    // splits 1.. hand (m, l, o) to split 0
-    if (split > 0) {
-      float *dst = mrg + (static_cast<int64_t>(split - 1) * BK + row) * (D + 2);
-      dst[0] = m;
-      dst[1] = l;
-#pragma unroll
-      for (int d = 0; d < D; ++d) dst[2 + d] = o[d];
-    }
-    __syncthreads();
-    if (split > 0) return;
-    float mt = m;
-#pragma unroll
-    for (int j = 0; j < KS - 1; ++j) mt = fmaxf(mt, mrg[(static_cast<int64_t>(j) * BK + row) * (D + 2)]);
-    const float a0 = exp2f(m - mt);
-    l *= a0;
-#pragma unroll
-    for (int d = 0; d < D; ++d) o[d] *= a0;
-#pragma unroll
-    for (int j = 0; j < KS - 1; ++j) {
-      const float *src = mrg + (static_cast<int64_t>(j) * BK + row) * (D + 2);
-      const float a = exp2f(src[0] - mt);
-      l = fmaf(src[1], a, l);
-#pragma unroll
-      for (int d = 0; d < D; ++d) o[d] = fmaf(src[2 + d], a, o[d]);
-    }
-    m = mt;
-  }
-  const bool real = row < blk_len[I];
-  const float inv = (real && l > 0.f) ? 1.f / l : 0.f;
+  // the four lane groups' sums, added in the same order on every lane of a query
+  const float l_pair = l_run + __shfl_xor(l_run, 16, 64);
+  const float l_tot = l_pair + __shfl_xor(l_pair, 32, 64);
+  const bool real = qrow < blk_len[I];
+  const float inv = (real && l_tot > 0.f) ? 1.f / l_tot : 0.f;
   if (!perm || (real && tok >= 0)) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) op[oofs + d] = o[d] * inv;
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4 *>(op + oofs + 16 * dt + 4 * g) =
+          make_float4(oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv);
   }
-  if (lse != nullptr) lse[static_cast<int64_t>(h) * nb * BK + qslot] = real ? (m + log2f(l)) * 0.6931471805599453f : 0.f;
+  if (lse != nullptr && g == 0)
+    lse[static_cast<int64_t>(h) * nb * BK + qslot] =
+        (real && l_tot > 0.f) ? (m_run + log2f(l_tot)) * 0.6931471805599453f : 0.f;
 }
 
 // Counting sort of each head's list rows by length, longest first (one
@@ -792,7 +785,7 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
     const float *q = static_cast<const float *>(qp), *k = static_cast<const float *>(kp),
                 *v = static_cast<const float *>(vp);
     float *o = static_cast<float *>(op);
-    const dim3 block(B * ((D * B <= 64 * 64) ? 4 : 1));  // F32Split<D, B>::KS threads per query
+    const dim3 block(B * 4);  // B / 16 waves of 16 queries
     if (D == 128 && B == 128) launch_k(hsa::attn_f32_kernel<128, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
     else if (D == 64 && B == 128) launch_k(hsa::attn_f32_kernel<64, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
     else if (D == 128 && B == 64) launch_k(hsa::attn_f32_kernel<128, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
