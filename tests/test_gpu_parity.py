@@ -951,16 +951,18 @@ def test_attn_bwd_wan_shape_sampled(hsa):
 
 # ---------------------------------------------------------------- edge cases
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("cap", [4, 16])
-def test_empty_lists_forward_backward(hsa, cap):
+def test_empty_lists_forward_backward(hsa, cap, dtype):
     """Query blocks with an empty list (kv_cnt = 0) attend to nothing: their
     output rows and log-sum-exp are zero, and they pass no gradient; the
     other rows match the oracle (per-head and shared lists, with and without
-    a processing order, list capacities 4 and 16)."""
-    _say(f"empty lists, capacity {cap}")
+    a processing order, list capacities 4 and 16, bf16 and float inputs)."""
+    _say(f"empty lists, capacity {cap}, {dtype}")
     T, H, W, nh, B, D = 4, 16, 16, 2, 64, 64
     g = torch.Generator().manual_seed(41)
-    q, k, v, do = (torch.randn((1, T * H * W, nh, D), generator=g).to(torch.bfloat16) for _ in range(4))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v, do = (torch.randn((1, T * H * W, nh, D), generator=g).to(tdt) for _ in range(4))
     perm, blk_len = hsa.hsa_plan(T, H, W, "hilbert", B, device=dev())
     nb = perm.numel() // B
     qp, kp, vp = hsa.hsa_perm([x.to(dev()) for x in (q, k, v)], perm, perm.numel())
@@ -983,8 +985,8 @@ def test_empty_lists_forward_backward(hsa, cap):
             dq, dk, dv = hsa.hsa_attn_bwd(qp, kp, vp, op, dop, lse, blk_len, kv_idx, kv_cnt, B)
             torch.cuda.synchronize()
             ref_op, ref_lse = oracle.attn_blocks(*(oracle.gather(x, p) for x in (q, k, v)), p, B, idx, cnt)
-            assert np.abs(to_np(op) - ref_op).max() <= TOL["bf16"]
-            assert np.abs(to_np(op0) - ref_op).max() <= TOL["bf16"]
+            assert np.abs(to_np(op) - ref_op).max() <= TOL[dtype]
+            assert np.abs(to_np(op0) - ref_op).max() <= TOL[dtype]
             assert np.abs(to_np(lse) - ref_lse).max() <= 1e-3
             empty = np.repeat(cnt[0 if G == 1 else slice(None)] == 0, B, axis=-1)
             empty = np.broadcast_to(empty, (nh, nb * B)) if G == 1 else empty
@@ -998,7 +1000,7 @@ def test_empty_lists_forward_backward(hsa, cap):
             assert torch.equal(rt.o_lse, hsa.hsa_unperm(op, perm, T * H * W))
             ref = oracle.attn_blocks_bwd(*(oracle.gather(x, p) for x in (q, k, v, do)), p, B, idx, cnt)
             for a, r in zip((dq, dk, dv), ref):
-                assert np.abs(to_np(a) - r).max() <= BWD_TOL["bf16"] * max(float(np.abs(r).max()), 1e-6)
+                assert np.abs(to_np(a) - r).max() <= BWD_TOL[dtype] * max(float(np.abs(r).max()), 1e-6)
 
 
 @pytest.mark.parametrize("shape,order,B", [((1, 1024, 1024), "hilbert", 128), ((1024, 1, 1), "hilbert", 64),
