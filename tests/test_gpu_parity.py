@@ -793,6 +793,43 @@ def test_lists_with_single_and_repeated_blocks(hsa):
     assert np.abs(to_np(r.o_lse) - ref).max() <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_short_key_blocks_take_one_stage(hsa, D):
+    """Frame tiles whose real keys fit in one 64-key stage (150-token frames:
+    a tile of 128 and one of 22) and tiles of 72 keys (two stages, the second
+    of 8), in lists of 1 .. nb entries (the kernel's list window slides at 64
+    and 128 entries): equal to the oracle, with and without the log-sum-exp,
+    and bit for bit equal to the gathered-K/V form."""
+    _say(f"short key blocks, D={D}")
+    B, nh = 128, 2
+    for (T, H, W) in ((66, 10, 15), (3, 10, 20)):
+        g = torch.Generator().manual_seed(D + T)
+        N = T * H * W
+        q, k, v = (torch.randn((1, N, nh, D), generator=g).to(torch.bfloat16) for _ in range(3))
+        perm, blk_len = hsa.hsa_plan(T, H, W, "frame", B, device=dev())
+        nb = perm.numel() // B
+        rng = np.random.default_rng(T * 7 + D)
+        lens = [1, 2, 63, 64, 65, 127, 128, 129, nb]
+        cnt = np.array([[lens[(h * nb + i) % len(lens)] if lens[(h * nb + i) % len(lens)] <= nb
+                         else int(rng.integers(1, nb + 1)) for i in range(nb)] for h in range(nh)],
+                       dtype=np.int32)
+        idx = np.full((nh, nb, nb), -1, dtype=np.int32)
+        for h in range(nh):
+            for i in range(nb):
+                idx[h, i, :cnt[h, i]] = np.sort(rng.choice(nb, cnt[h, i], replace=False))
+        qd, kd, vd = (x.to(dev()) for x in (q, k, v))
+        kv_idx, kv_cnt = torch.from_numpy(idx).to(dev()), torch.from_numpy(cnt).to(dev())
+        _, kp, vp = hsa.hsa_perm([qd, kd, vd], perm, perm.numel())
+        r = _attn(hsa.hsa_attn_tokens, qd, kp, vp, perm, blk_len, kv_idx, kv_cnt, B)
+        rg = _attn(hsa.hsa_attn_tokens, qd, kd, vd, perm, blk_len, kv_idx, kv_cnt, B)
+        torch.cuda.synchronize()
+        assert torch.equal(r[0], rg[0]) and torch.equal(r[1], rg[1])
+        p = perm.cpu().numpy().astype(np.int64)
+        ref, ref_lse = oracle.attn_blocks(*(oracle.gather(x, p) for x in (q, k, v)), p, B, idx, cnt)
+        ref_tok = oracle.scatter(ref, p, N)
+        assert np.abs(to_np(r[0]) - ref_tok).max() <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("G,nb,max_kv", [(3, 64, 64), (24, 929, 929), (1, 793, 273), (5, 7, 4095)])
 def test_attn_order_longest_first(hsa, G, nb, max_kv):
     """The processing order is a permutation of the list rows that keeps each
