@@ -72,7 +72,8 @@ __device__ __forceinline__ void row_bcast_clamped(int v, int (&tok)[N]) {
 // overlap of matrix and vector work comes from the pipelining alone. With
 // QT = 1 two workgroups of four waves share a CU, two waves per SIMD.
 // IO: 0 reordered Q/K/V/O; 1 token-major Q and O; 2 token-major Q, K, V, O.
-template <int D, int BK, int ST, int QT, bool LSE, int IO>
+// WK: walk the stages, leaving out empty ones (below).
+template <int D, int BK, int ST, int QT, bool LSE, int IO, bool WK = false>
 __global__ void __launch_bounds__(BK * 2 / QT, QT == 1 ? 2 : 1)
 attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restrict__ kp,
                       const uint16_t *__restrict__ vp, uint16_t *__restrict__ op,
@@ -152,10 +153,34 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   auto valid_of = [&](int e, int half) { return min(max(static_cast<int>(e & 255) - half * ST, 0), ST); };
   auto stage_ofs = [&](int t) { return ofs_of(entry_packed(t / NS), t % NS); };
   auto stage_valid = [&](int t) { return valid_of(entry_packed(t / NS), t % NS); };
-  // With two stages per block and contiguous tiles, iteration c only needs
-  // the entries of blocks c/2 and c/2 + 1 (ea, eb): read once per block, at
-  // even iterations, instead of once per use.
-  constexpr bool kPair = NS == 2 && !GKV;
+  // WK, with two stages per block and contiguous tiles: the stages are
+  // walked block by block, and a block's second stage is left out when its
+  // real keys fit in the first (a frame's last tile). That stage would only
+  // add masked keys, i.e. zero weights and an unchanged O, so the outputs
+  // are those of the full stage sequence. At the start of iteration c the
+  // walk holds stage c (entry wE0, half wH0; wX0: it exists) and stage c+1
+  // (wE1, wH1 at list position wB1; wX1); each iteration steps once, to
+  // stage c+2, reading at most one new entry. The walk costs each stage a
+  // few scalar instructions, so it is compiled only where such tiles are
+  // expected (the launch picks it for lists shared by all heads: the frame
+  // masks).
+  constexpr bool kWalk = WK && NS == 2 && !GKV;
+  int wE0 = 0, wH0 = 0, wE1 = 0, wH1 = 0, wB1 = 0;
+  bool wX0 = false, wX1 = false;
+  // the stage after (e, half) at list position b: its entry, half and
+  // position; false if there is none
+  auto walk_next = [&](int e, int half, int b, int &e2, int &h2, int &b2) {
+    const bool second = half == 0 && (e & 255) > ST;
+    const int en = entry_packed(b + 1);  // past the list: unused
+    e2 = second ? e : en;
+    h2 = second ? 1 : 0;
+    b2 = second ? b : b + 1;
+    return second || b + 1 < cnt;
+  };
+  // Otherwise, with two stages per block and contiguous tiles, iteration c
+  // only needs the entries of blocks c/2 and c/2 + 1 (ea, eb): read once per
+  // block, at even iterations, instead of once per use.
+  constexpr bool kPair = NS == 2 && !GKV && !kWalk;
   int ea = 0, eb = 0;
   // Gathered K/V: the token rows this lane's loads of stage t read. With
   // D = 128 a 16-lane row of the wave fills one tile row per load, so each
@@ -192,6 +217,15 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
       lo_E = hi_E;
       fetch(mbase + 64, hi_E);
       wait_vmcnt<0>();  // settle the window here, not at its first lane read
+    }
+  };
+  // (kWalk) keep list positions b .. b + 1 inside the window
+  auto slide_to = [&](int b) {
+    if (b - mbase >= 64) {
+      mbase += 64;
+      lo_E = hi_E;
+      fetch(mbase + 64, hi_E);
+      wait_vmcnt<0>();
     }
   };
 
@@ -428,9 +462,17 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
       offsets(t0, voff, ov);  // V(0)
       if (nst > 2) stage_rows(2, rn);
     } else {
-      if constexpr (kPair) eb = entry_packed(0);  // the first even iteration shifts it to ea
-      issue_tile<D, ST, NW>(kbase + stage_ofs(0), ldsK, w, koff);
-      if (nst > 1) issue_tile<D, ST, NW>(kbase + stage_ofs(1), ldsK + TILE * 2, w, koff);
+      if constexpr (kWalk) {
+        wE0 = entry_packed(0);
+        wX0 = true;
+        wX1 = walk_next(wE0, 0, 0, wE1, wH1, wB1);
+        issue_tile<D, ST, NW>(kbase + ofs_of(wE0, 0), ldsK, w, koff);
+        if (wX1) issue_tile<D, ST, NW>(kbase + ofs_of(wE1, wH1), ldsK + TILE * 2, w, koff);
+      } else {
+        if constexpr (kPair) eb = entry_packed(0);  // the first even iteration shifts it to ea
+        issue_tile<D, ST, NW>(kbase + stage_ofs(0), ldsK, w, koff);
+        if (nst > 1) issue_tile<D, ST, NW>(kbase + stage_ofs(1), ldsK + TILE * 2, w, koff);
+      }
     }
     wait_vmcnt<0>();
     if constexpr (GKV) {
@@ -439,7 +481,8 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     }
     __syncthreads();
     compute_s(sA, 0);
-    mask_tail(sA, stage_valid(0));
+    if constexpr (kWalk) mask_tail(sA, valid_of(wE0, 0));
+    else mask_tail(sA, stage_valid(0));
     // the first stage's own row max as the reference (no recomputation);
     // a stage without a real key leaves noref set
     bool found = false;
@@ -455,12 +498,20 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   }
   // Iteration c: issue K(c+2) and V(c); S(c+1), the exponentials of stage c
   // and P.V of stage c-1 in one region; then settle stage c.
+  int last = 0;  // (kWalk) the last stage run
   auto body2 = [&](auto with_pv, auto par, int c, f32x16 (&cur)[MT][QT], f32x16 (&nxt)[MT][QT],
                    bf16x8 (&pprev)[QT][PK], bf16x8 (&pcur)[QT][PK]) {
     constexpr int P = decltype(par)::value;  // c & 1
-    const bool has1 = c + 1 < nst, has2 = c + 2 < nst;
+    bool has1 = c + 1 < nst, has2 = c + 2 < nst;
     __syncthreads();  // K(c) and V(c-2) buffers are free, K(c+1) and V(c-1) visible
-    slide(c);
+    int wE2 = 0, wH2 = 0, wB2 = 0;  // (kWalk) stage c+2
+    if constexpr (kWalk) {
+      slide_to(wB1);
+      has1 = wX1;
+      has2 = wX1 && walk_next(wE1, wH1, wB1, wE2, wH2, wB2);
+    } else {
+      slide(c);
+    }
     // (kPair) K(c+2) is half P of block c/2 + 1, V(c) half P of block c/2;
     // the length of stage c+1 is half 1 of block c/2 (P = 0) or half 0 of
     // block c/2 + 1 (P = 1)
@@ -472,6 +523,9 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
       if (c + 3 < nst) stage_rows(c + 3, rn);
       if (has2) issue_tile_offs<D, ST, NW>(kbase, ldsK + P * TILE * 2, w, ok);
       issue_tile_offs<D, ST, NW>(vbase, ldsV + P * TILE * 2, w, ov);
+    } else if constexpr (kWalk) {
+      if (has2) issue_tile<D, ST, NW>(kbase + ofs_of(wE2, wH2), ldsK + P * TILE * 2, w, koff);
+      issue_tile<D, ST, NW>(vbase + ofs_of(wE0, wH0), ldsV + P * TILE * 2, w, voff);
     } else if constexpr (kPair) {
       if (has2) issue_tile<D, ST, NW>(kbase + ofs_of(eb, P), ldsK + P * TILE * 2, w, koff);
       issue_tile<D, ST, NW>(vbase + ofs_of(ea, P), ldsV + P * TILE * 2, w, voff);
@@ -492,10 +546,21 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
     if constexpr (LSE) __builtin_amdgcn_iglp_opt(3);
     settle(cur, pcur, rs, es);
     int v1 = 0;
-    if constexpr (kPair) v1 = valid_of(P == 0 ? ea : eb, P ^ 1);
+    if constexpr (kWalk) v1 = valid_of(wE1, wH1);
+    else if constexpr (kPair) v1 = valid_of(P == 0 ? ea : eb, P ^ 1);
     else if (has1) v1 = stage_valid(c + 1);
     mask_tail(nxt, has1 ? v1 : 0);
     wait_vmcnt<0>();
+    if constexpr (kWalk) {
+      wE0 = wE1;
+      wH0 = wH1;
+      wX0 = wX1;
+      wE1 = wE2;
+      wH1 = wH2;
+      wB1 = wB2;
+      wX1 = has2;
+      last = c;
+    }
     if constexpr (GKV) {
       offsets(rk1, voff, ov);  // V(c+1) reads K(c+1)'s rows
 #pragma unroll
@@ -504,15 +569,25 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
       offsets(rk, koff, ok);
     }
   };
+  // stage c exists (at the top of iteration c): c < nst, or the walk's flag
+  auto more = [&](int c) {
+    if constexpr (kWalk) return wX0;
+    else return c < nst;
+  };
   if (nst > 0) body2(std::false_type{}, std::integral_constant<int, 0>{}, 0, sA, sB, pY, pX);
-  for (int c = 1; c < nst; c += 2) {
+  for (int c = 1; more(c); c += 2) {
     body2(std::true_type{}, std::integral_constant<int, 1>{}, c, sB, sA, pX, pY);
-    if (c + 1 < nst) body2(std::true_type{}, std::integral_constant<int, 0>{}, c + 1, sA, sB, pY, pX);
+    if (more(c + 1)) body2(std::true_type{}, std::integral_constant<int, 0>{}, c + 1, sA, sB, pY, pX);
   }
   if (nst > 0) {
-    __syncthreads();  // V(nst-1) visible
-    if ((nst - 1) & 1) pv_only(pY, (nst - 1) & 1);
-    else pv_only(pX, (nst - 1) & 1);
+    __syncthreads();  // V of the last stage visible
+    if constexpr (kWalk) {
+      if (last & 1) pv_only(pY, 1);
+      else pv_only(pX, 0);
+    } else {
+      if ((nst - 1) & 1) pv_only(pY, (nst - 1) & 1);
+      else pv_only(pX, (nst - 1) & 1);
+    }
   }
 
 #pragma unroll
@@ -764,18 +839,29 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                    *v = static_cast<const uint16_t *>(vp);
     uint16_t *o = static_cast<uint16_t *>(op);
     const dim3 block(B * 2);
-#define HSA_ATTN_BF16(DD, BB, QQ, L, IO)                                                        \
-  launch_k(hsa::attn_bf16_pipe_kernel<DD, BB, (QQ == 2 ? 32 : 64), QQ, L, IO>, grid, dim3(BB * 2 / QQ), stream, \
+#define HSA_ATTN_BF16(DD, BB, QQ, L, IO, WK)                                                    \
+  launch_k(hsa::attn_bf16_pipe_kernel<DD, BB, (QQ == 2 ? 32 : 64), QQ, L, IO, WK>, grid, dim3(BB * 2 / QQ), stream, \
            q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, \
            kv_stride, o_stride)
 #define HSA_ATTN_BF16_IO(DD, BB)                                      \
   do {                                                                \
-    if (io == 2) { if (L) HSA_ATTN_BF16(DD, BB, 1, true, 2); else HSA_ATTN_BF16(DD, BB, 1, false, 2); }      \
-    else if (io == 1) { if (L) HSA_ATTN_BF16(DD, BB, 1, true, 1); else HSA_ATTN_BF16(DD, BB, 1, false, 1); } \
-    else { if (L) HSA_ATTN_BF16(DD, BB, 1, true, 0); else HSA_ATTN_BF16(DD, BB, 1, false, 0); }             \
+    if (io == 2) { if (L) HSA_ATTN_BF16(DD, BB, 1, true, 2, false); else HSA_ATTN_BF16(DD, BB, 1, false, 2, false); } \
+    else if (io == 1) {                                               \
+      if (L) HSA_ATTN_BF16(DD, BB, 1, true, 1, false);                \
+      else if (walk) HSA_ATTN_BF16(DD, BB, 1, false, 1, BB == 128);   \
+      else HSA_ATTN_BF16(DD, BB, 1, false, 1, false);                 \
+    } else {                                                          \
+      if (L) HSA_ATTN_BF16(DD, BB, 1, true, 0, false);                \
+      else if (walk) HSA_ATTN_BF16(DD, BB, 1, false, 0, BB == 128);   \
+      else HSA_ATTN_BF16(DD, BB, 1, false, 0, false);                 \
+    }                                                                 \
   } while (0)
     const int io = perm == nullptr ? 0 : (kv_stride > 0 ? 2 : 1);
     const bool L = lse != nullptr;
+    // Lists shared by all heads come from the frame masks, whose frame
+    // tiles end in short tiles: those launches walk the stages and leave
+    // out the empty ones (same outputs).
+    const bool walk = kv_shared != 0;
     if (D == 128 && B == 128) HSA_ATTN_BF16_IO(128, 128);
     else if (D == 64 && B == 128) HSA_ATTN_BF16_IO(64, 128);
     else if (D == 128 && B == 64) HSA_ATTN_BF16_IO(128, 64);

@@ -793,14 +793,16 @@ def test_lists_with_single_and_repeated_blocks(hsa):
     assert np.abs(to_np(r.o_lse) - ref).max() <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("D", [128, 64])
-def test_short_key_blocks_take_one_stage(hsa, D):
+@pytest.mark.parametrize("D,shared", [(128, False), (64, False), (128, True), (64, True)])
+def test_short_key_blocks_take_one_stage(hsa, D, shared):
     """Frame tiles whose real keys fit in one 64-key stage (150-token frames:
     a tile of 128 and one of 22) and tiles of 72 keys (two stages, the second
     of 8), in lists of 1 .. nb entries (the kernel's list window slides at 64
-    and 128 entries): equal to the oracle, with and without the log-sum-exp,
-    and bit for bit equal to the gathered-K/V form."""
-    _say(f"short key blocks, D={D}")
+    and 128 entries), per head or shared by all heads (shared lists without
+    the log-sum-exp take the stage walk that leaves out empty stages): equal
+    to the oracle, with and without the log-sum-exp (bit for bit), and bit
+    for bit equal to the gathered-K/V form, which runs every stage."""
+    _say(f"short key blocks, D={D}, shared={shared}")
     B, nh = 128, 2
     for (T, H, W) in ((66, 10, 15), (3, 10, 20)):
         g = torch.Generator().manual_seed(D + T)
@@ -810,11 +812,12 @@ def test_short_key_blocks_take_one_stage(hsa, D):
         nb = perm.numel() // B
         rng = np.random.default_rng(T * 7 + D)
         lens = [1, 2, 63, 64, 65, 127, 128, 129, nb]
+        G = 1 if shared else nh
         cnt = np.array([[lens[(h * nb + i) % len(lens)] if lens[(h * nb + i) % len(lens)] <= nb
-                         else int(rng.integers(1, nb + 1)) for i in range(nb)] for h in range(nh)],
+                         else int(rng.integers(1, nb + 1)) for i in range(nb)] for h in range(G)],
                        dtype=np.int32)
-        idx = np.full((nh, nb, nb), -1, dtype=np.int32)
-        for h in range(nh):
+        idx = np.full((G, nb, nb), -1, dtype=np.int32)
+        for h in range(G):
             for i in range(nb):
                 idx[h, i, :cnt[h, i]] = np.sort(rng.choice(nb, cnt[h, i], replace=False))
         qd, kd, vd = (x.to(dev()) for x in (q, k, v))
