@@ -293,13 +293,20 @@ def _measure(hsa, wl, w, io, K, W, n_sets, detailed):
     # real tokens, and list entries written
     G = L.kv_idx.shape[0]
     blk_len = L.blk_len.to(torch.int64)
+    # A launch whose lists are shared by all heads (bf16, 128-token blocks,
+    # no log-sum-exp, K/V not gathered) walks the 64-key stages and leaves
+    # out a block's empty second stage when it has at most 64 real keys:
+    # such a pair is half a computed tile.
+    walks = G == 1 and nh > 1 and esz == 2 and B == 128 and L.io != "tokens"
     tiles_steps, useful_steps, entries_steps = [], [], []
     for i in range(K):
         one_step(i)
         cnt = L.kv_cnt.to(torch.int64)
         valid = torch.arange(L.max_kv, device=dev)[None, None, :] < cnt[..., None]
-        keys = torch.where(valid, blk_len[L.kv_idx.clamp(0, nb - 1).to(torch.int64)], 0).sum(-1)
-        tiles_steps.append(int(cnt.sum().item()) * (nh // G))
+        ent_len = blk_len[L.kv_idx.clamp(0, nb - 1).to(torch.int64)]
+        keys = torch.where(valid, ent_len, 0).sum(-1)
+        halves = int((valid & (ent_len <= B // 2)).sum().item()) if walks else 0
+        tiles_steps.append((int(cnt.sum().item()) - 0.5 * halves) * (nh // G))
         useful_steps.append(int((keys * blk_len[None, :]).sum().item()) * (nh // G))
         entries_steps.append(int(cnt.sum().item()))
     torch.cuda.synchronize()
