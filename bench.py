@@ -293,11 +293,12 @@ def _measure(hsa, wl, w, io, K, W, n_sets, detailed):
     # real tokens, and list entries written
     G = L.kv_idx.shape[0]
     blk_len = L.blk_len.to(torch.int64)
-    # A launch whose lists are shared by all heads (bf16, 128-token blocks,
-    # no log-sum-exp, K/V not gathered) walks the 64-key stages and leaves
-    # out a block's empty second stage when it has at most 64 real keys:
-    # such a pair is half a computed tile.
-    walks = G == 1 and nh > 1 and esz == 2 and B == 128 and L.io != "tokens"
+    # A launch whose lists are shared by all heads, or whose plan has many
+    # short blocks (bf16, 128-token blocks, no log-sum-exp, K/V not
+    # gathered), walks the 64-key stages and leaves out a block's empty
+    # second stage when it has at most 64 real keys: such a pair is half a
+    # computed tile.
+    walks = ((G == 1 and nh > 1) or L.short_blocks) and esz == 2 and B == 128 and L.io != "tokens"
     tiles_steps, useful_steps, entries_steps = [], [], []
     for i in range(K):
         one_step(i)

@@ -236,13 +236,13 @@ def hsa_attn_order(kv_cnt, max_kv: int, out=None):
 
 
 def hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B: int, scale: float | None = None,
-             want_lse: bool = True, out=None, lse=None, order=None):
+             want_lse: bool = True, out=None, lse=None, order=None, short_blocks: bool = False):
     """-> (op [nh, n_pad, D] in the input dtype, lse float32 [nh, n_pad] or None).
     `order` (from hsa_attn_order) sets the processing order; results do not depend on it."""
     _need_device(qp, kp, vp, blk_len, kv_idx, kv_cnt, order)
     nh, n_pad, D = qp.shape
     nb = n_pad // B
-    shared = 1 if kv_idx.shape[0] == 1 and nh > 1 else 0
+    shared = (1 if kv_idx.shape[0] == 1 and nh > 1 else 0) | (2 if short_blocks else 0)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     if out is None:
         out = torch.empty_like(qp)
@@ -255,7 +255,7 @@ def hsa_attn(qp, kp, vp, blk_len, kv_idx, kv_cnt, B: int, scale: float | None = 
 
 
 def hsa_attn_tokens(q, k, v, perm, blk_len, kv_idx, kv_cnt, B: int, scale: float | None = None,
-                    want_lse: bool = True, out=None, lse=None, order=None):
+                    want_lse: bool = True, out=None, lse=None, order=None, short_blocks: bool = False):
     """q [1, N, nh, D] token-major (token stride may exceed nh*D, e.g. a slice of a fused QKV
     buffer); k, v either token-major like q (same token stride) or reordered [nh, n_pad, D]
     (hsa_perm outputs) -> (o [1, N, nh, D], lse float32 [nh, n_pad] or None). Equals
@@ -274,7 +274,7 @@ def hsa_attn_tokens(q, k, v, perm, blk_len, kv_idx, kv_cnt, B: int, scale: float
     else:
         _need_device(k, v)
         kv_stride = 0
-    shared = 1 if kv_idx.shape[0] == 1 and nh > 1 else 0
+    shared = (1 if kv_idx.shape[0] == 1 and nh > 1 else 0) | (2 if short_blocks else 0)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     if out is None:
         out = torch.empty((1, N, nh, D), dtype=q.dtype, device=q.device)

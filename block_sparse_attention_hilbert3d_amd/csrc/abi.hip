@@ -419,7 +419,7 @@ hsa_status_t hsa_attn(const void *qp, const void *kp, const void *vp, void *op, 
   if ((st = check_dtype(dtype)) != HSA_OK || (st = check_D(D)) != HSA_OK || (st = check_B(B)) != HSA_OK) return st;
   if (nh < 1 || nb < 1 || max_kv < 1) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn: nh=%d nb=%d max_kv=%d", nh, nb, max_kv);
   if (static_cast<int64_t>(nh) * nb >= (1ll << 31)) return fail(HSA_ERR_BAD_SHAPE, "hsa_attn: too many blocks");
-  if (kv_shared != 0 && kv_shared != 1) return fail(HSA_ERR_BAD_ARG, "hsa_attn: kv_shared must be 0 or 1");
+  if (kv_shared < 0 || kv_shared > 3) return fail(HSA_ERR_BAD_ARG, "hsa_attn: kv_shared must be 0..3");
   if (!(scale > 0.f) || !isfinite(scale)) return fail(HSA_ERR_BAD_ARG, "hsa_attn: scale must be finite and positive");
   if (!aligned16(qp) || !aligned16(kp) || !aligned16(vp) || !aligned16(op)) return fail(HSA_ERR_BAD_ARG, "hsa_attn: tensors must be 16-byte aligned");
   if (order && !aligned4(order)) return fail(HSA_ERR_BAD_ARG, "hsa_attn: order must be 4-byte aligned");
@@ -454,7 +454,7 @@ hsa_status_t hsa_attn_tokens(const void *q, const void *k, const void *v, void *
   // ... formed as token index x row bytes with 24-bit multiplies
   if (kv_stride > 0 && (N > (1 << 24) || kv_stride * es >= (1ll << 24)))
     return fail(HSA_ERR_UNSUPPORTED, "hsa_attn_tokens: gathered K/V need N <= 2^24 tokens and rows under 16 MiB; reorder them with hsa_perm");
-  if (kv_shared != 0 && kv_shared != 1) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: kv_shared must be 0 or 1");
+  if (kv_shared < 0 || kv_shared > 3) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: kv_shared must be 0..3");
   if (!(scale > 0.f) || !isfinite(scale)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: scale must be finite and positive");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: tensors must be 16-byte aligned");
   if (!aligned4(perm) || (order && !aligned4(order))) return fail(HSA_ERR_BAD_ARG, "hsa_attn_tokens: perm and order must be 4-byte aligned");

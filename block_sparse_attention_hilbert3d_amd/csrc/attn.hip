@@ -162,8 +162,8 @@ attn_bf16_pipe_kernel(const uint16_t *__restrict__ qp, const uint16_t *__restric
   // (wE1, wH1 at list position wB1; wX1); each iteration steps once, to
   // stage c+2, reading at most one new entry. The walk costs each stage a
   // few scalar instructions, so it is compiled only where such tiles are
-  // expected (the launch picks it for lists shared by all heads: the frame
-  // masks).
+  // expected (the launch picks it for lists shared by all heads, the frame
+  // masks, and when the caller says the blocks are often short).
   constexpr bool kWalk = WK && NS == 2 && !GKV;
   int wE0 = 0, wH0 = 0, wE1 = 0, wH1 = 0, wB1 = 0;
   bool wX0 = false, wX1 = false;
@@ -834,6 +834,7 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
   if (nb > (1 << 24)) return fail(HSA_ERR_UNSUPPORTED, "hsa_attn: nb %d > 2^24 blocks", nb);
   const float scale_log2 = scale * 1.4426950408889634f;
   const dim3 grid(nh * nb);
+  const int shared = kv_shared & 1;  // bit 1 only picks the stage walk
   if (dtype == HSA_BF16) {
     const uint16_t *q = static_cast<const uint16_t *>(qp), *k = static_cast<const uint16_t *>(kp),
                    *v = static_cast<const uint16_t *>(vp);
@@ -841,7 +842,7 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
     const dim3 block(B * 2);
 #define HSA_ATTN_BF16(DD, BB, QQ, L, IO, WK)                                                    \
   launch_k(hsa::attn_bf16_pipe_kernel<DD, BB, (QQ == 2 ? 32 : 64), QQ, L, IO, WK>, grid, dim3(BB * 2 / QQ), stream, \
-           q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, \
+           q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, shared, nh, nb, scale_log2, perm, q_stride, \
            kv_stride, o_stride)
 #define HSA_ATTN_BF16_IO(DD, BB)                                      \
   do {                                                                \
@@ -859,8 +860,9 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
     const int io = perm == nullptr ? 0 : (kv_stride > 0 ? 2 : 1);
     const bool L = lse != nullptr;
     // Lists shared by all heads come from the frame masks, whose frame
-    // tiles end in short tiles: those launches walk the stages and leave
-    // out the empty ones (same outputs).
+    // tiles end in short tiles: those launches, and those whose caller says
+    // the blocks are often short (bit 1), walk the stages and leave out the
+    // empty ones (same outputs).
     const bool walk = kv_shared != 0;
     if (D == 128 && B == 128) HSA_ATTN_BF16_IO(128, 128);
     else if (D == 64 && B == 128) HSA_ATTN_BF16_IO(64, 128);
@@ -873,10 +875,10 @@ hsa_status_t launch_attn(const void *qp, const void *kp, const void *vp, void *o
                 *v = static_cast<const float *>(vp);
     float *o = static_cast<float *>(op);
     const dim3 block(B * 4);  // B / 16 waves of 16 queries
-    if (D == 128 && B == 128) launch_k(hsa::attn_f32_kernel<128, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
-    else if (D == 64 && B == 128) launch_k(hsa::attn_f32_kernel<64, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
-    else if (D == 128 && B == 64) launch_k(hsa::attn_f32_kernel<128, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
-    else launch_k(hsa::attn_f32_kernel<64, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, kv_shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
+    if (D == 128 && B == 128) launch_k(hsa::attn_f32_kernel<128, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
+    else if (D == 64 && B == 128) launch_k(hsa::attn_f32_kernel<64, 128>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
+    else if (D == 128 && B == 64) launch_k(hsa::attn_f32_kernel<128, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
+    else launch_k(hsa::attn_f32_kernel<64, 64>, grid, block, stream, q, k, v, o, lse, blk_len, kv_idx, kv_cnt, order, max_kv, shared, nh, nb, scale_log2, perm, q_stride, kv_stride, o_stride);
   }
   return check_launch("hsa_attn");
 }

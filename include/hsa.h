@@ -272,7 +272,13 @@ hsa_status_t hsa_select_noalloc(const float *S, int32_t nh, int32_t nb, const hs
  *   aggregated block-wise). Non-causal. Unlisted blocks are never read.
  * qp, kp, vp, op: reordered [nh][nb*B][D]; op rows of pad slots are zero.
  * lse: optional float [nh][nb*B] natural-log log-sum-exp (NULL to skip).
- * kv_shared: 1 if the lists are [nb][max_kv] shared by all heads.
+ * kv_shared: bit 0 set if the lists are [nb][max_kv] shared by all heads;
+ *   bit 1 set to say that the listed blocks often hold at most 64 real keys
+ *   (frame tiles, clipped 2D/3D partition tiles): bf16 launches without lse
+ *   and with 128-slot blocks then walk each list by 64-key stages and leave
+ *   out such a block's empty second stage (same output bits; lists shared
+ *   by all heads are walked that way whether or not the bit is set).
+ *   Other bits must be zero.
  * order: optional int32 [G*nb] processing order from hsa_attn_order (G = nh,
  *   or 1 when shared): the b-th workgroup launched handles list row order[b]
  *   (when shared, the b-th group of nh workgroups handles block order[b] for

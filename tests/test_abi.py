@@ -194,7 +194,7 @@ def test_attn_and_unperm_validation(B):
     a = [FAKE] * 8
     assert L.hsa_attn(NULL, *a[1:4], NULL, *a[5:8], NULL, 4, 0, 2, 4, 64, 64, 1, 0.125, NULL) == 1
     assert L.hsa_attn(*a[:4], NULL, *a[5:8], NULL, 4, 0, 2, 4, 96, 64, 1, 0.125, NULL) == 4      # B
-    assert L.hsa_attn(*a[:4], NULL, *a[5:8], NULL, 4, 2, 2, 4, 64, 64, 1, 0.125, NULL) == 6      # kv_shared
+    assert L.hsa_attn(*a[:4], NULL, *a[5:8], NULL, 4, 4, 2, 4, 64, 64, 1, 0.125, NULL) == 6      # kv_shared
     assert L.hsa_attn(*a[:4], NULL, *a[5:8], NULL, 4, 0, 2, 4, 64, 64, 1, float("nan"), NULL) == 6
     assert L.hsa_attn(*a[:4], NULL, *a[5:8], ctypes.c_void_p(0x10002), 4, 0, 2, 4, 64, 64, 1, 0.125,
                       NULL) == 6                                                                 # order alignment

@@ -793,16 +793,18 @@ def test_lists_with_single_and_repeated_blocks(hsa):
     assert np.abs(to_np(r.o_lse) - ref).max() <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("D,shared", [(128, False), (64, False), (128, True), (64, True)])
-def test_short_key_blocks_take_one_stage(hsa, D, shared):
+@pytest.mark.parametrize("D,shared,hint", [(128, False, False), (64, False, False), (128, True, False),
+                                           (64, True, False), (128, False, True), (64, False, True)])
+def test_short_key_blocks_take_one_stage(hsa, D, shared, hint):
     """Frame tiles whose real keys fit in one 64-key stage (150-token frames:
     a tile of 128 and one of 22) and tiles of 72 keys (two stages, the second
     of 8), in lists of 1 .. nb entries (the kernel's list window slides at 64
-    and 128 entries), per head or shared by all heads (shared lists without
-    the log-sum-exp take the stage walk that leaves out empty stages): equal
+    and 128 entries), per head or shared by all heads (shared lists, or lists
+    passed with the short-block hint, take the stage walk that leaves out
+    empty stages when no log-sum-exp is asked for): equal
     to the oracle, with and without the log-sum-exp (bit for bit), and bit
     for bit equal to the gathered-K/V form, which runs every stage."""
-    _say(f"short key blocks, D={D}, shared={shared}")
+    _say(f"short key blocks, D={D}, shared={shared}, hint={hint}")
     B, nh = 128, 2
     for (T, H, W) in ((66, 10, 15), (3, 10, 20)):
         g = torch.Generator().manual_seed(D + T)
@@ -823,7 +825,7 @@ def test_short_key_blocks_take_one_stage(hsa, D, shared):
         qd, kd, vd = (x.to(dev()) for x in (q, k, v))
         kv_idx, kv_cnt = torch.from_numpy(idx).to(dev()), torch.from_numpy(cnt).to(dev())
         _, kp, vp = hsa.hsa_perm([qd, kd, vd], perm, perm.numel())
-        r = _attn(hsa.hsa_attn_tokens, qd, kp, vp, perm, blk_len, kv_idx, kv_cnt, B)
+        r = _attn(hsa.hsa_attn_tokens, qd, kp, vp, perm, blk_len, kv_idx, kv_cnt, B, short_blocks=hint)
         rg = _attn(hsa.hsa_attn_tokens, qd, kd, vd, perm, blk_len, kv_idx, kv_cnt, B)
         torch.cuda.synchronize()
         assert torch.equal(r[0], rg[0]) and torch.equal(r[1], rg[1])
